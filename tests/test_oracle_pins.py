@@ -1,0 +1,319 @@
+"""Pins of the float64 oracle against what the method pages and the mathematics fix (CPU only).
+
+Each test names the fact it checks.  None of them re-types an oracle formula: the references are printed
+values of the GPTQ tutorial page's worked examples (tests/golden/), textbook procedures with explicit
+inverses or least squares, brute force, closed-form identities, and library routines.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+
+
+def _load(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+def _sse(X, cand, w):
+    return float(np.sum((np.asarray(X) @ (np.asarray(cand) - np.asarray(w))) ** 2))
+
+
+# ------------------------------------------------------------------ worked examples of the GPTQ tutorial page
+def test_two_weight_example(golden_dir):
+    g = _load(golden_dir, "two_weight_example.json")
+    X = np.array(g["X"])
+    H = O.gram([X])
+    np.testing.assert_allclose(H, g["H"], atol=1e-12)
+    prep = O.prepare(H, 0.0)
+    np.testing.assert_allclose(prep["P"], g["P"], atol=1e-12)
+    U = prep["U"]
+    assert abs(U[1, 1] ** 2 - g["U11_squared"]) < 1e-12
+    assert abs(U[1, 1] ** 2 - prep["P"][1, 1]) > 0.1          # the factor is not the inverse's entry
+    w = np.array(g["w"])[:, None]
+    r = O.quantize_layer(w, U, bits=g["bits"], scales=np.array([g["scale"]], np.float32), record_trace=True)
+    q = (r["codes"][:, 0] - g["zero_point"]).astype(float)
+    np.testing.assert_allclose(q, g["quantized"], atol=0)
+    np.testing.assert_allclose(r["trace"][0][:, 0], g["weights_after_first_step"], atol=1e-12)
+    assert abs(_sse(X, r["trace"][0][:, 0], g["w"]) - g["output_error_after_first_step"]) < 1e-12
+    assert abs(_sse(X, q, g["w"]) - g["final_output_error"]) < 1e-12
+    assert abs(O.layer_objective(H, w, q[:, None]) - g["final_output_error"]) < 1e-12
+    rtn = O.fixed_grid_quantize(np.array(g["w"]))
+    assert abs(_sse(X, rtn, g["w"]) - g["rtn_output_error"]) < 1e-12
+    assert abs(np.mean((rtn - g["w"]) ** 2) - g["weight_mse_rtn"]) < 1e-12
+    assert abs(np.mean((q - g["w"]) ** 2) - g["weight_mse_final"]) < 1e-12
+    # first step written with the inverse directly: delta = -r P[:,0] / P[0,0]
+    P = np.array(g["P"])
+    delta = -(g["w"][0] - 0.0) * P[:, 0] / P[0, 0]
+    np.testing.assert_allclose(delta, g["first_step_update"], atol=1e-12)
+    seq = O.obq_sequential(H, g["w"], O.fixed_grid_quantize)
+    np.testing.assert_allclose(seq["trace"][0], g["weights_after_first_step"], atol=1e-12)
+
+
+def test_three_weight_counterexample(golden_dir):
+    g = _load(golden_dir, "three_weight_counterexample.json")
+    X = np.array(g["X"])
+    H = O.gram([X])
+    np.testing.assert_allclose(H, g["H"], atol=1e-12)
+    prep = O.prepare(H, 0.0)
+    np.testing.assert_allclose(prep["P"], g["P"], atol=1e-12)
+    np.testing.assert_allclose(prep["U"], g["U"], atol=1e-12)
+    np.testing.assert_allclose(np.array(g["H"]) @ np.array(g["P"]), np.eye(3), atol=1e-12)
+    w = np.array(g["w"])[:, None]
+    r = O.quantize_layer(w, prep["U"], bits=4, scales=np.array([1.0], np.float32), record_trace=True)
+    q = (r["codes"][:, 0] - 8).astype(float)
+    np.testing.assert_allclose(q, g["quantized"], atol=0)
+    assert abs(r["trace"][1][2, 0] - g["trace_step2_coord3"]) < 1e-12
+    assert abs(_sse(X, q, g["w"]) - g["sequential_output_error"]) < 1e-12
+    rtn = O.fixed_grid_quantize(np.array(g["w"]))
+    assert abs(_sse(X, rtn, g["w"]) - g["rtn_output_error"]) < 1e-12
+    grid = range(-8, 8)
+    assert len(grid) ** 3 == g["grid_points"]
+    best, arg = O.exhaustive_best(lambda c: _sse(X, c, g["w"]), 3, grid)
+    assert abs(best - g["best_output_error"]) < 1e-12
+    assert [list(map(float, a)) for a in arg] == [g["best"]]
+    assert _sse(X, q, g["w"]) > best                          # sequential is not the discrete optimum
+
+
+# ------------------------------------------------------------------ textbook and brute-force references
+@pytest.mark.parametrize("K,seed", [(2, 0), (3, 1), (5, 2), (8, 3), (8, 4)])
+def test_loop_equals_explicit_inverse_obq(K, seed):
+    """U-row algorithm == sequential compensation that re-inverts H[F,F] at every step (K <= 8)."""
+    rng = np.random.default_rng(seed)
+    Hd = workloads.random_spd(K, seed)
+    w = rng.normal(0, 2.0, size=K)
+    prep = O.prepare(Hd, 0.0)
+    r = O.quantize_layer(w[:, None], prep["U"], bits=4, scales=np.array([1.0], np.float32))
+    seq = O.obq_sequential(Hd, w, O.fixed_grid_quantize)
+    np.testing.assert_allclose(r["Q"][:, 0], seq["w"], atol=1e-12)
+    # per-step added objective r^2 / (2 P_F[q,q]) == 1/2 E_q^2
+    np.testing.assert_allclose(0.5 * r["E"][:, 0] ** 2, seq["added"], rtol=1e-9, atol=1e-14)
+
+
+def test_exhaustive_lower_bound():
+    """The sequential result can never beat the exhaustive optimum of the same grid (K = 3, 4)."""
+    for K, seed in [(3, 5), (4, 6)]:
+        Hd = workloads.random_spd(K, seed)
+        w = np.random.default_rng(seed).normal(0, 1.5, size=K)
+        prep = O.prepare(Hd, 0.0)
+        r = O.quantize_layer(w[:, None], prep["U"], bits=3, scales=np.array([1.0], np.float32))
+        obj = lambda c: 0.5 * (c - w) @ Hd @ (c - w)
+        best, _ = O.exhaustive_best(obj, K, range(-4, 4))
+        assert obj(r["Q"][:, 0]) >= best - 1e-12
+
+
+def test_factor_schur_property():
+    """[T4]: U[q:,q:]^T U[q:,q:] is the inverse of the remaining Hessian for every q."""
+    K = 12
+    Hd = workloads.random_spd(K, 7)
+    U = O.prepare(Hd, 0.0)["U"]
+    assert np.allclose(np.tril(U, -1), 0)
+    for q in range(K):
+        np.testing.assert_allclose(U[q:, q:].T @ U[q:, q:], np.linalg.inv(Hd[q:, q:]), rtol=1e-9, atol=1e-12)
+        assert abs(U[q, q] ** 2 - np.linalg.inv(Hd[q:, q:])[0, 0]) < 1e-10
+    # scipy's Cholesky of the inverse, read as upper factor, agrees
+    import scipy.linalg
+    np.testing.assert_allclose(U, scipy.linalg.cholesky(np.linalg.inv(Hd), lower=False), rtol=1e-8, atol=1e-12)
+
+
+@pytest.mark.parametrize("B", [7, 64, 128])
+def test_lazy_blocks_equal_eager(B):
+    """[T5]: lazy block updates are the same computation as updating every free weight at once."""
+    K, N = 300, 17
+    rng = np.random.default_rng(11)
+    H = O.gram([rng.normal(size=(600, K)) * np.exp(rng.normal(0, 1, K))])
+    prep = O.prepare(H, 0.01)
+    W = rng.normal(0, 0.02, size=(K, N))
+    a = O.quantize_layer(W, prep["U"], bits=3)
+    b = O.quantize_layer(W, prep["U"], bits=3, blocksize=B)
+    assert np.array_equal(a["codes"], b["codes"])
+    np.testing.assert_allclose(a["E"], b["E"], rtol=0, atol=1e-9 * np.abs(a["E"]).max())
+
+
+def test_loss_identity():
+    """Sum of 1/2 E^2 over a channel equals 1/2 d0^T H_d d0 with d0 = W_hat - W (dead rows zeroed)."""
+    K, N = 96, 9
+    rng = np.random.default_rng(12)
+    H = O.gram([rng.normal(size=(256, K))])
+    prep = O.prepare(H, 0.01)
+    W = rng.normal(0, 0.02, size=(K, N))
+    r = O.quantize_layer(W, prep["U"], bits=4, blocksize=32)
+    d0 = r["Q"] - r["W0"]
+    np.testing.assert_allclose(r["losses"], 0.5 * np.sum((prep["Hd"] @ d0) * d0, axis=0), rtol=1e-9)
+
+
+def test_codes_invariant_under_hessian_scaling():
+    """[T1], [T6]: normalising H by a constant rescales damping too, so codes do not change."""
+    K, N = 64, 16
+    rng = np.random.default_rng(13)
+    H = O.gram([rng.normal(size=(128, K)) * np.exp(rng.normal(0, 1, K))])
+    W = rng.normal(0, 0.02, size=(K, N))
+    a = O.quantize_layer(W, O.prepare(H, 0.01)["U"], bits=4)
+    b = O.quantize_layer(W, O.prepare(H * 0.25, 0.01)["U"], bits=4)      # power of two: exact
+    c = O.quantize_layer(W, O.prepare(H * 3.7, 0.01)["U"], bits=4)
+    assert np.array_equal(a["codes"], b["codes"])
+    assert np.array_equal(a["codes"], c["codes"])
+
+
+def test_dead_coordinates():
+    """[T6]: a zero-energy input coordinate gets diagonal 1, decouples, and its weight row goes to zero."""
+    K, N = 20, 6
+    rng = np.random.default_rng(14)
+    X = rng.normal(size=(64, K))
+    X[:, [3, 11]] = 0.0
+    H = O.gram([X])
+    prep = O.prepare(H, 0.01)
+    assert list(np.flatnonzero(prep["dead"])) == [3, 11]
+    np.testing.assert_allclose(prep["damp"], 0.01 * (np.trace(H) + 2) / K)
+    U = prep["U"]
+    for k in (3, 11):
+        off = np.concatenate([U[k, :k], U[k, k + 1:], U[:k, k], U[k + 1:, k]])
+        assert np.abs(off).max() < 1e-12
+        assert abs(U[k, k] - 1.0 / np.sqrt(1.0 + prep["damp"])) < 1e-12
+    W = rng.normal(0, 0.02, size=(K, N))
+    r = O.quantize_layer(W, U, bits=4, dead=prep["dead"])
+    assert np.all(r["codes"][[3, 11]] == 8)
+    np.testing.assert_allclose(r["scales"], O.channel_scales(W, 4))   # scales from W before zeroing
+
+
+def test_not_positive_definite():
+    with pytest.raises(O.NotPositiveDefinite):
+        O.prepare(np.array([[1.0, 2.0], [2.0, 1.0]]), 0.01)
+
+
+def test_channel_scale_rule_properties():
+    W = np.random.default_rng(15).normal(0, 0.02, size=(50, 7)).astype(np.float32)
+    W[:, 3] = 0.0
+    for b in (2, 3, 4, 8):
+        s = O.channel_scales(W, b)
+        assert s.dtype == np.float32
+        assert s[3] == 1.0
+        np.testing.assert_array_equal(s, O.channel_scales(-W, b))        # symmetric
+        amax = np.abs(W).max(0)
+        live = amax > 0
+        np.testing.assert_allclose(s[live] * (2 ** b - 1) / 2, amax[live], rtol=2e-7)
+    # 4-bit: codes 0..15 with zero point 8, as in the tutorial's fixed grid
+    r = O.quantize_layer(np.array([[-1.0], [0.51], [7.4]]), np.eye(3), bits=4,
+                         scales=np.array([1.0], np.float32))
+    assert list(r["codes"][:, 0]) == [7, 9, 15]
+
+
+def test_tie_codes_adopted_only_in_band():
+    U = np.eye(2)
+    W = np.array([[0.5, 0.5], [1.25, 0.3]])
+    base = O.quantize_layer(W, U, bits=4, scales=np.array([1.0, 1.0], np.float32))
+    assert base["codes"][0, 0] == 8                                   # 0.5 -> 0 (half to even)
+    forced = np.array([[9, 9], [0, 0]])
+    r = O.quantize_layer(W, U, bits=4, scales=np.array([1.0, 1.0], np.float32), tie_codes=forced)
+    assert r["codes"][0, 0] == 9 and r["codes"][0, 1] == 9 and r["n_adopted"] == 2
+    assert r["codes"][1, 0] == base["codes"][1, 0]                     # not in band: ignored
+
+
+# ------------------------------------------------------------------ Gram and asymmetric-calibration pieces
+def test_gram_identities(golden_dir):
+    rng = np.random.default_rng(16)
+    X = rng.normal(size=(200, 9))
+    H = O.gram([X[:70], X[70:150], X[150:]])
+    for _ in range(5):
+        v = rng.normal(size=9)
+        assert abs(np.sum((X @ v) ** 2) - 0.5 * v @ H @ v) < 1e-9 * np.sum((X @ v) ** 2)
+    np.testing.assert_allclose(H, H.T, atol=0)
+    brute = np.zeros((9, 9))
+    for t in range(200):
+        for i in range(9):
+            for j in range(9):
+                brute[i, j] += 2.0 * X[t, i] * X[t, j]
+    np.testing.assert_allclose(H, brute, rtol=1e-12)
+
+
+def test_bf16_round_matches_torch():
+    rng = np.random.default_rng(17)
+    x = np.concatenate([rng.normal(size=4000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 4000),
+                        np.array([0.0, -0.0, 1.00390625, 1.01171875, 3.0e38, -3.0e38, 1e-40, np.inf],
+                                 np.float32)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(O.bf16_round(x), ref)
+
+
+def test_row_scaled_gram():
+    rng = np.random.default_rng(18)
+    X = O.bf16_round(rng.normal(size=(100, 12)).astype(np.float32))
+    H = O.gram([X])
+    np.testing.assert_array_equal(O.gram_row_scaled(X, np.ones(100)), H)
+    np.testing.assert_array_equal(O.gram_row_scaled(X, np.full(100, 0.5)), H * 0.25)
+    rho = rng.uniform(0.5, 1.5, size=100)
+    Hg = O.gram_row_scaled(X, rho)
+    ref = torch.from_numpy((rho.astype(np.float32)[:, None] * X)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_allclose(Hg, 2.0 * ref.T @ ref, rtol=1e-12)
+
+
+def test_cross_gram_and_asym_objective():
+    rng = np.random.default_rng(19)
+    M, K, N = 80, 7, 3
+    Xf = rng.normal(size=(M, K))
+    X = Xf + 0.05 * np.abs(Xf) * rng.normal(size=(M, K))
+    H, A, G = O.gram([X]), O.cross_gram(Xf, X), O.gram([Xf])
+    np.testing.assert_allclose(H + A, 2.0 * Xf.T @ X, rtol=1e-12, atol=1e-12)  # X~^T X = X^T X + dX^T X
+    W = rng.normal(size=(K, N))
+    Wh = np.round(W * 4) / 4
+    direct = float(np.sum((X @ Wh - Xf @ W) ** 2))
+    assert abs(O.asym_objective(H, A, G, W, Wh) - direct) < 1e-9 * direct
+    np.testing.assert_allclose(O.cross_gram(X, X), 0.0)
+
+
+def test_asym_correction_forms_agree():
+    """[R] item 3's triangular form equals the per-step ridge least-squares definition and lstsq."""
+    rng = np.random.default_rng(20)
+    M, K = 200, 24
+    Xf = rng.normal(size=(M, K)) * np.exp(rng.normal(0, 0.7, K))
+    X = Xf + 0.05 * np.abs(Xf) * rng.normal(size=(M, K))
+    prep = O.prepare(O.gram([X]), 0.01)
+    A = O.cross_gram(Xf, X)
+    P_tri = O.asym_correction(prep["U"], A)
+    P_def = O.asym_correction_by_definition(prep["Hd"], A)
+    np.testing.assert_allclose(P_tri, P_def, rtol=1e-8, atol=1e-10 * np.abs(P_def).max())
+    assert np.allclose(np.tril(P_tri), 0)
+    lam = np.sqrt(prep["damp"] / 2.0)
+    dX = Xf - X
+    for q in (0, 5, K - 2):
+        rest = list(range(q + 1, K))
+        lhs = np.vstack([X[:, rest], lam * np.eye(len(rest))])
+        rhs = np.concatenate([dX[:, q], np.zeros(len(rest))])
+        np.testing.assert_allclose(P_tri[q, rest], np.linalg.lstsq(lhs, rhs, rcond=None)[0], rtol=1e-7,
+                                   atol=1e-10)
+    np.testing.assert_allclose(O.asym_correction(prep["U"], np.zeros((K, K))), 0.0)
+
+
+def test_asym_loop_equals_explicit_solves():
+    """GPTAQ loop with P1 == sequential compensation with explicit inverses plus a per-step lstsq."""
+    rng = np.random.default_rng(21)
+    M, K = 60, 6
+    Xf = rng.normal(size=(M, K))
+    X = Xf + 0.1 * np.abs(Xf) * rng.normal(size=(M, K))
+    prep = O.prepare(O.gram([X]), 0.01)
+    A = O.cross_gram(Xf, X)
+    P1 = O.asym_correction(prep["U"], A)
+    w = rng.normal(0, 1.5, size=K)
+    r = O.quantize_layer(w[:, None], prep["U"], bits=4, scales=np.array([1.0], np.float32), P1=P1)
+    seq = O.obq_sequential(prep["Hd"], w, O.fixed_grid_quantize, damp=prep["damp"], X_free_basis=(X, Xf - X))
+    np.testing.assert_allclose(r["Q"][:, 0], seq["w"], atol=1e-10)
+    rb = O.quantize_layer(w[:, None], prep["U"], bits=4, scales=np.array([1.0], np.float32), P1=P1,
+                          blocksize=4)
+    np.testing.assert_array_equal(rb["codes"], r["codes"])
+    # no input mismatch -> no correction -> plain GPTQ
+    r0 = O.quantize_layer(w[:, None], prep["U"], bits=4, scales=np.array([1.0], np.float32),
+                          P1=O.asym_correction(prep["U"], O.cross_gram(X, X)))
+    rg = O.quantize_layer(w[:, None], prep["U"], bits=4, scales=np.array([1.0], np.float32))
+    np.testing.assert_array_equal(r0["codes"], rg["codes"])
+
+
+def test_generator_asym_mismatch_is_bf16_exact():
+    cfg = workloads.CONFIGS["c4_up_proj_8b_gptaq"].scaled(K=64, N=8, M=512)
+    L = workloads.make_layer(cfg)
+    d = L["X_float"].float() - L["X"].float()
+    assert torch.equal(d.to(torch.bfloat16).float(), d)
