@@ -1,0 +1,189 @@
+/*
+ * gptq.h - C ABI of the MI355X (gfx950) GPTQ-family layer-quantisation library (libgptq_hip.so).
+ *
+ * The library implements the hot path of one linear layer's post-training quantisation:
+ *   1. gptq_accumulate_hessian  H += 2 X^T X over calibration batches           (a1; [T] section 1)
+ *                               [A += 2 (X~ - X)^T X for asymmetric calibration]  ([R] item 3, [A])
+ *   2. gptq_prepare             dead coordinates, damping, U with H_d^{-1} = U^T U (a2, a3; [T] sections 4, 6)
+ *   3. gptq_asym_correction     P1 = [(A U^T) masked strictly upper] U             (a4; [R] item 3)
+ *   4. gptq_quantize_layer      shared-order column loop with lazy block updates   (a5-a8; [T] sections 3-5)
+ *
+ * Sources, cited by page title and section:
+ *   [T] GPTQ tutorial page "GPTQ：量化一个权重之后怎样补偿输出误差" (charlestar.github.io, 2026-10-15); its
+ *       sections in order: 1 calibration objective and Hessian, 2 two-weight example, 3 one constrained
+ *       compensation, 4 Cholesky factor vs inverse, 5 shared order, layout and lazy blocks, 6 damping, dead
+ *       coordinates and grouping parameters, 7-8 worked checks, 9 grid values vs stored codes.
+ *   [R] "Rethinking Residual Errors in Compensation-based LLM Quantization" notes (ICLR 2026), "关键设计" 1-3.
+ *   [A] "GPTAQ: Efficient Finetuning-Free Quantization for Asymmetric Calibration" notes (ICML 2025).
+ *   [G] "G²PTQ: Improving LLM Post-Training Quantization with Generalized Gradient Compensation" digest
+ *       (output-channel groups that each own a Hessian; symmetric per-channel weight grids).
+ *
+ * Conventions shared by every call
+ *   - Layout follows [T]: X is M x K (tokens x input features), W is K x N (input features x output
+ *     channels).  Matrices are row-major with an explicit leading dimension unless strides are given.
+ *   - Every pointer named as "device" must point to device memory (hipMalloc / a torch CUDA tensor) of the
+ *     current HIP device.  The caller owns every buffer; the library never allocates or frees memory and
+ *     keeps no state between calls.  Scratch memory is passed in as `workspace` (device, 256-byte aligned,
+ *     size from gptq_workspace_bytes); its contents need not be initialised and are clobbered.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued on it in order.  Calls return
+ *     after enqueueing, except gptq_prepare and gptq_quantize_layer, which synchronise `stream` at their end
+ *     to report device-detected errors (non-positive pivot, non-finite input).
+ *   - Arguments are validated on the host before any HIP call; an invalid call returns GPTQ_ERR_ARG and
+ *     enqueues nothing.  No input is ever silently repaired, except by the two documented rules of [T]
+ *     section 6: dead coordinates and damping.
+ *   - Results are deterministic: no floating-point atomics are used, so two identical calls give
+ *     bit-identical outputs.
+ */
+#ifndef GPTQ_H
+#define GPTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GPTQ_OK = 0,
+    GPTQ_ERR_ARG = 1,        /* invalid argument: shape, leading dimension, bits, blocksize, NULL pointer */
+    GPTQ_ERR_NONFINITE = 2,  /* NaN or Inf found in an input (H diagonal, pivot, weights) */
+    GPTQ_ERR_NOT_PD = 3,     /* damped Hessian is not positive definite (a pivot <= 0) */
+    GPTQ_ERR_WORKSPACE = 4,  /* workspace NULL, misaligned or smaller than gptq_workspace_bytes */
+    GPTQ_ERR_HIP = 5         /* a HIP runtime call failed (launch, synchronisation, copy) */
+} gptq_status_t;
+
+typedef enum {
+    GPTQ_DTYPE_F32 = 0,      /* IEEE binary32 */
+    GPTQ_DTYPE_BF16 = 1      /* bfloat16 (top half of binary32) */
+} gptq_dtype_t;
+
+typedef enum {
+    GPTQ_CALL_ACCUMULATE_HESSIAN = 0,
+    GPTQ_CALL_PREPARE = 1,
+    GPTQ_CALL_ASYM_CORRECTION = 2,
+    GPTQ_CALL_QUANTIZE_LAYER = 3
+} gptq_call_t;
+
+/* Flags of gptq_quantize_layer. */
+#define GPTQ_FLAG_SCALES_GIVEN 1u  /* `scales` is an input (e.g. the fixed teaching grid of [T] section 2) */
+
+/*
+ * gptq_workspace_bytes - bytes of `workspace` a call needs for the given sizes.
+ *   call: which entry point; K, N, M: sizes as in that call (unused ones are ignored); flags: that
+ *   call's flags (for gptq_accumulate_hessian pass 1 when X_float is given, else 0).
+ * Returns 0 for an unknown call.  Never fails otherwise.
+ */
+size_t gptq_workspace_bytes(gptq_call_t call, int64_t K, int64_t N, int64_t M, unsigned flags);
+
+/*
+ * gptq_accumulate_hessian - H += 2 Xs^T Xs for one calibration batch ([T] section 1: the K x K statistic
+ * shared by all output channels is accumulated batch by batch; the unnormalised 2 X^T X is used).
+ *
+ *   H          device, K x K fp32 row-major (ld = K), read-modify-written; both triangles are updated and
+ *              stay symmetric.  Zero it before the first batch.
+ *   K          input features, >= 1.
+ *   X          device, M x K, dtype x_dtype, row-major with leading dimension ldx >= K (elements).
+ *   M          tokens in this batch, >= 0 (M == 0 enqueues nothing).
+ *   row_scale  NULL, or device fp32[M]: output-channel-group weights ([G]); then Xs = bf16(row_scale_t * x_t)
+ *              (fp32 product, rounded to nearest-even bf16).  Requires x_dtype == GPTQ_DTYPE_BF16.
+ *              Without it Xs = X.
+ *   X_float    NULL, or device M x K, same dtype, leading dimension ldxf >= K: the float stream X~ of
+ *              asymmetric calibration ([A], [R] item 3).  Then also A += 2 (X~ - X)^T X with the mismatch
+ *              formed in fp32 and rounded to bf16 (exact for bf16 streams whose difference is
+ *              bf16-representable).  Requires x_dtype == GPTQ_DTYPE_BF16 and row_scale == NULL.
+ *   A          device, K x K fp32 row-major, read-modify-written; required iff X_float != NULL.  Not
+ *              symmetric.
+ *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_ACCUMULATE_HESSIAN, K, 0, M, X_float != 0).
+ * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP.  Asynchronous.
+ */
+gptq_status_t gptq_accumulate_hessian(float* H, int64_t K,
+                                      const void* X, gptq_dtype_t x_dtype, int64_t M, int64_t ldx,
+                                      const float* row_scale,
+                                      const void* X_float, int64_t ldxf, float* A,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gptq_prepare - in place H -> U ([T] sections 4 and 6).
+ *   1. dead coordinates: every k with H_kk == 0 gets H_kk := 1 and dead[k] = 1 (else 0);
+ *   2. damping: damp = percdamp * mean_k(H_kk) (after step 1), H_d = H + damp * I;
+ *   3. U: the upper-triangular matrix with H_d^{-1} = U^T U (so that U_qq^2 is the inverse of the Hessian
+ *      left when q is the first free coordinate), computed as H_d = R R^T with R upper then U = R^{-1}.
+ *
+ *   H_to_U     device, K x K fp32 row-major, symmetric on entry (only the upper triangle is read); on
+ *              return holds U with the strictly lower triangle set to zero.
+ *   K          >= 1.
+ *   percdamp   >= 0 and finite (0 disables damping).
+ *   dead       device uint8[K], written.
+ *   damp_out   NULL or host float*: receives damp.   n_dead_out: NULL or host int64_t*: number of dead.
+ *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_PREPARE, K, 0, 0, 0).
+ * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_NONFINITE (non-finite diagonal or pivot),
+ * GPTQ_ERR_NOT_PD (a pivot <= 0; the contents of H_to_U are then unspecified), GPTQ_ERR_HIP.
+ * Synchronises `stream` before returning.
+ */
+gptq_status_t gptq_prepare(float* H_to_U, int64_t K, float percdamp,
+                           uint8_t* dead, float* damp_out, int64_t* n_dead_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gptq_asym_correction - GPTAQ correction matrix ([R] item 3; [A] closed form with channel
+ * parallelisation):  P1 = [(A U^T) (.) M] U, with M the strictly upper-triangular mask and U from
+ * gptq_prepare on the quantised-stream Hessian.  Row q of P1 is the ridge least-squares response of the
+ * coordinates after q to coordinate q's input mismatch.
+ *
+ *   U          device, K x K fp32 upper-triangular (strictly lower part zero), from gptq_prepare.
+ *   A          device, K x K fp32, from gptq_accumulate_hessian (same scaling as H).
+ *   P1         device, K x K fp32, written (strictly upper; lower triangle and diagonal written as 0).
+ *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_ASYM_CORRECTION, K, 0, 0, 0).
+ * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP.  Asynchronous.
+ */
+gptq_status_t gptq_asym_correction(const float* U, const float* A, float* P1, int64_t K,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gptq_quantize_layer - quantise every output channel of W in the natural (shared) input-coordinate order
+ * ([T] sections 3-5; symmetric per-channel grid of [G]).
+ *
+ *   Grid: zero point z = 2^(bits-1), codes c in [0, 2^bits - 1], value s_n (c - z).  Unless
+ *   GPTQ_FLAG_SCALES_GIVEN, s_n = fp32(2 * max_k |W_kn| / (2^bits - 1)), taken from W before dead rows
+ *   are zeroed, and 1 for an all-zero channel.
+ *   Loop, coordinate j = 0..K-1 for all channels at once (w = working copy, dead rows zeroed):
+ *     c = clamp(round_half_even(w_j / s) + z, 0, 2^bits - 1);  q = s (c - z);  E_j = (w_j - q) / U_jj
+ *     w_k -= U_jk E_j for the remaining k of the current block;  [P1: w_k += P1_jk * w_j(before rounding)]
+ *     after each block of `blocksize` coordinates the same updates are applied to all later coordinates
+ *     at once (lazy batch, [T] section 5).
+ *
+ *   W          device, K x N weights, dtype w_dtype, element (k, n) at W[k * w_rs + n * w_cs]
+ *              (row-major K x N: w_rs = ldw, w_cs = 1; an N x K nn.Linear weight: w_rs = 1, w_cs = K).
+ *   U          device, K x K fp32 from gptq_prepare.        dead: device uint8[K] from gptq_prepare or NULL.
+ *   P1         NULL, or device K x K fp32 from gptq_asym_correction (asymmetric calibration).
+ *   bits       2..8.   blocksize: 128 (the lazy-batch width; the only value this build accepts).
+ *   codes      device uint8, code of (k, n) written at codes[k * c_rs + n * c_cs].
+ *   scales     device fp32[N]: written, or read with GPTQ_FLAG_SCALES_GIVEN (then each > 0 and finite).
+ *   W_hat      NULL, or device, dtype w_dtype, s (c - z) evaluated in fp32 then converted, written at
+ *              W_hat[k * w_rs + n * w_cs] (same strides as W; may alias W).
+ *   losses     NULL, or device fp32[N]: per channel sum_j 1/2 E_j^2 ([T] section 3: the added objective).
+ *   pre_round  NULL, or device fp32, K x N row-major (ld = N): w_j / s just before rounding (diagnostic).
+ *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, flags | (P1?2:0)).
+ * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_NONFINITE (NaN/Inf weight or given scale),
+ * GPTQ_ERR_HIP.  Synchronises `stream` before returning.
+ */
+gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K, int64_t N,
+                                  int64_t w_rs, int64_t w_cs,
+                                  const float* U, const uint8_t* dead, const float* P1,
+                                  int bits, int blocksize, unsigned flags,
+                                  uint8_t* codes, int64_t c_rs, int64_t c_cs,
+                                  float* scales, void* W_hat, float* losses, float* pre_round,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* gptq_status_string(gptq_status_t status);
+
+/* Library version as "major.minor.patch" (static string). */
+const char* gptq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_H */

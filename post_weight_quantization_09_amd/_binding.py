@@ -1,0 +1,221 @@
+"""ctypes binding of libgptq_hip.so (the C ABI declared in include/gptq.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels.  torch supplies
+device memory (tensors, workspace) and the current HIP stream.  The functions carry the C names.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libgptq_hip.so")
+
+GPTQ_OK, GPTQ_ERR_ARG, GPTQ_ERR_NONFINITE, GPTQ_ERR_NOT_PD, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP = range(6)
+GPTQ_DTYPE_F32, GPTQ_DTYPE_BF16 = 0, 1
+GPTQ_CALL_ACCUMULATE_HESSIAN, GPTQ_CALL_PREPARE, GPTQ_CALL_ASYM_CORRECTION, GPTQ_CALL_QUANTIZE_LAYER = range(4)
+GPTQ_FLAG_SCALES_GIVEN = 1
+
+_i64, _f32, _u32, _ptr, _size = ctypes.c_int64, ctypes.c_float, ctypes.c_uint, ctypes.c_void_p, ctypes.c_size_t
+
+_SIGNATURES = {
+    "gptq_version": (ctypes.c_char_p, []),
+    "gptq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "gptq_workspace_bytes": (_size, [ctypes.c_int, _i64, _i64, _i64, _u32]),
+    "gptq_accumulate_hessian": (ctypes.c_int, [_ptr, _i64, _ptr, ctypes.c_int, _i64, _i64, _ptr, _ptr, _i64, _ptr,
+                                               _ptr, _size, _ptr]),
+    "gptq_prepare": (ctypes.c_int, [_ptr, _i64, _f32, _ptr, ctypes.POINTER(_f32), ctypes.POINTER(_i64), _ptr,
+                                    _size, _ptr]),
+    "gptq_asym_correction": (ctypes.c_int, [_ptr, _ptr, _ptr, _i64, _ptr, _size, _ptr]),
+    "gptq_quantize_layer": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
+                                           ctypes.c_int, ctypes.c_int, _u32, _ptr, _i64, _i64, _ptr, _ptr, _ptr,
+                                           _ptr, _ptr, _size, _ptr]),
+}
+
+_lib = None
+
+
+class GptqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Loads the in-tree library; raises if it has not been built (there is no fallback path)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it with `python -m post_weight_quantization_09_amd.build` "
+                           "(or __graft_entry__.build()); there is no CPU fallback")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().gptq_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return load().gptq_version().decode()
+
+
+def gptq_workspace_bytes(call: int, K: int, N: int = 0, M: int = 0, flags: int = 0) -> int:
+    return int(load().gptq_workspace_bytes(int(call), int(K), int(N), int(M), int(flags)))
+
+
+def _check(status: int, where: str):
+    if status != GPTQ_OK:
+        raise GptqError(status, where)
+
+
+def _dptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensor expected")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device, stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(call, K, N, M, flags, device, workspace):
+    need = gptq_workspace_bytes(call, K, N, M, flags)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace, ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
+def _contig(t: Optional[torch.Tensor], name: str, dtype=None):
+    """Matrices and vectors cross the C ABI as plain row-major pointers: refuse other layouts."""
+    if t is None:
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}")
+
+
+def _square(t: torch.Tensor, name: str, K: Optional[int] = None):
+    if t.dim() != 2 or t.shape[0] != t.shape[1] or (K is not None and t.shape[0] != K):
+        raise ValueError(f"{name} must be a square K x K matrix")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GPTQ_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return GPTQ_DTYPE_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def gptq_accumulate_hessian(H: torch.Tensor, X: torch.Tensor, row_scale: Optional[torch.Tensor] = None,
+                            X_float: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """H += 2 Xs^T Xs (and A += 2 (X_float - X)^T X).  X: M x K with unit column stride."""
+    K = H.shape[0]
+    M = X.shape[0]
+    _square(H, "H")
+    _contig(H, "H", torch.float32)
+    _contig(A, "A", torch.float32)
+    _contig(row_scale, "row_scale", torch.float32)
+    if X.dim() != 2 or X.shape[1] != K or X.stride(1) != 1:
+        raise ValueError("X must be M x K with contiguous rows")
+    if X_float is not None and (X_float.shape != X.shape or X_float.stride(1) != 1):
+        raise ValueError("X_float must match X")
+    flags = 1 if X_float is not None else 0
+    workspace, wp, wb = _workspace(GPTQ_CALL_ACCUMULATE_HESSIAN, K, 0, M, flags, H.device, workspace)
+    st = load().gptq_accumulate_hessian(
+        _dptr(H), K, _dptr(X), _dtype_code(X), M, X.stride(0) if M > 0 else K, _dptr(row_scale), _dptr(X_float),
+        X_float.stride(0) if X_float is not None and M > 0 else K, _dptr(A), wp, wb, _stream(H.device, stream))
+    _check(st, "gptq_accumulate_hessian")
+
+
+def gptq_prepare(H: torch.Tensor, percdamp: float, dead: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    """In place H -> U.  Returns (dead uint8[K], damp, n_dead)."""
+    K = H.shape[0]
+    _square(H, "H")
+    _contig(H, "H", torch.float32)
+    _contig(dead, "dead", torch.uint8)
+    if dead is None:
+        dead = torch.empty(K, dtype=torch.uint8, device=H.device)
+    workspace, wp, wb = _workspace(GPTQ_CALL_PREPARE, K, 0, 0, 0, H.device, workspace)
+    damp = _f32(0.0)
+    n_dead = _i64(0)
+    st = load().gptq_prepare(_dptr(H), K, float(percdamp), _dptr(dead), ctypes.byref(damp), ctypes.byref(n_dead), wp,
+                             wb, _stream(H.device, stream))
+    _check(st, "gptq_prepare")
+    return dead, float(damp.value), int(n_dead.value)
+
+
+def gptq_asym_correction(U: torch.Tensor, A: torch.Tensor, P1: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    K = U.shape[0]
+    for t, nm in ((U, "U"), (A, "A"), (P1, "P1")):
+        if t is not None:
+            _square(t, nm, K)
+    _contig(U, "U", torch.float32)
+    _contig(A, "A", torch.float32)
+    _contig(P1, "P1", torch.float32)
+    if P1 is None:
+        P1 = torch.empty(K, K, dtype=torch.float32, device=U.device)
+    workspace, wp, wb = _workspace(GPTQ_CALL_ASYM_CORRECTION, K, 0, 0, 0, U.device, workspace)
+    st = load().gptq_asym_correction(_dptr(U), _dptr(A), _dptr(P1), K, wp, wb, _stream(U.device, stream))
+    _check(st, "gptq_asym_correction")
+    return P1
+
+
+def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, dead: Optional[torch.Tensor] = None,
+                        P1: Optional[torch.Tensor] = None, blocksize: int = 128,
+                        scales: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
+                        W_hat: Optional[torch.Tensor] = None, losses: Optional[torch.Tensor] = None,
+                        pre_round: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> dict:
+    """Quantises W (K x N view, any strides) with U; given `scales` are used as the grid (fixed-grid mode).
+
+    Returns dict(codes uint8 K x N, scales fp32[N], W_hat, losses, pre_round) with the tensors written.
+    """
+    K, N = W.shape
+    dev = W.device
+    _square(U, "U", K)
+    if P1 is not None:
+        _square(P1, "P1", K)
+    _contig(U, "U", torch.float32)
+    _contig(P1, "P1", torch.float32)
+    _contig(dead, "dead", torch.uint8)
+    _contig(scales, "scales", torch.float32)
+    _contig(losses, "losses", torch.float32)
+    flags = 0
+    if scales is None:
+        scales = torch.empty(N, dtype=torch.float32, device=dev)
+    else:
+        flags |= GPTQ_FLAG_SCALES_GIVEN
+    if codes is None:
+        codes = torch.empty(K, N, dtype=torch.uint8, device=dev)
+    if W_hat is not None and (W_hat.shape != W.shape or W_hat.stride() != W.stride() or W_hat.dtype != W.dtype):
+        raise ValueError("W_hat must have W's shape, strides and dtype")
+    if pre_round is not None and (pre_round.shape != (K, N) or not pre_round.is_contiguous()):
+        raise ValueError("pre_round must be a contiguous K x N fp32 tensor")
+    ws_flags = flags | (2 if P1 is not None else 0)
+    workspace, wp, wb = _workspace(GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, ws_flags, dev, workspace)
+    st = load().gptq_quantize_layer(
+        _dptr(W), _dtype_code(W), K, N, W.stride(0), W.stride(1), _dptr(U), _dptr(dead), _dptr(P1), int(bits),
+        int(blocksize), flags, _dptr(codes), codes.stride(0), codes.stride(1), _dptr(scales), _dptr(W_hat),
+        _dptr(losses), _dptr(pre_round), wp, wb, _stream(dev, stream))
+    _check(st, "gptq_quantize_layer")
+    return {"codes": codes, "scales": scales, "W_hat": W_hat, "losses": losses, "pre_round": pre_round}

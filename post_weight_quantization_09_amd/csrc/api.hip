@@ -1,0 +1,164 @@
+// C ABI of libgptq_hip.so: argument validation, workspace sizing and launch order (see include/gptq.h).
+#include <algorithm>
+#include <cmath>
+
+#include "factor.hpp"
+#include "gemm_f32.hpp"
+#include "gram.hpp"
+#include "quantize.hpp"
+
+using namespace gptq;
+
+namespace {
+
+bool ws_ok(const void* ws, size_t have, size_t need) {
+    if (need == 0) return true;
+    return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) % kAlign) == 0 && have >= need;
+}
+
+// Split partials are reused by the symmetric Gram and then the cross term: size for the larger plan.
+size_t accumulate_partial_floats(int64_t K, int64_t M, bool cross) {
+    size_t f = gram_plan(K, M, false).partial_floats;
+    if (cross) f = std::max(f, gram_plan(K, M, true).partial_floats);
+    return f;
+}
+
+size_t accumulate_ws(int64_t K, int64_t M, bool cross) {
+    Carver c(nullptr);
+    c.take<DevStatus>(1);
+    c.take<float>(accumulate_partial_floats(K, M, cross));
+    return c.bytes();
+}
+
+size_t asym_ws(int64_t K) {
+    Carver c(nullptr);
+    c.take<DevStatus>(1);
+    c.take<float>((size_t)K * (size_t)K);
+    return c.bytes();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gptq_version(void) { return "0.1.0"; }
+
+const char* gptq_status_string(gptq_status_t s) {
+    switch (s) {
+        case GPTQ_OK: return "ok";
+        case GPTQ_ERR_ARG: return "invalid argument";
+        case GPTQ_ERR_NONFINITE: return "non-finite input";
+        case GPTQ_ERR_NOT_PD: return "damped Hessian not positive definite";
+        case GPTQ_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case GPTQ_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+size_t gptq_workspace_bytes(gptq_call_t call, int64_t K, int64_t N, int64_t M, unsigned flags) {
+    if (K < 1) K = 1;
+    if (N < 1) N = 1;
+    if (M < 0) M = 0;
+    switch (call) {
+        case GPTQ_CALL_ACCUMULATE_HESSIAN: return accumulate_ws(K, M, (flags & 1u) != 0);
+        case GPTQ_CALL_PREPARE: return prepare_workspace_bytes(K);
+        case GPTQ_CALL_ASYM_CORRECTION: return asym_ws(K);
+        case GPTQ_CALL_QUANTIZE_LAYER: return quantize_workspace_bytes(K, N, (flags & 2u) != 0);
+    }
+    return 0;
+}
+
+gptq_status_t gptq_accumulate_hessian(float* H, int64_t K, const void* X, gptq_dtype_t x_dtype, int64_t M,
+                                      int64_t ldx, const float* row_scale, const void* X_float, int64_t ldxf,
+                                      float* A, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!H || K < 1 || M < 0 || (M > 0 && !X) || ldx < K) return GPTQ_ERR_ARG;
+    if (x_dtype != GPTQ_DTYPE_F32 && x_dtype != GPTQ_DTYPE_BF16) return GPTQ_ERR_ARG;
+    if (row_scale && x_dtype != GPTQ_DTYPE_BF16) return GPTQ_ERR_ARG;
+    const bool cross = X_float != nullptr;
+    if (cross && (x_dtype != GPTQ_DTYPE_BF16 || !A || ldxf < K || row_scale)) return GPTQ_ERR_ARG;
+    if (!cross && A) return GPTQ_ERR_ARG;
+    const size_t need = x_dtype == GPTQ_DTYPE_BF16 ? accumulate_ws(K, M, cross) : 0;
+    if (!ws_ok(workspace, workspace_bytes, need)) return GPTQ_ERR_WORKSPACE;
+    if (M == 0) return GPTQ_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (x_dtype == GPTQ_DTYPE_F32) {
+        // fp32 activations: H += 2 X^T X on fp32 MFMA (A(m,k) = X[k][m], B(k,n) = X[k][n]).
+        GemmArgs g;
+        g.M = K; g.N = K; g.K1 = M;
+        g.A1 = static_cast<const float*>(X); g.lda1 = ldx; g.transA = true;
+        g.B1 = static_cast<const float*>(X); g.ldb1 = ldx;
+        g.C = H; g.ldc = K;
+        g.alpha = 2.f; g.beta = 1.f;
+        return gemm_f32(g, 1, st) == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
+    }
+    Carver c(workspace);
+    c.take<DevStatus>(1);
+    const GramPlan pl = gram_plan(K, M, false);
+    float* partial = c.take<float>(accumulate_partial_floats(K, M, cross));
+    hipError_t e = gram_bf16(pl, static_cast<const uint16_t*>(X), ldx, nullptr, 0, row_scale, M, K, partial, H, st);
+    if (e != hipSuccess) return GPTQ_ERR_HIP;
+    if (cross) {
+        const GramPlan px = gram_plan(K, M, true);
+        e = gram_bf16(px, static_cast<const uint16_t*>(X), ldx, static_cast<const uint16_t*>(X_float), ldxf, nullptr,
+                      M, K, partial, A, st);
+        if (e != hipSuccess) return GPTQ_ERR_HIP;
+    }
+    return GPTQ_OK;
+}
+
+gptq_status_t gptq_prepare(float* H_to_U, int64_t K, float percdamp, uint8_t* dead, float* damp_out,
+                           int64_t* n_dead_out, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!H_to_U || K < 1 || !dead || !std::isfinite(percdamp) || percdamp < 0.f) return GPTQ_ERR_ARG;
+    if (K > (int64_t)1 << 20) return GPTQ_ERR_ARG;
+    if (!ws_ok(workspace, workspace_bytes, prepare_workspace_bytes(K))) return GPTQ_ERR_WORKSPACE;
+    return prepare(H_to_U, K, percdamp, dead, damp_out, n_dead_out, workspace, static_cast<hipStream_t>(stream));
+}
+
+gptq_status_t gptq_asym_correction(const float* U, const float* A, float* P1, int64_t K, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (!U || !A || !P1 || K < 1) return GPTQ_ERR_ARG;
+    if (!ws_ok(workspace, workspace_bytes, asym_ws(K))) return GPTQ_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Carver c(workspace);
+    c.take<DevStatus>(1);
+    float* T = c.take<float>((size_t)K * (size_t)K);
+    // T = A U^T  (only the part on or above the diagonal is used)
+    GemmArgs g1;
+    g1.M = K; g1.N = K; g1.K1 = K;
+    g1.A1 = A; g1.lda1 = K;
+    g1.B1 = U; g1.ldb1 = K; g1.transB = true;       // B(k, n) = U[n][k], zero for k < n
+    g1.C = T; g1.ldc = K;
+    g1.flags = kGemmBLower | kGemmCUpper;
+    if (gemm_f32(g1, 1, st) != hipSuccess) return GPTQ_ERR_HIP;
+    // P1 = (T masked to k > m) U
+    GemmArgs g2;
+    g2.M = K; g2.N = K; g2.K1 = K;
+    g2.A1 = T; g2.lda1 = K;
+    g2.B1 = U; g2.ldb1 = K;                          // upper: zero for k > n
+    g2.C = P1; g2.ldc = K;
+    g2.flags = kGemmAStrictUpperMask | kGemmBUpper;
+    if (gemm_f32(g2, 1, st) != hipSuccess) return GPTQ_ERR_HIP;
+    return GPTQ_OK;
+}
+
+gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K, int64_t N, int64_t w_rs,
+                                  int64_t w_cs, const float* U, const uint8_t* dead, const float* P1, int bits,
+                                  int blocksize, unsigned flags, uint8_t* codes, int64_t c_rs, int64_t c_cs,
+                                  float* scales, void* W_hat, float* losses, float* pre_round, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    if (!W || !U || !codes || !scales || K < 1 || N < 1) return GPTQ_ERR_ARG;
+    if (w_dtype != GPTQ_DTYPE_F32 && w_dtype != GPTQ_DTYPE_BF16) return GPTQ_ERR_ARG;
+    if (bits < 2 || bits > 8 || blocksize != 128) return GPTQ_ERR_ARG;
+    if ((flags & ~GPTQ_FLAG_SCALES_GIVEN) != 0) return GPTQ_ERR_ARG;
+    if (w_rs < 1 || w_cs < 1 || c_rs < 1 || c_cs < 1) return GPTQ_ERR_ARG;
+    if (K > (int64_t)1 << 24 || N > (int64_t)1 << 28) return GPTQ_ERR_ARG;
+    if (!ws_ok(workspace, workspace_bytes, quantize_workspace_bytes(K, N, P1 != nullptr))) return GPTQ_ERR_WORKSPACE;
+    QuantizeArgs a;
+    a.W = W; a.w_dtype = w_dtype; a.K = K; a.N = N; a.w_rs = w_rs; a.w_cs = w_cs;
+    a.U = U; a.dead = dead; a.P1 = P1; a.bits = bits; a.scales_given = (flags & GPTQ_FLAG_SCALES_GIVEN) != 0;
+    a.codes = codes; a.c_rs = c_rs; a.c_cs = c_cs; a.scales = scales; a.W_hat = W_hat; a.losses = losses;
+    a.pre_round = pre_round;
+    return quantize_layer(a, workspace, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

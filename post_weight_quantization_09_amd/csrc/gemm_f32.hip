@@ -1,0 +1,220 @@
+// fp32 MFMA GEMM for gfx950: C = beta*C + alpha*(A1 B1 + a2_scale * A2 B2), optionally batched.
+//
+// Every dense contraction of the path runs here: the trailing updates of the blocked factorisation, the
+// merges of the triangular inverse, the lazy-batch trailing update of the column loop ([T] section 5:
+// after a block, the far weights are updated with one matrix product) and the two products of the GPTAQ
+// correction ([R] item 3).
+//
+// Tiling: 256 threads = 4 waves, a 128 x 128 tile of C per workgroup, 64 x 64 per wave as 2 x 2
+// v_mfma_f32_32x32x2_f32 accumulators.  k advances 16 at a time through double-buffered LDS tiles stored
+// k-major (As[k][m], Bs[k][n]) so that every MFMA operand read is a conflict-free ds_read_b32.
+#include "gemm_f32.hpp"
+
+namespace gptq {
+
+namespace {
+
+constexpr int kTM = 128, kTN = 128, kTK = 16, kPad = 4;
+
+// MFMA 32x32x2 f32 output layout: lane l, accumulator register r -> (row, col) inside the 32 x 32 block.
+__device__ inline int mfma32_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+template <bool TA, bool TB>
+struct TileIO {
+    // A(m,k): TA ? A[k*lda + m] : A[m*lda + k].   B(k,n): TB ? B[n*ldb + k] : B[k*ldb + n].
+    f32x4 a[2], b[2];
+
+    __device__ static inline f32x4 load4(const float* base, int64_t idx0, int64_t step, int valid, bool vec) {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (valid >= 4 && vec) {
+            v = *reinterpret_cast<const f32x4*>(base + idx0);
+        } else {
+            for (int e = 0; e < 4; ++e)
+                if (e < valid) v[e] = base[idx0 + e * step];
+        }
+        return v;
+    }
+
+    // Loads the A tile rows [m0, m0+128) x cols [k0, k0+16) of pair operand (ptr, ld) into registers.
+    __device__ inline void load_a(const float* A, int64_t lda, int64_t M, int64_t kEnd, int64_t m0, int64_t k0,
+                                  bool vec, float scale, bool strict_upper_mask, int tid) {
+        for (int i = 0; i < 2; ++i) {
+            int64_t m, k;
+            if (!TA) { m = m0 + (tid >> 2) + 64 * i; k = k0 + (tid & 3) * 4; }
+            else     { k = k0 + (tid >> 5) + 8 * i;  m = m0 + (tid & 31) * 4; }
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (!TA) {
+                if (m < M && k < kEnd) {
+                    int valid = (int)min<int64_t>(4, kEnd - k);
+                    v = load4(A, m * lda + k, 1, valid, vec);
+                }
+            } else {
+                if (k < kEnd && m < M) {
+                    int valid = (int)min<int64_t>(4, M - m);
+                    v = load4(A, k * lda + m, 1, valid, vec);
+                }
+            }
+            if (strict_upper_mask) {
+                for (int e = 0; e < 4; ++e) {
+                    int64_t me = TA ? m + e : m, ke = TA ? k : k + e;
+                    if (ke <= me) v[e] = 0.f;
+                }
+            }
+            a[i] = v * scale;
+        }
+    }
+
+    __device__ inline void load_b(const float* B, int64_t ldb, int64_t N, int64_t kEnd, int64_t n0, int64_t k0,
+                                  bool vec, int tid) {
+        for (int i = 0; i < 2; ++i) {
+            int64_t n, k;
+            if (!TB) { k = k0 + (tid >> 5) + 8 * i;  n = n0 + (tid & 31) * 4; }
+            else     { n = n0 + (tid >> 2) + 64 * i; k = k0 + (tid & 3) * 4; }
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (!TB) {
+                if (k < kEnd && n < N) {
+                    int valid = (int)min<int64_t>(4, N - n);
+                    v = load4(B, k * ldb + n, 1, valid, vec);
+                }
+            } else {
+                if (n < N && k < kEnd) {
+                    int valid = (int)min<int64_t>(4, kEnd - k);
+                    v = load4(B, n * ldb + k, 1, valid, vec);
+                }
+            }
+            b[i] = v;
+        }
+    }
+
+    __device__ inline void store(float (*As)[kTM + kPad], float (*Bs)[kTN + kPad], int tid) const {
+        for (int i = 0; i < 2; ++i) {
+            if (!TA) {
+                int r = (tid >> 2) + 64 * i, kc = (tid & 3) * 4;
+                for (int e = 0; e < 4; ++e) As[kc + e][r] = a[i][e];
+            } else {
+                int kr = (tid >> 5) + 8 * i, mc = (tid & 31) * 4;
+                *reinterpret_cast<f32x4*>(&As[kr][mc]) = a[i];
+            }
+            if (!TB) {
+                int kr = (tid >> 5) + 8 * i, nc = (tid & 31) * 4;
+                *reinterpret_cast<f32x4*>(&Bs[kr][nc]) = b[i];
+            } else {
+                int r = (tid >> 2) + 64 * i, kc = (tid & 3) * 4;
+                for (int e = 0; e < 4; ++e) Bs[kc + e][r] = b[i][e];
+            }
+        }
+    }
+};
+
+template <bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
+    __shared__ __attribute__((aligned(16))) float As[2][kTK][kTM + kPad];
+    __shared__ __attribute__((aligned(16))) float Bs[2][kTK][kTN + kPad];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int64_t m0 = (int64_t)blockIdx.y * kTM;
+    const int64_t n0 = (int64_t)blockIdx.x * kTN;
+    const int64_t bz = blockIdx.z;
+    if (m0 >= p.M || n0 >= p.N) return;
+    if ((p.flags & kGemmCUpper) && m0 >= n0 + kTN) return;
+
+    const float* A1 = p.A1 + bz * p.strideA1;
+    const float* B1 = p.B1 + bz * p.strideB1;
+    const float* A2 = p.A2 ? p.A2 + bz * p.strideA2 : nullptr;
+    const float* B2 = p.B2 ? p.B2 + bz * p.strideB2 : nullptr;
+    float* C = p.C + bz * p.strideC;
+
+    int64_t klo = 0, khi = p.K1;
+    if (p.flags & (kGemmAUpper | kGemmAStrictUpperMask)) klo = max<int64_t>(klo, m0);
+    if (p.flags & kGemmBLower) klo = max<int64_t>(klo, n0);
+    if (p.flags & kGemmBUpper) khi = min<int64_t>(khi, n0 + kTN);
+    klo = (klo / kTK) * kTK;
+    const int64_t nt1 = khi > klo ? ceil_div(khi - klo, kTK) : 0;
+    const int64_t nt2 = (A2 && p.K2 > 0) ? ceil_div(p.K2, kTK) : 0;
+    const int64_t nt = nt1 + nt2;
+    const bool mask = (p.flags & kGemmAStrictUpperMask) != 0;
+
+    f32x16 acc[2][2];
+    for (int a = 0; a < 2; ++a)
+        for (int b = 0; b < 2; ++b)
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    TileIO<TA, TB> io;
+    auto load = [&](int64_t t) {
+        if (t < nt1) {
+            int64_t k0 = klo + t * kTK;
+            io.load_a(A1, p.lda1, p.M, p.K1, m0, k0, p.vecA1, 1.0f, mask, tid);
+            io.load_b(B1, p.ldb1, p.N, p.K1, n0, k0, p.vecB1, tid);
+        } else {
+            int64_t k0 = (t - nt1) * kTK;
+            io.load_a(A2, p.lda2, p.M, p.K2, m0, k0, p.vecA2, p.a2_scale, false, tid);
+            io.load_b(B2, p.ldb2, p.N, p.K2, n0, k0, p.vecB2, tid);
+        }
+    };
+
+    if (nt > 0) {
+        load(0);
+        io.store(As[0], Bs[0], tid);
+    }
+    __syncthreads();
+    for (int64_t t = 0; t < nt; ++t) {
+        const int buf = (int)(t & 1);
+        if (t + 1 < nt) load(t + 1);
+#pragma unroll
+        for (int kk = 0; kk < kTK / 2; ++kk) {
+            const int k = 2 * kk + (lane >> 5);
+            float av[2], bv[2];
+            for (int a = 0; a < 2; ++a) av[a] = As[buf][k][wm * 64 + 32 * a + (lane & 31)];
+            for (int b = 0; b < 2; ++b) bv[b] = Bs[buf][k][wn * 64 + 32 * b + (lane & 31)];
+            for (int a = 0; a < 2; ++a)
+                for (int b = 0; b < 2; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
+        }
+        if (t + 1 < nt) io.store(As[buf ^ 1], Bs[buf ^ 1], tid);
+        __syncthreads();
+    }
+
+    // Epilogue: C = alpha * acc + beta * C.
+    for (int a = 0; a < 2; ++a) {
+        for (int b = 0; b < 2; ++b) {
+            const int64_t col = n0 + wn * 64 + 32 * b + (lane & 31);
+            if (col >= p.N) continue;
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * 64 + 32 * a + mfma32_row(r, lane);
+                if (row >= p.M) continue;
+                float* cp = C + row * p.ldc + col;
+                float v = p.alpha * acc[a][b][r];
+                if (p.beta != 0.f) v += p.beta * *cp;
+                *cp = v;
+            }
+        }
+    }
+}
+
+inline bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+}  // namespace
+
+hipError_t gemm_f32(GemmArgs p, int64_t batch, hipStream_t stream) {
+    if (p.M <= 0 || p.N <= 0 || batch <= 0) return hipSuccess;
+    // 16-byte vector loads need an aligned base, a leading dimension (and batch stride) that is a multiple
+    // of 4 floats; otherwise the tile loads fall back to scalar accesses.
+    auto vec_ok = [&](const float* ptr, int64_t ld, int64_t stride) {
+        return ptr && aligned16(ptr) && ld % 4 == 0 && (batch == 1 || stride % 4 == 0);
+    };
+    p.vecA1 = vec_ok(p.A1, p.lda1, p.strideA1);
+    p.vecB1 = vec_ok(p.B1, p.ldb1, p.strideB1);
+    p.vecA2 = vec_ok(p.A2, p.lda2, p.strideA2);
+    p.vecB2 = vec_ok(p.B2, p.ldb2, p.strideB2);
+    dim3 grid((unsigned)ceil_div(p.N, kTN), (unsigned)ceil_div(p.M, kTM), (unsigned)batch);
+    if (grid.y > 65535u || grid.z > 65535u) return hipErrorInvalidValue;
+    if (!p.transA && !p.transB) hipLaunchKernelGGL((gemm_f32_kernel<false, false>), grid, dim3(256), 0, stream, p);
+    else if (!p.transA && p.transB) hipLaunchKernelGGL((gemm_f32_kernel<false, true>), grid, dim3(256), 0, stream, p);
+    else if (p.transA && !p.transB) hipLaunchKernelGGL((gemm_f32_kernel<true, false>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((gemm_f32_kernel<true, true>), grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace gptq

@@ -1,0 +1,395 @@
+// Shared-order column loop with lazy block updates on gfx950.
+//
+// [T] section 3: fixing coordinate q to its grid value moves the still-free weights along the OBS direction.
+// [T] section 4: with U the upper factor of H_d^{-1}, that move is w_k -= U_qk E_q with E_q = (w_q - Q(w_q)) / U_qq.
+// [T] section 5: every output channel uses the same coordinate order, so all channels share U; inside a
+// block of 128 coordinates the updates are applied at once, the rest of the matrix is updated once per
+// block by one matrix product (W[b1:] -= U[B, b1:]^T E_B), here an fp32 MFMA GEMM.
+// [R] item 3 / [A]: the asymmetric variant adds w_k += P1_qk * w_q(before rounding), in block and in the
+// lazy product (a second operand pair of the same GEMM).
+// [G] / [T] section 2: symmetric per-channel grid, codes 0..2^b-1, zero point 2^(b-1), value s (c - z).
+//
+// Data layout: the working weights are kept transposed, Wt[n][k] (fp32, N x ldt, ldt = K rounded up to
+// 128), so that one channel's block of 128 coordinates is contiguous.  The block kernel gives each
+// channel 16 lanes (one DPP row); lane l holds coordinates 16 m + l, m = 0..7, of the current block in
+// registers, so that the coordinates still free after step j = 16 m + l0 are exactly the slots >= m and
+// the triangular work shrinks with m.  The U panel (and P1 panel) of the block sits in LDS, permuted so
+// that a lane's eight coefficients of row j are two 16-byte reads.  At step j the value w_j is broadcast
+// from its owner lane to the row with DPP row_newbcast; every lane of the row then evaluates the same
+// rounding and error (no further communication), updates its own slots, and the owner keeps the code.
+#include <algorithm>
+#include <utility>
+
+#include "gemm_f32.hpp"
+#include "quantize.hpp"
+
+namespace gptq {
+
+namespace {
+
+constexpr int kB = 128;          // block (lazy batch) width
+constexpr int kChPerWG = 16;     // channels per workgroup of the block kernel
+
+__global__ void quant_init_kernel(DevStatus* st, uint32_t* amax_bits, float* loss_acc, int64_t N) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i == 0) { st->flags = 0; st->n_dead = 0; st->damp = 0.f; }
+    if (i < N) { amax_bits[i] = 0u; loss_acc[i] = 0.f; }
+}
+
+// W (K x N view with strides) -> Wt (N x ldt fp32, dead rows zeroed, padding zero) and per-channel max |w|
+// taken before dead rows are zeroed.  64 x 64 tiles transposed through LDS.
+template <bool BF16>
+__global__ __launch_bounds__(256) void convert_kernel(const void* Wv, int64_t K, int64_t N, int64_t w_rs,
+                                                     int64_t w_cs, const uint8_t* dead, float* Wt, int64_t ldt,
+                                                     uint32_t* amax_bits, DevStatus* st) {
+    __shared__ float tile[64][65];
+    const int tid = threadIdx.x;
+    const int64_t k0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+    const bool n_fast = (w_cs == 1) || (w_rs != 1 && w_cs <= w_rs);
+    unsigned bad = 0;
+    for (int i = 0; i < 16; ++i) {
+        const int idx = tid + 256 * i;
+        const int a = idx >> 6, b = idx & 63;         // (slow, fast)
+        const int kk = n_fast ? a : b, nn = n_fast ? b : a;
+        const int64_t k = k0 + kk, n = n0 + nn;
+        float v = 0.f;
+        if (k < K && n < N) {
+            const int64_t off = k * w_rs + n * w_cs;
+            if (BF16) v = __uint_as_float((uint32_t)(static_cast<const uint16_t*>(Wv)[off]) << 16);
+            else v = static_cast<const float*>(Wv)[off];
+            if (!isfinite(v)) bad = 1;
+        }
+        tile[kk][nn] = v;
+    }
+    __syncthreads();
+    // column max over this tile's 64 rows, 4 threads per channel
+    {
+        const int nn = tid >> 2, part = tid & 3;
+        float m = 0.f;
+        for (int kk = part; kk < 64; kk += 4) m = fmaxf(m, fabsf(tile[kk][nn]));
+        m = fmaxf(m, __shfl_xor(m, 1, 4));
+        m = fmaxf(m, __shfl_xor(m, 2, 4));
+        if (part == 0 && n0 + nn < N && m > 0.f) atomicMax(&amax_bits[n0 + nn], __float_as_uint(m));
+    }
+    for (int i = 0; i < 16; ++i) {
+        const int idx = tid + 256 * i;
+        const int nn = idx >> 6, kk = idx & 63;
+        const int64_t k = k0 + kk, n = n0 + nn;
+        if (n < N && k < ldt) {
+            float v = (k < K) ? tile[kk][nn] : 0.f;
+            if (k < K && dead && dead[k]) v = 0.f;
+            Wt[n * ldt + k] = v;
+        }
+    }
+    if (bad) atomicOr(&st->flags, (uint32_t)kDevNonFinite);
+}
+
+__global__ void scales_kernel(const uint32_t* amax_bits, float* scales, float* rscale, int64_t N, int bits,
+                              bool given, DevStatus* st) {
+    const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    float s;
+    if (given) {
+        s = scales[n];
+        if (!(isfinite(s) && s > 0.f)) {
+            atomicOr(&st->flags, (uint32_t)kDevNonFinite);
+            s = 1.f;
+        }
+    } else {
+        const float amax = __uint_as_float(amax_bits[n]);
+        const float qmax = (float)((1 << bits) - 1);
+        s = amax > 0.f ? (2.0f * amax) / qmax : 1.0f;   // IEEE division, round to nearest even
+        scales[n] = s;
+    }
+    rscale[n] = 1.0f / s;
+}
+
+// Broadcast lane `src` of each 16-lane row to the whole row (DPP row_newbcast, gfx90a+).
+__device__ inline float row_bcast(float x, int src) {
+    const int xi = __float_as_int(x);
+    int r;
+    switch (src) {
+#define GPTQ_BC(i) case i: r = __builtin_amdgcn_update_dpp(0, xi, 0x150 + i, 0xF, 0xF, false); break;
+        GPTQ_BC(0) GPTQ_BC(1) GPTQ_BC(2) GPTQ_BC(3) GPTQ_BC(4) GPTQ_BC(5) GPTQ_BC(6) GPTQ_BC(7)
+        GPTQ_BC(8) GPTQ_BC(9) GPTQ_BC(10) GPTQ_BC(11) GPTQ_BC(12) GPTQ_BC(13) GPTQ_BC(14) GPTQ_BC(15)
+#undef GPTQ_BC
+        default: r = xi;
+    }
+    return __int_as_float(r);
+}
+
+struct BlockArgs {
+    float* Wt; int64_t ldt;         // working weights, transposed
+    const float* U; const float* P1; int64_t K;
+    int64_t N;
+    int64_t b0; int bs;             // block start and size (<= 128)
+    const float* scales; const float* rscale;
+    int bits;
+    uint8_t* codes_t;               // N x ldt
+    float* E;                       // N x 128
+    float* Wpre;                    // N x 128 (asymmetric only)
+    float* loss_acc;                // N
+    float* pre_round;               // optional, K x N
+    const DevStatus* st;
+};
+
+// Per-lane state of the block kernel: 8 strided coordinates of one channel.
+struct LaneState {
+    float w[8], e[8], pre[8];
+    uint32_t code[8];
+    float loss;
+};
+
+struct StepConst {
+    const float* Up; const float* Pp; const float* rdiag;
+    float s, rs, z, qmax;
+    int l;
+    float* pre_round; int64_t prow_off; int64_t N; bool live;
+};
+
+// One step j of the loop (j compile-time so that slots, DPP lane and LDS offsets are immediates).
+template <int J, bool ASYM>
+__device__ __forceinline__ void loop_step(LaneState& st, const StepConst& k) {
+    constexpr int m = J >> 4, lj = J & 15;
+    const float wj = row_bcast(st.w[m], lj);
+    const float v = wj * k.rs;
+    const float c = fminf(fmaxf(rintf(v) + k.z, 0.f), k.qmax);
+    const float q = (c - k.z) * k.s;
+    const float e = (wj - q) * k.rdiag[J];
+    st.loss = fmaf(e, e, st.loss);
+    const f32x4* urow = reinterpret_cast<const f32x4*>(k.Up + (J * 16 + k.l) * 8);
+    const f32x4 u0 = urow[0], u1 = urow[1];
+    const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    if constexpr (ASYM) {
+        const f32x4* prow = reinterpret_cast<const f32x4*>(k.Pp + (J * 16 + k.l) * 8);
+        const f32x4 p0 = prow[0], p1 = prow[1];
+        const float pp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+        for (int mm = m; mm < 8; ++mm) st.w[mm] = fmaf(pp[mm], wj, fmaf(-uu[mm], e, st.w[mm]));
+    } else {
+#pragma unroll
+        for (int mm = m; mm < 8; ++mm) st.w[mm] = fmaf(-uu[mm], e, st.w[mm]);
+    }
+    const bool owner = (k.l == lj);
+    st.w[m] = owner ? q : st.w[m];
+    st.code[m] = owner ? (uint32_t)c : st.code[m];
+    st.e[m] = owner ? e : st.e[m];
+    if constexpr (ASYM) st.pre[m] = owner ? wj : st.pre[m];
+    if (k.pre_round && owner && k.live) k.pre_round[(int64_t)J * k.N + k.prow_off] = v;
+}
+
+template <bool ASYM, int... Js>
+__device__ __forceinline__ void run_steps(LaneState& st, const StepConst& k, int bs,
+                                          std::integer_sequence<int, Js...>) {
+    ((Js < bs ? loop_step<Js, ASYM>(st, k) : (void)0), ...);
+}
+
+template <bool ASYM>
+__global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
+    __shared__ __attribute__((aligned(16))) float Up[kB * kB];               // [row j][16 lanes][8 slots]
+    __shared__ __attribute__((aligned(16))) float Pp[ASYM ? kB * kB : 4];    // same layout (asymmetric)
+    __shared__ float rdiag[kB];
+
+    if (p.st->flags) return;   // an input was rejected earlier in this call
+    const int tid = threadIdx.x;
+    const int64_t b0 = p.b0;
+    const int bs = p.bs;
+    // stage the U (and P1) panel rows b0..b0+bs-1, columns b0..b0+127 (zero beyond the block)
+    for (int idx = tid; idx < kB * kB; idx += 256) {
+        const int j = idx >> 7, c = idx & 127;       // row j, column c = 16 m + l
+        const int l = c & 15, m = c >> 4;
+        float u = 0.f, pv = 0.f;
+        if (j < bs && c < bs) {
+            u = p.U[(b0 + j) * p.K + b0 + c];
+            if (ASYM) pv = p.P1[(b0 + j) * p.K + b0 + c];
+        }
+        Up[(j * 16 + l) * 8 + m] = u;
+        if (ASYM) Pp[(j * 16 + l) * 8 + m] = pv;
+    }
+    for (int j = tid; j < kB; j += 256) rdiag[j] = (j < bs) ? 1.0f / p.U[(b0 + j) * p.K + b0 + j] : 0.f;
+    __syncthreads();
+
+    const int lane = tid & 63, l = lane & 15;
+    const int64_t n = (int64_t)blockIdx.x * kChPerWG + (tid >> 4);
+    const bool live = n < p.N;
+    const int64_t nn = live ? n : 0;
+
+    LaneState st;
+    const float* wrow = p.Wt + nn * p.ldt + b0;
+    for (int m = 0; m < 8; ++m) {
+        st.w[m] = wrow[16 * m + l];
+        st.e[m] = 0.f;
+        st.pre[m] = 0.f;
+        st.code[m] = 0;
+    }
+    st.loss = 0.f;
+    StepConst k;
+    k.Up = Up; k.Pp = Pp; k.rdiag = rdiag;
+    k.s = p.scales[nn]; k.rs = p.rscale[nn];
+    k.z = (float)(1 << (p.bits - 1));
+    k.qmax = (float)((1 << p.bits) - 1);
+    k.l = l;
+    k.pre_round = p.pre_round ? p.pre_round + b0 * p.N : nullptr;
+    k.prow_off = n; k.N = p.N; k.live = live;
+    run_steps<ASYM>(st, k, bs, std::make_integer_sequence<int, kB>{});
+
+    if (!live) return;
+    uint8_t* crow = p.codes_t + n * p.ldt + b0;
+    float* erow = p.E + n * kB;
+    for (int m = 0; m < 8; ++m) {
+        const int c = 16 * m + l;
+        if (c < bs) crow[c] = (uint8_t)st.code[m];
+        erow[c] = st.e[m];
+        if (ASYM) p.Wpre[n * kB + c] = st.pre[m];
+    }
+    if (l == 0) p.loss_acc[n] += 0.5f * st.loss;
+}
+
+// codes_t (N x ldt) -> codes (K x N view with strides); W_hat = s (c - z) in the weight dtype; losses copy.
+template <bool BF16>
+__global__ __launch_bounds__(256) void finalize_kernel(const uint8_t* codes_t, int64_t ldt, int64_t K, int64_t N,
+                                                      uint8_t* codes, int64_t c_rs, int64_t c_cs, void* W_hat,
+                                                      int64_t w_rs, int64_t w_cs, const float* scales, int bits) {
+    __shared__ uint8_t tile[64][65];
+    const int tid = threadIdx.x;
+    const int64_t k0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+    for (int i = 0; i < 16; ++i) {
+        const int idx = tid + 256 * i;
+        const int nn = idx >> 6, kk = idx & 63;
+        const int64_t k = k0 + kk, n = n0 + nn;
+        tile[kk][nn] = (k < K && n < N) ? codes_t[n * ldt + k] : (uint8_t)0;
+    }
+    __syncthreads();
+    const bool n_fast_c = (c_cs == 1) || (c_rs != 1 && c_cs <= c_rs);
+    const bool n_fast_w = (w_cs == 1) || (w_rs != 1 && w_cs <= w_rs);
+    const float z = (float)(1 << (bits - 1));
+    for (int i = 0; i < 16; ++i) {
+        const int idx = tid + 256 * i;
+        const int a = idx >> 6, b = idx & 63;
+        {
+            const int kk = n_fast_c ? a : b, nn = n_fast_c ? b : a;
+            const int64_t k = k0 + kk, n = n0 + nn;
+            if (k < K && n < N) codes[k * c_rs + n * c_cs] = tile[kk][nn];
+        }
+        if (W_hat) {
+            const int kk = n_fast_w ? a : b, nn = n_fast_w ? b : a;
+            const int64_t k = k0 + kk, n = n0 + nn;
+            if (k < K && n < N) {
+                const float v = ((float)tile[kk][nn] - z) * scales[n];
+                if (BF16) static_cast<__bf16*>(W_hat)[k * w_rs + n * w_cs] = (__bf16)v;
+                else static_cast<float*>(W_hat)[k * w_rs + n * w_cs] = v;
+            }
+        }
+    }
+}
+
+__global__ void copy_losses_kernel(const float* src, float* dst, int64_t N) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < N) dst[i] = src[i];
+}
+
+struct QuantLayout {
+    DevStatus* st;
+    uint32_t* amax;
+    float* rscale;
+    float* loss_acc;
+    float* Wt;
+    uint8_t* codes_t;
+    float* E;
+    float* Wpre;
+    size_t bytes;
+};
+
+QuantLayout carve(void* ws, int64_t K, int64_t N, bool asym) {
+    const int64_t ldt = ceil_div(std::max<int64_t>(K, 1), kB) * kB;
+    Carver c(ws);
+    QuantLayout L;
+    L.st = c.take<DevStatus>(1);
+    L.amax = c.take<uint32_t>((size_t)N);
+    L.rscale = c.take<float>((size_t)N);
+    L.loss_acc = c.take<float>((size_t)N);
+    L.Wt = c.take<float>((size_t)N * ldt);
+    L.codes_t = c.take<uint8_t>((size_t)N * ldt);
+    L.E = c.take<float>((size_t)N * kB);
+    L.Wpre = asym ? c.take<float>((size_t)N * kB) : nullptr;
+    L.bytes = c.bytes();
+    return L;
+}
+
+}  // namespace
+
+size_t quantize_workspace_bytes(int64_t K, int64_t N, bool asym) { return carve(nullptr, K, N, asym).bytes; }
+
+gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t stream) {
+    const bool asym = a.P1 != nullptr;
+    const int64_t K = a.K, N = a.N;
+    const int64_t ldt = ceil_div(std::max<int64_t>(K, 1), kB) * kB;
+    QuantLayout L = carve(workspace, K, N, asym);
+
+    hipLaunchKernelGGL(quant_init_kernel, grid1d(std::max<int64_t>(N, 1), 256), dim3(256), 0, stream, L.st, L.amax,
+                       L.loss_acc, N);
+    GPTQ_LAUNCH_CHECK();
+    {
+        dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(ldt, 64));
+        if (a.w_dtype == GPTQ_DTYPE_BF16)
+            hipLaunchKernelGGL((convert_kernel<true>), grid, dim3(256), 0, stream, a.W, K, N, a.w_rs, a.w_cs, a.dead,
+                               L.Wt, ldt, L.amax, L.st);
+        else
+            hipLaunchKernelGGL((convert_kernel<false>), grid, dim3(256), 0, stream, a.W, K, N, a.w_rs, a.w_cs, a.dead,
+                               L.Wt, ldt, L.amax, L.st);
+        GPTQ_LAUNCH_CHECK();
+    }
+    hipLaunchKernelGGL(scales_kernel, grid1d(N, 256), dim3(256), 0, stream, L.amax, a.scales, L.rscale, N, a.bits,
+                       a.scales_given, L.st);
+    GPTQ_LAUNCH_CHECK();
+
+    for (int64_t b0 = 0; b0 < K; b0 += kB) {
+        const int bs = (int)std::min<int64_t>(kB, K - b0);
+        BlockArgs p;
+        p.Wt = L.Wt; p.ldt = ldt; p.U = a.U; p.P1 = a.P1; p.K = K; p.N = N; p.b0 = b0; p.bs = bs;
+        p.scales = a.scales; p.rscale = L.rscale; p.bits = a.bits; p.codes_t = L.codes_t; p.E = L.E;
+        p.Wpre = L.Wpre; p.loss_acc = L.loss_acc; p.pre_round = a.pre_round; p.st = L.st;
+        dim3 grid((unsigned)ceil_div(N, kChPerWG));
+        if (asym) hipLaunchKernelGGL((quant_block_kernel<true>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((quant_block_kernel<false>), grid, dim3(256), 0, stream, p);
+        GPTQ_LAUNCH_CHECK();
+        const int64_t b1 = b0 + bs;
+        if (b1 < K) {
+            // Lazy batch: Wt[:, b1:] -= E_B U[B, b1:]  (+ Wpre_B P1[B, b1:] for the asymmetric term)
+            GemmArgs g;
+            g.M = N; g.N = K - b1; g.K1 = bs;
+            g.A1 = L.E; g.lda1 = kB;
+            g.B1 = a.U + b0 * K + b1; g.ldb1 = K;
+            if (asym) {
+                g.K2 = bs;
+                g.A2 = L.Wpre; g.lda2 = kB;
+                g.B2 = a.P1 + b0 * K + b1; g.ldb2 = K;
+                g.a2_scale = -1.f;
+            }
+            g.C = L.Wt + b1; g.ldc = ldt;
+            g.alpha = -1.f; g.beta = 1.f;
+            if (gemm_f32(g, 1, stream) != hipSuccess) return GPTQ_ERR_HIP;
+        }
+    }
+    {
+        dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(K, 64));
+        if (a.w_dtype == GPTQ_DTYPE_BF16)
+            hipLaunchKernelGGL((finalize_kernel<true>), grid, dim3(256), 0, stream, L.codes_t, ldt, K, N, a.codes, a.c_rs,
+                               a.c_cs, a.W_hat, a.w_rs, a.w_cs, a.scales, a.bits);
+        else
+            hipLaunchKernelGGL((finalize_kernel<false>), grid, dim3(256), 0, stream, L.codes_t, ldt, K, N, a.codes, a.c_rs,
+                               a.c_cs, a.W_hat, a.w_rs, a.w_cs, a.scales, a.bits);
+        GPTQ_LAUNCH_CHECK();
+    }
+    if (a.losses) {
+        hipLaunchKernelGGL(copy_losses_kernel, grid1d(N, 256), dim3(256), 0, stream, L.loss_acc, a.losses, N);
+        GPTQ_LAUNCH_CHECK();
+    }
+    DevStatus hst;
+    GPTQ_HIP_CHECK(hipMemcpyAsync(&hst, L.st, sizeof(DevStatus), hipMemcpyDeviceToHost, stream));
+    GPTQ_HIP_CHECK(hipStreamSynchronize(stream));
+    if (hst.flags & kDevNonFinite) return GPTQ_ERR_NONFINITE;
+    return GPTQ_OK;
+}
+
+}  // namespace gptq

@@ -1,0 +1,23 @@
+// Host interface of the column loop (see quantize.hip).
+#pragma once
+
+#include "gptq_common.hpp"
+
+namespace gptq {
+
+struct QuantizeArgs {
+    const void* W = nullptr; gptq_dtype_t w_dtype = GPTQ_DTYPE_F32;
+    int64_t K = 0, N = 0, w_rs = 0, w_cs = 0;
+    const float* U = nullptr; const uint8_t* dead = nullptr; const float* P1 = nullptr;
+    int bits = 4;
+    bool scales_given = false;
+    uint8_t* codes = nullptr; int64_t c_rs = 0, c_cs = 0;
+    float* scales = nullptr; void* W_hat = nullptr; float* losses = nullptr; float* pre_round = nullptr;
+};
+
+size_t quantize_workspace_bytes(int64_t K, int64_t N, bool asym);
+
+// Runs the whole loop on `stream` and synchronises it; returns GPTQ_ERR_NONFINITE for rejected inputs.
+gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t stream);
+
+}  // namespace gptq

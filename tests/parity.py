@@ -1,0 +1,61 @@
+"""Comparison helpers of the parity tests (GPU path vs float64 oracle).  Test infrastructure only.
+
+Tolerances (the bar of the parity suite):
+  * H, A: relative Frobenius error <= 1e-4.
+  * codes: identical, except at coordinates where the oracle's pre-rounding value w/s lies within 1e-4 of a
+    rounding midpoint; there both neighbouring codes are correct, and the oracle follows the GPU's choice
+    (it must be one of the two nearest codes) so that the rest of the channel stays comparable.
+  * per-channel losses sum 1/2 E^2 and the layer objective 1/2 tr(D^T H D): relative error <= 1e-3.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle as O
+
+BAND = 1e-4
+H_TOL = 1e-4
+OBJ_TOL = 1e-3
+
+
+def np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().double().numpy()
+
+
+def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def check_codes(gpu: dict, W: np.ndarray, U_ref: np.ndarray, bits: int, dead=None, P1=None, scales=None,
+                H_obj: np.ndarray | None = None, label: str = "") -> dict:
+    """Runs the oracle loop with tie-following and asserts the GPU codes, scales, losses and objective."""
+    codes = gpu["codes"].cpu().numpy().astype(np.int64)
+    s_gpu = gpu["scales"].cpu().numpy()
+    ref = O.quantize_layer(W, U_ref, bits, dead=dead, scales=scales, blocksize=128, P1=P1, tie_codes=codes,
+                           band=BAND)
+    assert np.array_equal(s_gpu, ref["scales"]), f"{label}: scales differ"
+    bad = codes != ref["codes"]
+    n_bad = int(bad.sum())
+    if n_bad:
+        k, n = np.argwhere(bad)[0]
+        v = ref["V"][k, n]
+        raise AssertionError(f"{label}: {n_bad} code mismatches outside the tie band; first at (k={k}, n={n}) "
+                             f"gpu={codes[k, n]} oracle={ref['codes'][k, n]} v={v!r}")
+    info = {"n_inband": ref["n_inband"], "n_adopted": ref["n_adopted"], "ref": ref}
+    if gpu.get("losses") is not None:
+        lg = gpu["losses"].cpu().double().numpy()
+        lr = ref["losses"]
+        err = np.abs(lg - lr) / np.maximum(np.abs(lr), 1e-30)
+        live = lr > 1e-30 * max(1.0, lr.max())
+        assert (err[live] <= OBJ_TOL).all(), f"{label}: loss rel err max {err[live].max():.3e}"
+        info["loss_rel_max"] = float(err[live].max()) if live.any() else 0.0
+    if H_obj is not None:
+        z = 2 ** (bits - 1)
+        W_hat = s_gpu.astype(np.float64)[None, :] * (codes - z)
+        Jg = O.layer_objective(H_obj, W, W_hat)
+        Jr = O.layer_objective(H_obj, W, ref["Q"])
+        assert abs(Jg - Jr) <= OBJ_TOL * abs(Jr), f"{label}: objective {Jg} vs {Jr}"
+        info["J_gpu"], info["J_ref"] = Jg, Jr
+    return info

@@ -1,0 +1,299 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle, on seeded synthetic layers.
+
+Sizes span several 128/256 tiles and ragged tails; edge cases: M = 0, K = 1, dead coordinates, not-PD and
+non-finite inputs, the fixed teaching grid of the tutorial's worked examples, both weight layouts.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+from tests.parity import BAND, H_TOL, check_codes, np64, rel_fro
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import post_weight_quantization_09_amd as pkg
+    pkg.load()
+    return pkg
+
+
+def _bf16_layer(K, N, M, seed=0, base="c2_q_proj_8b", **kw):
+    # the rotated recipe needs a power-of-two K; other sizes use the same recipe unrotated
+    kw.setdefault("hadamard", workloads.CONFIGS[base].hadamard and K & (K - 1) == 0)
+    cfg = workloads.CONFIGS[base].scaled(K=K, N=N, M=M, **kw)
+    return cfg, workloads.make_layer(cfg, device="cpu", seed=seed)
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------------------------------------ Gram
+@pytest.mark.parametrize("K,M", [(256, 4096), (300, 1000), (520, 8200), (64, 0), (1, 33), (1024, 2048)])
+def test_gram_bf16(g, K, M):
+    cfg, L = _bf16_layer(K, 8, M)
+    X = L["X"].to(DEV)
+    H = torch.zeros(K, K, device=DEV)
+    half = M // 2
+    g.gptq_accumulate_hessian(H, X[:half])
+    g.gptq_accumulate_hessian(H, X[half:])
+    ref = O.gram([L["X"].float().numpy()], K=K)
+    if M == 0:
+        assert torch.count_nonzero(H) == 0
+        return
+    err = rel_fro(np64(H), ref)
+    _print(f"gram bf16 K={K} M={M} rel={err:.3e}")
+    assert err <= H_TOL
+    Hn = np64(H)
+    assert np.array_equal(Hn, Hn.T)
+
+
+def test_gram_f32(g):
+    cfg = workloads.CONFIGS["c1_512"]
+    L = workloads.make_layer(cfg, device="cpu")
+    H = torch.zeros(cfg.K, cfg.K, device=DEV)
+    g.gptq_accumulate_hessian(H, L["X"].to(DEV))
+    err = rel_fro(np64(H), O.gram([L["X"].numpy()]))
+    _print(f"gram f32 c1 rel={err:.3e}")
+    assert err <= H_TOL
+
+
+def test_gram_row_scaled(g):
+    cfg, L = _bf16_layer(300, 8, 3000, base="c3_down_proj_8b_g4", groups=4)
+    rho = L["rho"]
+    H = torch.zeros(cfg.K, cfg.K, device=DEV)
+    g.gptq_accumulate_hessian(H, L["X"].to(DEV), row_scale=rho[1].to(DEV).contiguous())
+    ref = O.gram_row_scaled(L["X"].float().numpy(), rho[1].numpy())
+    err = rel_fro(np64(H), ref)
+    _print(f"gram row-scaled rel={err:.3e}")
+    assert err <= H_TOL
+
+
+def test_gram_cross(g):
+    cfg, L = _bf16_layer(300, 8, 2500, base="c4_up_proj_8b_gptaq")
+    X, Xf = L["X"].to(DEV), L["X_float"].to(DEV)
+    H = torch.zeros(cfg.K, cfg.K, device=DEV)
+    A = torch.zeros(cfg.K, cfg.K, device=DEV)
+    g.gptq_accumulate_hessian(H, X, X_float=Xf, A=A)
+    eh = rel_fro(np64(H), O.gram([L["X"].float().numpy()]))
+    ea = rel_fro(np64(A), O.cross_gram(L["X_float"].float().numpy(), L["X"].float().numpy()))
+    _print(f"gram cross: H rel={eh:.3e} A rel={ea:.3e}")
+    assert eh <= H_TOL and ea <= H_TOL
+
+
+def test_gram_deterministic(g):
+    cfg, L = _bf16_layer(512, 8, 20000)
+    X = L["X"].to(DEV)
+    H1 = torch.zeros(512, 512, device=DEV)
+    H2 = torch.zeros(512, 512, device=DEV)
+    g.gptq_accumulate_hessian(H1, X)
+    g.gptq_accumulate_hessian(H2, X)
+    assert torch.equal(H1, H2)
+
+
+# ------------------------------------------------------------------------------------------------ prepare
+def _workload_H(K, M=None, seed=0, dead_cols=()):
+    cfg, L = _bf16_layer(K, 8, M or max(4 * K, 2048), seed=seed)
+    X = L["X"].float().numpy()
+    if dead_cols:
+        X[:, list(dead_cols)] = 0.0
+    return O.gram([X]).astype(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 127, 128, 129, 300, 1024])
+def test_prepare(g, K):
+    dead_cols = [k for k in (0, 5, K - 1) if k < K and K > 3]
+    H = _workload_H(K, seed=K, dead_cols=dead_cols)
+    Ht = torch.tensor(H, dtype=torch.float32, device=DEV)
+    dead, damp, n_dead = g.gptq_prepare(Ht, 0.01)
+    ref = O.prepare(H, 0.01)
+    U = np64(Ht)
+    assert np.array_equal(dead.cpu().numpy().astype(bool), ref["dead"])
+    assert n_dead == int(ref["dead"].sum())
+    assert abs(damp - ref["damp"]) <= 1e-6 * ref["damp"]
+    assert np.count_nonzero(np.tril(U, -1)) == 0
+    err = np.abs(U - ref["U"]).max() / np.abs(ref["U"]).max()
+    _print(f"prepare K={K} U max rel err={err:.3e}")
+    assert err <= 1e-4
+
+
+def test_prepare_errors(g):
+    H = torch.tensor([[1.0, 2.0], [2.0, 1.0]], device=DEV)
+    with pytest.raises(g.GptqError) as e:
+        g.gptq_prepare(H, 0.01)
+    assert e.value.status == g.GPTQ_ERR_NOT_PD
+    H = torch.tensor([[1.0, 0.0], [0.0, float("nan")]], device=DEV)
+    with pytest.raises(g.GptqError) as e:
+        g.gptq_prepare(H, 0.01)
+    assert e.value.status == g.GPTQ_ERR_NONFINITE
+
+
+# ------------------------------------------------------------------------------------------------ page examples
+def test_page_examples_on_gpu(g, golden_dir):
+    for name, want in (("two_weight_example.json", None), ("three_weight_counterexample.json", None)):
+        with open(os.path.join(golden_dir, name)) as f:
+            ex = json.load(f)
+        H = torch.tensor(ex["H"], dtype=torch.float32, device=DEV)
+        g.gptq_prepare(H, 0.0)
+        if "U" in ex:
+            np.testing.assert_allclose(np64(H), ex["U"], atol=1e-6)
+        W = torch.tensor(ex["w"], dtype=torch.float32, device=DEV)[:, None].contiguous()
+        out = g.gptq_quantize_layer(W, H, 4, scales=torch.ones(1, device=DEV))
+        q = out["codes"].cpu().numpy()[:, 0].astype(int) - 8
+        assert list(q) == [int(v) for v in ex["quantized"]], (name, q)
+
+
+# ------------------------------------------------------------------------------------------------ column loop
+@pytest.mark.parametrize("K,N,bits,layout,wdt", [
+    (256, 96, 4, "KN", "bf16"), (300, 77, 3, "KN", "bf16"), (640, 130, 2, "NK", "bf16"),
+    (512, 512, 4, "KN", "f32"), (129, 33, 8, "NK", "f32"), (1, 5, 4, "KN", "f32")])
+def test_quantize_stage(g, K, N, bits, layout, wdt):
+    H = _workload_H(K, seed=K + N)
+    ref = O.prepare(H, 0.01)
+    U32 = np.ascontiguousarray(ref["U"], dtype=np.float32)
+    rng = np.random.default_rng(K * N)
+    W = (rng.normal(0, 0.02, size=(K, N))).astype(np.float32)
+    tw = torch.tensor(W)
+    if wdt == "bf16":
+        tw = tw.to(torch.bfloat16)
+        W = tw.float().numpy()
+    if layout == "KN":
+        Wd = tw.to(DEV)
+    else:
+        Wd = tw.t().contiguous().to(DEV).t()      # N x K storage viewed as K x N
+    losses = torch.empty(N, device=DEV)
+    W_hat = torch.empty_like(Wd)
+    pre = torch.empty(K, N, device=DEV)
+    out = g.gptq_quantize_layer(Wd, torch.tensor(U32, device=DEV), bits, losses=losses, W_hat=W_hat, pre_round=pre)
+    info = check_codes(out, W, U32.astype(np.float64), bits, H_obj=H, label=f"K={K} N={N} b={bits}")
+    codes = out["codes"].cpu().numpy()
+    s = out["scales"].cpu().numpy()
+    deq = torch.tensor(O.dequantize_fp32(codes, s, bits))
+    if wdt == "bf16":
+        deq = deq.to(torch.bfloat16)
+    assert torch.equal(W_hat.cpu(), deq)
+    drift = np.abs(pre.cpu().double().numpy() - info["ref"]["V"]).max()
+    _print(f"quantize K={K} N={N} bits={bits} {layout}/{wdt}: inband={info['n_inband']} adopted={info['n_adopted']}"
+           f" loss_rel={info.get('loss_rel_max', 0):.2e} pre_round drift={drift:.2e}")
+    assert drift < BAND
+
+
+def test_quantize_dead_rows(g):
+    K, N = 300, 40
+    H = _workload_H(K, seed=3, dead_cols=(7, 128, 299))
+    Ht = torch.tensor(H, dtype=torch.float32, device=DEV)
+    dead, damp, n_dead = g.gptq_prepare(Ht, 0.01)
+    assert n_dead == 3
+    W = np.random.default_rng(4).normal(0, 0.02, size=(K, N)).astype(np.float32)
+    out = g.gptq_quantize_layer(torch.tensor(W, device=DEV), Ht, 4, dead=dead, losses=torch.empty(N, device=DEV))
+    ref = O.prepare(H, 0.01)
+    check_codes(out, W, ref["U"], 4, dead=ref["dead"], H_obj=H, label="dead")
+    assert (out["codes"].cpu().numpy()[[7, 128, 299]] == 8).all()
+
+
+def test_quantize_rejects_nonfinite_weight(g):
+    W = torch.zeros(64, 8, device=DEV)
+    W[3, 2] = float("inf")
+    U = torch.eye(64, device=DEV)
+    with pytest.raises(g.GptqError) as e:
+        g.gptq_quantize_layer(W, U, 4)
+    assert e.value.status == g.GPTQ_ERR_NONFINITE
+
+
+# ------------------------------------------------------------------------------------------------ asymmetric
+def test_asym_correction_parity(g):
+    cfg, L = _bf16_layer(384, 8, 4096, base="c4_up_proj_8b_gptaq")
+    X, Xf = L["X"].float().numpy(), L["X_float"].float().numpy()
+    H = O.gram([X]).astype(np.float32).astype(np.float64)
+    A = O.cross_gram(Xf, X).astype(np.float32).astype(np.float64)
+    U = np.ascontiguousarray(O.prepare(H, 0.01)["U"], dtype=np.float32).astype(np.float64)
+    P_ref = O.asym_correction(U, A)
+    P = g.gptq_asym_correction(torch.tensor(U, dtype=torch.float32, device=DEV),
+                               torch.tensor(A, dtype=torch.float32, device=DEV))
+    err = rel_fro(np64(P), P_ref)
+    _print(f"P1 rel fro err={err:.3e}")
+    assert err <= 1e-4
+    assert np.count_nonzero(np.tril(np64(P))) == 0
+
+
+# ------------------------------------------------------------------------------------------------ end to end
+def _pipeline(g, X, W, bits, percdamp=0.01, row_scale=None, X_float=None):
+    K = X.shape[1]
+    H = torch.zeros(K, K, device=DEV)
+    A = torch.zeros(K, K, device=DEV) if X_float is not None else None
+    g.gptq_accumulate_hessian(H, X, row_scale=row_scale, X_float=X_float, A=A)
+    dead, damp, n_dead = g.gptq_prepare(H, percdamp)
+    P1 = g.gptq_asym_correction(H, A) if A is not None else None
+    losses = torch.empty(W.shape[1], device=DEV)
+    out = g.gptq_quantize_layer(W, H, bits, dead=dead, P1=P1, losses=losses)
+    return out
+
+
+def test_end_to_end_c1(g):
+    cfg = workloads.CONFIGS["c1_512"]
+    L = workloads.make_layer(cfg, device="cpu")
+    out = _pipeline(g, L["X"].to(DEV), L["W"].to(DEV), cfg.bits)
+    H = O.gram([L["X"].numpy()])
+    ref = O.prepare(H, cfg.percdamp)
+    info = check_codes(out, L["W"].numpy(), ref["U"], cfg.bits, dead=ref["dead"], H_obj=H, label="c1")
+    _print(f"c1 end-to-end: inband={info['n_inband']} adopted={info['n_adopted']} J={info['J_gpu']:.6e}/"
+           f"{info['J_ref']:.6e}")
+
+
+@pytest.mark.parametrize("K,N,M", [(300, 77, 3000), (768, 256, 6000)])
+def test_end_to_end_bf16(g, K, N, M):
+    cfg, L = _bf16_layer(K, N, M, seed=7, base="c5_down_proj_70b", dead_frac=0.01)
+    out = _pipeline(g, L["X"].to(DEV), L["W"].to(DEV), cfg.bits)
+    H = O.gram([L["X"].float().numpy()])
+    ref = O.prepare(H, cfg.percdamp)
+    info = check_codes(out, L["W"].float().numpy(), ref["U"], cfg.bits, dead=ref["dead"], H_obj=H,
+                       label=f"e2e K={K}")
+    _print(f"e2e bf16 K={K} N={N}: dead={int(ref['dead'].sum())} inband={info['n_inband']} "
+           f"adopted={info['n_adopted']}")
+
+
+def test_end_to_end_groups(g):
+    cfg, L = _bf16_layer(256, 128, 4096, seed=8, base="c3_down_proj_8b_g4")
+    X = L["X"].to(DEV)
+    W = L["W"].to(DEV)
+    Wn = L["W"].float().numpy()
+    gs = cfg.N // cfg.groups
+    for gi in range(cfg.groups):
+        rho = L["rho"][gi]
+        Wg = W[:, gi * gs:(gi + 1) * gs]                    # column slice, row stride N
+        out = _pipeline(g, X, Wg, cfg.bits, row_scale=rho.to(DEV).contiguous())
+        H = O.gram_row_scaled(L["X"].float().numpy(), rho.numpy())
+        ref = O.prepare(H, cfg.percdamp)
+        info = check_codes(out, Wn[:, gi * gs:(gi + 1) * gs], ref["U"], cfg.bits, dead=ref["dead"], H_obj=H,
+                           label=f"group {gi}")
+        _print(f"group {gi}: inband={info['n_inband']} adopted={info['n_adopted']}")
+
+
+def test_end_to_end_gptaq(g):
+    cfg, L = _bf16_layer(256, 192, 4096, seed=9, base="c4_up_proj_8b_gptaq")
+    out = _pipeline(g, L["X"].to(DEV), L["W"].to(DEV), cfg.bits, X_float=L["X_float"].to(DEV))
+    X, Xf = L["X"].float().numpy(), L["X_float"].float().numpy()
+    H = O.gram([X])
+    ref = O.prepare(H, cfg.percdamp)
+    P1 = O.asym_correction(ref["U"], O.cross_gram(Xf, X))
+    info = check_codes(out, L["W"].float().numpy(), ref["U"], cfg.bits, dead=ref["dead"], P1=P1, label="gptaq")
+    Wn = L["W"].float().numpy()
+    codes = out["codes"].cpu().numpy().astype(np.int64)
+    s = out["scales"].cpu().numpy().astype(np.float64)
+    Wh = s[None, :] * (codes - 2 ** (cfg.bits - 1))
+    G = O.gram([Xf])
+    A = O.cross_gram(Xf, X)
+    Jg = O.asym_objective(H, A, G, Wn, Wh)
+    Jr = O.asym_objective(H, A, G, Wn, info["ref"]["Q"])
+    _print(f"gptaq: inband={info['n_inband']} adopted={info['n_adopted']} J_asym={Jg:.6e}/{Jr:.6e}")
+    assert abs(Jg - Jr) <= 1e-3 * abs(Jr)
