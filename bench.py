@@ -1,0 +1,247 @@
+"""Layer-quantisation benchmark on one MI355X.
+
+One step = the whole hot path for one K x N linear layer with its calibration activations already resident
+in HBM:  H = 0;  H += 2 X^T X over all M tokens (gptq_accumulate_hessian);  dead/damp + U (gptq_prepare);
+[GPTAQ: P1 (gptq_asym_correction)];  shared-order column loop with lazy trailing GEMMs (gptq_quantize_layer).
+Output groups (G2PTQ-style workloads) repeat Gram/prepare/quantize per group.
+
+Prints one JSON line: layer time (ms, lower is better) plus the Gram's MFMA roofline fraction and the float64
+oracle timed on a bounded sample of the same workload on the host cores.
+
+    python bench.py [--gpus 1] [--steps 3] [--warmup 1] [--config c2_q_proj_8b] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import post_weight_quantization_09_amd as G  # noqa: E402
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gram_flops(cfg) -> float:
+    """Algorithmic work of one Gram launch: the upper triangle incl. diagonal, M multiply-adds each."""
+    per = float(cfg.M) * cfg.K * (cfg.K + 1)
+    if cfg.asym_noise > 0:
+        per += 2.0 * cfg.M * cfg.K * cfg.K          # the cross term is a full K x K product
+    return per
+
+
+def trailing_flops(cfg) -> float:
+    """Lazy-batch GEMMs of the column loop: N * K * (K - B) multiply-adds x2 (x2 again with the P1 term)."""
+    n = cfg.N
+    f = 0.0
+    for b0 in range(0, cfg.K, cfg.blocksize):
+        b1 = min(b0 + cfg.blocksize, cfg.K)
+        f += 2.0 * n * (b1 - b0) * (cfg.K - b1)
+    return f * (2 if cfg.asym_noise > 0 else 1)
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "post_weight_quantization_09_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, src_hash: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if taken on the current source."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_hash") != src_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+class Layer:
+    def __init__(self, cfg, dev):
+        self.cfg, self.dev = cfg, dev
+        t0 = time.time()
+        self.W = workloads.make_weights(cfg, device=dev)
+        self.X = torch.empty(cfg.M, cfg.K, dtype=cfg.torch_x_dtype, device=dev)
+        self.Xf = torch.empty_like(self.X) if cfg.asym_noise > 0 else None
+        workloads.ActivationSource(cfg, dev).fill(self.X, self.Xf)
+        self.rho = workloads.make_group_row_weights(cfg, device=dev)
+        torch.cuda.synchronize()
+        log(f"generated {cfg.name}: X {tuple(self.X.shape)} {self.X.dtype} in {time.time() - t0:.1f}s")
+        K, N, M = cfg.K, cfg.N, cfg.M
+        self.H = torch.empty(K, K, dtype=torch.float32, device=dev)
+        self.A = torch.empty(K, K, dtype=torch.float32, device=dev) if self.Xf is not None else None
+        self.P1 = torch.empty(K, K, dtype=torch.float32, device=dev) if self.Xf is not None else None
+        self.dead = torch.empty(K, dtype=torch.uint8, device=dev)
+        gs = N // cfg.groups
+        self.gs = gs
+        self.codes = torch.empty(K, N, dtype=torch.uint8, device=dev)
+        self.scales = torch.empty(N, dtype=torch.float32, device=dev)
+        self.losses = torch.empty(N, dtype=torch.float32, device=dev)
+        flags = 1 if self.Xf is not None else 0
+        ws = max(G.gptq_workspace_bytes(G.GPTQ_CALL_ACCUMULATE_HESSIAN, K, 0, M, flags),
+                 G.gptq_workspace_bytes(G.GPTQ_CALL_PREPARE, K),
+                 G.gptq_workspace_bytes(G.GPTQ_CALL_ASYM_CORRECTION, K),
+                 G.gptq_workspace_bytes(G.GPTQ_CALL_QUANTIZE_LAYER, K, gs, 0, 2 if self.Xf is not None else 0))
+        self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.ev = []
+
+    def step(self, record: bool):
+        """One pass of the hot path; with record=True returns per-stage HIP events (current stream)."""
+        cfg = self.cfg
+        evs = []
+
+        def mark():
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                evs.append(e)
+
+        for gi in range(cfg.groups):
+            self.H.zero_()
+            if self.A is not None:
+                self.A.zero_()
+            rs = self.rho[gi].contiguous() if self.rho is not None else None
+            mark()
+            G.gptq_accumulate_hessian(self.H, self.X, row_scale=rs, X_float=self.Xf, A=self.A, workspace=self.ws)
+            mark()
+            self.dead, self.damp, self.n_dead = G.gptq_prepare(self.H, cfg.percdamp, dead=self.dead,
+                                                               workspace=self.ws)
+            P1 = None
+            if self.A is not None:
+                P1 = G.gptq_asym_correction(self.H, self.A, self.P1, workspace=self.ws)
+            mark()
+            sl = slice(gi * self.gs, (gi + 1) * self.gs)
+            G.gptq_quantize_layer(self.W[:, sl], self.H, cfg.bits, dead=self.dead, P1=P1, blocksize=cfg.blocksize,
+                                  scales=None, codes=self.codes[:, sl], losses=None, workspace=self.ws)
+            mark()
+        return evs
+
+
+def cpu_baseline(layer: Layer, budget_s: float = 20.0) -> dict:
+    """The float64 oracle on a bounded sample of the same workload, projected to the full layer."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    cfg = layer.cfg
+    cores = len(os.sched_getaffinity(0))
+    Ms = min(cfg.M, 8192 if cfg.K > 8192 else 16384)
+    Xs = layer.X[:Ms].float().cpu().numpy()
+    t0 = time.perf_counter()
+    H = O.gram([Xs])
+    if layer.Xf is not None:
+        O.cross_gram(layer.Xf[:Ms].float().cpu().numpy(), Xs)
+    t_gram = (time.perf_counter() - t0) * (cfg.M / Ms)
+    t0 = time.perf_counter()
+    prep = O.prepare(H, cfg.percdamp)
+    t_prep = time.perf_counter() - t0
+    Ns = min(layer.gs, 128)
+    Wsub = layer.W[:, :Ns].float().cpu().numpy()
+    t0 = time.perf_counter()
+    O.quantize_layer(Wsub, prep["U"], cfg.bits, dead=prep["dead"], blocksize=cfg.blocksize)
+    t_loop = (time.perf_counter() - t0) * (layer.gs / Ns)
+    per_group = t_gram + t_prep + t_loop
+    total_ms = 1e3 * per_group * cfg.groups
+    return {"value": round(total_ms, 1), "unit": "ms", "cores": int(min(cores, threads or cores)), "kind": "oracle",
+            "sample": f"float64 numpy/BLAS oracle: Gram on {Ms} of {cfg.M} tokens (scaled x{cfg.M / Ms:.0f}), full "
+                      f"{cfg.K}x{cfg.K} prepare, blocked loop on {Ns} of {layer.gs} channels (scaled); "
+                      f"stage seconds gram={t_gram:.1f} prepare={t_prep:.1f} loop={t_loop:.1f} per group",
+            "host_cores_visible": cores}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", default="c2_q_proj_8b", choices=sorted(workloads.CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer path is single-GPU here",
+              file=sys.stderr)
+        sys.exit(2)
+    cfg = workloads.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    G.load()
+    layer = Layer(cfg, dev)
+    for i in range(args.warmup):
+        layer.step(record=False)
+        log(f"warmup step {i} done")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    stage = {"gram": 0.0, "prepare": 0.0, "quantize": 0.0}
+    ev_all = []
+    for i in range(args.steps):
+        ev_all.append(layer.step(record=True))
+        log(f"timed step {i} enqueued/done")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for evs in ev_all:
+        for gi in range(cfg.groups):
+            e = evs[4 * gi: 4 * gi + 4]
+            stage["gram"] += e[0].elapsed_time(e[1])
+            stage["prepare"] += e[1].elapsed_time(e[2])
+            stage["quantize"] += e[2].elapsed_time(e[3])
+    for k in stage:
+        stage[k] /= args.steps
+    ms = 1e3 * wall / args.steps
+    gflop = gram_flops(cfg) * cfg.groups
+    gram_launch_ms = stage["gram"] / cfg.groups
+    achieved = gram_flops(cfg) / (gram_launch_ms * 1e-3) / 1e12
+    src = source_hash("gram.hip")
+    traffic = measured_traffic("gram_bf16", src)
+    out = {
+        "metric": "layer quantize time (ms) + Gram/trailing TFLOP/s vs MFMA peak, KxN layer",
+        "value": round(ms, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 MFMA Gram (fp32 accumulate) + fp32 factor/loop",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "K": cfg.K, "N": cfg.N, "M": cfg.M, "x_dtype": cfg.x_dtype,
+                   "w_dtype": cfg.w_dtype, "bits": cfg.bits, "blocksize": cfg.blocksize, "percdamp": cfg.percdamp,
+                   "groups": cfg.groups, "hadamard": cfg.hadamard, "asymmetric": cfg.asym_noise > 0,
+                   "dead_frac": cfg.dead_frac},
+        "stages_ms": {k: round(v, 3) for k, v in stage.items()},
+        "gram_tflops": round(gflop / (stage["gram"] * 1e-3) / 1e12, 1),
+        "trailing_gemm_gflop": round(trailing_flops(cfg) * 1e-9, 1),
+        "roofline": {"bound": "mfma", "kernel": "gram_bf16_kernel + gram_reduce_kernel (one accumulate call)",
+                     "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_flop_per_launch": gram_flops(cfg), "launch_ms": round(gram_launch_ms, 3)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(layer)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
