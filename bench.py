@@ -177,6 +177,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="c2_q_proj_8b", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["gram", "copy"], default=None,
+                    help="profiling aids: run only the Gram launch per step, or a 1 GiB device copy (the "
+                         "reference for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer path is single-GPU here",
@@ -185,7 +188,23 @@ def main():
     cfg = workloads.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     G.load()
+    if args.only == "copy":
+        a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(args.warmup + args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": a.numel() * 4, "copy_bytes_written": b.numel() * 4,
+                          "launches": args.warmup + args.steps}), flush=True)
+        return
     layer = Layer(cfg, dev)
+    if args.only == "gram":
+        for i in range(args.warmup + args.steps):
+            layer.H.zero_()
+            G.gptq_accumulate_hessian(layer.H, layer.X, workspace=layer.ws)
+        torch.cuda.synchronize()
+        log(f"gram-only: {args.warmup + args.steps} launches")
+        return
     for i in range(args.warmup):
         layer.step(record=False)
         log(f"warmup step {i} done")

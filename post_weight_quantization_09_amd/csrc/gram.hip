@@ -7,13 +7,14 @@
 //
 // Design (256 threads, 4 waves, one 256 x 256 output tile per workgroup, 128 x 128 per wave):
 //   * X is row-major (tokens x features), so both MFMA operands have the reduction index (tokens) as the
-//     slow dimension.  A 32-token x 256-column slab of each operand is staged in LDS in its natural row
-//     layout with 16-byte global loads (coalesced: 32 lanes read one 512-byte token row).
-//   * Each lane reads 8 token rows x 4 columns (ds_read_b64) and transposes them in registers with
-//     v_perm_b32 into four 8-token operand vectors, one per column.  Lane l of MFMA "a" then holds column
-//     4*(l%32)+a over tokens 8*(l/32)..+7; A and B use the same token <-> (lane group, slot) map, so each
-//     v_mfma_f32_32x32x16_bf16 sums over the same 16 tokens on both sides.  The column permutation is
-//     undone when the result is written.
+//     slow dimension.  32-token x 256-column slabs of the two operands are staged in LDS in their natural
+//     row layout (16-byte chunks XOR-swizzled by 4 * (row % 4) so that the reads below are bank-conflict
+//     free).
+//   * Operands are read with ds_read_b64_tr_b16: within each 16-lane group, output lane j, element e comes
+//     from input lane 4 e + j / 4, element j % 4.  Letting input lane i address token row T0 + i / 4 and
+//     columns C0 + 4 (i % 4) .. +3 gives output lane j column C0 + j over tokens T0 .. T0+3, i.e. an MFMA
+//     operand fragment with no register shuffles; two such reads give the 8 tokens of a
+//     v_mfma_f32_32x32x16_bf16 lane.  A and B use the same token <-> (lane half, slot) map.
 //   * Only tiles on or above the diagonal are computed (H is symmetric); the cross term computes all.
 //   * The token range is split across workgroups when there are too few tiles to fill 256 CUs.  Splits are
 //     assigned XCD by XCD (workgroup id mod 8) so that the workgroups sharing an XCD's L2 stream the same
@@ -70,19 +71,117 @@ __device__ inline u32x4 diff_bf16(u32x4 xf, u32x4 x) {
     return o;
 }
 
-// 8 rows (tokens) x 4 bf16 columns -> 4 column vectors of 8 tokens.
-__device__ inline void transpose8x4(const u32x2 (&raw)[8], u32x4 (&out)[4]) {
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+#ifndef GPTQ_GRAM_TR
+#define GPTQ_GRAM_TR 0          // operand fragments by transposing LDS reads (else b64 reads + v_perm)
+#endif
+#ifndef GPTQ_GRAM_SWIZZLE
+#define GPTQ_GRAM_SWIZZLE GPTQ_GRAM_TR
+#endif
+#ifndef GPTQ_GRAM_RING
+#define GPTQ_GRAM_RING 4        // LDS ring slots of the direct-to-LDS kernel (32 KB each)
+#endif
+#ifndef GPTQ_GRAM_DMA
+#define GPTQ_GRAM_DMA 1         // plain bf16 Gram through the direct-to-LDS kernel when the layout allows
+#endif
+#ifndef GPTQ_GRAM_MAP
+#define GPTQ_GRAM_MAP 0         // 0: token splits grouped by XCD; 1: split-major (all XCDs on the same tokens)
+#endif
+#ifndef GPTQ_GRAM_INTERLEAVE
+#define GPTQ_GRAM_INTERLEAVE 1
+#endif
+
+// XOR mask applied to the 16-byte chunk index of a slab row.
+__device__ __forceinline__ int chunk_swz(int row) { return GPTQ_GRAM_SWIZZLE ? ((row & 3) << 2) : 0; }
+
+// Physical short offset of (row, col) in a 32 x 256 bf16 slab: 16-byte chunk c of row r is stored at
+// chunk c ^ (4 (r % 4)).
+__device__ __forceinline__ int slab_off(int row, int col) {
+    return row * kGT + (((col >> 3) ^ chunk_swz(row)) << 3) + (col & 7);
+}
+
+// MFMA fragments of one 16-token k-step for 4 x 32 columns starting at column `base` of a slab.
+// Transposing reads: frag[a] holds, for lane l, column base + 32 a + l % 32 over tokens 16 ks + 8 (l / 32)
+// + 0..7.  b64 reads + v_perm: frag[a] holds column base + 4 (l % 32) + a over the same tokens.
+__device__ __forceinline__ void load_frags(const uint16_t* slab, int base, int ks, int lane, u32x4 (&frag)[4]) {
+#if GPTQ_GRAM_TR
+    const int q = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int row = ks * 16 + 8 * (q >> 1) + 4 * h + (i >> 2);
+            const int col = base + 32 * a + 16 * (q & 1) + 4 * (i & 3);
+            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slab + slab_off(row, col)));
+            const u32x2 w = __builtin_bit_cast(u32x2, v);
+            frag[a][2 * h] = w.x;
+            frag[a][2 * h + 1] = w.y;
+        }
+    }
+#else
+    const int g = lane >> 5, r32 = lane & 31;
+    u32x2 raw[8];
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+        const int row = ks * 16 + 8 * g + s8;
+        raw[s8] = *reinterpret_cast<const u32x2*>(slab + slab_off(row, base + 4 * r32));
+    }
+    // 8 token rows x 4 columns -> 4 column vectors of 8 tokens
+#pragma unroll
     for (int s = 0; s < 4; ++s) {
-        const uint32_t lo0 = raw[2 * s].x, lo1 = raw[2 * s + 1].x;   // columns 0,1
-        const uint32_t hi0 = raw[2 * s].y, hi1 = raw[2 * s + 1].y;   // columns 2,3
-        out[0][s] = __builtin_amdgcn_perm(lo1, lo0, 0x05040100u);
-        out[1][s] = __builtin_amdgcn_perm(lo1, lo0, 0x07060302u);
-        out[2][s] = __builtin_amdgcn_perm(hi1, hi0, 0x05040100u);
-        out[3][s] = __builtin_amdgcn_perm(hi1, hi0, 0x07060302u);
+        const uint32_t lo0 = raw[2 * s].x, lo1 = raw[2 * s + 1].x;
+        const uint32_t hi0 = raw[2 * s].y, hi1 = raw[2 * s + 1].y;
+        frag[0][s] = __builtin_amdgcn_perm(lo1, lo0, 0x05040100u);
+        frag[1][s] = __builtin_amdgcn_perm(lo1, lo0, 0x07060302u);
+        frag[2][s] = __builtin_amdgcn_perm(hi1, hi0, 0x05040100u);
+        frag[3][s] = __builtin_amdgcn_perm(hi1, hi0, 0x07060302u);
+    }
+#endif
+}
+
+// (row, col) of accumulator element r of MFMA block (a, b) for `lane` inside a wave's 128 x 128 quadrant.
+__device__ __forceinline__ int acc_row(int a, int r, int lane) {
+    return GPTQ_GRAM_TR ? 32 * a + mfma32_row(r, lane) : 4 * mfma32_row(r, lane) + a;
+}
+__device__ __forceinline__ int acc_col(int b, int lane) { return GPTQ_GRAM_TR ? 32 * b + (lane & 31) : 4 * (lane & 31) + b; }
+
+// Raw global data of one 32-token stage held in registers while it is in flight; the per-token weight and
+// the float-stream mismatch are applied when the stage is written to LDS, so that no arithmetic waits on
+// an outstanding load.
+template <bool CROSS, bool SCALED>
+struct StageRegs {
+    u32x4 a[4], b[4];
+    u32x4 f[CROSS ? 4 : 1];
+    float s[SCALED ? 4 : 1];
+};
+
+// Scheduling hint (gfx9 sched_group_barrier masks): spread the 16 transposing LDS reads of one k-step over
+// the 16 MFMAs of the other, so the matrix core keeps a queue while operands are fetched.
+__device__ __forceinline__ void interleave_kstep() {
+    if (!GPTQ_GRAM_INTERLEAVE) return;
+    if (GPTQ_GRAM_TR) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU (v_perm)
+        }
     }
 }
 
-template <bool CROSS, bool SCALED>
+template <bool CROSS, bool SCALED, bool FAST>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gram_bf16_kernel(GramArgs p) {
     __shared__ __attribute__((aligned(16))) uint16_t sA[2][kGK][kGPitch];
@@ -109,87 +208,219 @@ void gram_bf16_kernel(GramArgs p) {
     const int64_t colA = (int64_t)bi * kGT, colB = (int64_t)bj * kGT;
     const int64_t t0 = (int64_t)split * p.tokens_per_split;
     const int64_t t1 = min<int64_t>(p.M, t0 + p.tokens_per_split);
-    const int64_t nst = t1 > t0 ? ceil_div(t1 - t0, kGK) : 0;
+    // Stage count rounded up to even (the pipeline handles stages in pairs); a padding stage holds only
+    // tokens >= t1, which are written to LDS as zeros.
+    const int64_t nst = t1 > t0 ? (ceil_div(t1 - t0, kGK) + 1) & ~(int64_t)1 : 0;
 
     f32x16 acc[4][4];
     for (int a = 0; a < 4; ++a)
         for (int b = 0; b < 4; ++b)
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    // Prefetch registers: 4 chunks of 16 bytes per side per thread.
-    u32x4 ra[4], rb[4];
-    auto gload = [&](int64_t st) {
+    typedef StageRegs<CROSS, SCALED> Regs;
+    // thread -> (token row, 8-column chunk) of a stage: chunk c = tid + 256 i, row c / 32, chunk c % 32
+    auto ld = [&](const uint16_t* base, int64_t ldb, int64_t tok, int64_t col) -> u32x4 {
+        if (FAST) return *reinterpret_cast<const u32x4*>(base + (tok < t1 ? tok : t1 - 1) * ldb + col);
+        return load8(base, ldb, tok, t1, col, p.K, p.vec);
+    };
+    auto gload = [&](int64_t st, Regs& R) {
         const int64_t tb = t0 + st * kGK;
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = tid + 256 * i;
-            const int tr = c >> 5, cc = c & 31;
-            const int64_t tok = tb + tr;
-            u32x4 x = load8(p.X, p.ldx, tok, t1, colA + cc * 8, p.K, p.vec);
-            if (CROSS) {
-                u32x4 xf = load8(p.Xf, p.ldxf, tok, t1, colA + cc * 8, p.K, p.vec);
-                ra[i] = diff_bf16(xf, x);
-                rb[i] = load8(p.X, p.ldx, tok, t1, colB + cc * 8, p.K, p.vec);
-            } else {
-                if (SCALED) {
-                    const float s = tok < t1 ? p.rho[tok] : 0.f;
-                    x = scale_row_bf16(x, s);
-                }
-                ra[i] = x;
-                u32x4 y = load8(p.X, p.ldx, tok, t1, colB + cc * 8, p.K, p.vec);
-                if (SCALED) {
-                    const float s = tok < t1 ? p.rho[tok] : 0.f;
-                    y = scale_row_bf16(y, s);
-                }
-                rb[i] = y;
-            }
+            const int64_t tok = tb + (c >> 5);
+            const int64_t col = (c & 31) * 8;
+            R.a[i] = ld(p.X, p.ldx, tok, colA + col);
+            R.b[i] = ld(p.X, p.ldx, tok, colB + col);
+            if constexpr (CROSS) R.f[i] = ld(p.Xf, p.ldxf, tok, colA + col);
+            if constexpr (SCALED) R.s[i] = p.rho[tok < t1 ? tok : t1 - 1];
         }
     };
-    auto lstore = [&](int buf) {
+    auto lstore = [&](int64_t st, const Regs& R, int buf) {
+        const int64_t tb = t0 + st * kGK;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = tid + 256 * i;
             const int tr = c >> 5, cc = c & 31;
-            *reinterpret_cast<u32x4*>(&sA[buf][tr][cc * 8]) = ra[i];
-            *reinterpret_cast<u32x4*>(&sB[buf][tr][cc * 8]) = rb[i];
+            const bool ok = tb + tr < t1;
+            u32x4 va = R.a[i], vb = R.b[i];
+            if constexpr (CROSS) va = diff_bf16(R.f[i], R.a[i]);
+            if constexpr (SCALED) {
+                va = scale_row_bf16(va, R.s[i]);
+                vb = scale_row_bf16(vb, R.s[i]);
+            }
+            *reinterpret_cast<u32x4*>(&sA[buf][0][0] + slab_off(tr, cc * 8)) = ok ? va : zero;
+            *reinterpret_cast<u32x4*>(&sB[buf][0][0] + slab_off(tr, cc * 8)) = ok ? vb : zero;
+        }
+    };
+    auto prep = [&](int buf, int ks, u32x4 (&va)[4], u32x4 (&vb)[4]) {
+        load_frags(&sA[buf][0][0], wi * 128, ks, lane, va);
+        load_frags(&sB[buf][0][0], wj * 128, ks, lane, vb);
+    };
+    auto mfma = [&](const u32x4 (&va)[4], const u32x4 (&vb)[4]) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const bf16x8 av = __builtin_bit_cast(bf16x8, va[a]);
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, vb[b]), acc[a][b],
+                                                                   0, 0, 0);
         }
     };
 
-    if (nst > 0) {
-        gload(0);
-        lstore(0);
-    }
+    // Software pipeline over stages st (LDS buffer st & 1):
+    //   stage s is read from global at iteration s-3, written to LDS at iteration s-1;
+    //   iteration st: [MFMA (st, k0) || LDS reads of (st, k1)]  [LDS write of st+1; loads of st+3]  barrier
+    //                 [MFMA (st, k1) || LDS reads of (st+1, k0)]
+    Regs R0, R1;
+    u32x4 k0a[4], k0b[4], k1a[4], k1b[4];
+    if (nst > 0) gload(0, R0);
+    if (nst > 1) gload(1, R1);
+    if (nst > 0) lstore(0, R0, 0);
+    if (nst > 2) gload(2, R0);
     __syncthreads();
-    const int g = lane >> 5, r32 = lane & 31;
-    for (int64_t st = 0; st < nst; ++st) {
+    if (nst > 0) prep(0, 0, k0a, k0b);
+
+    auto body = [&](int64_t st, Regs& Rn) {
         const int buf = (int)(st & 1);
-        if (st + 1 < nst) gload(st + 1);
-        {
-            const uint16_t(*pA)[kGPitch] = sA[buf];
-            const uint16_t(*pB)[kGPitch] = sB[buf];
-#pragma unroll
-            for (int ks = 0; ks < kGK / 16; ++ks) {
-                u32x2 rawA[8], rawB[8];
-                const int trow = ks * 16 + 8 * g;
-#pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    rawA[s] = *reinterpret_cast<const u32x2*>(&pA[trow + s][wi * 128 + 4 * r32]);
-                    rawB[s] = *reinterpret_cast<const u32x2*>(&pB[trow + s][wj * 128 + 4 * r32]);
-                }
-                u32x4 va[4], vb[4];
-                transpose8x4(rawA, va);
-                transpose8x4(rawB, vb);
-#pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const bf16x8 av = __builtin_bit_cast(bf16x8, va[a]);
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) {
-                        const bf16x8 bv = __builtin_bit_cast(bf16x8, vb[b]);
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[a][b], 0, 0, 0);
-                    }
-                }
-            }
-        }
-        if (st + 1 < nst) lstore(buf ^ 1);
+        prep(buf, 1, k1a, k1b);
+        mfma(k0a, k0b);
+        interleave_kstep();
+        if (st + 1 < nst) lstore(st + 1, Rn, buf ^ 1);
+        if (st + 3 < nst) gload(st + 3, Rn);
         __syncthreads();
+        if (st + 1 < nst) prep(buf ^ 1, 0, k0a, k0b);
+        mfma(k1a, k1b);
+        interleave_kstep();
+    };
+#pragma clang loop unroll(disable)
+    for (int64_t st = 0; st < nst; st += 2) {
+        body(st, R1);
+        body(st + 1, R0);
+    }
+
+    if (!active) return;
+    float* out = p.partial + (((int64_t)split * p.ntiles + tile) * 4 + wave) * (256 * 64);
+    for (int a = 0; a < 4; ++a)
+        for (int b = 0; b < 4; ++b)
+            for (int r = 0; r < 16; ++r) out[((a * 4 + b) * 16 + r) * 64 + lane] = acc[a][b][r];
+}
+
+// Plain symmetric Gram, fast layout (K a multiple of 256, 16-byte aligned rows, every split a whole number
+// of 32-token stages): activations go straight from global memory into a 4-stage LDS ring with
+// global_load_lds_dwordx4 (no register staging), so three stages (~100 KB per CU) are in flight while one
+// is consumed.  Wait counts and barriers are explicit: the compiler cannot see that a DMA'd stage belongs
+// to a different ring slot than the one being read and would otherwise drain all loads at every barrier.
+// Per stage st:  [MFMA (st, k-step 0) || LDS reads + v_perm of (st, k-step 1)]
+//                [wait for this wave's loads of st+1; barrier; issue loads of st+3 into the freed slot]
+//                [MFMA (st, k-step 1) || LDS reads + v_perm of (st+1, k-step 0)]
+constexpr int kRing = GPTQ_GRAM_RING;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Wait until at most `later` stages (8 DMA instructions each) of this wave are still in flight, then
+// synchronise the workgroup.
+__device__ __forceinline__ void wait_vm_and_barrier(int later) {
+    if (later >= 3) asm volatile("s_waitcnt vmcnt(24) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (later == 2) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gram_bf16_lds_kernel(GramArgs p) {
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[kRing][2][kGK][kGT];   // 128 KB
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int wi = wave >> 1, wj = wave & 1;
+    int split, tile;
+    const int bid = blockIdx.x;
+    if (GPTQ_GRAM_MAP == 0 && p.splits % 8 == 0) {
+        const int x = bid & 7, q = bid >> 3, per = p.splits / 8;
+        split = x * per + q / p.ntiles;
+        tile = q % p.ntiles;
+    } else {
+        split = bid / p.ntiles;
+        tile = bid % p.ntiles;
+    }
+    int bi, bj;
+    tile_coords(tile, p.nb, false, bi, bj);
+    if (bi >= p.nb || bj >= p.nb || split >= p.splits) return;
+    const bool active = !(bi == bj && wi == 1 && wj == 0);
+    const int64_t t0 = (int64_t)split * p.tokens_per_split;
+    const int64_t t1 = min<int64_t>(p.M, t0 + p.tokens_per_split);
+    const int64_t nst = t1 > t0 ? (t1 - t0) / kGK : 0;       // whole stages (checked on the host)
+
+    f32x16 acc[4][4];
+    for (int a = 0; a < 4; ++a)
+        for (int b = 0; b < 4; ++b)
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    // This wave DMAs token rows 8*wave .. 8*wave+7 of both slabs: 8 instructions of 1 KB (two 512-byte
+    // rows each: lanes 0-31 the first row, lanes 32-63 the second).  Lane l lands in LDS chunk l % 32 of its
+    // row, so it fetches the global chunk that the slab swizzle stores there.
+    // Instruction i covers rows 8 wave + 2 i + (lane / 32), whose row % 4 alternates between two values
+    // with the parity of i, hence two swizzled source chunks per lane.
+    const int lrow = 8 * wave + (lane >> 5);
+    const int gchunk0 = (lane & 31) ^ chunk_swz(lrow);
+    const int gchunk1 = (lane & 31) ^ chunk_swz(lrow + 2);
+    const uint16_t* srcA0 = p.X + (int64_t)bi * kGT + gchunk0 * 8;
+    const uint16_t* srcA1 = p.X + (int64_t)bi * kGT + gchunk1 * 8;
+    const uint16_t* srcB0 = p.X + (int64_t)bj * kGT + gchunk0 * 8;
+    const uint16_t* srcB1 = p.X + (int64_t)bj * kGT + gchunk1 * 8;
+    auto issue = [&](int64_t st) {
+        const int slot = (int)(st % kRing);
+        const int64_t tb = t0 + st * kGK + lrow;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t tok = tb + 2 * i;
+            const uint16_t* sa = (i & 1) ? srcA1 : srcA0;
+            const uint16_t* sb = (i & 1) ? srcB1 : srcB0;
+            __builtin_amdgcn_global_load_lds((const void*)(sa + tok * p.ldx),
+                                             (lds_void_t*)&ring[slot][0][8 * wave + 2 * i][0], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(sb + tok * p.ldx),
+                                             (lds_void_t*)&ring[slot][1][8 * wave + 2 * i][0], 16, 0, 0);
+        }
+    };
+    auto prep = [&](int64_t st, int ks, u32x4 (&va)[4], u32x4 (&vb)[4]) {
+        const int slot = (int)(st % kRing);
+        load_frags(&ring[slot][0][0][0], wi * 128, ks, lane, va);
+        load_frags(&ring[slot][1][0][0], wj * 128, ks, lane, vb);
+    };
+    auto mfma = [&](const u32x4 (&va)[4], const u32x4 (&vb)[4]) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const bf16x8 av = __builtin_bit_cast(bf16x8, va[a]);
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, vb[b]), acc[a][b],
+                                                                   0, 0, 0);
+        }
+    };
+
+    // Stage s is DMA'd kRing-1 stages ahead of its use: issued after the barrier of iteration s-kRing+1,
+    // waited for before the barrier of iteration s-1.
+    u32x4 k0a[4], k0b[4], k1a[4], k1b[4];
+    if (nst > 0) {
+        const int64_t pre = nst < kRing - 1 ? nst : kRing - 1;
+        for (int64_t s0 = 0; s0 < pre; ++s0) issue(s0);
+        wait_vm_and_barrier((int)pre - 1);           // stage 0 landed for every wave
+        prep(0, 0, k0a, k0b);
+    }
+#pragma clang loop unroll(disable)
+    for (int64_t st = 0; st < nst; ++st) {
+        prep(st, 1, k1a, k1b);
+        mfma(k0a, k0b);
+        interleave_kstep();
+        if (st + 1 < nst) {
+            // own loads of st+1 landed (stages st+2 .. st+kRing-2 may be pending); everyone is past st-1
+            const int64_t last = st + kRing - 2 < nst - 1 ? st + kRing - 2 : nst - 1;
+            wait_vm_and_barrier((int)(last - (st + 1)));
+            if (st + kRing - 1 < nst) issue(st + kRing - 1);
+            prep(st + 1, 0, k0a, k0b);
+        }
+        mfma(k1a, k1b);
+        interleave_kstep();
     }
 
     if (!active) return;
@@ -223,8 +454,8 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(GramArgs p, float* Out
         float s = 0.f;
         for (int sp = 0; sp < p.splits; ++sp) s += base[sp * qstride + ri * 64 + lane];
         const int a = ri >> 6, b = (ri >> 4) & 3, r = ri & 15;
-        const int row = 4 * mfma32_row(r, lane) + a;
-        const int col = 4 * (lane & 31) + b;
+        const int row = acc_row(a, r, lane);
+        const int col = acc_col(b, lane);
         T[row][col] = 2.0f * s;
     }
     __syncthreads();
@@ -249,15 +480,21 @@ GramPlan gram_plan(int64_t K, int64_t M, bool cross) {
     pl.cross = cross;
     pl.nb = (int)ceil_div(K, kGT);
     pl.ntiles = cross ? pl.nb * pl.nb : pl.nb * (pl.nb + 1) / 2;
-    // Enough workgroups for ~8 rounds over 256 CUs, with at least 4096 tokens per split.
-    int64_t s = 1;
-    if (pl.ntiles < 2048) {
-        s = ceil_div(2048, pl.ntiles);
-        if (s >= 8) s = ceil_div(s, 8) * 8;
-        const int64_t cap = std::max<int64_t>(1, M / 4096);
-        if (s > cap) s = cap >= 8 ? (cap / 8) * 8 : cap;
+    // One workgroup per CU (256 CUs).  With few tiles the token range is split so that the workgroup
+    // count fills whole rounds of 256: the split count (a multiple of 8, so that splits map to XCDs)
+    // minimising the idle fraction of the last round, keeping >= 8192 tokens per split.
+    int64_t best = 1;
+    if (pl.ntiles < 1024) {
+        double best_eff = -1.0;
+        for (int64_t s = 8; s <= 64; s += 8) {
+            if (s > 8 && M / s < 8192) break;
+            const double wgs = (double)pl.ntiles * s;
+            const double eff = wgs / (ceil_div((int64_t)wgs, 256) * 256.0);
+            if (eff > best_eff + 1e-9) { best_eff = eff; best = s; }
+        }
+        if (M < 8 * 4096) best = std::max<int64_t>(1, std::min<int64_t>(8, M / 4096));
     }
-    pl.splits = (int)std::max<int64_t>(1, s);
+    pl.splits = (int)best;
     pl.tokens_per_split = ceil_div(ceil_div(std::max<int64_t>(M, 1), pl.splits), kGK) * kGK;
     pl.partial_floats = (size_t)pl.splits * pl.ntiles * 4 * 256 * 64;
     return pl;
@@ -275,9 +512,20 @@ hipError_t gram_bf16(const GramPlan& pl, const uint16_t* X, int64_t ldx, const u
     auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
     p.vec = al16(X) && ldx % 8 == 0 && (!cross || (al16(Xf) && ldxf % 8 == 0));
     const unsigned nblk = (unsigned)((int64_t)pl.ntiles * pl.splits);
-    if (cross) hipLaunchKernelGGL((gram_bf16_kernel<true, false>), dim3(nblk), dim3(256), 0, stream, p);
-    else if (rho) hipLaunchKernelGGL((gram_bf16_kernel<false, true>), dim3(nblk), dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((gram_bf16_kernel<false, false>), dim3(nblk), dim3(256), 0, stream, p);
+    // Fast path: whole 256-column tiles and 16-byte aligned rows (no per-element guards in the main loop).
+    const bool fast = p.vec && K % kGT == 0;
+    const bool whole_stages = p.tokens_per_split % kGK == 0 && M % kGK == 0;
+    if (GPTQ_GRAM_DMA && fast && !cross && !rho && whole_stages) {
+        hipLaunchKernelGGL(gram_bf16_lds_kernel, dim3(nblk), dim3(256), 0, stream, p);
+    } else if (fast) {
+        if (cross) hipLaunchKernelGGL((gram_bf16_kernel<true, false, true>), dim3(nblk), dim3(256), 0, stream, p);
+        else if (rho) hipLaunchKernelGGL((gram_bf16_kernel<false, true, true>), dim3(nblk), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((gram_bf16_kernel<false, false, true>), dim3(nblk), dim3(256), 0, stream, p);
+    } else {
+        if (cross) hipLaunchKernelGGL((gram_bf16_kernel<true, false, false>), dim3(nblk), dim3(256), 0, stream, p);
+        else if (rho) hipLaunchKernelGGL((gram_bf16_kernel<false, true, false>), dim3(nblk), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((gram_bf16_kernel<false, false, false>), dim3(nblk), dim3(256), 0, stream, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned nred = (unsigned)(pl.ntiles * 4);
