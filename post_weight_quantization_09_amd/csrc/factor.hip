@@ -67,51 +67,153 @@ __global__ __launch_bounds__(1024) void dead_damp_kernel(float* H, int64_t K, fl
     }
 }
 
-// In place on the n x n diagonal block D (ld): reads its upper triangle (a symmetric block S), factors
-// S = R R^T with R upper, and writes U22 = R^{-1} (upper, strictly lower part zeroed).
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// In place on the n x n diagonal block D (ld, n <= 128): reads its upper triangle (a symmetric block S),
+// factors S = R R^T with R upper and writes U22 = R^{-1} (upper, strictly lower part zeroed).
+//   Factorisation from the last coordinate backwards in panels of 16 columns: wave 0 factors a panel with the
+//   panel held in registers (rows lane and lane + 64; pivots and column entries broadcast with readlane), then
+//   all threads apply the rank-16 update to the remaining upper-left block (4 x 4 register tiles).
+//   Inverse by recursive doubling: the eight 16 x 16 diagonal blocks are inverted by back substitution (one
+//   wave each), then adjacent blocks are merged, U_ac = -U_aa (R_ac U_cc), for block sizes 16, 32 and 64.
+//   Rows and columns n..127 are padded with the identity, which leaves the leading n x n result unchanged.
 __global__ __launch_bounds__(1024) void chol_ul_inv_kernel(float* D, int64_t ld, int n, DevStatus* st) {
     __shared__ float S[kNB][kNB + 1];
     __shared__ float R[kNB][kNB + 1];
-    const int tid = threadIdx.x;
-    for (int idx = tid; idx < n * n; idx += 1024) {
-        const int i = idx / n, k = idx % n;
-        if (i <= k) S[i][k] = D[(int64_t)i * ld + k];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    for (int idx = tid; idx < kNB * kNB; idx += 1024) {
+        const int i = idx >> 7, k = idx & (kNB - 1);
+        float v = 0.f;
+        if (i < n && k < n && i <= k) v = D[(int64_t)i * ld + k];
+        S[i][k] = v;
+        R[i][k] = (i == k && i >= n) ? 1.0f : 0.0f;
     }
     __syncthreads();
     unsigned bad = 0;
-    // Factorisation from the last coordinate backwards: column j of R is the current column j of the
-    // Schur complement divided by the square root of its pivot; the rest of the upper-left block is updated.
-    for (int j = n - 1; j >= 0; --j) {
-        float d = S[j][j];
-        if (!(d > 0.0f)) {
-            bad |= isfinite(d) ? kDevNotPD : kDevNonFinite;
-            d = 1.0f;
+
+    for (int p1 = n; p1 > 0; p1 -= 16) {
+        const int p0 = p1 > 16 ? p1 - 16 : 0;
+        const int pw = p1 - p0;
+        if (wave == 0) {
+            float pn[2][16];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int c = 0; c < 16; ++c) pn[s2][c] = (c < pw) ? S[lane + 64 * s2][p0 + c] : 0.f;
+#pragma unroll
+            for (int c = 15; c >= 0; --c) {
+                if (c < pw) {
+                    const int j = p0 + c;
+                    float d = j < 64 ? readlane_f(pn[0][c], j) : readlane_f(pn[1][c], j - 64);
+                    if (!(d > 0.0f)) {
+                        bad |= isfinite(d) ? kDevNotPD : kDevNonFinite;
+                        d = 1.0f;
+                    }
+                    const float r = sqrtf(d);
+                    float cj[2];
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        const int row = lane + 64 * s2;
+                        cj[s2] = row < j ? pn[s2][c] / r : (row == j ? r : 0.f);
+                        if (row < n) R[row][j] = cj[s2];
+                    }
+#pragma unroll
+                    for (int cc = 0; cc < c; ++cc) {
+                        const int k = p0 + cc;
+                        const float ck = k < 64 ? readlane_f(cj[0], k) : readlane_f(cj[1], k - 64);
+#pragma unroll
+                        for (int s2 = 0; s2 < 2; ++s2) pn[s2][cc] = fmaf(-cj[s2], ck, pn[s2][cc]);
+                    }
+                }
+            }
         }
-        const float invd = 1.0f / d;
-        const float r = sqrtf(d);
-        if (tid <= j) R[tid][j] = (tid == j) ? r : S[tid][j] / r;
-        for (int m = 0; m < (kNB * kNB) / 1024; ++m) {
-            const int idx = tid + 1024 * m;
-            const int i = idx >> 7, k = idx & (kNB - 1);
-            if (i <= k && k < j) S[i][k] = fmaf(-S[i][j] * invd, S[k][j], S[i][k]);
+        __syncthreads();
+        if (p0 > 0) {
+            const int i0 = (tid >> 5) * 4, k0 = (tid & 31) * 4;
+            if (i0 < p0 && k0 < p0 && i0 <= k0 + 3) {
+                float acc[4][4] = {};
+                for (int c = 0; c < pw; ++c) {
+                    float a4[4], b4[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        a4[u] = R[i0 + u][p0 + c];
+                        b4[u] = R[k0 + u][p0 + c];
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a4[u], b4[v], acc[u][v]);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        if (i0 + u < p0 && k0 + v < p0 && i0 + u <= k0 + v) S[i0 + u][k0 + v] -= acc[u][v];
+            }
         }
         __syncthreads();
     }
-    // Inverse of the upper-triangular R, row by row from the bottom:
-    //   U_ii = 1 / R_ii;  U_ik = -U_ii * sum_{i<m<=k} R_im U_mk   (k > i).
-    // 8 threads share one output column k and combine their partial sums with lane shuffles.
-    const int kk = tid >> 3, part = tid & 7;
-    for (int i = n - 1; i >= 0; --i) {
-        const float uii = 1.0f / R[i][i];
-        float acc = 0.0f;
-        if (kk > i && kk < n)
-            for (int m = i + 1 + part; m <= kk; m += 8) acc = fmaf(R[i][m], S[m][kk], acc);
-        acc += __shfl_xor(acc, 1, 8);
-        acc += __shfl_xor(acc, 2, 8);
-        acc += __shfl_xor(acc, 4, 8);
-        if (part == 0 && kk < n) {
-            if (kk == i) S[i][i] = uii;
-            else if (kk > i) S[i][kk] = -uii * acc;
+
+    // Inverse of the (padded) 128 x 128 upper-triangular R, written into S.
+    // Level 0: 16 x 16 diagonal blocks, column j = lane of block `wave` (lanes 0..15), back substitution.
+    if (wave < 8 && lane < 16) {
+        const int b0 = 16 * wave, j = lane;
+        float u[16];
+#pragma unroll
+        for (int i = 15; i >= 0; --i) {
+            const float rii = R[b0 + i][b0 + i];
+            float acc = 0.f;
+#pragma unroll
+            for (int m = i + 1; m < 16; ++m) acc = fmaf(R[b0 + i][b0 + m], (m <= j) ? u[m] : 0.f, acc);
+            u[i] = (i == j) ? 1.0f / rii : (i < j ? -acc / rii : 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) S[b0 + i][b0 + j] = u[i];
+    }
+    __syncthreads();
+    // Levels: merge pairs (a, c) of size s: T = R_ac U_cc (kept in registers, then stored over R_ac);
+    // U_ac = -U_aa T.  Each level has 64 s outputs per product, spread over the 1024 threads.
+    for (int s = 16; s < kNB; s *= 2) {
+        const int per = (64 * s) / 1024;                 // outputs per thread: 1, 2, 4
+        float t[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            t[e] = 0.f;
+            if (e < per) {
+                const int o = tid * per + e;               // output index
+                const int pair = o / (s * s), w = o % (s * s);
+                const int i = w / s, k = w % s;
+                const int a0 = 2 * s * pair, c0 = a0 + s;
+                float acc = 0.f;
+                for (int m = 0; m <= k; ++m) acc = fmaf(R[a0 + i][c0 + m], S[c0 + m][c0 + k], acc);
+                t[e] = acc;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (e < per) {
+                const int o = tid * per + e;
+                const int pair = o / (s * s), w = o % (s * s);
+                const int i = w / s, k = w % s;
+                const int a0 = 2 * s * pair, c0 = a0 + s;
+                R[a0 + i][c0 + k] = t[e];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (e < per) {
+                const int o = tid * per + e;
+                const int pair = o / (s * s), w = o % (s * s);
+                const int i = w / s, k = w % s;
+                const int a0 = 2 * s * pair, c0 = a0 + s;
+                float acc = 0.f;
+                for (int m = i; m < s; ++m) acc = fmaf(S[a0 + i][a0 + m], R[a0 + m][c0 + k], acc);
+                S[a0 + i][c0 + k] = -acc;
+            }
         }
         __syncthreads();
     }
