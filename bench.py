@@ -96,7 +96,7 @@ class Layer:
         self.codes = torch.empty(K, N, dtype=torch.uint8, device=dev)
         self.scales = torch.empty(N, dtype=torch.float32, device=dev)
         self.losses = torch.empty(N, dtype=torch.float32, device=dev)
-        flags = 1 if self.Xf is not None else 0
+        flags = (1 if self.Xf is not None else 0) | (2 if self.rho is not None else 0)
         ws = max(G.gptq_workspace_bytes(G.GPTQ_CALL_ACCUMULATE_HESSIAN, K, 0, M, flags),
                  G.gptq_workspace_bytes(G.GPTQ_CALL_PREPARE, K),
                  G.gptq_workspace_bytes(G.GPTQ_CALL_ASYM_CORRECTION, K),

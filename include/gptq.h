@@ -70,8 +70,9 @@ typedef enum {
 
 /*
  * gptq_workspace_bytes - bytes of `workspace` a call needs for the given sizes.
- *   call: which entry point; K, N, M: sizes as in that call (unused ones are ignored); flags: that
- *   call's flags (for gptq_accumulate_hessian pass 1 when X_float is given, else 0).
+ *   call: which entry point; K, N, M: sizes as in that call (unused ones are ignored); flags: for
+ *   gptq_accumulate_hessian 1 if X_float will be given | 2 if row_scale will be given; for
+ *   gptq_quantize_layer its flags | 2 if P1 will be given; else 0.
  * Returns 0 for an unknown call.  Never fails otherwise.
  */
 size_t gptq_workspace_bytes(gptq_call_t call, int64_t K, int64_t N, int64_t M, unsigned flags);
@@ -94,7 +95,9 @@ size_t gptq_workspace_bytes(gptq_call_t call, int64_t K, int64_t N, int64_t M, u
  *              bf16-representable).  Requires x_dtype == GPTQ_DTYPE_BF16 and row_scale == NULL.
  *   A          device, K x K fp32 row-major, read-modify-written; required iff X_float != NULL.  Not
  *              symmetric.
- *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_ACCUMULATE_HESSIAN, K, 0, M, X_float != 0).
+ *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_ACCUMULATE_HESSIAN, K, 0, M, flags) with flags
+ *              (X_float != 0) | 2 (row_scale != 0).  With a transformed operand (row_scale or X_float), K a
+ *              multiple of 256 and M a multiple of 32 it includes M x K bf16 of staging for that operand.
  * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP.  Asynchronous.
  */
 gptq_status_t gptq_accumulate_hessian(float* H, int64_t K,

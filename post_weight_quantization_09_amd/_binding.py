@@ -137,7 +137,7 @@ def gptq_accumulate_hessian(H: torch.Tensor, X: torch.Tensor, row_scale: Optiona
         raise ValueError("X must be M x K with contiguous rows")
     if X_float is not None and (X_float.shape != X.shape or X_float.stride(1) != 1):
         raise ValueError("X_float must match X")
-    flags = 1 if X_float is not None else 0
+    flags = (1 if X_float is not None else 0) | (2 if row_scale is not None else 0)
     workspace, wp, wb = _workspace(GPTQ_CALL_ACCUMULATE_HESSIAN, K, 0, M, flags, H.device, workspace)
     st = load().gptq_accumulate_hessian(
         _dptr(H), K, _dptr(X), _dtype_code(X), M, X.stride(0) if M > 0 else K, _dptr(row_scale), _dptr(X_float),

@@ -23,10 +23,11 @@ size_t accumulate_partial_floats(int64_t K, int64_t M, bool cross) {
     return f;
 }
 
-size_t accumulate_ws(int64_t K, int64_t M, bool cross) {
+size_t accumulate_ws(int64_t K, int64_t M, bool cross, bool scaled) {
     Carver c(nullptr);
     c.take<DevStatus>(1);
     c.take<float>(accumulate_partial_floats(K, M, cross));
+    c.take<uint16_t>(gram_staging_elems(K, M, cross || scaled));
     return c.bytes();
 }
 
@@ -60,7 +61,7 @@ size_t gptq_workspace_bytes(gptq_call_t call, int64_t K, int64_t N, int64_t M, u
     if (N < 1) N = 1;
     if (M < 0) M = 0;
     switch (call) {
-        case GPTQ_CALL_ACCUMULATE_HESSIAN: return accumulate_ws(K, M, (flags & 1u) != 0);
+        case GPTQ_CALL_ACCUMULATE_HESSIAN: return accumulate_ws(K, M, (flags & 1u) != 0, (flags & 2u) != 0);
         case GPTQ_CALL_PREPARE: return prepare_workspace_bytes(K);
         case GPTQ_CALL_ASYM_CORRECTION: return asym_ws(K);
         case GPTQ_CALL_QUANTIZE_LAYER: return quantize_workspace_bytes(K, N, (flags & 2u) != 0);
@@ -77,7 +78,7 @@ gptq_status_t gptq_accumulate_hessian(float* H, int64_t K, const void* X, gptq_d
     const bool cross = X_float != nullptr;
     if (cross && (x_dtype != GPTQ_DTYPE_BF16 || !A || ldxf < K || row_scale)) return GPTQ_ERR_ARG;
     if (!cross && A) return GPTQ_ERR_ARG;
-    const size_t need = x_dtype == GPTQ_DTYPE_BF16 ? accumulate_ws(K, M, cross) : 0;
+    const size_t need = x_dtype == GPTQ_DTYPE_BF16 ? accumulate_ws(K, M, cross, row_scale != nullptr) : 0;
     if (!ws_ok(workspace, workspace_bytes, need)) return GPTQ_ERR_WORKSPACE;
     if (M == 0) return GPTQ_OK;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -95,12 +96,15 @@ gptq_status_t gptq_accumulate_hessian(float* H, int64_t K, const void* X, gptq_d
     c.take<DevStatus>(1);
     const GramPlan pl = gram_plan(K, M, false);
     float* partial = c.take<float>(accumulate_partial_floats(K, M, cross));
-    hipError_t e = gram_bf16(pl, static_cast<const uint16_t*>(X), ldx, nullptr, 0, row_scale, M, K, partial, H, st);
+    const size_t nstage = gram_staging_elems(K, M, cross || row_scale != nullptr);
+    uint16_t* staging = nstage ? c.take<uint16_t>(nstage) : nullptr;
+    hipError_t e = gram_bf16(pl, static_cast<const uint16_t*>(X), ldx, nullptr, 0, row_scale, M, K, partial, staging,
+                             H, st);
     if (e != hipSuccess) return GPTQ_ERR_HIP;
     if (cross) {
         const GramPlan px = gram_plan(K, M, true);
         e = gram_bf16(px, static_cast<const uint16_t*>(X), ldx, static_cast<const uint16_t*>(X_float), ldxf, nullptr,
-                      M, K, partial, A, st);
+                      M, K, partial, staging, A, st);
         if (e != hipSuccess) return GPTQ_ERR_HIP;
     }
     return GPTQ_OK;

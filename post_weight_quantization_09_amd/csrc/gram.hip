@@ -327,6 +327,7 @@ __device__ __forceinline__ void wait_vm_and_barrier(int later) {
     else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+template <bool CROSS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gram_bf16_lds_kernel(GramArgs p) {
     __shared__ __attribute__((aligned(1024))) uint16_t ring[kRing][2][kGK][kGT];   // 128 KB
@@ -344,9 +345,9 @@ void gram_bf16_lds_kernel(GramArgs p) {
         tile = bid % p.ntiles;
     }
     int bi, bj;
-    tile_coords(tile, p.nb, false, bi, bj);
+    tile_coords(tile, p.nb, CROSS, bi, bj);
     if (bi >= p.nb || bj >= p.nb || split >= p.splits) return;
-    const bool active = !(bi == bj && wi == 1 && wj == 0);
+    const bool active = CROSS || !(bi == bj && wi == 1 && wj == 0);
     const int64_t t0 = (int64_t)split * p.tokens_per_split;
     const int64_t t1 = min<int64_t>(p.M, t0 + p.tokens_per_split);
     const int64_t nst = t1 > t0 ? (t1 - t0) / kGK : 0;       // whole stages (checked on the host)
@@ -364,8 +365,10 @@ void gram_bf16_lds_kernel(GramArgs p) {
     const int lrow = 8 * wave + (lane >> 5);
     const int gchunk0 = (lane & 31) ^ chunk_swz(lrow);
     const int gchunk1 = (lane & 31) ^ chunk_swz(lrow + 2);
-    const uint16_t* srcA0 = p.X + (int64_t)bi * kGT + gchunk0 * 8;
-    const uint16_t* srcA1 = p.X + (int64_t)bi * kGT + gchunk1 * 8;
+    const uint16_t* XA = p.XA ? p.XA : p.X;          // A-side operand (the mismatch for the cross term)
+    const int64_t lda = p.XA ? p.ldxa : p.ldx;
+    const uint16_t* srcA0 = XA + (int64_t)bi * kGT + gchunk0 * 8;
+    const uint16_t* srcA1 = XA + (int64_t)bi * kGT + gchunk1 * 8;
     const uint16_t* srcB0 = p.X + (int64_t)bj * kGT + gchunk0 * 8;
     const uint16_t* srcB1 = p.X + (int64_t)bj * kGT + gchunk1 * 8;
     auto issue = [&](int64_t st) {
@@ -376,7 +379,7 @@ void gram_bf16_lds_kernel(GramArgs p) {
             const int64_t tok = tb + 2 * i;
             const uint16_t* sa = (i & 1) ? srcA1 : srcA0;
             const uint16_t* sb = (i & 1) ? srcB1 : srcB0;
-            __builtin_amdgcn_global_load_lds((const void*)(sa + tok * p.ldx),
+            __builtin_amdgcn_global_load_lds((const void*)(sa + tok * lda),
                                              (lds_void_t*)&ring[slot][0][8 * wave + 2 * i][0], 16, 0, 0);
             __builtin_amdgcn_global_load_lds((const void*)(sb + tok * p.ldx),
                                              (lds_void_t*)&ring[slot][1][8 * wave + 2 * i][0], 16, 0, 0);
@@ -428,6 +431,24 @@ void gram_bf16_lds_kernel(GramArgs p) {
     for (int a = 0; a < 4; ++a)
         for (int b = 0; b < 4; ++b)
             for (int r = 0; r < 16; ++r) out[((a * 4 + b) * 16 + r) * 64 + lane] = acc[a][b][r];
+}
+
+// Elementwise operand preparation for the fast Gram path: Xs = bf16(rho_t * x) (group weights) or
+// dX = bf16(X~ - X) (asymmetric cross term), written densely (ld = K).  HBM-bound, 8 elements per thread.
+template <bool DIFF>
+__global__ __launch_bounds__(256) void gram_operand_kernel(const uint16_t* X, int64_t ldx, const uint16_t* Xf,
+                                                           int64_t ldxf, const float* rho, int64_t M, int64_t K,
+                                                           uint16_t* out) {
+    const int64_t chunks_per_row = K / 8;
+    const int64_t total = M * chunks_per_row;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = c / chunks_per_row, k = (c % chunks_per_row) * 8;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(X + t * ldx + k);
+        u32x4 o;
+        if (DIFF) o = diff_bf16(*reinterpret_cast<const u32x4*>(Xf + t * ldxf + k), x);
+        else o = scale_row_bf16(x, rho[t]);
+        *reinterpret_cast<u32x4*>(out + t * K + k) = o;
+    }
 }
 
 // Sums the split partials of one 128 x 128 quadrant in split order, scales by 2 and adds into the output
@@ -500,8 +521,14 @@ GramPlan gram_plan(int64_t K, int64_t M, bool cross) {
     return pl;
 }
 
+size_t gram_staging_elems(int64_t K, int64_t M, bool transformed) {
+    // The fast path stages a transformed operand (group-weighted X or the cross mismatch) densely in bf16.
+    return transformed && K % kGT == 0 && M % kGK == 0 ? (size_t)M * (size_t)K : 0;
+}
+
 hipError_t gram_bf16(const GramPlan& pl, const uint16_t* X, int64_t ldx, const uint16_t* Xf, int64_t ldxf,
-                     const float* rho, int64_t M, int64_t K, float* partial, float* Out, hipStream_t stream) {
+                     const float* rho, int64_t M, int64_t K, float* partial, uint16_t* staging, float* Out,
+                     hipStream_t stream) {
     if (M <= 0) return hipSuccess;
     const bool cross = Xf != nullptr;
     if (pl.cross != cross) return hipErrorInvalidValue;     // the plan's tile count is mode specific
@@ -512,11 +539,28 @@ hipError_t gram_bf16(const GramPlan& pl, const uint16_t* X, int64_t ldx, const u
     auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
     p.vec = al16(X) && ldx % 8 == 0 && (!cross || (al16(Xf) && ldxf % 8 == 0));
     const unsigned nblk = (unsigned)((int64_t)pl.ntiles * pl.splits);
-    // Fast path: whole 256-column tiles and 16-byte aligned rows (no per-element guards in the main loop).
+    // Fast path: whole 256-column tiles, 16-byte aligned rows, whole 32-token stages in every split.
     const bool fast = p.vec && K % kGT == 0;
     const bool whole_stages = p.tokens_per_split % kGK == 0 && M % kGK == 0;
-    if (GPTQ_GRAM_DMA && fast && !cross && !rho && whole_stages) {
-        hipLaunchKernelGGL(gram_bf16_lds_kernel, dim3(nblk), dim3(256), 0, stream, p);
+    const bool transformed = cross || rho != nullptr;
+    if (GPTQ_GRAM_DMA && fast && whole_stages && (!transformed || staging)) {
+        if (transformed) {
+            // stage bf16(rho * X) or bf16(X~ - X) once, then run the plain streaming kernel on it
+            const int64_t chunks = M * (K / 8);
+            const unsigned g = (unsigned)std::min<int64_t>(ceil_div(chunks, 256), 256 * 64);
+            if (cross)
+                hipLaunchKernelGGL((gram_operand_kernel<true>), dim3(g), dim3(256), 0, stream, X, ldx, Xf, ldxf,
+                                   nullptr, M, K, staging);
+            else
+                hipLaunchKernelGGL((gram_operand_kernel<false>), dim3(g), dim3(256), 0, stream, X, ldx, nullptr,
+                                   (int64_t)0, rho, M, K, staging);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            if (cross) { p.XA = staging; p.ldxa = K; }
+            else { p.X = staging; p.ldx = K; }
+        }
+        if (cross) hipLaunchKernelGGL(gram_bf16_lds_kernel<true>, dim3(nblk), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL(gram_bf16_lds_kernel<false>, dim3(nblk), dim3(256), 0, stream, p);
     } else if (fast) {
         if (cross) hipLaunchKernelGGL((gram_bf16_kernel<true, false, true>), dim3(nblk), dim3(256), 0, stream, p);
         else if (rho) hipLaunchKernelGGL((gram_bf16_kernel<false, true, true>), dim3(nblk), dim3(256), 0, stream, p);

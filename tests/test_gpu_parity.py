@@ -68,26 +68,28 @@ def test_gram_f32(g):
     assert err <= H_TOL
 
 
-def test_gram_row_scaled(g):
-    cfg, L = _bf16_layer(300, 8, 3000, base="c3_down_proj_8b_g4", groups=4)
+@pytest.mark.parametrize("K,M", [(300, 3000), (512, 4096)])
+def test_gram_row_scaled(g, K, M):
+    cfg, L = _bf16_layer(K, 8, M, base="c3_down_proj_8b_g4", groups=4)
     rho = L["rho"]
     H = torch.zeros(cfg.K, cfg.K, device=DEV)
     g.gptq_accumulate_hessian(H, L["X"].to(DEV), row_scale=rho[1].to(DEV).contiguous())
     ref = O.gram_row_scaled(L["X"].float().numpy(), rho[1].numpy())
     err = rel_fro(np64(H), ref)
-    _print(f"gram row-scaled rel={err:.3e}")
+    _print(f"gram row-scaled K={K} M={M} rel={err:.3e}")
     assert err <= H_TOL
 
 
-def test_gram_cross(g):
-    cfg, L = _bf16_layer(300, 8, 2500, base="c4_up_proj_8b_gptaq")
+@pytest.mark.parametrize("K,M", [(300, 2500), (512, 4096)])
+def test_gram_cross(g, K, M):
+    cfg, L = _bf16_layer(K, 8, M, base="c4_up_proj_8b_gptaq")
     X, Xf = L["X"].to(DEV), L["X_float"].to(DEV)
     H = torch.zeros(cfg.K, cfg.K, device=DEV)
     A = torch.zeros(cfg.K, cfg.K, device=DEV)
     g.gptq_accumulate_hessian(H, X, X_float=Xf, A=A)
     eh = rel_fro(np64(H), O.gram([L["X"].float().numpy()]))
     ea = rel_fro(np64(A), O.cross_gram(L["X_float"].float().numpy(), L["X"].float().numpy()))
-    _print(f"gram cross: H rel={eh:.3e} A rel={ea:.3e}")
+    _print(f"gram cross K={K} M={M}: H rel={eh:.3e} A rel={ea:.3e}")
     assert eh <= H_TOL and ea <= H_TOL
 
 
