@@ -7,14 +7,18 @@
 //
 // U is computed without forming H_d^{-1}: H_d = R R^T with R upper triangular (the Cholesky factorisation
 // taken from the bottom-right corner), then U = R^{-1}, since H_d^{-1} = R^{-T} R^{-1} = U^T U with U upper.
-// Both steps are blocked with nb = 128:
-//   * per diagonal block (bottom-up): an LDS kernel factors the 128 x 128 block and inverts it in place
-//     (the diagonal block of U is the inverse of the diagonal block of R); the panel above becomes
-//     R12 = H12 U22^T and the trailing upper triangle is updated H11 -= R12 R12^T, both on fp32 MFMA.
-//   * the off-diagonal blocks of U follow by recursive doubling: for adjacent blocks a (upper left) and
-//     c, U_ac = -U_aa R_ac U_cc, merged for block sizes 128, 256, ... as two batched triangular GEMMs.
+// Factor and inverse run as one recursion over a 2 x 2 split of the block (top part n1 a multiple of 128):
+//     H = [H11 H12; . H22],  R = [R11 R12; 0 R22],  U = [U11 U12; 0 U22]
+//   1. recurse on H22 -> U22                      (H22 = R22 R22^T)
+//   2. R12 = H12 U22^T                             (from H12 = R12 R22^T)
+//   3. H11 <- H11 - R12 R12^T  (upper triangle)    (H11 = R11 R11^T + R12 R12^T)
+//   4. X = R12 U22
+//   5. recurse on H11 -> U11
+//   6. U12 = -U11 X                                (U R = I gives U11 R12 + U12 R22 = 0)
+// Steps 2, 3, 4 and 6 are fp32 MFMA GEMMs; the recursion ends in 128 x 128 (or smaller) diagonal blocks that
+// one LDS kernel factors and inverts.  Since the split points are multiples of 128 from the top, every
+// GEMM tile is aligned with the diagonal blocks.
 #include <algorithm>
-#include <vector>
 
 #include "factor.hpp"
 #include "gemm_f32.hpp"
@@ -72,154 +76,145 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 }
 
 // In place on the n x n diagonal block D (ld, n <= 128): reads its upper triangle (a symmetric block S),
-// factors S = R R^T with R upper and writes U22 = R^{-1} (upper, strictly lower part zeroed).
-//   Factorisation from the last coordinate backwards in panels of 16 columns: wave 0 factors a panel with the
-//   panel held in registers (rows lane and lane + 64; pivots and column entries broadcast with readlane), then
-//   all threads apply the rank-16 update to the remaining upper-left block (4 x 4 register tiles).
-//   Inverse by recursive doubling: the eight 16 x 16 diagonal blocks are inverted by back substitution (one
-//   wave each), then adjacent blocks are merged, U_ac = -U_aa (R_ac U_cc), for block sizes 16, 32 and 64.
-//   Rows and columns n..127 are padded with the identity, which leaves the leading n x n result unchanged.
+// factors S = R R^T with R upper and writes U = R^{-1} (upper, strictly lower part zeroed).
+//   The block sits in the bottom-right corner of a 128 x 128 frame whose top-left is the identity, so every
+//   loop below has a fixed trip count; the identity factors and inverts to itself.
+//   Factorisation from the last coordinate backwards in panels of 16 columns: wave 0 factors a panel held in
+//   registers (rows lane and lane + 64; pivot and column entries broadcast with readlane; the column is
+//   scaled by the reciprocal square root of the pivot), then the rank-16 update of the remaining upper-left
+//   block runs on v_mfma_f32_32x32x2_f32, one 32 x 32 tile per wave.
+//   Inverse by recursive doubling: the eight 16 x 16 diagonal blocks are inverted by back substitution, then
+//   adjacent blocks a (upper) and c are merged, U_ac = -U_aa (R_ac U_cc), for block sizes 16, 32 and 64,
+//   each product on v_mfma_f32_16x16x4_f32, one 16 x 16 tile per wave.
 __global__ __launch_bounds__(1024) void chol_ul_inv_kernel(float* D, int64_t ld, int n, DevStatus* st) {
     __shared__ float S[kNB][kNB + 1];
     __shared__ float R[kNB][kNB + 1];
+    __shared__ float Rinv[kNB];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int o = kNB - n;
     for (int idx = tid; idx < kNB * kNB; idx += 1024) {
         const int i = idx >> 7, k = idx & (kNB - 1);
-        float v = 0.f;
-        if (i < n && k < n && i <= k) v = D[(int64_t)i * ld + k];
+        float v = (i == k) ? 1.0f : 0.0f;
+        if (i >= o && i <= k) v = D[(int64_t)(i - o) * ld + (k - o)];
         S[i][k] = v;
-        R[i][k] = (i == k && i >= n) ? 1.0f : 0.0f;
     }
     __syncthreads();
     unsigned bad = 0;
 
-    for (int p1 = n; p1 > 0; p1 -= 16) {
-        const int p0 = p1 > 16 ? p1 - 16 : 0;
-        const int pw = p1 - p0;
+    for (int P = kNB / 16 - 1; P >= 0; --P) {
+        const int p0 = 16 * P;
         if (wave == 0) {
+            const bool hi = p0 >= 64;   // the panel's rows p0..p0+15 sit in register half 1
             float pn[2][16];
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-                for (int c = 0; c < 16; ++c) pn[s2][c] = (c < pw) ? S[lane + 64 * s2][p0 + c] : 0.f;
+                for (int c = 0; c < 16; ++c) pn[s2][c] = S[lane + 64 * s2][p0 + c];
 #pragma unroll
             for (int c = 15; c >= 0; --c) {
-                if (c < pw) {
-                    const int j = p0 + c;
-                    float d = j < 64 ? readlane_f(pn[0][c], j) : readlane_f(pn[1][c], j - 64);
-                    if (!(d > 0.0f)) {
-                        bad |= isfinite(d) ? kDevNotPD : kDevNonFinite;
-                        d = 1.0f;
-                    }
-                    const float r = sqrtf(d);
-                    float cj[2];
+                const int j = p0 + c;
+                float d = readlane_f(hi ? pn[1][c] : pn[0][c], j & 63);
+                if (!(d > 0.0f)) {
+                    bad |= isfinite(d) ? kDevNotPD : kDevNonFinite;
+                    d = 1.0f;
+                }
+                float rinv = __builtin_amdgcn_rsqf(d);
+                rinv = rinv * fmaf(-0.5f * d * rinv, rinv, 1.5f);   // one Newton step on 1/sqrt(d)
+                const float r = d * rinv;
+                float cj[2];
 #pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) {
-                        const int row = lane + 64 * s2;
-                        cj[s2] = row < j ? pn[s2][c] / r : (row == j ? r : 0.f);
-                        if (row < n) R[row][j] = cj[s2];
-                    }
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const int row = lane + 64 * s2;
+                    cj[s2] = row < j ? pn[s2][c] * rinv : (row == j ? r : 0.f);
+                    R[row][j] = cj[s2];
+                }
+                if (lane == 0) Rinv[j] = rinv;
 #pragma unroll
-                    for (int cc = 0; cc < c; ++cc) {
-                        const int k = p0 + cc;
-                        const float ck = k < 64 ? readlane_f(cj[0], k) : readlane_f(cj[1], k - 64);
+                for (int cc = 0; cc < c; ++cc) {
+                    const float ck = readlane_f(hi ? cj[1] : cj[0], (p0 + cc) & 63);
 #pragma unroll
-                        for (int s2 = 0; s2 < 2; ++s2) pn[s2][cc] = fmaf(-cj[s2], ck, pn[s2][cc]);
-                    }
+                    for (int s2 = 0; s2 < 2; ++s2) pn[s2][cc] = fmaf(-cj[s2], ck, pn[s2][cc]);
                 }
             }
         }
         __syncthreads();
         if (p0 > 0) {
-            const int i0 = (tid >> 5) * 4, k0 = (tid & 31) * 4;
-            if (i0 < p0 && k0 < p0 && i0 <= k0 + 3) {
-                float acc[4][4] = {};
-                for (int c = 0; c < pw; ++c) {
-                    float a4[4], b4[4];
+            // S[i][k] -= sum_c R[i][p0+c] R[k][p0+c] for i <= k < p0, over the upper 32 x 32 tiles.
+            const int T = (p0 + 31) >> 5;
+            int bi = 0, bk = wave, cnt = T;
+            while (bk >= cnt && cnt > 0) { bk -= cnt; ++bi; --cnt; }   // wave -> (bi, bi + bk)
+            if (bi < T) {
+                bk += bi;
+                f32x16 acc;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        a4[u] = R[i0 + u][p0 + c];
-                        b4[u] = R[k0 + u][p0 + c];
-                    }
+                for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-#pragma unroll
-                        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a4[u], b4[v], acc[u][v]);
+                for (int s2 = 0; s2 < 8; ++s2) {
+                    const int c = p0 + 2 * s2 + (lane >> 5);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(R[32 * bi + (lane & 31)][c],
+                                                               R[32 * bk + (lane & 31)][c], acc, 0, 0, 0);
                 }
+                const int col = 32 * bk + (lane & 31);
 #pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        if (i0 + u < p0 && k0 + v < p0 && i0 + u <= k0 + v) S[i0 + u][k0 + v] -= acc[u][v];
+                for (int r = 0; r < 16; ++r) {
+                    const int row = 32 * bi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    if (row <= col && col < p0) S[row][col] -= acc[r];
+                }
             }
         }
         __syncthreads();
     }
 
-    // Inverse of the (padded) 128 x 128 upper-triangular R, written into S.
+    // Inverse of the upper-triangular R (128 x 128), written into S (whose strictly lower part is zero).
     // Level 0: 16 x 16 diagonal blocks, column j = lane of block `wave` (lanes 0..15), back substitution.
     if (wave < 8 && lane < 16) {
         const int b0 = 16 * wave, j = lane;
         float u[16];
 #pragma unroll
         for (int i = 15; i >= 0; --i) {
-            const float rii = R[b0 + i][b0 + i];
             float acc = 0.f;
 #pragma unroll
-            for (int m = i + 1; m < 16; ++m) acc = fmaf(R[b0 + i][b0 + m], (m <= j) ? u[m] : 0.f, acc);
-            u[i] = (i == j) ? 1.0f / rii : (i < j ? -acc / rii : 0.f);
+            for (int m = i + 1; m < 16; ++m) acc = fmaf(R[b0 + i][b0 + m], u[m], acc);
+            const float ri = Rinv[b0 + i];
+            u[i] = (i == j) ? ri : (i < j ? -acc * ri : 0.f);
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) S[b0 + i][b0 + j] = u[i];
     }
     __syncthreads();
-    // Levels: merge pairs (a, c) of size s: T = R_ac U_cc (kept in registers, then stored over R_ac);
-    // U_ac = -U_aa T.  Each level has 64 s outputs per product, spread over the 1024 threads.
+    // Merges of pairs (a, c) of size s: T = R_ac U_cc (then stored over R_ac), U_ac = -U_aa T.
     for (int s = 16; s < kNB; s *= 2) {
-        const int per = (64 * s) / 1024;                 // outputs per thread: 1, 2, 4
-        float t[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            t[e] = 0.f;
-            if (e < per) {
-                const int o = tid * per + e;               // output index
-                const int pair = o / (s * s), w = o % (s * s);
-                const int i = w / s, k = w % s;
-                const int a0 = 2 * s * pair, c0 = a0 + s;
-                float acc = 0.f;
-                for (int m = 0; m <= k; ++m) acc = fmaf(R[a0 + i][c0 + m], S[c0 + m][c0 + k], acc);
-                t[e] = acc;
-            }
+        const int per_side = s >> 4, tpp = per_side * per_side;
+        const int ntile = (kNB / (2 * s)) * tpp;   // 4, 8, 16 tiles of 16 x 16
+        const int pair = wave / tpp, w = wave % tpp;
+        const int ti = w / per_side, tk = w % per_side;
+        const int a0 = 2 * s * pair, c0 = a0 + s;
+        const int ar = 16 * ti + (lane & 15), kq = lane >> 4, oc = 16 * tk + (lane & 15);
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+        if (wave < ntile) {
+            for (int m4 = 0; m4 < s; m4 += 4)
+                t = __builtin_amdgcn_mfma_f32_16x16x4f32(R[a0 + ar][c0 + m4 + kq], S[c0 + m4 + kq][c0 + oc], t,
+                                                         0, 0, 0);
         }
         __syncthreads();
+        if (wave < ntile) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (e < per) {
-                const int o = tid * per + e;
-                const int pair = o / (s * s), w = o % (s * s);
-                const int i = w / s, k = w % s;
-                const int a0 = 2 * s * pair, c0 = a0 + s;
-                R[a0 + i][c0 + k] = t[e];
-            }
+            for (int r = 0; r < 4; ++r) R[a0 + 16 * ti + 4 * kq + r][c0 + oc] = t[r];
         }
         __syncthreads();
+        if (wave < ntile) {
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+            for (int m4 = 0; m4 < s; m4 += 4)
+                u = __builtin_amdgcn_mfma_f32_16x16x4f32(S[a0 + ar][a0 + m4 + kq], R[a0 + m4 + kq][c0 + oc], u,
+                                                         0, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (e < per) {
-                const int o = tid * per + e;
-                const int pair = o / (s * s), w = o % (s * s);
-                const int i = w / s, k = w % s;
-                const int a0 = 2 * s * pair, c0 = a0 + s;
-                float acc = 0.f;
-                for (int m = i; m < s; ++m) acc = fmaf(S[a0 + i][a0 + m], R[a0 + m][c0 + k], acc);
-                S[a0 + i][c0 + k] = -acc;
-            }
+            for (int r = 0; r < 4; ++r) S[a0 + 16 * ti + 4 * kq + r][c0 + oc] = -u[r];
         }
         __syncthreads();
     }
-    for (int idx = tid; idx < n * n; idx += 1024) {
-        const int i = idx / n, k = idx % n;
-        D[(int64_t)i * ld + k] = (i <= k) ? S[i][k] : 0.0f;
+    for (int idx = tid; idx < kNB * kNB; idx += 1024) {
+        const int i = idx >> 7, k = idx & (kNB - 1);
+        if (i >= o && k >= o) D[(int64_t)(i - o) * ld + (k - o)] = (i <= k) ? S[i][k] : 0.0f;
     }
     if (bad && tid == 0) atomicOr(&st->flags, bad);
 }
@@ -239,109 +234,111 @@ __global__ void clear_status_kernel(DevStatus* st) {
 
 }  // namespace
 
-// Scratch of the inverse merges: at block size s at most (K + 128) / (2 s) pairs of s x s products with
-// 2 s <= K + 128, i.e. at most (K + 128)^2 / 4 floats.
-static size_t merge_scratch_floats(int64_t K) { return (size_t)(K + kNB) * (size_t)(K + kNB) / 4 + kNB * kNB; }
+// Split of an n-block (n > 128): the top part n1 is a multiple of 128, the bottom part n2 = n - n1 > 0.
+static inline int64_t split_top(int64_t n) { return ((n + kNB - 1) / kNB / 2) * kNB; }
+
+// Scratch floats of the recursion on an n-block: X (n1 x n2) lives across the recursion on H11, the
+// temporary R12 (n1 x n2) only before it.
+static size_t recursion_scratch_floats(int64_t n) {
+    if (n <= kNB) return 0;
+    const int64_t n1 = split_top(n), n2 = n - n1;
+    const size_t x = (size_t)n1 * (size_t)n2;
+    return std::max(recursion_scratch_floats(n2), x + std::max(x, recursion_scratch_floats(n1)));
+}
 
 size_t prepare_workspace_bytes(int64_t K) {
     Carver c(nullptr);
     c.take<DevStatus>(1);
-    c.take<float>(merge_scratch_floats(K));
+    c.take<float>(std::max<size_t>(recursion_scratch_floats(K), 1));
     return c.bytes();
 }
+
+namespace {
+
+struct Recursion {
+    float* H;
+    int64_t K;
+    DevStatus* st;
+    hipStream_t stream;
+
+    gptq_status_t run(int64_t o, int64_t n, float* T) {
+        float* D = H + o * K + o;
+        if (n <= kNB) {
+            hipLaunchKernelGGL(chol_ul_inv_kernel, dim3(1), dim3(1024), 0, stream, D, K, (int)n, st);
+            return hipGetLastError() == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
+        }
+        const int64_t n1 = split_top(n), n2 = n - n1;
+        float* H12 = D + n1;
+        float* D22 = D + n1 * K + n1;
+        float* X = T;
+        float* R12 = T + n1 * n2;
+        gptq_status_t r = run(o + n1, n2, T);
+        if (r != GPTQ_OK) return r;
+        {   // R12 = H12 U22^T
+            GemmArgs g;
+            g.M = n1; g.N = n2; g.K1 = n2;
+            g.A1 = H12; g.lda1 = K;
+            g.B1 = D22; g.ldb1 = K; g.transB = true;   // B(k, c) = U22[c][k], zero for k < c
+            g.C = R12; g.ldc = n2;
+            g.flags = kGemmBLower;
+            if (gemm_f32(g, 1, stream) != hipSuccess) return GPTQ_ERR_HIP;
+        }
+        {   // H11 -= R12 R12^T on the upper triangle
+            GemmArgs g;
+            g.M = n1; g.N = n1; g.K1 = n2;
+            g.A1 = R12; g.lda1 = n2;
+            g.B1 = R12; g.ldb1 = n2; g.transB = true;
+            g.C = D; g.ldc = K;
+            g.alpha = -1.f; g.beta = 1.f;
+            g.flags = kGemmCUpper;
+            if (gemm_f32(g, 1, stream) != hipSuccess) return GPTQ_ERR_HIP;
+        }
+        {   // X = R12 U22
+            GemmArgs g;
+            g.M = n1; g.N = n2; g.K1 = n2;
+            g.A1 = R12; g.lda1 = n2;
+            g.B1 = D22; g.ldb1 = K;
+            g.C = X; g.ldc = n2;
+            g.flags = kGemmBUpper;
+            if (gemm_f32(g, 1, stream) != hipSuccess) return GPTQ_ERR_HIP;
+        }
+        r = run(o, n1, T + n1 * n2);
+        if (r != GPTQ_OK) return r;
+        {   // U12 = -U11 X
+            GemmArgs g;
+            g.M = n1; g.N = n2; g.K1 = n1;
+            g.A1 = D; g.lda1 = K;
+            g.B1 = X; g.ldb1 = n2;
+            g.C = H12; g.ldc = K;
+            g.alpha = -1.f; g.beta = 0.f;
+            g.flags = kGemmAUpper;
+            if (gemm_f32(g, 1, stream) != hipSuccess) return GPTQ_ERR_HIP;
+        }
+        return GPTQ_OK;
+    }
+};
+
+}  // namespace
 
 gptq_status_t prepare(float* H, int64_t K, float percdamp, uint8_t* dead, float* damp_out, int64_t* n_dead_out,
                       void* workspace, hipStream_t stream) {
     Carver c(workspace);
     DevStatus* st = c.take<DevStatus>(1);
-    float* T = c.take<float>(merge_scratch_floats(K));
+    float* T = c.take<float>(std::max<size_t>(recursion_scratch_floats(K), 1));
 
     hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, stream, st);
     hipLaunchKernelGGL(dead_damp_kernel, dim3(1), dim3(1024), 0, stream, H, K, percdamp, dead, st);
     GPTQ_LAUNCH_CHECK();
-
-    // Blocked factorisation H_d = R R^T from the bottom-right; diagonal blocks become U_ii = R_ii^{-1}.
-    for (int64_t p1 = K; p1 > 0;) {
-        const int64_t p0 = std::max<int64_t>(0, p1 - kNB);
-        const int n = (int)(p1 - p0);
-        hipLaunchKernelGGL(chol_ul_inv_kernel, dim3(1), dim3(1024), 0, stream, H + p0 * K + p0, K, n, st);
-        GPTQ_LAUNCH_CHECK();
-        if (p0 > 0) {
-            // R12 = H12 U22^T  (in place; one workgroup owns all n <= 128 columns of each row tile)
-            GemmArgs g;
-            g.M = p0; g.N = n; g.K1 = n;
-            g.A1 = H + p0; g.lda1 = K;
-            g.B1 = H + p0 * K + p0; g.ldb1 = K; g.transB = true;   // B(k, c) = U22[c][k]
-            g.C = H + p0; g.ldc = K;
-            g.alpha = 1.f; g.beta = 0.f;
-            g.flags = kGemmBLower;
-            if (gemm_f32(g, 1, stream) != hipSuccess) return GPTQ_ERR_HIP;
-            // H11 -= R12 R12^T on the upper triangle
-            GemmArgs s;
-            s.M = p0; s.N = p0; s.K1 = n;
-            s.A1 = H + p0; s.lda1 = K;
-            s.B1 = H + p0; s.ldb1 = K; s.transB = true;            // B(k, c) = R12[c][k]
-            s.C = H; s.ldc = K;
-            s.alpha = -1.f; s.beta = 1.f;
-            s.flags = kGemmCUpper;
-            if (gemm_f32(s, 1, stream) != hipSuccess) return GPTQ_ERR_HIP;
-        }
-        p1 = p0;
-    }
-
-    // The merges read whole square blocks of U as triangular operands: clear the stale lower triangle.
+    // Only the upper triangle of H is read.  The GEMMs treat the strictly lower parts of U blocks as stored
+    // zeros, and no step writes below the diagonal outside the diagonal blocks (which the block kernel
+    // clears), so clearing the lower triangle once keeps it zero throughout.
     hipLaunchKernelGGL(zero_lower_kernel, dim3((unsigned)K), dim3(256), 0, stream, H, K);
     GPTQ_LAUNCH_CHECK();
 
-    // Off-diagonal blocks of U = R^{-1} by recursive doubling.  The blocks are aligned to the top-left
-    // corner in steps of 128 starting from the factorisation's top block, which may be shorter.
-    const int64_t first = K - ((K - 1) / kNB) * kNB;   // size of the top (ragged) block, in 1..128
-    // Offsets of block boundaries measured from the top: 0, first, first+128, ...
-    // Merging uses "virtual" coordinates v = x + (128 - first) so that blocks are 128-aligned.
-    const int64_t shift = kNB - first;
-    for (int64_t s = kNB; s < K + shift; s *= 2) {
-        // pairs (a, c): a = [i*2s, i*2s+s), c = [i*2s+s, i*2s+2s) in virtual coordinates
-        std::vector<int64_t> full, partial_pairs;
-        for (int64_t v0 = 0; v0 + s < K + shift; v0 += 2 * s) {
-            const int64_t a0 = std::max<int64_t>(0, v0 - shift), a1 = v0 + s - shift;
-            const int64_t c0 = a1, c1 = std::min<int64_t>(K, v0 + 2 * s - shift);
-            if (a1 - a0 == s && c1 - c0 == s) full.push_back(a0);
-            else partial_pairs.push_back(v0);
-        }
-        auto merge = [&](int64_t a0, int64_t sa, int64_t c0, int64_t sc, int64_t batch, int64_t bstride)
-            -> gptq_status_t {
-            // T = R_ac U_cc   (sa x sc) ;  U_ac = -U_aa T
-            GemmArgs g1;
-            g1.M = sa; g1.N = sc; g1.K1 = sc;
-            g1.A1 = H + a0 * K + c0; g1.lda1 = K; g1.strideA1 = bstride;
-            g1.B1 = H + c0 * K + c0; g1.ldb1 = K; g1.strideB1 = bstride;
-            g1.C = T; g1.ldc = sc; g1.strideC = sa * sc;
-            g1.flags = kGemmBUpper;
-            if (gemm_f32(g1, batch, stream) != hipSuccess) return GPTQ_ERR_HIP;
-            GemmArgs g2;
-            g2.M = sa; g2.N = sc; g2.K1 = sa;
-            g2.A1 = H + a0 * K + a0; g2.lda1 = K; g2.strideA1 = bstride;
-            g2.B1 = T; g2.ldb1 = sc; g2.strideB1 = sa * sc;
-            g2.C = H + a0 * K + c0; g2.ldc = K; g2.strideC = bstride;
-            g2.alpha = -1.f; g2.beta = 0.f;
-            g2.flags = kGemmAUpper;
-            if (gemm_f32(g2, batch, stream) != hipSuccess) return GPTQ_ERR_HIP;
-            return GPTQ_OK;
-        };
-        if (!full.empty()) {
-            // full pairs are equally spaced by 2s along the diagonal
-            const int64_t a0 = full.front();
-            const int64_t bstride = 2 * s * (K + 1);
-            gptq_status_t r = merge(a0, s, a0 + s, s, (int64_t)full.size(), bstride);
-            if (r != GPTQ_OK) return r;
-        }
-        for (int64_t v0 : partial_pairs) {
-            const int64_t a0 = std::max<int64_t>(0, v0 - shift), a1 = v0 + s - shift;
-            const int64_t c0 = a1, c1 = std::min<int64_t>(K, v0 + 2 * s - shift);
-            gptq_status_t r = merge(a0, a1 - a0, c0, c1 - c0, 1, 0);
-            if (r != GPTQ_OK) return r;
-        }
-    }
+    Recursion rec{H, K, st, stream};
+    gptq_status_t r = rec.run(0, K, T);
+    if (r != GPTQ_OK) return r;
+
     DevStatus hst;
     GPTQ_HIP_CHECK(hipMemcpyAsync(&hst, st, sizeof(DevStatus), hipMemcpyDeviceToHost, stream));
     GPTQ_HIP_CHECK(hipStreamSynchronize(stream));

@@ -19,18 +19,23 @@ constexpr int kTM = 128, kTN = 128, kTK = 16, kPad = 4;
 // MFMA 32x32x2 f32 output layout: lane l, accumulator register r -> (row, col) inside the 32 x 32 block.
 __device__ inline int mfma32_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-template <bool TA, bool TB>
+template <bool TA, bool TB, bool FULL>
 struct TileIO {
     // A(m,k): TA ? A[k*lda + m] : A[m*lda + k].   B(k,n): TB ? B[n*ldb + k] : B[k*ldb + n].
+    // Raw values only: the scale and the triangular mask are applied when the tile is written to LDS, so no
+    // arithmetic waits on an outstanding load.  FULL: the tile is entirely in range and 16-byte aligned.
     f32x4 a[2], b[2];
+    float a_scale;
+    bool a_mask;
+    int64_t am0, ak0;   // A tile origin (for the mask)
 
-    __device__ static inline f32x4 load4(const float* base, int64_t idx0, int64_t step, int valid, bool vec) {
+    __device__ static inline f32x4 load4(const float* base, int64_t idx0, int valid, bool vec) {
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
         if (valid >= 4 && vec) {
             v = *reinterpret_cast<const f32x4*>(base + idx0);
         } else {
             for (int e = 0; e < 4; ++e)
-                if (e < valid) v[e] = base[idx0 + e * step];
+                if (e < valid) v[e] = base[idx0 + e];
         }
         return v;
     }
@@ -38,62 +43,68 @@ struct TileIO {
     // Loads the A tile rows [m0, m0+128) x cols [k0, k0+16) of pair operand (ptr, ld) into registers.
     __device__ inline void load_a(const float* A, int64_t lda, int64_t M, int64_t kEnd, int64_t m0, int64_t k0,
                                   bool vec, float scale, bool strict_upper_mask, int tid) {
+        a_scale = scale;
+        a_mask = strict_upper_mask;
+        am0 = m0;
+        ak0 = k0;
+#pragma unroll
         for (int i = 0; i < 2; ++i) {
             int64_t m, k;
             if (!TA) { m = m0 + (tid >> 2) + 64 * i; k = k0 + (tid & 3) * 4; }
             else     { k = k0 + (tid >> 5) + 8 * i;  m = m0 + (tid & 31) * 4; }
+            if (FULL) {
+                a[i] = *reinterpret_cast<const f32x4*>(A + (TA ? k * lda + m : m * lda + k));
+                continue;
+            }
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
             if (!TA) {
-                if (m < M && k < kEnd) {
-                    int valid = (int)min<int64_t>(4, kEnd - k);
-                    v = load4(A, m * lda + k, 1, valid, vec);
-                }
+                if (m < M && k < kEnd) v = load4(A, m * lda + k, (int)min<int64_t>(4, kEnd - k), vec);
             } else {
-                if (k < kEnd && m < M) {
-                    int valid = (int)min<int64_t>(4, M - m);
-                    v = load4(A, k * lda + m, 1, valid, vec);
-                }
+                if (k < kEnd && m < M) v = load4(A, k * lda + m, (int)min<int64_t>(4, M - m), vec);
             }
-            if (strict_upper_mask) {
-                for (int e = 0; e < 4; ++e) {
-                    int64_t me = TA ? m + e : m, ke = TA ? k : k + e;
-                    if (ke <= me) v[e] = 0.f;
-                }
-            }
-            a[i] = v * scale;
+            a[i] = v;
         }
     }
 
     __device__ inline void load_b(const float* B, int64_t ldb, int64_t N, int64_t kEnd, int64_t n0, int64_t k0,
                                   bool vec, int tid) {
+#pragma unroll
         for (int i = 0; i < 2; ++i) {
             int64_t n, k;
             if (!TB) { k = k0 + (tid >> 5) + 8 * i;  n = n0 + (tid & 31) * 4; }
             else     { n = n0 + (tid >> 2) + 64 * i; k = k0 + (tid & 3) * 4; }
+            if (FULL) {
+                b[i] = *reinterpret_cast<const f32x4*>(B + (TB ? n * ldb + k : k * ldb + n));
+                continue;
+            }
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
             if (!TB) {
-                if (k < kEnd && n < N) {
-                    int valid = (int)min<int64_t>(4, N - n);
-                    v = load4(B, k * ldb + n, 1, valid, vec);
-                }
+                if (k < kEnd && n < N) v = load4(B, k * ldb + n, (int)min<int64_t>(4, N - n), vec);
             } else {
-                if (n < N && k < kEnd) {
-                    int valid = (int)min<int64_t>(4, kEnd - k);
-                    v = load4(B, n * ldb + k, 1, valid, vec);
-                }
+                if (n < N && k < kEnd) v = load4(B, n * ldb + k, (int)min<int64_t>(4, kEnd - k), vec);
             }
             b[i] = v;
         }
     }
 
     __device__ inline void store(float (*As)[kTM + kPad], float (*Bs)[kTN + kPad], int tid) const {
+#pragma unroll
         for (int i = 0; i < 2; ++i) {
+            f32x4 va = a[i] * a_scale;
+            if (a_mask) {
+                for (int e = 0; e < 4; ++e) {
+                    int64_t me, ke;
+                    if (!TA) { me = am0 + (tid >> 2) + 64 * i; ke = ak0 + (tid & 3) * 4 + e; }
+                    else     { ke = ak0 + (tid >> 5) + 8 * i;  me = am0 + (tid & 31) * 4 + e; }
+                    if (ke <= me) va[e] = 0.f;
+                }
+            }
             if (!TA) {
                 int r = (tid >> 2) + 64 * i, kc = (tid & 3) * 4;
-                for (int e = 0; e < 4; ++e) As[kc + e][r] = a[i][e];
+                for (int e = 0; e < 4; ++e) As[kc + e][r] = va[e];
             } else {
                 int kr = (tid >> 5) + 8 * i, mc = (tid & 31) * 4;
-                *reinterpret_cast<f32x4*>(&As[kr][mc]) = a[i];
+                *reinterpret_cast<f32x4*>(&As[kr][mc]) = va;
             }
             if (!TB) {
                 int kr = (tid >> 5) + 8 * i, nc = (tid & 31) * 4;
@@ -106,7 +117,7 @@ struct TileIO {
     }
 };
 
-template <bool TA, bool TB>
+template <bool TA, bool TB, bool FULL>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(16))) float As[2][kTK][kTM + kPad];
     __shared__ __attribute__((aligned(16))) float Bs[2][kTK][kTN + kPad];
@@ -141,7 +152,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
         for (int b = 0; b < 2; ++b)
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    TileIO<TA, TB> io;
+    TileIO<TA, TB, FULL> io;
     auto load = [&](int64_t t) {
         if (t < nt1) {
             int64_t k0 = klo + t * kTK;
@@ -210,10 +221,17 @@ hipError_t gemm_f32(GemmArgs p, int64_t batch, hipStream_t stream) {
     p.vecB2 = vec_ok(p.B2, p.ldb2, p.strideB2);
     dim3 grid((unsigned)ceil_div(p.N, kTN), (unsigned)ceil_div(p.M, kTM), (unsigned)batch);
     if (grid.y > 65535u || grid.z > 65535u) return hipErrorInvalidValue;
-    if (!p.transA && !p.transB) hipLaunchKernelGGL((gemm_f32_kernel<false, false>), grid, dim3(256), 0, stream, p);
-    else if (!p.transA && p.transB) hipLaunchKernelGGL((gemm_f32_kernel<false, true>), grid, dim3(256), 0, stream, p);
-    else if (p.transA && !p.transB) hipLaunchKernelGGL((gemm_f32_kernel<true, false>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((gemm_f32_kernel<true, true>), grid, dim3(256), 0, stream, p);
+    // Whole tiles only, every operand 16-byte vectorisable: no per-element guards in the k-loop.
+    const bool full = p.M % kTM == 0 && p.N % kTN == 0 && p.K1 % kTK == 0 && p.vecA1 && p.vecB1 &&
+                      (!p.A2 || (p.K2 % kTK == 0 && p.vecA2 && p.vecB2));
+#define GPTQ_GEMM_LAUNCH(TA_, TB_)                                                                          \
+    if (full) hipLaunchKernelGGL((gemm_f32_kernel<TA_, TB_, true>), grid, dim3(256), 0, stream, p);       \
+    else hipLaunchKernelGGL((gemm_f32_kernel<TA_, TB_, false>), grid, dim3(256), 0, stream, p);
+    if (!p.transA && !p.transB) { GPTQ_GEMM_LAUNCH(false, false) }
+    else if (!p.transA && p.transB) { GPTQ_GEMM_LAUNCH(false, true) }
+    else if (p.transA && !p.transB) { GPTQ_GEMM_LAUNCH(true, false) }
+    else { GPTQ_GEMM_LAUNCH(true, true) }
+#undef GPTQ_GEMM_LAUNCH
     return hipGetLastError();
 }
 

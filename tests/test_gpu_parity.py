@@ -112,7 +112,7 @@ def _workload_H(K, M=None, seed=0, dead_cols=()):
     return O.gram([X]).astype(np.float32).astype(np.float64)
 
 
-@pytest.mark.parametrize("K", [1, 2, 3, 127, 128, 129, 300, 1024])
+@pytest.mark.parametrize("K", [1, 2, 3, 127, 128, 129, 300, 640, 1000, 1024, 2048])
 def test_prepare(g, K):
     dead_cols = [k for k in (0, 5, K - 1) if k < K and K > 3]
     H = _workload_H(K, seed=K, dead_cols=dead_cols)
