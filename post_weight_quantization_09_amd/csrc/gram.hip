@@ -35,13 +35,42 @@ constexpr int kGPitch = kGT;  // LDS row pitch in bf16 elements (512 B; all read
 
 __device__ inline int mfma32_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-// Tile t -> (row block, column block): row-major over all nb x nb blocks (cross term) or over the upper
-// triangle.  Out-of-range t gives bi = nb (callers return early).
+#ifndef GPTQ_GRAM_GROUP
+#define GPTQ_GRAM_GROUP 8       // tiles are enumerated in G x G groups (see tile_coords)
+#endif
+
+// Tile t -> (row block, column block) over all nb x nb blocks (cross term) or over the upper triangle.
+// Tiles are enumerated group by group, G x G blocks at a time (groups row-major; inside a group row-major,
+// upper part only on diagonal groups of the symmetric case).  The workgroups that run together on one XCD
+// take consecutive tiles of one token split, so a compact group makes them share the same few column slabs
+// in that XCD's L2.  Out-of-range t gives bi = nb (callers return early).
 __device__ inline void tile_coords(int t, int nb, bool full, int& bi, int& bj) {
-    if (full) { bi = t / nb; bj = t % nb; return; }
-    int b = 0, rem = t;
-    while (b < nb && rem >= nb - b) { rem -= nb - b; ++b; }
-    bi = b; bj = b + rem;
+    constexpr int G = GPTQ_GRAM_GROUP;
+    const int ng = (nb + G - 1) / G;
+    int rem = t;
+    for (int I = 0; I < ng; ++I) {
+        const int gi = min(G, nb - I * G);
+        for (int J = full ? 0 : I; J < ng; ++J) {
+            const int gj = min(G, nb - J * G);
+            const bool diag = !full && I == J;
+            const int cnt = diag ? gi * (gi + 1) / 2 : gi * gj;
+            if (rem < cnt) {
+                if (diag) {
+                    int b = 0;
+                    while (rem >= gi - b) { rem -= gi - b; ++b; }
+                    bi = I * G + b;
+                    bj = I * G + b + rem;
+                } else {
+                    bi = I * G + rem / gj;
+                    bj = J * G + rem % gj;
+                }
+                return;
+            }
+            rem -= cnt;
+        }
+    }
+    bi = nb;
+    bj = nb;
 }
 
 // Loads 8 consecutive bf16 (16 bytes) of row `tok`, columns [col, col+8), zero outside [0,M) x [0,K).
