@@ -59,3 +59,23 @@ def check_codes(gpu: dict, W: np.ndarray, U_ref: np.ndarray, bits: int, dead=Non
         assert abs(Jg - Jr) <= OBJ_TOL * abs(Jr), f"{label}: objective {Jg} vs {Jr}"
         info["J_gpu"], info["J_ref"] = Jg, Jr
     return info
+
+
+def inverse_factor_residual(H32: np.ndarray, U_rows: np.ndarray, rows: np.ndarray, dead: np.ndarray,
+                            damp: float, chunk: int = 2048) -> np.ndarray:
+    """(U H_d U^T)[rows, rows] - I in float64, from the full fp32 Hessian and the sampled rows of U.
+
+    H_d is H with dead diagonal entries set to 1 and damp added to the diagonal.  UᵀU = H_d⁻¹ with U upper
+    is equivalent to U H_d Uᵀ = I (U invertible), a property that holds at any size, so sampled rows of U
+    can be checked without a full-size reference factorisation.  H is streamed in row chunks.
+    """
+    K = H32.shape[0]
+    Us = np.asarray(U_rows, np.float64)                      # len(rows) x K
+    Y = np.empty((K, Us.shape[0]))
+    for r0 in range(0, K, chunk):
+        Y[r0:r0 + chunk] = H32[r0:r0 + chunk].astype(np.float64) @ Us.T
+    fix = np.full(K, float(damp))
+    d = np.asarray(dead, bool)
+    fix[d] += 1.0 - H32[np.flatnonzero(d), np.flatnonzero(d)].astype(np.float64)
+    Y += fix[:, None] * Us.T
+    return Us @ Y - np.eye(len(rows))

@@ -9,7 +9,7 @@ import torch
 
 import oracle as O
 import workloads
-from tests.parity import H_TOL, check_codes, np64, rel_fro
+from tests.parity import H_TOL, check_codes, inverse_factor_residual, np64, rel_fro
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -76,3 +76,137 @@ def test_c2_prepare_and_quantize_sampled_channels(g, c2):
     info = check_codes(sub, Wn, ref["U"], cfg.bits, dead=ref["dead"], H_obj=Hs, label="c2 full-size")
     print(f"c2 quantize (64 sampled channels of {cfg.N}): inband={info['n_inband']} adopted={info['n_adopted']} "
           f"loss rel max={info['loss_rel_max']:.2e} J={info['J_gpu']:.6e}/{info['J_ref']:.6e}", flush=True)
+
+
+# ------------------------------------------------------------------------------------------------------------
+# The other layer workloads at full size: C3 (down_proj 8B, K = 14336, four output-channel groups with their
+# own token-weighted Hessians), C4 (up_proj 8B with asymmetric calibration), C5 (70B down_proj, K = 28672, with
+# 287 dead input channels).  Gram blocks are checked exactly on sampled coordinates; U through the
+# U H_d U^T = I property on sampled rows (no full-size reference factorisation is needed); the column loop on
+# sampled channels against the oracle run with the library's own U (and P1), so that each stage is checked
+# on its own inputs.
+# ------------------------------------------------------------------------------------------------------------
+RESID_TOL = 1e-4   # |U H_d U^T - I| on sampled rows: fp32 rounding gives ~1e-6 here; a 1% damping error gives ~1e-2
+
+
+def _make(cfg):
+    W = workloads.make_weights(cfg, device=DEV)
+    X = torch.empty(cfg.M, cfg.K, dtype=cfg.torch_x_dtype, device=DEV)
+    Xf = torch.empty_like(X) if cfg.asym_noise > 0 else None
+    workloads.ActivationSource(cfg, DEV).fill(X, Xf)
+    rho = workloads.make_group_row_weights(cfg, device=DEV)
+    torch.cuda.synchronize()
+    print(f"generated {cfg.name}: X {tuple(X.shape)}", flush=True)
+    return W, X, Xf, rho
+
+
+def _sample(K, n, seed, extra=()):
+    rng = np.random.default_rng(seed)
+    S = rng.choice(K, size=min(n, K), replace=False)
+    return np.unique(np.concatenate([S, [0, K - 1], np.asarray(extra, np.int64)])).astype(np.int64)
+
+
+def _cols(T, S):
+    return T.index_select(1, torch.tensor(S, device=T.device)).float().cpu().numpy()
+
+
+def _block_err(Hg, ref, S, label):
+    got = np64(Hg)[np.ix_(S, S)] if isinstance(Hg, torch.Tensor) else Hg
+    err = rel_fro(got, ref)
+    print(f"{label}: sampled {len(S)}x{len(S)} block rel fro {err:.3e}", flush=True)
+    return err
+
+
+def _prepare_and_check(g, H, cfg, label, rows_seed):
+    """Full-size prepare on the GPU; checks dead set, damping and the factor property on sampled rows."""
+    H32 = H.cpu().numpy()
+    diag = np.diag(H32).astype(np.float64)
+    dead_ref = diag == 0.0
+    damp_ref = cfg.percdamp * np.where(dead_ref, 1.0, diag).mean()
+    dead, damp, n_dead = g.gptq_prepare(H, cfg.percdamp)
+    assert np.array_equal(dead.cpu().numpy().astype(bool), dead_ref)
+    assert n_dead == int(dead_ref.sum())
+    assert abs(damp - damp_ref) <= 1e-6 * damp_ref
+    rows = _sample(cfg.K, 24, rows_seed, extra=np.flatnonzero(dead_ref)[:2])
+    Ur = H.index_select(0, torch.tensor(rows, device=H.device)).cpu().numpy()
+    for i, r in enumerate(rows):
+        assert np.count_nonzero(Ur[i, :r]) == 0, f"{label}: row {r} of U not upper triangular"
+    R = inverse_factor_residual(H32, Ur, rows, dead_ref, damp)
+    print(f"{label}: prepare n_dead={n_dead} damp={damp:.6e} |U H_d U^T - I| max on {len(rows)} rows "
+          f"{np.abs(R).max():.3e}", flush=True)
+    assert np.abs(R).max() <= RESID_TOL
+    return dead, dead_ref
+
+
+def _loop_check(g, W, U, dead, bits, chans, label, P1=None):
+    out = g.gptq_quantize_layer(W, U, bits, dead=dead, P1=P1, losses=torch.empty(W.shape[1], device=DEV))
+    C = torch.tensor(chans, device=DEV)
+    sub = {"codes": out["codes"][:, C], "scales": out["scales"][C], "losses": out["losses"][C]}
+    U64 = np64(U)
+    P64 = np64(P1) if P1 is not None else None
+    info = check_codes(sub, W.float().cpu().numpy()[:, chans], U64, bits, dead=dead.cpu().numpy().astype(bool),
+                       P1=P64, label=label)
+    print(f"{label}: column loop on {len(chans)} sampled channels: inband={info['n_inband']} "
+          f"adopted={info['n_adopted']} loss rel max={info['loss_rel_max']:.2e}", flush=True)
+
+
+def test_c3_group_gram_prepare_loop(g):
+    cfg = workloads.CONFIGS["c3_down_proj_8b_g4"]
+    W, X, _, rho = _make(cfg)
+    gi = 2
+    H = torch.zeros(cfg.K, cfg.K, device=DEV)
+    g.gptq_accumulate_hessian(H, X, row_scale=rho[gi].contiguous())
+    S = _sample(cfg.K, 40, 31)
+    ref = O.gram_row_scaled(_cols(X, S), rho[gi].cpu().numpy())
+    assert _block_err(H, ref, S, "c3 group 2 Gram") <= H_TOL
+    del X
+    torch.cuda.empty_cache()
+    dead, _ = _prepare_and_check(g, H, cfg, "c3 group 2", 32)
+    gs = cfg.N // cfg.groups
+    Wg = W[:, gi * gs:(gi + 1) * gs]
+    _loop_check(g, Wg, H, dead, cfg.bits, np.sort(np.random.default_rng(33).choice(gs, 16, replace=False)),
+                "c3 group 2")
+
+
+def test_c4_gptaq_gram_prepare_asym_loop(g):
+    cfg = workloads.CONFIGS["c4_up_proj_8b_gptaq"]
+    W, X, Xf, _ = _make(cfg)
+    H = torch.zeros(cfg.K, cfg.K, device=DEV)
+    A = torch.zeros(cfg.K, cfg.K, device=DEV)
+    g.gptq_accumulate_hessian(H, X, X_float=Xf, A=A)
+    S = _sample(cfg.K, 40, 41)
+    Xs, Xfs = _cols(X, S), _cols(Xf, S)
+    assert _block_err(H, O.gram([Xs]), S, "c4 Gram") <= H_TOL
+    assert _block_err(A, O.cross_gram(Xfs, Xs), S, "c4 cross Gram") <= H_TOL
+    del X, Xf
+    torch.cuda.empty_cache()
+    H64 = np64(H)
+    dead, damp, n_dead = g.gptq_prepare(H, cfg.percdamp)
+    ref = O.prepare(H64, cfg.percdamp)
+    U64 = np64(H)
+    uerr = float(np.abs(U64 - ref["U"]).max() / np.abs(ref["U"]).max())
+    print(f"c4 prepare K={cfg.K}: U max rel err {uerr:.3e}", flush=True)
+    assert uerr <= 1e-3
+    P1 = g.gptq_asym_correction(H, A)
+    P1_ref = O.asym_correction(U64, np64(A))
+    perr = rel_fro(np64(P1), P1_ref)
+    print(f"c4 P1 (full {cfg.K}x{cfg.K}) rel fro {perr:.3e}", flush=True)
+    assert perr <= 1e-4
+    _loop_check(g, W, H, dead, cfg.bits, np.sort(np.random.default_rng(43).choice(cfg.N, 16, replace=False)),
+                "c4", P1=P1)
+
+
+def test_c5_gram_prepare_loop(g):
+    cfg = workloads.CONFIGS["c5_down_proj_70b"]
+    W, X, _, _ = _make(cfg)
+    dead_idx = workloads.dead_channels(cfg)
+    assert len(dead_idx) == round(0.01 * cfg.K)
+    H = torch.zeros(cfg.K, cfg.K, device=DEV)
+    g.gptq_accumulate_hessian(H, X)
+    S = _sample(cfg.K, 40, 51, extra=dead_idx[:3])
+    assert _block_err(H, O.gram([_cols(X, S)]), S, "c5 Gram") <= H_TOL
+    del X
+    torch.cuda.empty_cache()
+    dead, dead_ref = _prepare_and_check(g, H, cfg, "c5", 52)
+    assert np.array_equal(np.flatnonzero(dead_ref), dead_idx)
+    _loop_check(g, W, H, dead, cfg.bits, np.sort(np.random.default_rng(53).choice(cfg.N, 16, replace=False)), "c5")
