@@ -5,29 +5,52 @@
 // after a block, the far weights are updated with one matrix product) and the two products of the GPTAQ
 // correction ([R] item 3).
 //
-// Tiling: 256 threads = 4 waves, a 128 x 128 tile of C per workgroup, 64 x 64 per wave as 2 x 2
-// v_mfma_f32_32x32x2_f32 accumulators.  k advances 16 at a time through double-buffered LDS tiles stored
-// k-major (As[k][m], Bs[k][n]) so that every MFMA operand read is a conflict-free ds_read_b32.
+// Tiling: 256 threads = 4 waves in 2 x 2, a TM x TN tile of C per workgroup (64 x 64 in use), each wave
+// (TM/2) x (TN/2) as 32 x 32 v_mfma_f32_32x32x2_f32 accumulators.  k advances TK = 16 at a time through
+// double-buffered LDS tiles stored k-major (As[k][m], Bs[k][n]) so that every MFMA operand read is a
+// conflict-free ds_read_b32.
 #include "gemm_f32.hpp"
 
 namespace gptq {
 
 namespace {
 
-constexpr int kTM = 128, kTN = 128, kTK = 16, kPad = 4;
+constexpr int kPad = 4;
 
 // MFMA 32x32x2 f32 output layout: lane l, accumulator register r -> (row, col) inside the 32 x 32 block.
 __device__ inline int mfma32_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
-template <bool TA, bool TB, bool FULL>
+// Tile configuration: TM x TN outputs per workgroup (4 waves in 2 x 2, each (TM/2) x (TN/2) as 32 x 32 MFMA
+// blocks), TK reduction steps per LDS stage.
+template <int TM, int TN, int TK>
+struct Tile {
+    static constexpr int MA = TM / 64, NB = TN / 64;       // 32 x 32 blocks per wave along m and n
+    static constexpr int NVA = TM * TK / 1024;             // f32x4 loads per thread for the A tile
+    static constexpr int NVB = TN * TK / 1024;
+    static_assert(TM % 64 == 0 && TN % 64 == 0 && TK % 4 == 0 && NVA >= 1 && NVB >= 1, "tile shape");
+};
+
+template <int TM, int TN, int TK, bool TA, bool TB, bool FULL>
 struct TileIO {
+    using T = Tile<TM, TN, TK>;
     // A(m,k): TA ? A[k*lda + m] : A[m*lda + k].   B(k,n): TB ? B[n*ldb + k] : B[k*ldb + n].
     // Raw values only: the scale and the triangular mask are applied when the tile is written to LDS, so no
     // arithmetic waits on an outstanding load.  FULL: the tile is entirely in range and 16-byte aligned.
-    f32x4 a[2], b[2];
+    f32x4 a[T::NVA], b[T::NVB];
     float a_scale;
     bool a_mask;
     int64_t am0, ak0;   // A tile origin (for the mask)
+
+    // Element (m, k) of the i-th A vector of thread tid (relative to the tile origin); the vector runs along
+    // k (not TA) or along m (TA).
+    __device__ static inline void a_pos(int i, int tid, int& m, int& k) {
+        if (!TA) { constexpr int C = TK / 4; m = tid / C + (256 / C) * i; k = (tid % C) * 4; }
+        else     { constexpr int C = TM / 4; k = tid / C + (256 / C) * i; m = (tid % C) * 4; }
+    }
+    __device__ static inline void b_pos(int i, int tid, int& n, int& k) {
+        if (!TB) { constexpr int C = TN / 4; k = tid / C + (256 / C) * i; n = (tid % C) * 4; }
+        else     { constexpr int C = TK / 4; n = tid / C + (256 / C) * i; k = (tid % C) * 4; }
+    }
 
     __device__ static inline f32x4 load4(const float* base, int64_t idx0, int valid, bool vec) {
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
@@ -40,7 +63,6 @@ struct TileIO {
         return v;
     }
 
-    // Loads the A tile rows [m0, m0+128) x cols [k0, k0+16) of pair operand (ptr, ld) into registers.
     __device__ inline void load_a(const float* A, int64_t lda, int64_t M, int64_t kEnd, int64_t m0, int64_t k0,
                                   bool vec, float scale, bool strict_upper_mask, int tid) {
         a_scale = scale;
@@ -48,10 +70,10 @@ struct TileIO {
         am0 = m0;
         ak0 = k0;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int64_t m, k;
-            if (!TA) { m = m0 + (tid >> 2) + 64 * i; k = k0 + (tid & 3) * 4; }
-            else     { k = k0 + (tid >> 5) + 8 * i;  m = m0 + (tid & 31) * 4; }
+        for (int i = 0; i < T::NVA; ++i) {
+            int mi, ki;
+            a_pos(i, tid, mi, ki);
+            const int64_t m = m0 + mi, k = k0 + ki;
             if (FULL) {
                 a[i] = *reinterpret_cast<const f32x4*>(A + (TA ? k * lda + m : m * lda + k));
                 continue;
@@ -69,10 +91,10 @@ struct TileIO {
     __device__ inline void load_b(const float* B, int64_t ldb, int64_t N, int64_t kEnd, int64_t n0, int64_t k0,
                                   bool vec, int tid) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            int64_t n, k;
-            if (!TB) { k = k0 + (tid >> 5) + 8 * i;  n = n0 + (tid & 31) * 4; }
-            else     { n = n0 + (tid >> 2) + 64 * i; k = k0 + (tid & 3) * 4; }
+        for (int i = 0; i < T::NVB; ++i) {
+            int ni, ki;
+            b_pos(i, tid, ni, ki);
+            const int64_t n = n0 + ni, k = k0 + ki;
             if (FULL) {
                 b[i] = *reinterpret_cast<const f32x4*>(B + (TB ? n * ldb + k : k * ldb + n));
                 continue;
@@ -87,49 +109,51 @@ struct TileIO {
         }
     }
 
-    __device__ inline void store(float (*As)[kTM + kPad], float (*Bs)[kTN + kPad], int tid) const {
+    __device__ inline void store(float (*As)[TM + kPad], float (*Bs)[TN + kPad], int tid) const {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < T::NVA; ++i) {
+            int mi, ki;
+            a_pos(i, tid, mi, ki);
             f32x4 va = a[i] * a_scale;
             if (a_mask) {
                 for (int e = 0; e < 4; ++e) {
-                    int64_t me, ke;
-                    if (!TA) { me = am0 + (tid >> 2) + 64 * i; ke = ak0 + (tid & 3) * 4 + e; }
-                    else     { ke = ak0 + (tid >> 5) + 8 * i;  me = am0 + (tid & 31) * 4 + e; }
+                    const int64_t me = am0 + mi + (TA ? e : 0), ke = ak0 + ki + (TA ? 0 : e);
                     if (ke <= me) va[e] = 0.f;
                 }
             }
             if (!TA) {
-                int r = (tid >> 2) + 64 * i, kc = (tid & 3) * 4;
-                for (int e = 0; e < 4; ++e) As[kc + e][r] = va[e];
+                for (int e = 0; e < 4; ++e) As[ki + e][mi] = va[e];
             } else {
-                int kr = (tid >> 5) + 8 * i, mc = (tid & 31) * 4;
-                *reinterpret_cast<f32x4*>(&As[kr][mc]) = va;
+                *reinterpret_cast<f32x4*>(&As[ki][mi]) = va;
             }
+        }
+#pragma unroll
+        for (int i = 0; i < T::NVB; ++i) {
+            int ni, ki;
+            b_pos(i, tid, ni, ki);
             if (!TB) {
-                int kr = (tid >> 5) + 8 * i, nc = (tid & 31) * 4;
-                *reinterpret_cast<f32x4*>(&Bs[kr][nc]) = b[i];
+                *reinterpret_cast<f32x4*>(&Bs[ki][ni]) = b[i];
             } else {
-                int r = (tid >> 2) + 64 * i, kc = (tid & 3) * 4;
-                for (int e = 0; e < 4; ++e) Bs[kc + e][r] = b[i][e];
+                for (int e = 0; e < 4; ++e) Bs[ki + e][ni] = b[i][e];
             }
         }
     }
 };
 
-template <bool TA, bool TB, bool FULL>
+template <int TM, int TN, int TK, bool TA, bool TB, bool FULL>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) float As[2][kTK][kTM + kPad];
-    __shared__ __attribute__((aligned(16))) float Bs[2][kTK][kTN + kPad];
+    using T = Tile<TM, TN, TK>;
+    __shared__ __attribute__((aligned(16))) float As[2][TK][TM + kPad];
+    __shared__ __attribute__((aligned(16))) float Bs[2][TK][TN + kPad];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = (int64_t)blockIdx.y * kTM;
-    const int64_t n0 = (int64_t)blockIdx.x * kTN;
+    const int64_t m0 = (int64_t)blockIdx.y * TM;
+    const int64_t n0 = (int64_t)blockIdx.x * TN;
     const int64_t bz = blockIdx.z;
     if (m0 >= p.M || n0 >= p.N) return;
-    if ((p.flags & kGemmCUpper) && m0 >= n0 + kTN) return;
+    if ((p.flags & kGemmCUpper) && m0 >= n0 + TN) return;
 
     const float* A1 = p.A1 + bz * p.strideA1;
     const float* B1 = p.B1 + bz * p.strideB1;
@@ -140,26 +164,26 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
     int64_t klo = 0, khi = p.K1;
     if (p.flags & (kGemmAUpper | kGemmAStrictUpperMask)) klo = max<int64_t>(klo, m0);
     if (p.flags & kGemmBLower) klo = max<int64_t>(klo, n0);
-    if (p.flags & kGemmBUpper) khi = min<int64_t>(khi, n0 + kTN);
-    klo = (klo / kTK) * kTK;
-    const int64_t nt1 = khi > klo ? ceil_div(khi - klo, kTK) : 0;
-    const int64_t nt2 = (A2 && p.K2 > 0) ? ceil_div(p.K2, kTK) : 0;
+    if (p.flags & kGemmBUpper) khi = min<int64_t>(khi, n0 + TN);
+    klo = (klo / TK) * TK;
+    const int64_t nt1 = khi > klo ? ceil_div(khi - klo, TK) : 0;
+    const int64_t nt2 = (A2 && p.K2 > 0) ? ceil_div(p.K2, TK) : 0;
     const int64_t nt = nt1 + nt2;
     const bool mask = (p.flags & kGemmAStrictUpperMask) != 0;
 
-    f32x16 acc[2][2];
-    for (int a = 0; a < 2; ++a)
-        for (int b = 0; b < 2; ++b)
+    f32x16 acc[T::MA][T::NB];
+    for (int a = 0; a < T::MA; ++a)
+        for (int b = 0; b < T::NB; ++b)
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    TileIO<TA, TB, FULL> io;
+    TileIO<TM, TN, TK, TA, TB, FULL> io;
     auto load = [&](int64_t t) {
         if (t < nt1) {
-            int64_t k0 = klo + t * kTK;
+            int64_t k0 = klo + t * TK;
             io.load_a(A1, p.lda1, p.M, p.K1, m0, k0, p.vecA1, 1.0f, mask, tid);
             io.load_b(B1, p.ldb1, p.N, p.K1, n0, k0, p.vecB1, tid);
         } else {
-            int64_t k0 = (t - nt1) * kTK;
+            int64_t k0 = (t - nt1) * TK;
             io.load_a(A2, p.lda2, p.M, p.K2, m0, k0, p.vecA2, p.a2_scale, false, tid);
             io.load_b(B2, p.ldb2, p.N, p.K2, n0, k0, p.vecB2, tid);
         }
@@ -174,13 +198,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
         const int buf = (int)(t & 1);
         if (t + 1 < nt) load(t + 1);
 #pragma unroll
-        for (int kk = 0; kk < kTK / 2; ++kk) {
+        for (int kk = 0; kk < TK / 2; ++kk) {
             const int k = 2 * kk + (lane >> 5);
-            float av[2], bv[2];
-            for (int a = 0; a < 2; ++a) av[a] = As[buf][k][wm * 64 + 32 * a + (lane & 31)];
-            for (int b = 0; b < 2; ++b) bv[b] = Bs[buf][k][wn * 64 + 32 * b + (lane & 31)];
-            for (int a = 0; a < 2; ++a)
-                for (int b = 0; b < 2; ++b)
+            float av[T::MA], bv[T::NB];
+            for (int a = 0; a < T::MA; ++a) av[a] = As[buf][k][wm * (TM / 2) + 32 * a + (lane & 31)];
+            for (int b = 0; b < T::NB; ++b) bv[b] = Bs[buf][k][wn * (TN / 2) + 32 * b + (lane & 31)];
+            for (int a = 0; a < T::MA; ++a)
+                for (int b = 0; b < T::NB; ++b)
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
         }
         if (t + 1 < nt) io.store(As[buf ^ 1], Bs[buf ^ 1], tid);
@@ -188,12 +212,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
     }
 
     // Epilogue: C = alpha * acc + beta * C.
-    for (int a = 0; a < 2; ++a) {
-        for (int b = 0; b < 2; ++b) {
-            const int64_t col = n0 + wn * 64 + 32 * b + (lane & 31);
+    for (int a = 0; a < T::MA; ++a) {
+        for (int b = 0; b < T::NB; ++b) {
+            const int64_t col = n0 + wn * (TN / 2) + 32 * b + (lane & 31);
             if (col >= p.N) continue;
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = m0 + wm * 64 + 32 * a + mfma32_row(r, lane);
+                const int64_t row = m0 + wm * (TM / 2) + 32 * a + mfma32_row(r, lane);
                 if (row >= p.M) continue;
                 float* cp = C + row * p.ldc + col;
                 float v = p.alpha * acc[a][b][r];
@@ -205,6 +229,25 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 }
 
 inline bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+
+template <int TM, int TN, int TK>
+hipError_t launch(const GemmArgs& p, int64_t batch, hipStream_t stream) {
+    dim3 grid((unsigned)ceil_div(p.N, TN), (unsigned)ceil_div(p.M, TM), (unsigned)batch);
+    if (grid.y > 65535u || grid.z > 65535u) return hipErrorInvalidValue;
+    // Whole tiles only, every operand 16-byte vectorisable: no per-element guards in the k-loop.
+    const bool full = p.M % TM == 0 && p.N % TN == 0 && p.K1 % TK == 0 && p.vecA1 && p.vecB1 &&
+                      (!p.A2 || (p.K2 % TK == 0 && p.vecA2 && p.vecB2));
+#define GPTQ_GEMM_LAUNCH(TA_, TB_)                                                                          \
+    if (full) hipLaunchKernelGGL((gemm_f32_kernel<TM, TN, TK, TA_, TB_, true>), grid, dim3(256), 0, stream, p); \
+    else hipLaunchKernelGGL((gemm_f32_kernel<TM, TN, TK, TA_, TB_, false>), grid, dim3(256), 0, stream, p);
+    if (!p.transA && !p.transB) { GPTQ_GEMM_LAUNCH(false, false) }
+    else if (!p.transA && p.transB) { GPTQ_GEMM_LAUNCH(false, true) }
+    else if (p.transA && !p.transB) { GPTQ_GEMM_LAUNCH(true, false) }
+    else { GPTQ_GEMM_LAUNCH(true, true) }
+#undef GPTQ_GEMM_LAUNCH
+    return hipGetLastError();
+}
 
 }  // namespace
 
@@ -219,20 +262,10 @@ hipError_t gemm_f32(GemmArgs p, int64_t batch, hipStream_t stream) {
     p.vecB1 = vec_ok(p.B1, p.ldb1, p.strideB1);
     p.vecA2 = vec_ok(p.A2, p.lda2, p.strideA2);
     p.vecB2 = vec_ok(p.B2, p.ldb2, p.strideB2);
-    dim3 grid((unsigned)ceil_div(p.N, kTN), (unsigned)ceil_div(p.M, kTM), (unsigned)batch);
-    if (grid.y > 65535u || grid.z > 65535u) return hipErrorInvalidValue;
-    // Whole tiles only, every operand 16-byte vectorisable: no per-element guards in the k-loop.
-    const bool full = p.M % kTM == 0 && p.N % kTN == 0 && p.K1 % kTK == 0 && p.vecA1 && p.vecB1 &&
-                      (!p.A2 || (p.K2 % kTK == 0 && p.vecA2 && p.vecB2));
-#define GPTQ_GEMM_LAUNCH(TA_, TB_)                                                                          \
-    if (full) hipLaunchKernelGGL((gemm_f32_kernel<TA_, TB_, true>), grid, dim3(256), 0, stream, p);       \
-    else hipLaunchKernelGGL((gemm_f32_kernel<TA_, TB_, false>), grid, dim3(256), 0, stream, p);
-    if (!p.transA && !p.transB) { GPTQ_GEMM_LAUNCH(false, false) }
-    else if (!p.transA && p.transB) { GPTQ_GEMM_LAUNCH(false, true) }
-    else if (p.transA && !p.transB) { GPTQ_GEMM_LAUNCH(true, false) }
-    else { GPTQ_GEMM_LAUNCH(true, true) }
-#undef GPTQ_GEMM_LAUNCH
-    return hipGetLastError();
+    // 64 x 64 tiles: measured on gfx950 they match 128 x 128 tiles on large products and beat them on the
+    // triangular ones (finer skipping), on the depth-128 trailing updates and on small products (more
+    // workgroups in flight); larger tiles lose occupancy.
+    return launch<64, 64, 16>(p, batch, stream);
 }
 
 }  // namespace gptq
