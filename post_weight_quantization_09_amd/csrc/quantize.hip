@@ -147,41 +147,66 @@ struct StepConst {
     float* pre_round; int64_t prow_off; int64_t N; bool live;
 };
 
-// One step j of the loop (j compile-time so that slots, DPP lane and LDS offsets are immediates).
+// Per-step operands read from LDS: this lane's 8 entries of U row J (and of P1 row J), 1 / U_JJ.  Step J
+// reads the operands of step J + 1 while it runs, so no LDS latency sits on the chain of dependent steps.
+struct StepOps {
+    f32x4 u0, u1, p0, p1;
+    float rd;
+};
+
 template <int J, bool ASYM>
-__device__ __forceinline__ void loop_step(LaneState& st, const StepConst& k) {
+__device__ __forceinline__ void load_ops(StepOps& o, const StepConst& k) {
+    if constexpr (J < kB) {
+        const f32x4* urow = reinterpret_cast<const f32x4*>(k.Up + (J * 16 + k.l) * 8);
+        o.u0 = urow[0];
+        o.u1 = urow[1];
+        if constexpr (ASYM) {
+            const f32x4* prow = reinterpret_cast<const f32x4*>(k.Pp + (J * 16 + k.l) * 8);
+            o.p0 = prow[0];
+            o.p1 = prow[1];
+        }
+        o.rd = k.rdiag[J];
+    }
+}
+
+// One step j of the loop (j compile-time so that slots, DPP lane and LDS offsets are immediates).
+template <int J, bool ASYM, bool PRE>
+__device__ __forceinline__ void loop_step(LaneState& st, const StepConst& k, StepOps (&ops)[2]) {
     constexpr int m = J >> 4, lj = J & 15;
+    const StepOps& o = ops[J & 1];
+    load_ops<J + 1, ASYM>(ops[(J + 1) & 1], k);
     const float wj = row_bcast(st.w[m], lj);
     const float v = wj * k.rs;
     const float c = fminf(fmaxf(rintf(v) + k.z, 0.f), k.qmax);
     const float q = (c - k.z) * k.s;
-    const float e = (wj - q) * k.rdiag[J];
-    st.loss = fmaf(e, e, st.loss);
-    const f32x4* urow = reinterpret_cast<const f32x4*>(k.Up + (J * 16 + k.l) * 8);
-    const f32x4 u0 = urow[0], u1 = urow[1];
-    const float uu[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-    if constexpr (ASYM) {
-        const f32x4* prow = reinterpret_cast<const f32x4*>(k.Pp + (J * 16 + k.l) * 8);
-        const f32x4 p0 = prow[0], p1 = prow[1];
-        const float pp[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-        for (int mm = m; mm < 8; ++mm) st.w[mm] = fmaf(pp[mm], wj, fmaf(-uu[mm], e, st.w[mm]));
-    } else {
-#pragma unroll
-        for (int mm = m; mm < 8; ++mm) st.w[mm] = fmaf(-uu[mm], e, st.w[mm]);
-    }
+    const float e = (wj - q) * o.rd;
+    const float uu[8] = {o.u0.x, o.u0.y, o.u0.z, o.u0.w, o.u1.x, o.u1.y, o.u1.z, o.u1.w};
     const bool owner = (k.l == lj);
-    st.w[m] = owner ? q : st.w[m];
+    if constexpr (ASYM) {
+        const float pp[8] = {o.p0.x, o.p0.y, o.p0.z, o.p0.w, o.p1.x, o.p1.y, o.p1.z, o.p1.w};
+        st.w[m] = owner ? q : fmaf(pp[m], wj, fmaf(-uu[m], e, st.w[m]));
+#pragma unroll
+        for (int mm = m + 1; mm < 8; ++mm) st.w[mm] = fmaf(pp[mm], wj, fmaf(-uu[mm], e, st.w[mm]));
+    } else {
+        st.w[m] = owner ? q : fmaf(-uu[m], e, st.w[m]);
+#pragma unroll
+        for (int mm = m + 1; mm < 8; ++mm) st.w[mm] = fmaf(-uu[mm], e, st.w[mm]);
+    }
+    st.loss = fmaf(e, e, st.loss);
     st.code[m] = owner ? (uint32_t)c : st.code[m];
     st.e[m] = owner ? e : st.e[m];
     if constexpr (ASYM) st.pre[m] = owner ? wj : st.pre[m];
-    if (k.pre_round && owner && k.live) k.pre_round[(int64_t)J * k.N + k.prow_off] = v;
+    if constexpr (PRE) {
+        if (owner && k.live) k.pre_round[(int64_t)J * k.N + k.prow_off] = v;
+    }
 }
 
-template <bool ASYM, int... Js>
+template <bool ASYM, bool PRE, int... Js>
 __device__ __forceinline__ void run_steps(LaneState& st, const StepConst& k, int bs,
                                           std::integer_sequence<int, Js...>) {
-    ((Js < bs ? loop_step<Js, ASYM>(st, k) : (void)0), ...);
+    StepOps ops[2];
+    load_ops<0, ASYM>(ops[0], k);
+    ((Js < bs ? loop_step<Js, ASYM, PRE>(st, k, ops) : (void)0), ...);
 }
 
 template <bool ASYM>
@@ -194,17 +219,39 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
     const int tid = threadIdx.x;
     const int64_t b0 = p.b0;
     const int bs = p.bs;
-    // stage the U (and P1) panel rows b0..b0+bs-1, columns b0..b0+127 (zero beyond the block)
-    for (int idx = tid; idx < kB * kB; idx += 256) {
-        const int j = idx >> 7, c = idx & 127;       // row j, column c = 16 m + l
-        const int l = c & 15, m = c >> 4;
-        float u = 0.f, pv = 0.f;
-        if (j < bs && c < bs) {
-            u = p.U[(b0 + j) * p.K + b0 + c];
-            if (ASYM) pv = p.P1[(b0 + j) * p.K + b0 + c];
+    // Stage the U (and P1) panel rows b0..b0+bs-1, columns b0..b0+127 (zero beyond the block) as
+    // [row j][lane l][slot m] for column 16 m + l.  All global loads are issued before the LDS stores.
+    {
+        constexpr int kV = kB * kB / 4 / 256;     // 16-byte vectors per thread
+        const bool vec = p.bs == kB && (p.K % 4) == 0 && (b0 % 4) == 0;
+        f32x4 uv[kV], pv[ASYM ? kV : 1];
+#pragma unroll
+        for (int i = 0; i < kV; ++i) {
+            const int idx = tid + 256 * i, j = idx >> 5, c = (idx & 31) * 4;
+            const int64_t off = (b0 + j) * p.K + b0 + c;
+            f32x4 u = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
+            if (vec) {
+                u = *reinterpret_cast<const f32x4*>(p.U + off);
+                if constexpr (ASYM) q = *reinterpret_cast<const f32x4*>(p.P1 + off);
+            } else if (j < bs) {
+                for (int e = 0; e < 4; ++e)
+                    if (c + e < bs) {
+                        u[e] = p.U[off + e];
+                        if constexpr (ASYM) q[e] = p.P1[off + e];
+                    }
+            }
+            uv[i] = u;
+            if constexpr (ASYM) pv[i] = q;
         }
-        Up[(j * 16 + l) * 8 + m] = u;
-        if (ASYM) Pp[(j * 16 + l) * 8 + m] = pv;
+#pragma unroll
+        for (int i = 0; i < kV; ++i) {
+            const int idx = tid + 256 * i, j = idx >> 5, c = (idx & 31) * 4;
+            for (int e = 0; e < 4; ++e) {
+                const int l = (c + e) & 15, m = (c + e) >> 4;
+                Up[(j * 16 + l) * 8 + m] = uv[i][e];
+                if constexpr (ASYM) Pp[(j * 16 + l) * 8 + m] = pv[i][e];
+            }
+        }
     }
     for (int j = tid; j < kB; j += 256) rdiag[j] = (j < bs) ? 1.0f / p.U[(b0 + j) * p.K + b0 + j] : 0.f;
     __syncthreads();
@@ -231,7 +278,8 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
     k.l = l;
     k.pre_round = p.pre_round ? p.pre_round + b0 * p.N : nullptr;
     k.prow_off = n; k.N = p.N; k.live = live;
-    run_steps<ASYM>(st, k, bs, std::make_integer_sequence<int, kB>{});
+    if (k.pre_round) run_steps<ASYM, true>(st, k, bs, std::make_integer_sequence<int, kB>{});
+    else run_steps<ASYM, false>(st, k, bs, std::make_integer_sequence<int, kB>{});
 
     if (!live) return;
     uint8_t* crow = p.codes_t + n * p.ldt + b0;
