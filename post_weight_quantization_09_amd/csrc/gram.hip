@@ -496,17 +496,29 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(GramArgs p, float* Out
     const bool mirror = !CROSS && !(same && wi == wj);
     const int64_t R0 = (int64_t)bi * kGT + wi * 128, C0 = (int64_t)bj * kGT + wj * 128;
 
-    const int lane = tid & 63, rg = tid >> 6;
+    // The partial of (split, tile, wave) is 256 registers x 64 lanes, contiguous.  Thread t sums elements
+    // 4 (t + 256 i) .. +3 over the splits in split order (the order of the original sequential sum), with
+    // eight splits' 16-byte loads in flight at a time.
     const int64_t qstride = (int64_t)p.ntiles * 4 * 256 * 64;
     const float* base = p.partial + ((int64_t)tile * 4 + wave) * (256 * 64);
-    for (int k = 0; k < 64; ++k) {
-        const int ri = rg * 64 + k;
-        float s = 0.f;
-        for (int sp = 0; sp < p.splits; ++sp) s += base[sp * qstride + ri * 64 + lane];
+    constexpr int kInFlight = 8;
+    for (int i = 0; i < 16; ++i) {
+        const int e = (tid + 256 * i) * 4;            // element (ri, lane0 .. lane0+3)
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+        int sp = 0;
+        for (; sp + kInFlight <= p.splits; sp += kInFlight) {
+            f32x4 v[kInFlight];
+#pragma unroll
+            for (int u = 0; u < kInFlight; ++u)
+                v[u] = *reinterpret_cast<const f32x4*>(base + (int64_t)(sp + u) * qstride + e);
+#pragma unroll
+            for (int u = 0; u < kInFlight; ++u) s += v[u];
+        }
+        for (; sp < p.splits; ++sp) s += *reinterpret_cast<const f32x4*>(base + (int64_t)sp * qstride + e);
+        const int ri = e >> 6, lane0 = e & 63;
         const int a = ri >> 6, b = (ri >> 4) & 3, r = ri & 15;
-        const int row = acc_row(a, r, lane);
-        const int col = acc_col(b, lane);
-        T[row][col] = 2.0f * s;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) T[acc_row(a, r, lane0 + q)][acc_col(b, lane0 + q)] = 2.0f * s[q];
     }
     __syncthreads();
     for (int i = 0; i < 64; ++i) {
