@@ -251,7 +251,7 @@ def main():
         "stages_ms": {k: round(v, 3) for k, v in stage.items()},
         "gram_tflops": round(gflop / (stage["gram"] * 1e-3) / 1e12, 1),
         "trailing_gemm_gflop": round(trailing_flops(cfg) * 1e-9, 1),
-        "roofline": {"bound": "mfma", "kernel": "gram_bf16_kernel + gram_reduce_kernel (one accumulate call)",
+        "roofline": {"bound": "mfma", "kernel": "gram_bf16_lds_kernel + gram_reduce_kernel (one accumulate call)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flop_per_launch": gram_flops(cfg), "launch_ms": round(gram_launch_ms, 3)},
