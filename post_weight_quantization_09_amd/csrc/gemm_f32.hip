@@ -5,10 +5,10 @@
 // after a block, the far weights are updated with one matrix product) and the two products of the GPTAQ
 // correction ([R] item 3).
 //
-// Tiling: 256 threads = 4 waves in 2 x 2, a TM x TN tile of C per workgroup (64 x 64 in use), each wave
-// (TM/2) x (TN/2) as 32 x 32 v_mfma_f32_32x32x2_f32 accumulators.  k advances TK = 16 at a time through
-// double-buffered LDS tiles stored k-major (As[k][m], Bs[k][n]) so that every MFMA operand read is a
-// conflict-free ds_read_b32.
+// Tiling: 256 threads = 4 waves in 2 x 2, a TM x TN tile of C per workgroup (64 x 64, or 128 x 128 for large
+// products), each wave (TM/2) x (TN/2) as 32 x 32 v_mfma_f32_32x32x2_f32 accumulators.  k advances TK = 16 at a
+// time through double-buffered LDS tiles stored k-major (As[k][m], Bs[k][n]) so that every MFMA operand read
+// is a conflict-free ds_read_b32.
 #include "gemm_f32.hpp"
 
 namespace gptq {
@@ -262,9 +262,10 @@ hipError_t gemm_f32(GemmArgs p, int64_t batch, hipStream_t stream) {
     p.vecB1 = vec_ok(p.B1, p.ldb1, p.strideB1);
     p.vecA2 = vec_ok(p.A2, p.lda2, p.strideA2);
     p.vecB2 = vec_ok(p.B2, p.ldb2, p.strideB2);
-    // 64 x 64 tiles: measured on gfx950 they match 128 x 128 tiles on large products and beat them on the
-    // triangular ones (finer skipping), on the depth-128 trailing updates and on small products (more
-    // workgroups in flight); larger tiles lose occupancy.
+    // Tile shape, measured on gfx950: 64 x 64 matches 128 x 128 on large products and beats it on triangular
+    // ones (finer skipping), on the depth-128 trailing updates and on small products (more workgroups in
+    // flight); from about 12k x 12k outputs on, 128 x 128 is ~5% faster (half the L2 traffic per flop).
+    if (p.M >= 12288 && p.N >= 12288 && p.K1 >= 1024) return launch<128, 128, 16>(p, batch, stream);
     return launch<64, 64, 16>(p, batch, stream);
 }
 
