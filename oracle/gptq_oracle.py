@@ -30,11 +30,14 @@ Readings where the pages are silent (each is listed with its reason in the desig
     reconstruction s*(c - z), round half to even then clamp; s from W before dead rows are zeroed
   * GPTAQ mask strictly upper, L = U^T, Hessian of the quantised stream (damped), coefficient = the
     coordinate's pre-rounding value at its step.
+  * CAE term: P2 from 2 X~^T X = H + A (no separate Gram, as [R] item 3 notes), same mask and L; its
+    coefficient is w0_q - w_q with w0 the original weight after dead rows are zeroed.
 
 Pins (tests/test_oracle_pins.py): the two- and three-weight worked examples of [T2]/[T7]/[T8] with their
 printed values, explicit-inverse sequential compensation and exhaustive search on tiny inputs, the factor's
 Schur property, lazy == eager blocks, the per-channel loss identity, invariance under H -> cH, dead
-coordinates, P1 against a per-step least-squares solve, Gram identities and bf16 rounding against torch.
+coordinates, P1 and P2 against per-step least-squares solves (and the CAE loop against an explicit per-step
+solve of the r1 + r2 residual), Gram identities and bf16 rounding against torch.
 Parity unpinned by the pages: the scale rule of channel_scales (s = 2*absmax/(2^b-1)) and the value 1 given
 to dead diagonals are readings the pages leave open; their implementation is pinned only to their own
 stated definition (properties in the tests), not to a value the pages print.
@@ -48,7 +51,8 @@ import numpy as np
 
 __all__ = [
     "bf16_round", "gram", "gram_row_scaled", "cross_gram", "prepare", "channel_scales", "quantize_layer",
-    "asym_correction", "asym_correction_by_definition", "layer_objective", "asym_objective",
+    "asym_correction", "asym_correction_by_definition", "cae_correction", "cae_correction_by_definition",
+    "layer_objective", "asym_objective",
     "obq_sequential", "exhaustive_best", "fixed_grid_quantize", "dequantize_fp32",
 ]
 
@@ -169,7 +173,7 @@ def dequantize_fp32(codes: np.ndarray, scales: np.ndarray, bits: int) -> np.ndar
 def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, dead: Optional[np.ndarray] = None,
                    scales: Optional[np.ndarray] = None, blocksize: Optional[int] = None,
                    P1: Optional[np.ndarray] = None, tie_codes: Optional[np.ndarray] = None,
-                   band: float = 1e-4, record_trace: bool = False) -> dict:
+                   band: float = 1e-4, record_trace: bool = False, P2: Optional[np.ndarray] = None) -> dict:
     """Quantise every output channel of W (K x N) in the natural coordinate order.
 
     For coordinate j (same j for every channel):
@@ -177,7 +181,9 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, dead: Optional[np.nd
         E_j = (w_j - q) / U_jj
         w_k -= U_jk E_j                      for every still-free k > j            [T3], [T4]
         w_k += P1_jk * w_j(pre-rounding)     for every k > j, asymmetric variant   [R] item 3
+        w_k += P2_jk * (w0_j - w_j(pre))     for every k > j, CAE term             [R] items 2, 3
         w_j  = q
+    (w0 is the original weight, after dead rows are zeroed.)
     blocksize=None applies every update at once (the literal sequential reading).  blocksize=B applies the
     updates inside the current block at once and the rest for the whole block at its end (lazy batch,
     [T5]); the two are the same computation up to rounding order.
@@ -236,6 +242,8 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, dead: Optional[np.nd
                 Wk[j + 1:hi_k] -= np.outer(U[j, j + 1:hi_k], e)
                 if P1 is not None:
                     Wk[j + 1:hi_k] += np.outer(P1[j, j + 1:hi_k], w)
+                if P2 is not None:
+                    Wk[j + 1:hi_k] += np.outer(P2[j, j + 1:hi_k], W0[j] - w)
             Wk[j] = q
             if record_trace:
                 trace.append(Wk.copy())
@@ -243,6 +251,8 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, dead: Optional[np.nd
             Wk[b1:] -= U[b0:b1, b1:].T @ E[b0:b1]
             if P1 is not None:
                 Wk[b1:] += P1[b0:b1, b1:].T @ Wpre[b0:b1]
+            if P2 is not None:
+                Wk[b1:] += P2[b0:b1, b1:].T @ (W0[b0:b1] - Wpre[b0:b1])
     losses = 0.5 * np.sum(E * E, axis=0)
     return {
         "codes": codes, "scales": s32, "Q": Q, "E": E, "V": V, "W_pre": Wpre, "W0": W0,
@@ -272,6 +282,31 @@ def asym_correction_by_definition(Hd: np.ndarray, A: np.ndarray) -> np.ndarray:
         F = slice(q + 1, K)
         P1[q, F] = np.linalg.solve(Hd[F, F], A[q, F])     # H_FF symmetric
     return P1
+
+
+# ----------------------------------------------------------------------------------------------------------
+# CAE term.  [R] item 2: aligning every step to the fixed float output W0 X~ splits the residual into
+# r1 = w^(q)(X~ - X) (the GPTAQ term) and the compensation-aware error r2 = (w^(0) - w^(q)) X~; item 3 makes
+# r2 a per-coordinate term with the precomputed P2 = [(X~ X^T L) (.) M_U] L^T and the extra update
+# (W0_q - W^(q)_q) P2[q, q:].  In this layout L = U^T and X~^T X = X^T X + dX^T X, i.e. 2 X~^T X = H + A.
+# ----------------------------------------------------------------------------------------------------------
+def cae_correction(U: np.ndarray, H: np.ndarray, A: Optional[np.ndarray] = None) -> np.ndarray:
+    """P2 = [((H + A) U^T) masked to the strictly upper triangle] U, H = 2 X^T X, A = 2 (X~ - X)^T X."""
+    U = np.asarray(U, np.float64)
+    G = np.asarray(H, np.float64) + (0.0 if A is None else np.asarray(A, np.float64))
+    return np.triu(G @ U.T, 1) @ U
+
+
+def cae_correction_by_definition(Hd: np.ndarray, G: np.ndarray) -> np.ndarray:
+    """Row q of P2 is the ridge least-squares response of the free coordinates F = {q+1..K-1} to coordinate
+    q's float-stream input X~_q:  P2[q, F] = G[q, F] (H_d[F, F])^{-1} with G = 2 X~^T X (the r2 part of the
+    r X^T H^{-1}_{-q} term, split per coordinate)."""
+    K = Hd.shape[0]
+    P2 = np.zeros((K, K))
+    for q in range(K - 1):
+        F = slice(q + 1, K)
+        P2[q, F] = np.linalg.solve(Hd[F, F], G[q, F])
+    return P2
 
 
 # ----------------------------------------------------------------------------------------------------------
@@ -305,7 +340,7 @@ def fixed_grid_quantize(v: np.ndarray, lo: int = -8, hi: int = 7) -> np.ndarray:
 
 
 def obq_sequential(H: np.ndarray, w: np.ndarray, quant, order=None, A: Optional[np.ndarray] = None,
-                   damp: float = 0.0, X_free_basis: Optional[np.ndarray] = None) -> dict:
+                   damp: float = 0.0, X_free_basis: Optional[np.ndarray] = None, cae: bool = False) -> dict:
     """Sequential constrained compensation with an explicit inverse of the free block at every step.
 
     [T3]: with free set F (current coordinate q first) and P_F = (H[F,F])^{-1}, fixing w_q to its grid
@@ -313,11 +348,13 @@ def obq_sequential(H: np.ndarray, w: np.ndarray, quant, order=None, A: Optional[
     objective is r^2 / (2 P_F[q, q]).
     Asymmetric variant: additionally the coordinates after q absorb coordinate q's input mismatch by
     ridge least squares; X_free_basis = (X, dX) pairs it is solved from directly (lstsq), independent of
-    the P1 closed form.
+    the P1 closed form.  cae=True adds the compensation-aware residual of coordinate q, (w0_q - w_q) X~_q with
+    X~ = X + dX and w0 the starting weights, to the same least-squares right-hand side ([R] items 2, 3).
     """
     H = np.asarray(H, np.float64)
     K = H.shape[0]
     w = np.array(w, np.float64, copy=True)
+    w0 = w.copy()
     order = list(range(K)) if order is None else list(order)
     added = []
     trace = []
@@ -337,7 +374,10 @@ def obq_sequential(H: np.ndarray, w: np.ndarray, quant, order=None, A: Optional[
             Xr = Xq[:, rest]
             lam = np.sqrt(damp / 2.0)
             lhs = np.vstack([Xr, lam * np.eye(len(rest))])
-            rhs = np.concatenate([dXq[:, q] * pre, np.zeros(len(rest))])
+            resid = dXq[:, q] * pre
+            if cae:
+                resid = resid + (Xq[:, q] + dXq[:, q]) * (w0[q] - pre)
+            rhs = np.concatenate([resid, np.zeros(len(rest))])
             sol = np.linalg.lstsq(lhs, rhs, rcond=None)[0]
             w[rest] += sol
         trace.append(w.copy())

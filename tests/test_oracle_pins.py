@@ -317,3 +317,73 @@ def test_generator_asym_mismatch_is_bf16_exact():
     L = workloads.make_layer(cfg)
     d = L["X_float"].float() - L["X"].float()
     assert torch.equal(d.to(torch.bfloat16).float(), d)
+
+
+# ------------------------------------------------------------------------------------------------ CAE term
+def _cae_problem(seed, K=6, M=60, dead=()):
+    rng = np.random.default_rng(seed)
+    Xf = rng.normal(size=(M, K))
+    X = Xf + 0.1 * np.abs(Xf) * rng.normal(size=(M, K))
+    for k in dead:
+        X[:, k] = 0.0
+        Xf[:, k] = 0.0
+    H = O.gram([X])
+    prep = O.prepare(H, 0.01)
+    A = O.cross_gram(Xf, X)
+    return rng, X, Xf, H, prep, A
+
+
+def test_cae_correction_forms_agree():
+    """P2 from the masked-U form equals the per-row ridge solve of [R] item 3's decomposition."""
+    _, X, Xf, H, prep, A = _cae_problem(31, K=9)
+    P2 = O.cae_correction(prep["U"], H, A)
+    P2d = O.cae_correction_by_definition(prep["Hd"], 2.0 * (Xf.T @ X))
+    np.testing.assert_allclose(P2, P2d, rtol=1e-9, atol=1e-12)
+    assert np.count_nonzero(np.tril(P2)) == 0
+
+
+@pytest.mark.parametrize("dead", [(), (2,)])
+def test_cae_correction_closed_form(dead):
+    """H_d U^T = R is upper triangular with R_jj = 1/U_jj, and damping and the dead fix are diagonal, so
+    P2 = P1 + I - diag(U)^-1 U exactly (the identity the library uses instead of a third K x K product)."""
+    _, X, Xf, H, prep, A = _cae_problem(32, K=8, dead=dead)
+    U = prep["U"]
+    P1 = O.asym_correction(U, A)
+    P2 = O.cae_correction(U, H, A)
+    closed = P1 + np.eye(len(U)) - U / np.diag(U)[:, None]
+    np.testing.assert_allclose(P2, closed, atol=1e-12 * np.abs(P2).max())
+    # with no input mismatch P2 is I - diag(U)^-1 U
+    np.testing.assert_allclose(O.cae_correction(U, H), np.eye(len(U)) - U / np.diag(U)[:, None],
+                               atol=1e-12 * np.abs(P2).max())
+
+
+@pytest.mark.parametrize("asym", [False, True])
+def test_cae_loop_equals_explicit_solves(asym):
+    """Loop with P2 (and P1) == sequential compensation with explicit inverses plus a per-step lstsq of the
+    r1 + r2 residual; with the closed form the same update reads w_k -= (U_jk/U_jj)(w0_j - q_j) + P1_jk w0_j."""
+    rng, X, Xf, H, prep, A = _cae_problem(33 + asym, K=7)
+    if not asym:
+        Xf = X.copy()
+        A = np.zeros_like(H)
+    U = prep["U"]
+    P1 = O.asym_correction(U, A) if asym else None
+    P2 = O.cae_correction(U, H, A)
+    w = rng.normal(0, 1.5, size=len(U))
+    one = np.array([1.0], np.float32)
+    r = O.quantize_layer(w[:, None], U, bits=4, scales=one, P1=P1, P2=P2)
+    seq = O.obq_sequential(prep["Hd"], w, O.fixed_grid_quantize, damp=prep["damp"], X_free_basis=(X, Xf - X),
+                           cae=True)
+    np.testing.assert_allclose(r["Q"][:, 0], seq["w"], atol=1e-10)
+    rb = O.quantize_layer(w[:, None], U, bits=4, scales=one, P1=P1, P2=P2, blocksize=3)
+    np.testing.assert_array_equal(rb["codes"], r["codes"])
+    # the CAE term changes the result on this input (so the test would see it dropped)
+    plain = O.quantize_layer(w[:, None], U, bits=4, scales=one, P1=P1)
+    assert not np.allclose(plain["W_pre"], r["W_pre"])
+    # closed form of the combined step, coordinate by coordinate
+    z = 8
+    Wk = w.copy()
+    for j in range(len(U)):
+        q = float(np.clip(np.rint(Wk[j]) + z, 0, 15) - z)
+        Wk[j + 1:] += -(U[j, j + 1:] / U[j, j]) * (w[j] - q) + (P1[j, j + 1:] * w[j] if asym else 0.0)
+        Wk[j] = q
+    np.testing.assert_allclose(Wk, r["Q"][:, 0], atol=1e-10)
