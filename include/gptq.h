@@ -67,12 +67,13 @@ typedef enum {
 
 /* Flags of gptq_quantize_layer. */
 #define GPTQ_FLAG_SCALES_GIVEN 1u  /* `scales` is an input (e.g. the fixed teaching grid of [T] section 2) */
+#define GPTQ_FLAG_CAE 4u           /* add the compensation-aware error term of [R] items 2-3 (gptq_quantize_layer) */
 
 /*
  * gptq_workspace_bytes - bytes of `workspace` a call needs for the given sizes.
  *   call: which entry point; K, N, M: sizes as in that call (unused ones are ignored); flags: for
  *   gptq_accumulate_hessian 1 if X_float will be given | 2 if row_scale will be given; for
- *   gptq_quantize_layer its flags | 2 if P1 will be given; else 0.
+ *   gptq_quantize_layer its flags (GPTQ_FLAG_CAE matters) | 2 if P1 will be given; else 0.
  * Returns 0 for an unknown call.  Never fails otherwise.
  */
 size_t gptq_workspace_bytes(gptq_call_t call, int64_t K, int64_t N, int64_t M, unsigned flags);
@@ -155,6 +156,12 @@ gptq_status_t gptq_asym_correction(const float* U, const float* A, float* P1, in
  *     w_k -= U_jk E_j for the remaining k of the current block;  [P1: w_k += P1_jk * w_j(before rounding)]
  *     after each block of `blocksize` coordinates the same updates are applied to all later coordinates
  *     at once (lazy batch, [T] section 5).
+ *   GPTQ_FLAG_CAE ([R] items 2-3): every step also aligns to the original float output, adding
+ *     w_k += P2_jk (w0_j - w_j(before rounding)) with w0 the original weights (dead rows zeroed) and
+ *     P2 = [((H + A) U^T) masked strictly upper] U (A = 0 without P1).  Because H_d U^T is upper triangular
+ *     with diagonal 1/U_jj, and damping and the dead fix are diagonal, P2 = P1 + I - diag(U)^-1 U, so the
+ *     step becomes w_k -= (U_jk / U_jj)(w0_j - q) [+ P1_jk w0_j]: no extra input is needed.  Works with or
+ *     without P1; losses still report the step errors E_j above.
  *
  *   W          device, K x N weights, dtype w_dtype, element (k, n) at W[k * w_rs + n * w_cs]
  *              (row-major K x N: w_rs = ldw, w_cs = 1; an N x K nn.Linear weight: w_rs = 1, w_cs = K).
@@ -167,7 +174,9 @@ gptq_status_t gptq_asym_correction(const float* U, const float* A, float* P1, in
  *              W_hat[k * w_rs + n * w_cs] (same strides as W; may alias W).
  *   losses     NULL, or device fp32[N]: per channel sum_j 1/2 E_j^2 ([T] section 3: the added objective).
  *   pre_round  NULL, or device fp32, K x N row-major (ld = N): w_j / s just before rounding (diagnostic).
- *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, flags | (P1?2:0)).
+ *   flags      GPTQ_FLAG_SCALES_GIVEN | GPTQ_FLAG_CAE (others rejected).
+ *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, flags | (P1?2:0))
+ *              (with GPTQ_FLAG_CAE it also holds a copy of the original weights, N x K fp32).
  * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_NONFINITE (NaN/Inf weight or given scale),
  * GPTQ_ERR_HIP.  Synchronises `stream` before returning.
  */

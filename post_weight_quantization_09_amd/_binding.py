@@ -18,6 +18,7 @@ GPTQ_OK, GPTQ_ERR_ARG, GPTQ_ERR_NONFINITE, GPTQ_ERR_NOT_PD, GPTQ_ERR_WORKSPACE, 
 GPTQ_DTYPE_F32, GPTQ_DTYPE_BF16 = 0, 1
 GPTQ_CALL_ACCUMULATE_HESSIAN, GPTQ_CALL_PREPARE, GPTQ_CALL_ASYM_CORRECTION, GPTQ_CALL_QUANTIZE_LAYER = range(4)
 GPTQ_FLAG_SCALES_GIVEN = 1
+GPTQ_FLAG_CAE = 4
 
 _i64, _f32, _u32, _ptr, _size = ctypes.c_int64, ctypes.c_float, ctypes.c_uint, ctypes.c_void_p, ctypes.c_size_t
 
@@ -185,8 +186,9 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, dead: Optio
                         scales: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
                         W_hat: Optional[torch.Tensor] = None, losses: Optional[torch.Tensor] = None,
                         pre_round: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                        stream=None) -> dict:
-    """Quantises W (K x N view, any strides) with U; given `scales` are used as the grid (fixed-grid mode).
+                        stream=None, cae: bool = False) -> dict:
+    """Quantises W (K x N view, any strides) with U; given `scales` are used as the grid (fixed-grid mode);
+    cae=True adds the compensation-aware error term (GPTQ_FLAG_CAE).
 
     Returns dict(codes uint8 K x N, scales fp32[N], W_hat, losses, pre_round) with the tensors written.
     """
@@ -205,6 +207,8 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, dead: Optio
         scales = torch.empty(N, dtype=torch.float32, device=dev)
     else:
         flags |= GPTQ_FLAG_SCALES_GIVEN
+    if cae:
+        flags |= GPTQ_FLAG_CAE
     if codes is None:
         codes = torch.empty(K, N, dtype=torch.uint8, device=dev)
     if W_hat is not None and (W_hat.shape != W.shape or W_hat.stride() != W.stride() or W_hat.dtype != W.dtype):

@@ -64,7 +64,8 @@ size_t gptq_workspace_bytes(gptq_call_t call, int64_t K, int64_t N, int64_t M, u
         case GPTQ_CALL_ACCUMULATE_HESSIAN: return accumulate_ws(K, M, (flags & 1u) != 0, (flags & 2u) != 0);
         case GPTQ_CALL_PREPARE: return prepare_workspace_bytes(K);
         case GPTQ_CALL_ASYM_CORRECTION: return asym_ws(K);
-        case GPTQ_CALL_QUANTIZE_LAYER: return quantize_workspace_bytes(K, N, (flags & 2u) != 0);
+        case GPTQ_CALL_QUANTIZE_LAYER:
+            return quantize_workspace_bytes(K, N, (flags & 2u) != 0, (flags & GPTQ_FLAG_CAE) != 0);
     }
     return 0;
 }
@@ -153,13 +154,15 @@ gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K
     if (!W || !U || !codes || !scales || K < 1 || N < 1) return GPTQ_ERR_ARG;
     if (w_dtype != GPTQ_DTYPE_F32 && w_dtype != GPTQ_DTYPE_BF16) return GPTQ_ERR_ARG;
     if (bits < 2 || bits > 8 || blocksize != 128) return GPTQ_ERR_ARG;
-    if ((flags & ~GPTQ_FLAG_SCALES_GIVEN) != 0) return GPTQ_ERR_ARG;
+    if ((flags & ~(GPTQ_FLAG_SCALES_GIVEN | GPTQ_FLAG_CAE)) != 0) return GPTQ_ERR_ARG;
     if (w_rs < 1 || w_cs < 1 || c_rs < 1 || c_cs < 1) return GPTQ_ERR_ARG;
     if (K > (int64_t)1 << 24 || N > (int64_t)1 << 28) return GPTQ_ERR_ARG;
-    if (!ws_ok(workspace, workspace_bytes, quantize_workspace_bytes(K, N, P1 != nullptr))) return GPTQ_ERR_WORKSPACE;
+    if (!ws_ok(workspace, workspace_bytes, quantize_workspace_bytes(K, N, P1 != nullptr, (flags & GPTQ_FLAG_CAE) != 0)))
+        return GPTQ_ERR_WORKSPACE;
     QuantizeArgs a;
     a.W = W; a.w_dtype = w_dtype; a.K = K; a.N = N; a.w_rs = w_rs; a.w_cs = w_cs;
     a.U = U; a.dead = dead; a.P1 = P1; a.bits = bits; a.scales_given = (flags & GPTQ_FLAG_SCALES_GIVEN) != 0;
+    a.cae = (flags & GPTQ_FLAG_CAE) != 0;
     a.codes = codes; a.c_rs = c_rs; a.c_cs = c_cs; a.scales = scales; a.W_hat = W_hat; a.losses = losses;
     a.pre_round = pre_round;
     return quantize_layer(a, workspace, static_cast<hipStream_t>(stream));

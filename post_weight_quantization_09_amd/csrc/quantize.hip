@@ -127,7 +127,8 @@ struct BlockArgs {
     int bits;
     uint8_t* codes_t;               // N x ldt
     float* E;                       // N x 128
-    float* Wpre;                    // N x 128 (asymmetric only)
+    float* Wpre;                    // N x 128 (asymmetric without CAE)
+    const float* W0t;               // N x ldt original weights (CAE only)
     float* loss_acc;                // N
     float* pre_round;               // optional, K x N
     const DevStatus* st;
@@ -135,7 +136,7 @@ struct BlockArgs {
 
 // Per-lane state of the block kernel: 8 strided coordinates of one channel.
 struct LaneState {
-    float w[8], e[8], pre[8];
+    float w[8], e[8], pre[8], w0[8];
     uint32_t code[8];
     float loss;
 };
@@ -170,7 +171,10 @@ __device__ __forceinline__ void load_ops(StepOps& o, const StepConst& k) {
 }
 
 // One step j of the loop (j compile-time so that slots, DPP lane and LDS offsets are immediates).
-template <int J, bool ASYM, bool PRE>
+// CAE: the step's update uses the original weight w0_j in place of the pre-rounding value, both in the
+// error that multiplies U (w0_j - q) / U_jj and in the P1 coefficient; the step error E_j itself still feeds
+// the loss.  This is the P2 = P1 + I - diag(U)^-1 U form of the CAE term.
+template <int J, bool ASYM, bool CAE, bool PRE>
 __device__ __forceinline__ void loop_step(LaneState& st, const StepConst& k, StepOps (&ops)[2]) {
     constexpr int m = J >> 4, lj = J & 15;
     const StepOps& o = ops[J & 1];
@@ -180,36 +184,38 @@ __device__ __forceinline__ void loop_step(LaneState& st, const StepConst& k, Ste
     const float c = fminf(fmaxf(rintf(v) + k.z, 0.f), k.qmax);
     const float q = (c - k.z) * k.s;
     const float e = (wj - q) * o.rd;
+    const float wu = CAE ? row_bcast(st.w0[m], lj) : wj;      // value the update is taken from
+    const float eu = CAE ? (wu - q) * o.rd : e;
     const float uu[8] = {o.u0.x, o.u0.y, o.u0.z, o.u0.w, o.u1.x, o.u1.y, o.u1.z, o.u1.w};
     const bool owner = (k.l == lj);
     if constexpr (ASYM) {
         const float pp[8] = {o.p0.x, o.p0.y, o.p0.z, o.p0.w, o.p1.x, o.p1.y, o.p1.z, o.p1.w};
-        st.w[m] = owner ? q : fmaf(pp[m], wj, fmaf(-uu[m], e, st.w[m]));
+        st.w[m] = owner ? q : fmaf(pp[m], wu, fmaf(-uu[m], eu, st.w[m]));
 #pragma unroll
-        for (int mm = m + 1; mm < 8; ++mm) st.w[mm] = fmaf(pp[mm], wj, fmaf(-uu[mm], e, st.w[mm]));
+        for (int mm = m + 1; mm < 8; ++mm) st.w[mm] = fmaf(pp[mm], wu, fmaf(-uu[mm], eu, st.w[mm]));
     } else {
-        st.w[m] = owner ? q : fmaf(-uu[m], e, st.w[m]);
+        st.w[m] = owner ? q : fmaf(-uu[m], eu, st.w[m]);
 #pragma unroll
-        for (int mm = m + 1; mm < 8; ++mm) st.w[mm] = fmaf(-uu[mm], e, st.w[mm]);
+        for (int mm = m + 1; mm < 8; ++mm) st.w[mm] = fmaf(-uu[mm], eu, st.w[mm]);
     }
     st.loss = fmaf(e, e, st.loss);
     st.code[m] = owner ? (uint32_t)c : st.code[m];
-    st.e[m] = owner ? e : st.e[m];
+    st.e[m] = owner ? eu : st.e[m];
     if constexpr (ASYM) st.pre[m] = owner ? wj : st.pre[m];
     if constexpr (PRE) {
         if (owner && k.live) k.pre_round[(int64_t)J * k.N + k.prow_off] = v;
     }
 }
 
-template <bool ASYM, bool PRE, int... Js>
+template <bool ASYM, bool CAE, bool PRE, int... Js>
 __device__ __forceinline__ void run_steps(LaneState& st, const StepConst& k, int bs,
                                           std::integer_sequence<int, Js...>) {
     StepOps ops[2];
     load_ops<0, ASYM>(ops[0], k);
-    ((Js < bs ? loop_step<Js, ASYM, PRE>(st, k, ops) : (void)0), ...);
+    ((Js < bs ? loop_step<Js, ASYM, CAE, PRE>(st, k, ops) : (void)0), ...);
 }
 
-template <bool ASYM>
+template <bool ASYM, bool CAE>
 __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
     __shared__ __attribute__((aligned(16))) float Up[kB * kB];               // [row j][16 lanes][8 slots]
     __shared__ __attribute__((aligned(16))) float Pp[ASYM ? kB * kB : 4];    // same layout (asymmetric)
@@ -263,8 +269,10 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
 
     LaneState st;
     const float* wrow = p.Wt + nn * p.ldt + b0;
+    const float* w0row = CAE ? p.W0t + nn * p.ldt + b0 : nullptr;
     for (int m = 0; m < 8; ++m) {
         st.w[m] = wrow[16 * m + l];
+        if constexpr (CAE) st.w0[m] = w0row[16 * m + l];
         st.e[m] = 0.f;
         st.pre[m] = 0.f;
         st.code[m] = 0;
@@ -278,8 +286,8 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
     k.l = l;
     k.pre_round = p.pre_round ? p.pre_round + b0 * p.N : nullptr;
     k.prow_off = n; k.N = p.N; k.live = live;
-    if (k.pre_round) run_steps<ASYM, true>(st, k, bs, std::make_integer_sequence<int, kB>{});
-    else run_steps<ASYM, false>(st, k, bs, std::make_integer_sequence<int, kB>{});
+    if (k.pre_round) run_steps<ASYM, CAE, true>(st, k, bs, std::make_integer_sequence<int, kB>{});
+    else run_steps<ASYM, CAE, false>(st, k, bs, std::make_integer_sequence<int, kB>{});
 
     if (!live) return;
     uint8_t* crow = p.codes_t + n * p.ldt + b0;
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
         const int c = 16 * m + l;
         if (c < bs) crow[c] = (uint8_t)st.code[m];
         erow[c] = st.e[m];
-        if (ASYM) p.Wpre[n * kB + c] = st.pre[m];
+        if (ASYM && !CAE) p.Wpre[n * kB + c] = st.pre[m];
     }
     if (l == 0) p.loss_acc[n] += 0.5f * st.loss;
 }
@@ -345,10 +353,11 @@ struct QuantLayout {
     uint8_t* codes_t;
     float* E;
     float* Wpre;
+    float* W0t;
     size_t bytes;
 };
 
-QuantLayout carve(void* ws, int64_t K, int64_t N, bool asym) {
+QuantLayout carve(void* ws, int64_t K, int64_t N, bool asym, bool cae) {
     const int64_t ldt = ceil_div(std::max<int64_t>(K, 1), kB) * kB;
     Carver c(ws);
     QuantLayout L;
@@ -359,20 +368,24 @@ QuantLayout carve(void* ws, int64_t K, int64_t N, bool asym) {
     L.Wt = c.take<float>((size_t)N * ldt);
     L.codes_t = c.take<uint8_t>((size_t)N * ldt);
     L.E = c.take<float>((size_t)N * kB);
-    L.Wpre = asym ? c.take<float>((size_t)N * kB) : nullptr;
+    L.Wpre = asym && !cae ? c.take<float>((size_t)N * kB) : nullptr;
+    L.W0t = cae ? c.take<float>((size_t)N * ldt) : nullptr;
     L.bytes = c.bytes();
     return L;
 }
 
 }  // namespace
 
-size_t quantize_workspace_bytes(int64_t K, int64_t N, bool asym) { return carve(nullptr, K, N, asym).bytes; }
+size_t quantize_workspace_bytes(int64_t K, int64_t N, bool asym, bool cae) {
+    return carve(nullptr, K, N, asym, cae).bytes;
+}
 
 gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t stream) {
     const bool asym = a.P1 != nullptr;
     const int64_t K = a.K, N = a.N;
     const int64_t ldt = ceil_div(std::max<int64_t>(K, 1), kB) * kB;
-    QuantLayout L = carve(workspace, K, N, asym);
+    const bool cae = a.cae;
+    QuantLayout L = carve(workspace, K, N, asym, cae);
 
     hipLaunchKernelGGL(quant_init_kernel, grid1d(std::max<int64_t>(N, 1), 256), dim3(256), 0, stream, L.st, L.amax,
                        L.loss_acc, N);
@@ -390,27 +403,34 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
     hipLaunchKernelGGL(scales_kernel, grid1d(N, 256), dim3(256), 0, stream, L.amax, a.scales, L.rscale, N, a.bits,
                        a.scales_given, L.st);
     GPTQ_LAUNCH_CHECK();
+    if (cae)   // the original weights (dead rows zeroed), read by every step and by the trailing updates
+        GPTQ_HIP_CHECK(hipMemcpyAsync(L.W0t, L.Wt, sizeof(float) * (size_t)N * (size_t)ldt, hipMemcpyDeviceToDevice,
+                                      stream));
 
     for (int64_t b0 = 0; b0 < K; b0 += kB) {
         const int bs = (int)std::min<int64_t>(kB, K - b0);
         BlockArgs p;
         p.Wt = L.Wt; p.ldt = ldt; p.U = a.U; p.P1 = a.P1; p.K = K; p.N = N; p.b0 = b0; p.bs = bs;
         p.scales = a.scales; p.rscale = L.rscale; p.bits = a.bits; p.codes_t = L.codes_t; p.E = L.E;
-        p.Wpre = L.Wpre; p.loss_acc = L.loss_acc; p.pre_round = a.pre_round; p.st = L.st;
+        p.Wpre = L.Wpre; p.W0t = L.W0t; p.loss_acc = L.loss_acc; p.pre_round = a.pre_round; p.st = L.st;
         dim3 grid((unsigned)ceil_div(N, kChPerWG));
-        if (asym) hipLaunchKernelGGL((quant_block_kernel<true>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((quant_block_kernel<false>), grid, dim3(256), 0, stream, p);
+        if (asym && cae) hipLaunchKernelGGL((quant_block_kernel<true, true>), grid, dim3(256), 0, stream, p);
+        else if (asym) hipLaunchKernelGGL((quant_block_kernel<true, false>), grid, dim3(256), 0, stream, p);
+        else if (cae) hipLaunchKernelGGL((quant_block_kernel<false, true>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((quant_block_kernel<false, false>), grid, dim3(256), 0, stream, p);
         GPTQ_LAUNCH_CHECK();
         const int64_t b1 = b0 + bs;
         if (b1 < K) {
-            // Lazy batch: Wt[:, b1:] -= E_B U[B, b1:]  (+ Wpre_B P1[B, b1:] for the asymmetric term)
+            // Lazy batch: Wt[:, b1:] -= E_B U[B, b1:]  (+ Wpre_B P1[B, b1:] for the asymmetric term; with CAE,
+            // E holds (w0 - q) / U_jj and the P1 term takes the original weights W0_B)
             GemmArgs g;
             g.M = N; g.N = K - b1; g.K1 = bs;
             g.A1 = L.E; g.lda1 = kB;
             g.B1 = a.U + b0 * K + b1; g.ldb1 = K;
             if (asym) {
                 g.K2 = bs;
-                g.A2 = L.Wpre; g.lda2 = kB;
+                g.A2 = cae ? L.W0t + b0 : L.Wpre;
+                g.lda2 = cae ? ldt : kB;
                 g.B2 = a.P1 + b0 * K + b1; g.ldb2 = K;
                 g.a2_scale = -1.f;
             }

@@ -11,11 +11,12 @@ struct QuantizeArgs {
     const float* U = nullptr; const uint8_t* dead = nullptr; const float* P1 = nullptr;
     int bits = 4;
     bool scales_given = false;
+    bool cae = false;               // compensation-aware error term (P2 = P1 + I - diag(U)^-1 U)
     uint8_t* codes = nullptr; int64_t c_rs = 0, c_cs = 0;
     float* scales = nullptr; void* W_hat = nullptr; float* losses = nullptr; float* pre_round = nullptr;
 };
 
-size_t quantize_workspace_bytes(int64_t K, int64_t N, bool asym);
+size_t quantize_workspace_bytes(int64_t K, int64_t N, bool asym, bool cae);
 
 // Runs the whole loop on `stream` and synchronises it; returns GPTQ_ERR_NONFINITE for rejected inputs.
 gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t stream);

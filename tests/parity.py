@@ -29,12 +29,12 @@ def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
 
 
 def check_codes(gpu: dict, W: np.ndarray, U_ref: np.ndarray, bits: int, dead=None, P1=None, scales=None,
-                H_obj: np.ndarray | None = None, label: str = "") -> dict:
+                H_obj: np.ndarray | None = None, label: str = "", P2=None) -> dict:
     """Runs the oracle loop with tie-following and asserts the GPU codes, scales, losses and objective."""
     codes = gpu["codes"].cpu().numpy().astype(np.int64)
     s_gpu = gpu["scales"].cpu().numpy()
     ref = O.quantize_layer(W, U_ref, bits, dead=dead, scales=scales, blocksize=128, P1=P1, tie_codes=codes,
-                           band=BAND)
+                           band=BAND, P2=P2)
     assert np.array_equal(s_gpu, ref["scales"]), f"{label}: scales differ"
     bad = codes != ref["codes"]
     n_bad = int(bad.sum())

@@ -138,14 +138,16 @@ def _prepare_and_check(g, H, cfg, label, rows_seed):
     return dead, dead_ref
 
 
-def _loop_check(g, W, U, dead, bits, chans, label, P1=None):
-    out = g.gptq_quantize_layer(W, U, bits, dead=dead, P1=P1, losses=torch.empty(W.shape[1], device=DEV))
+def _loop_check(g, W, U, dead, bits, chans, label, P1=None, P2=None):
+    """P2 given: the loop runs with GPTQ_FLAG_CAE and the oracle with that P2."""
+    out = g.gptq_quantize_layer(W, U, bits, dead=dead, P1=P1, losses=torch.empty(W.shape[1], device=DEV),
+                                cae=P2 is not None)
     C = torch.tensor(chans, device=DEV)
     sub = {"codes": out["codes"][:, C], "scales": out["scales"][C], "losses": out["losses"][C]}
     U64 = np64(U)
     P64 = np64(P1) if P1 is not None else None
     info = check_codes(sub, W.float().cpu().numpy()[:, chans], U64, bits, dead=dead.cpu().numpy().astype(bool),
-                       P1=P64, label=label)
+                       P1=P64, P2=P2, label=label)
     print(f"{label}: column loop on {len(chans)} sampled channels: inband={info['n_inband']} "
           f"adopted={info['n_adopted']} loss rel max={info['loss_rel_max']:.2e}", flush=True)
 
@@ -192,8 +194,10 @@ def test_c4_gptaq_gram_prepare_asym_loop(g):
     perr = rel_fro(np64(P1), P1_ref)
     print(f"c4 P1 (full {cfg.K}x{cfg.K}) rel fro {perr:.3e}", flush=True)
     assert perr <= 1e-4
-    _loop_check(g, W, H, dead, cfg.bits, np.sort(np.random.default_rng(43).choice(cfg.N, 16, replace=False)),
-                "c4", P1=P1)
+    chans = np.sort(np.random.default_rng(43).choice(cfg.N, 16, replace=False))
+    _loop_check(g, W, H, dead, cfg.bits, chans, "c4", P1=P1)
+    P2 = O.cae_correction(U64, H64, np64(A))      # the CAE term from the same U, H and A
+    _loop_check(g, W, H, dead, cfg.bits, chans, "c4 with the CAE term", P1=P1, P2=P2)
 
 
 def test_c5_gram_prepare_loop(g):

@@ -229,7 +229,7 @@ def test_asym_correction_parity(g):
 
 
 # ------------------------------------------------------------------------------------------------ end to end
-def _pipeline(g, X, W, bits, percdamp=0.01, row_scale=None, X_float=None):
+def _pipeline(g, X, W, bits, percdamp=0.01, row_scale=None, X_float=None, cae=False):
     K = X.shape[1]
     H = torch.zeros(K, K, device=DEV)
     A = torch.zeros(K, K, device=DEV) if X_float is not None else None
@@ -237,7 +237,7 @@ def _pipeline(g, X, W, bits, percdamp=0.01, row_scale=None, X_float=None):
     dead, damp, n_dead = g.gptq_prepare(H, percdamp)
     P1 = g.gptq_asym_correction(H, A) if A is not None else None
     losses = torch.empty(W.shape[1], device=DEV)
-    out = g.gptq_quantize_layer(W, H, bits, dead=dead, P1=P1, losses=losses)
+    out = g.gptq_quantize_layer(W, H, bits, dead=dead, P1=P1, losses=losses, cae=cae)
     return out
 
 
@@ -299,3 +299,27 @@ def test_end_to_end_gptaq(g):
     Jr = O.asym_objective(H, A, G, Wn, info["ref"]["Q"])
     _print(f"gptaq: inband={info['n_inband']} adopted={info['n_adopted']} J_asym={Jg:.6e}/{Jr:.6e}")
     assert abs(Jg - Jr) <= 1e-3 * abs(Jr)
+
+
+# ------------------------------------------------------------------------------------------------ CAE term
+@pytest.mark.parametrize("K,N,M,asym", [(300, 77, 3000, False), (512, 130, 4096, False), (300, 77, 3000, True),
+                                        (640, 96, 5000, True)])
+def test_cae_loop_parity(g, K, N, M, asym):
+    """GPTQ_FLAG_CAE against the oracle's explicit P2 = [((H + A) U^T) (.) M_U] U loop (with and without P1)."""
+    base = "c4_up_proj_8b_gptaq" if asym else "c5_down_proj_70b"
+    cfg, L = _bf16_layer(K, N, M, seed=11 + K, base=base, **({} if asym else {"dead_frac": 0.01}))
+    Xf_t = L["X_float"].to(DEV) if asym else None
+    out = _pipeline(g, L["X"].to(DEV), L["W"].to(DEV), cfg.bits, X_float=Xf_t, cae=True)
+    X = L["X"].float().numpy()
+    H = O.gram([X])
+    ref = O.prepare(H, cfg.percdamp)
+    A = O.cross_gram(L["X_float"].float().numpy(), X) if asym else None
+    P1 = O.asym_correction(ref["U"], A) if asym else None
+    P2 = O.cae_correction(ref["U"], H, A)
+    info = check_codes(out, L["W"].float().numpy(), ref["U"], cfg.bits, dead=ref["dead"], P1=P1, P2=P2,
+                       label=f"cae K={K} asym={asym}")
+    plain = O.quantize_layer(L["W"].float().numpy(), ref["U"], cfg.bits, dead=ref["dead"], blocksize=128, P1=P1)
+    n_diff = int((plain["codes"] != info["ref"]["codes"]).sum())
+    _print(f"cae K={K} N={N} asym={asym}: inband={info['n_inband']} adopted={info['n_adopted']} "
+           f"loss rel max={info['loss_rel_max']:.2e}; codes differing from the loop without the term: {n_diff}")
+    assert n_diff > 0
