@@ -52,7 +52,7 @@ import numpy as np
 __all__ = [
     "bf16_round", "gram", "gram_row_scaled", "cross_gram", "prepare", "channel_scales", "quantize_layer",
     "asym_correction", "asym_correction_by_definition", "cae_correction", "cae_correction_by_definition",
-    "layer_objective", "asym_objective",
+    "pack_codes", "unpack_codes", "layer_objective", "asym_objective",
     "obq_sequential", "exhaustive_best", "fixed_grid_quantize", "dequantize_fp32",
 ]
 
@@ -307,6 +307,39 @@ def cae_correction_by_definition(Hd: np.ndarray, G: np.ndarray) -> np.ndarray:
         F = slice(q + 1, K)
         P2[q, F] = np.linalg.solve(Hd[F, F], G[q, F])
     return P2
+
+
+# ----------------------------------------------------------------------------------------------------------
+# Packing.  [T9]: the loop's results are grid values s(c - z); storing them means turning them into integer
+# codes packed into a wider integer container together with scale, zero point and layout.  The pages fix no
+# bit layout; the reading used here: each output channel's K codes form one little-endian bitstream, code k
+# occupying stream bits [bits*k, bits*k + bits), stored as 32-bit words along K (bit i of the stream is bit
+# i % 32 of word i // 32).  Written bit by bit so the layout can be read off the code.
+# ----------------------------------------------------------------------------------------------------------
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """codes (K x N ints in [0, 2^bits)) -> words (ceil(K*bits/32) x N uint32)."""
+    codes = np.asarray(codes, np.int64)
+    K, N = codes.shape
+    assert codes.min(initial=0) >= 0 and codes.max(initial=0) < (1 << bits)
+    nw = (K * bits + 31) // 32
+    out = np.zeros((nw, N), np.uint64)
+    for k in range(K):
+        for t in range(bits):
+            bit = k * bits + t
+            out[bit // 32] |= ((codes[k] >> t) & 1).astype(np.uint64) << np.uint64(bit % 32)
+    return out.astype(np.uint32)
+
+
+def unpack_codes(words: np.ndarray, K: int, bits: int) -> np.ndarray:
+    """Inverse of pack_codes: words (ceil(K*bits/32) x N) -> codes (K x N int64)."""
+    words = np.asarray(words, np.uint64)
+    N = words.shape[1]
+    codes = np.zeros((K, N), np.int64)
+    for k in range(K):
+        for t in range(bits):
+            bit = k * bits + t
+            codes[k] |= (((words[bit // 32] >> np.uint64(bit % 32)) & np.uint64(1)).astype(np.int64)) << t
+    return codes
 
 
 # ----------------------------------------------------------------------------------------------------------

@@ -387,3 +387,36 @@ def test_cae_loop_equals_explicit_solves(asym):
         Wk[j + 1:] += -(U[j, j + 1:] / U[j, j]) * (w[j] - q) + (P1[j, j + 1:] * w[j] if asym else 0.0)
         Wk[j] = q
     np.testing.assert_allclose(Wk, r["Q"][:, 0], atol=1e-10)
+
+
+# ------------------------------------------------------------------------------------------------ packing
+def test_pack_codes_worked_examples():
+    """Hand-worked words of the bitstream layout (code k at stream bits [b k, b k + b))."""
+    c = np.zeros((32, 1), np.int64)
+    c[0, 0] = 1                  # bit 0
+    c[10, 0] = 7                 # bits 30, 31, 32 -> word 0 bits 30-31, word 1 bit 0
+    c[31, 0] = 5                 # bits 93..95 = 1, 0, 1 -> word 2 bits 29 and 31
+    w = O.pack_codes(c, 3)
+    assert w.shape == (3, 1)
+    assert int(w[0, 0]) == (1 | (1 << 30) | (1 << 31))
+    assert int(w[1, 0]) == 1
+    assert int(w[2, 0]) == ((1 << 29) | (1 << 31))
+    assert int(O.pack_codes(np.full((32, 1), 7), 3)[1, 0]) == 0xFFFFFFFF
+    # 4-bit: codes 0..15 in order -> nibbles 0x76543210, 0xFEDCBA98
+    w4 = O.pack_codes(np.arange(16)[:, None], 4)
+    assert [int(v) for v in w4[:, 0]] == [0x76543210, 0xFEDCBA98]
+    # 2-bit: 3, 0, 1, 2 -> 0b10_01_00_11 = 0x93; K = 5 leaves the rest of the word zero
+    w2 = O.pack_codes(np.array([[3], [0], [1], [2], [3]]), 2)
+    assert w2.shape == (1, 1) and int(w2[0, 0]) == 0x93 | (3 << 8)
+    # 8-bit: bytes in order
+    assert int(O.pack_codes(np.array([[0x11], [0x22], [0x33], [0x44]]), 8)[0, 0]) == 0x44332211
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 8])
+def test_pack_round_trip(bits):
+    rng = np.random.default_rng(bits)
+    for K in (1, 31, 32, 33, 100):
+        c = rng.integers(0, 1 << bits, size=(K, 7))
+        w = O.pack_codes(c, bits)
+        assert w.shape == ((K * bits + 31) // 32, 7)
+        np.testing.assert_array_equal(O.unpack_codes(w, K, bits), c)
