@@ -188,6 +188,35 @@ gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K
                                   float* scales, void* W_hat, float* losses, float* pre_round,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * gptq_pack_codes - store codes in 32-bit words ([T] section 9: the integer codes, not the grid values, are what
+ * a quantised layer stores, packed into a wider integer container with scale, zero point and layout kept
+ * alongside; the pages fix no bit layout, the one below is this library's).
+ *
+ *   Layout: each channel's K codes form one little-endian bitstream, code k in stream bits
+ *   [bits * k, bits * k + bits), stream bit i being bit i % 32 of word i / 32.  Word w of channel n is written
+ *   at packed[w * ldp + n], w < gptq_packed_words(K, bits) = ceil(K * bits / 32).
+ *   codes   device uint8, code (k, n) at codes[k * c_rs + n * c_cs]; each < 2^bits (higher bits are dropped).
+ *   bits    1..8.   packed: device uint32, ldp >= N.
+ * Errors: GPTQ_ERR_ARG, GPTQ_ERR_HIP.  Asynchronous.
+ */
+gptq_status_t gptq_pack_codes(const uint8_t* codes, int64_t c_rs, int64_t c_cs, int64_t K, int64_t N, int bits,
+                              uint32_t* packed, int64_t ldp, void* stream);
+
+/* Number of 32-bit words per channel that gptq_pack_codes writes: ceil(K * bits / 32). */
+int64_t gptq_packed_words(int64_t K, int bits);
+
+/*
+ * gptq_unpack_codes - read packed codes back (layout of gptq_pack_codes) and optionally dequantise them.
+ *   codes   NULL, or device uint8: code (k, n) written at codes[k * c_rs + n * c_cs].
+ *   W_hat   NULL, or device, dtype w_dtype: s_n (c - z), z = 2^(bits-1), evaluated in fp32 then converted
+ *           (the values gptq_quantize_layer writes), at W_hat[k * w_rs + n * w_cs]; needs `scales` (fp32[N]).
+ * Errors: GPTQ_ERR_ARG, GPTQ_ERR_HIP.  Asynchronous.
+ */
+gptq_status_t gptq_unpack_codes(const uint32_t* packed, int64_t ldp, int64_t K, int64_t N, int bits,
+                                const float* scales, uint8_t* codes, int64_t c_rs, int64_t c_cs,
+                                void* W_hat, gptq_dtype_t w_dtype, int64_t w_rs, int64_t w_cs, void* stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 const char* gptq_status_string(gptq_status_t status);
 

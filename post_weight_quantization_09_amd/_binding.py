@@ -34,6 +34,10 @@ _SIGNATURES = {
     "gptq_quantize_layer": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
                                            ctypes.c_int, ctypes.c_int, _u32, _ptr, _i64, _i64, _ptr, _ptr, _ptr,
                                            _ptr, _ptr, _size, _ptr]),
+    "gptq_packed_words": (_i64, [_i64, ctypes.c_int]),
+    "gptq_pack_codes": (ctypes.c_int, [_ptr, _i64, _i64, _i64, _i64, ctypes.c_int, _ptr, _i64, _ptr]),
+    "gptq_unpack_codes": (ctypes.c_int, [_ptr, _i64, _i64, _i64, ctypes.c_int, _ptr, _ptr, _i64, _i64, _ptr,
+                                         ctypes.c_int, _i64, _i64, _ptr]),
 }
 
 _lib = None
@@ -223,3 +227,49 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, dead: Optio
         _dptr(losses), _dptr(pre_round), wp, wb, _stream(dev, stream))
     _check(st, "gptq_quantize_layer")
     return {"codes": codes, "scales": scales, "W_hat": W_hat, "losses": losses, "pre_round": pre_round}
+
+
+def gptq_packed_words(K: int, bits: int) -> int:
+    return int(load().gptq_packed_words(int(K), int(bits)))
+
+
+def gptq_pack_codes(codes: torch.Tensor, bits: int, packed: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """codes: K x N uint8 view (any strides) -> packed words, ceil(K*bits/32) x N, held as int32 (bit patterns of
+    the uint32 words)."""
+    if codes.dtype != torch.uint8 or codes.dim() != 2:
+        raise ValueError("codes must be a 2-D uint8 tensor")
+    K, N = codes.shape
+    nw = gptq_packed_words(K, bits)
+    if packed is None:
+        packed = torch.empty(nw, N, dtype=torch.int32, device=codes.device)
+    if packed.shape != (nw, N) or packed.dtype != torch.int32 or packed.stride(1) != 1:
+        raise ValueError(f"packed must be int32 of shape ({nw}, {N}) with unit column stride")
+    st = load().gptq_pack_codes(_dptr(codes), codes.stride(0), codes.stride(1), K, N, int(bits), _dptr(packed),
+                                packed.stride(0), _stream(codes.device, stream))
+    _check(st, "gptq_pack_codes")
+    return packed
+
+
+def gptq_unpack_codes(packed: torch.Tensor, K: int, bits: int, scales: Optional[torch.Tensor] = None,
+                      codes: Optional[torch.Tensor] = None, W_hat: Optional[torch.Tensor] = None,
+                      stream=None) -> dict:
+    """Inverse of gptq_pack_codes; with `scales` (and W_hat, or a new fp32 K x N) also s (c - z)."""
+    if packed.dtype != torch.int32 or packed.dim() != 2 or packed.stride(1) != 1:
+        raise ValueError("packed must be a 2-D int32 tensor with unit column stride")
+    N = packed.shape[1]
+    dev = packed.device
+    if codes is None:
+        codes = torch.empty(K, N, dtype=torch.uint8, device=dev)
+    if scales is not None:
+        _contig(scales, "scales", torch.float32)
+        if W_hat is None:
+            W_hat = torch.empty(K, N, dtype=torch.float32, device=dev)
+    if W_hat is not None and scales is None:
+        raise ValueError("W_hat needs scales")
+    st = load().gptq_unpack_codes(_dptr(packed), packed.stride(0), K, N, int(bits), _dptr(scales), _dptr(codes),
+                                  codes.stride(0), codes.stride(1), _dptr(W_hat),
+                                  _dtype_code(W_hat) if W_hat is not None else 0,
+                                  W_hat.stride(0) if W_hat is not None else 0,
+                                  W_hat.stride(1) if W_hat is not None else 0, _stream(dev, stream))
+    _check(st, "gptq_unpack_codes")
+    return {"codes": codes, "W_hat": W_hat}

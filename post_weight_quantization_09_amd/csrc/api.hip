@@ -6,6 +6,7 @@
 #include "gemm_f32.hpp"
 #include "gram.hpp"
 #include "quantize.hpp"
+#include "pack.hpp"
 
 using namespace gptq;
 
@@ -166,6 +167,33 @@ gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K
     a.codes = codes; a.c_rs = c_rs; a.c_cs = c_cs; a.scales = scales; a.W_hat = W_hat; a.losses = losses;
     a.pre_round = pre_round;
     return quantize_layer(a, workspace, static_cast<hipStream_t>(stream));
+}
+
+int64_t gptq_packed_words(int64_t K, int bits) {
+    if (K < 0 || bits < 1 || bits > 8) return -1;
+    return packed_words(K, bits);
+}
+
+gptq_status_t gptq_pack_codes(const uint8_t* codes, int64_t c_rs, int64_t c_cs, int64_t K, int64_t N, int bits,
+                              uint32_t* packed, int64_t ldp, void* stream) {
+    if (!codes || !packed || K < 1 || N < 1 || bits < 1 || bits > 8) return GPTQ_ERR_ARG;
+    if (c_rs < 1 || c_cs < 1 || ldp < N) return GPTQ_ERR_ARG;
+    return pack_codes(codes, c_rs, c_cs, K, N, bits, packed, ldp, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? GPTQ_OK
+               : GPTQ_ERR_HIP;
+}
+
+gptq_status_t gptq_unpack_codes(const uint32_t* packed, int64_t ldp, int64_t K, int64_t N, int bits,
+                                const float* scales, uint8_t* codes, int64_t c_rs, int64_t c_cs, void* W_hat,
+                                gptq_dtype_t w_dtype, int64_t w_rs, int64_t w_cs, void* stream) {
+    if (!packed || K < 1 || N < 1 || bits < 1 || bits > 8 || ldp < N) return GPTQ_ERR_ARG;
+    if (codes && (c_rs < 1 || c_cs < 1)) return GPTQ_ERR_ARG;
+    if (W_hat && (!scales || w_rs < 1 || w_cs < 1)) return GPTQ_ERR_ARG;
+    if (W_hat && w_dtype != GPTQ_DTYPE_F32 && w_dtype != GPTQ_DTYPE_BF16) return GPTQ_ERR_ARG;
+    return unpack_codes(packed, ldp, K, N, bits, scales, codes, c_rs, c_cs, W_hat, w_dtype == GPTQ_DTYPE_BF16, w_rs,
+                        w_cs, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? GPTQ_OK
+               : GPTQ_ERR_HIP;
 }
 
 }  // extern "C"

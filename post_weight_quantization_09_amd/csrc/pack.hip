@@ -1,0 +1,87 @@
+// Code packing on gfx950: integer codes -> 32-bit words, and packed words -> codes and dequantised values.
+//
+// [T] section 9: the loop's results are grid values s (c - z); storing a quantised layer means the integer
+// codes packed into a wider container together with the scale, zero point and layout.  Layout used here:
+// each output channel's K codes form one little-endian bitstream, code k in stream bits [b k, b k + b), stored
+// as 32-bit words along K (bit i of the stream is bit i % 32 of word i / 32).  For b = 3, 32 codes fill three
+// words and one code in ten straddles a word boundary.
+//
+// Both kernels are HBM-bound elementwise passes: one thread per (word, channel) for packing and per (code,
+// channel) for unpacking, channels fastest so that the uint8 codes, the words and the values are all read and
+// written by consecutive lanes at consecutive addresses in the common K x N row-major layouts.
+#include "pack.hpp"
+
+#include <algorithm>
+
+namespace gptq {
+
+namespace {
+
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* codes, int64_t c_rs, int64_t c_cs, int64_t K,
+                                                   int64_t N, int bits, uint32_t* packed, int64_t ldp, int64_t nw) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    for (int64_t w = blockIdx.y; w < nw; w += gridDim.y) {
+        const int64_t bit0 = 32 * w;                   // first stream bit of this word
+        const int64_t k0 = bit0 / bits;                // first code overlapping the word
+        const int64_t k1 = min<int64_t>(K, (bit0 + 32 + bits - 1) / bits);
+        const uint32_t mask = (1u << bits) - 1u;
+        uint32_t word = 0;
+        for (int64_t k = k0; k < k1; ++k) {
+            const uint32_t c = codes[k * c_rs + n * c_cs] & mask;
+            const int64_t sh = k * bits - bit0;        // in (-bits, 32)
+            if (sh >= 0) word |= c << sh;
+            else word |= c >> (-sh);
+        }
+        packed[w * ldp + n] = word;
+    }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void unpack_kernel(const uint32_t* packed, int64_t ldp, int64_t K, int64_t N,
+                                                     int bits, const float* scales, uint8_t* codes, int64_t c_rs,
+                                                     int64_t c_cs, void* W_hat, int64_t w_rs, int64_t w_cs) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    for (int64_t k = blockIdx.y; k < K; k += gridDim.y) {
+        const int64_t bit = k * bits, w = bit >> 5;
+        const int o = (int)(bit & 31);
+        uint32_t v = packed[w * ldp + n] >> o;
+        if (o + bits > 32) v |= packed[(w + 1) * ldp + n] << (32 - o);
+        const uint32_t c = v & ((1u << bits) - 1u);
+        if (codes) codes[k * c_rs + n * c_cs] = (uint8_t)c;
+        if (W_hat) {
+            const float z = (float)(1 << (bits - 1));
+            const float x = ((float)c - z) * scales[n];
+            if (BF16) static_cast<__bf16*>(W_hat)[k * w_rs + n * w_cs] = (__bf16)x;
+            else static_cast<float*>(W_hat)[k * w_rs + n * w_cs] = x;
+        }
+    }
+}
+
+}  // namespace
+
+int64_t packed_words(int64_t K, int bits) { return (K * bits + 31) / 32; }
+
+hipError_t pack_codes(const uint8_t* codes, int64_t c_rs, int64_t c_cs, int64_t K, int64_t N, int bits,
+                      uint32_t* packed, int64_t ldp, hipStream_t stream) {
+    const int64_t nw = packed_words(K, bits);
+    dim3 grid((unsigned)ceil_div(N, 256), (unsigned)std::min<int64_t>(nw, 65535));
+    hipLaunchKernelGGL(pack_kernel, grid, dim3(256), 0, stream, codes, c_rs, c_cs, K, N, bits, packed, ldp, nw);
+    return hipGetLastError();
+}
+
+hipError_t unpack_codes(const uint32_t* packed, int64_t ldp, int64_t K, int64_t N, int bits, const float* scales,
+                        uint8_t* codes, int64_t c_rs, int64_t c_cs, void* W_hat, bool bf16, int64_t w_rs,
+                        int64_t w_cs, hipStream_t stream) {
+    dim3 grid((unsigned)ceil_div(N, 256), (unsigned)std::min<int64_t>(K, 65535));
+    if (bf16)
+        hipLaunchKernelGGL((unpack_kernel<true>), grid, dim3(256), 0, stream, packed, ldp, K, N, bits, scales, codes,
+                           c_rs, c_cs, W_hat, w_rs, w_cs);
+    else
+        hipLaunchKernelGGL((unpack_kernel<false>), grid, dim3(256), 0, stream, packed, ldp, K, N, bits, scales, codes,
+                           c_rs, c_cs, W_hat, w_rs, w_cs);
+    return hipGetLastError();
+}
+
+}  // namespace gptq

@@ -105,6 +105,11 @@ def test_quantize_validation(lib):
     assert call(flags=8) == b.GPTQ_ERR_ARG
     assert call(wcs=0) == b.GPTQ_ERR_ARG
     assert call(wsb=100) == b.GPTQ_ERR_WORKSPACE
+    # the CAE term keeps a copy of the original weights in the workspace
+    plain = lib.gptq_workspace_bytes(b.GPTQ_CALL_QUANTIZE_LAYER, 64, 64, 0, 0)
+    cae = lib.gptq_workspace_bytes(b.GPTQ_CALL_QUANTIZE_LAYER, 64, 64, 0, b.GPTQ_FLAG_CAE)
+    assert cae >= plain + 64 * 128 * 4
+    assert call(flags=b.GPTQ_FLAG_CAE, wsb=plain) == b.GPTQ_ERR_WORKSPACE
 
 
 def test_asym_validation(lib):
@@ -117,3 +122,18 @@ def test_asym_validation(lib):
 def test_binding_refuses_missing_library(tmp_path):
     with pytest.raises(RuntimeError):
         b.load(str(tmp_path / "missing.so"))
+
+
+def test_pack_validation(lib):
+    assert lib.gptq_packed_words(32, 3) == 3 and lib.gptq_packed_words(33, 3) == 4 and lib.gptq_packed_words(5, 2) == 1
+    assert lib.gptq_packed_words(8, 0) < 0 and lib.gptq_packed_words(8, 9) < 0
+    assert lib.gptq_pack_codes(FAKE, 8, 1, 16, 8, 0, FAKE, 8, None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_pack_codes(FAKE, 8, 1, 16, 8, 9, FAKE, 8, None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_pack_codes(None, 8, 1, 16, 8, 3, FAKE, 8, None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_pack_codes(FAKE, 8, 1, 16, 8, 3, FAKE, 4, None) == b.GPTQ_ERR_ARG      # ldp < N
+    assert lib.gptq_pack_codes(FAKE, 0, 1, 16, 8, 3, FAKE, 8, None) == b.GPTQ_ERR_ARG
+    un = lib.gptq_unpack_codes
+    assert un(None, 8, 16, 8, 3, None, FAKE, 8, 1, None, 0, 0, 0, None) == b.GPTQ_ERR_ARG
+    assert un(FAKE, 8, 16, 8, 3, None, FAKE, 8, 1, FAKE, 0, 8, 1, None) == b.GPTQ_ERR_ARG  # W_hat without scales
+    assert un(FAKE, 8, 16, 8, 3, FAKE, None, 0, 0, FAKE, 7, 8, 1, None) == b.GPTQ_ERR_ARG  # bad dtype
+    assert un(FAKE, 8, 0, 8, 3, None, FAKE, 8, 1, None, 0, 0, 0, None) == b.GPTQ_ERR_ARG

@@ -214,3 +214,22 @@ def test_c5_gram_prepare_loop(g):
     dead, dead_ref = _prepare_and_check(g, H, cfg, "c5", 52)
     assert np.array_equal(np.flatnonzero(dead_ref), dead_idx)
     _loop_check(g, W, H, dead, cfg.bits, np.sort(np.random.default_rng(53).choice(cfg.N, 16, replace=False)), "c5")
+
+
+def test_c5_pack_codes_full_size(g):
+    """Codes of the 70B down_proj shape (K = 28672, N = 8192, 4-bit) packed and read back; sampled channels
+    against the oracle's bitstream."""
+    cfg = workloads.CONFIGS["c5_down_proj_70b"]
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(55)
+    codes = torch.randint(0, 1 << cfg.bits, (cfg.K, cfg.N), generator=gen, device=DEV, dtype=torch.int32).to(torch.uint8)
+    packed = g.gptq_pack_codes(codes, cfg.bits)
+    assert packed.shape == (cfg.K * cfg.bits // 32, cfg.N)
+    chans = np.sort(np.random.default_rng(56).choice(cfg.N, 16, replace=False))
+    C = torch.tensor(chans, device=DEV)
+    ref = O.pack_codes(codes[:, C].cpu().numpy().astype(np.int64), cfg.bits)
+    assert np.array_equal(packed[:, C].cpu().numpy().view(np.uint32), ref)
+    back = g.gptq_unpack_codes(packed, cfg.K, cfg.bits)
+    assert torch.equal(back["codes"], codes)
+    print(f"c5 packing: {cfg.K}x{cfg.N} {cfg.bits}-bit codes -> {tuple(packed.shape)} words, round trip exact",
+          flush=True)

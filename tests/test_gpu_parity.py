@@ -323,3 +323,38 @@ def test_cae_loop_parity(g, K, N, M, asym):
     _print(f"cae K={K} N={N} asym={asym}: inband={info['n_inband']} adopted={info['n_adopted']} "
            f"loss rel max={info['loss_rel_max']:.2e}; codes differing from the loop without the term: {n_diff}")
     assert n_diff > 0
+
+
+# ------------------------------------------------------------------------------------------------ packing
+@pytest.mark.parametrize("K,N,bits,layout", [(1, 1, 3, "KN"), (31, 77, 3, "KN"), (33, 64, 2, "NK"), (300, 130, 4, "KN"),
+                                             (129, 5, 8, "NK"), (4096, 256, 3, "KN")])
+def test_pack_parity(g, K, N, bits, layout):
+    rng = np.random.default_rng(K * 7 + bits)
+    c = rng.integers(0, 1 << bits, size=(K, N)).astype(np.uint8)
+    ct = torch.tensor(c, device=DEV) if layout == "KN" else torch.tensor(np.ascontiguousarray(c.T), device=DEV).T
+    packed = g.gptq_pack_codes(ct, bits)
+    ref = O.pack_codes(c.astype(np.int64), bits)
+    got = packed.cpu().numpy().view(np.uint32)
+    assert np.array_equal(got, ref)
+    s = (rng.random(N) * 0.01 + 1e-3).astype(np.float32)
+    out = g.gptq_unpack_codes(packed, K, bits, scales=torch.tensor(s, device=DEV))
+    assert np.array_equal(out["codes"].cpu().numpy(), c)
+    assert np.array_equal(out["W_hat"].cpu().numpy(), O.dequantize_fp32(c.astype(np.int64), s, bits).astype(np.float32))
+    Wb = torch.empty(K, N, dtype=torch.bfloat16, device=DEV)
+    g.gptq_unpack_codes(packed, K, bits, scales=torch.tensor(s, device=DEV), W_hat=Wb)
+    assert torch.equal(Wb.cpu(), out["W_hat"].cpu().to(torch.bfloat16))
+
+
+def test_pack_after_quantize_round_trip(g):
+    """quantize_layer -> pack -> unpack gives back the codes and exactly the W_hat the loop wrote."""
+    cfg, L = _bf16_layer(300, 77, 3000, seed=5, base="c5_down_proj_70b", dead_frac=0.01)
+    X, W = L["X"].to(DEV), L["W"].to(DEV)
+    H = torch.zeros(cfg.K, cfg.K, device=DEV)
+    g.gptq_accumulate_hessian(H, X)
+    dead, _, _ = g.gptq_prepare(H, cfg.percdamp)
+    W_hat = torch.empty_like(W)
+    out = g.gptq_quantize_layer(W, H, cfg.bits, dead=dead, W_hat=W_hat)
+    packed = g.gptq_pack_codes(out["codes"], cfg.bits)
+    back = g.gptq_unpack_codes(packed, cfg.K, cfg.bits, scales=out["scales"], W_hat=torch.empty_like(W))
+    assert torch.equal(back["codes"], out["codes"])
+    assert torch.equal(back["W_hat"], W_hat)
