@@ -52,7 +52,7 @@ import numpy as np
 __all__ = [
     "bf16_round", "gram", "gram_row_scaled", "cross_gram", "prepare", "channel_scales", "quantize_layer",
     "asym_correction", "asym_correction_by_definition", "cae_correction", "cae_correction_by_definition",
-    "pack_codes", "unpack_codes", "layer_objective", "asym_objective",
+    "pack_codes", "unpack_codes", "sylvester", "hadamard_rotate_rows", "layer_objective", "asym_objective",
     "obq_sequential", "exhaustive_best", "fixed_grid_quantize", "dequantize_fp32",
 ]
 
@@ -307,6 +307,29 @@ def cae_correction_by_definition(Hd: np.ndarray, G: np.ndarray) -> np.ndarray:
         F = slice(q + 1, K)
         P2[q, F] = np.linalg.solve(Hd[F, F], G[q, F])
     return P2
+
+
+# ----------------------------------------------------------------------------------------------------------
+# Randomised Hadamard rotation.  [G] (setup paragraph): a Hadamard rotation is applied before quantisation.
+# Reading: rows x of length K = 2^n (activation rows, and weight rows in the nn.Linear N x K layout) become
+# x' = (x * d) H_K / sqrt(K) with d a +-1 vector and H_K the Sylvester Hadamard matrix, an orthogonal map that
+# keeps x W^T unchanged when both sides are rotated.
+# ----------------------------------------------------------------------------------------------------------
+def sylvester(K: int) -> np.ndarray:
+    """H_1 = [1], H_2m = [[H_m, H_m], [H_m, -H_m]]."""
+    assert K >= 1 and K & (K - 1) == 0
+    H = np.ones((1, 1))
+    while H.shape[0] < K:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+def hadamard_rotate_rows(x: np.ndarray, signs: Optional[np.ndarray] = None) -> np.ndarray:
+    """Each row of x (R x K) -> (row * signs) H_K / sqrt(K), in float64."""
+    x = np.asarray(x, np.float64)
+    K = x.shape[1]
+    d = np.ones(K) if signs is None else np.asarray(signs, np.float64)
+    return (x * d[None, :]) @ sylvester(K) / np.sqrt(K)
 
 
 # ----------------------------------------------------------------------------------------------------------

@@ -420,3 +420,30 @@ def test_pack_round_trip(bits):
         w = O.pack_codes(c, bits)
         assert w.shape == ((K * bits + 31) // 32, 7)
         np.testing.assert_array_equal(O.unpack_codes(w, K, bits), c)
+
+
+# ------------------------------------------------------------------------------------------------ Hadamard rotation
+def test_sylvester_against_scipy_and_orthogonality():
+    import scipy.linalg
+    for K in (1, 2, 4, 64, 512):
+        H = O.sylvester(K)
+        np.testing.assert_array_equal(H, scipy.linalg.hadamard(K))
+        np.testing.assert_array_equal(H @ H.T, K * np.eye(K))
+    np.testing.assert_array_equal(O.sylvester(2), [[1, 1], [1, -1]])
+
+
+def test_hadamard_rotation_properties():
+    rng = np.random.default_rng(3)
+    K = 256
+    x = rng.normal(size=(5, K))
+    d = rng.choice([-1.0, 1.0], size=K)
+    y = O.hadamard_rotate_rows(x, d)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-12)
+    # unit vector e_k -> d_k * row k of H / sqrt(K)
+    e = np.zeros((1, K)); e[0, 7] = 1.0
+    np.testing.assert_allclose(O.hadamard_rotate_rows(e, d)[0], d[7] * O.sylvester(K)[7] / 16.0, atol=1e-15)
+    # rotating activations and nn.Linear-layout weight rows the same way keeps x W^T
+    W = rng.normal(size=(9, K))
+    np.testing.assert_allclose(y @ O.hadamard_rotate_rows(W, d).T, x @ W.T, rtol=1e-10, atol=1e-10)
+    # without signs the rotation is its own inverse
+    np.testing.assert_allclose(O.hadamard_rotate_rows(O.hadamard_rotate_rows(x)), x, atol=1e-12)
