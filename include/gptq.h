@@ -189,6 +189,20 @@ gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gptq_hadamard_rotate - randomised Hadamard rotation of rows, the step before quantisation in [G] (setup
+ * paragraph): out_r = (in_r * signs) H_K / sqrt(K) for every row r, H_K the Sylvester Hadamard matrix.  Rotating
+ * the activation rows (M x K) and the weight rows in the nn.Linear layout (N x K) with the same signs keeps
+ * X W^T unchanged.
+ *
+ *   in, out   device, rows x K, dtype (F32 or BF16), row r at in + r * ld_in (out + r * ld_out); in == out with
+ *             ld_in == ld_out rotates in place.  Arithmetic in fp32; BF16 output is rounded to nearest even.
+ *   K         a power of two, 16 <= K <= 16384.     signs: NULL (all +1) or device int8[K] of +-1.
+ * Errors: GPTQ_ERR_ARG, GPTQ_ERR_HIP.  Asynchronous.
+ */
+gptq_status_t gptq_hadamard_rotate(const void* in, int64_t ld_in, void* out, int64_t ld_out, gptq_dtype_t dtype,
+                                   int64_t rows, int64_t K, const int8_t* signs, void* stream);
+
+/*
  * gptq_pack_codes - store codes in 32-bit words ([T] section 9: the integer codes, not the grid values, are what
  * a quantised layer stores, packed into a wider integer container with scale, zero point and layout kept
  * alongside; the pages fix no bit layout, the one below is this library's).

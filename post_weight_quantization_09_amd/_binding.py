@@ -35,6 +35,7 @@ _SIGNATURES = {
                                            ctypes.c_int, ctypes.c_int, _u32, _ptr, _i64, _i64, _ptr, _ptr, _ptr,
                                            _ptr, _ptr, _size, _ptr]),
     "gptq_packed_words": (_i64, [_i64, ctypes.c_int]),
+    "gptq_hadamard_rotate": (ctypes.c_int, [_ptr, _i64, _ptr, _i64, ctypes.c_int, _i64, _i64, _ptr, _ptr]),
     "gptq_pack_codes": (ctypes.c_int, [_ptr, _i64, _i64, _i64, _i64, ctypes.c_int, _ptr, _i64, _ptr]),
     "gptq_unpack_codes": (ctypes.c_int, [_ptr, _i64, _i64, _i64, ctypes.c_int, _ptr, _ptr, _i64, _i64, _ptr,
                                          ctypes.c_int, _i64, _i64, _ptr]),
@@ -273,3 +274,21 @@ def gptq_unpack_codes(packed: torch.Tensor, K: int, bits: int, scales: Optional[
                                   W_hat.stride(1) if W_hat is not None else 0, _stream(dev, stream))
     _check(st, "gptq_unpack_codes")
     return {"codes": codes, "W_hat": W_hat}
+
+
+def gptq_hadamard_rotate(x: torch.Tensor, signs: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                         stream=None) -> torch.Tensor:
+    """Rows of x (R x K, unit column stride, fp32 or bf16) -> (row * signs) H_K / sqrt(K); out=x rotates in place."""
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    R, K = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or out.stride(1) != 1:
+        raise ValueError("out must match x")
+    if signs is not None and (signs.dtype != torch.int8 or signs.numel() != K or not signs.is_contiguous()):
+        raise ValueError("signs must be a contiguous int8 tensor of K entries")
+    st = load().gptq_hadamard_rotate(_dptr(x), x.stride(0), _dptr(out), out.stride(0), _dtype_code(x), R, K,
+                                     _dptr(signs), _stream(x.device, stream))
+    _check(st, "gptq_hadamard_rotate")
+    return out

@@ -7,6 +7,7 @@
 #include "gram.hpp"
 #include "quantize.hpp"
 #include "pack.hpp"
+#include "hadamard.hpp"
 
 using namespace gptq;
 
@@ -167,6 +168,20 @@ gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K
     a.codes = codes; a.c_rs = c_rs; a.c_cs = c_cs; a.scales = scales; a.W_hat = W_hat; a.losses = losses;
     a.pre_round = pre_round;
     return quantize_layer(a, workspace, static_cast<hipStream_t>(stream));
+}
+
+gptq_status_t gptq_hadamard_rotate(const void* in, int64_t ld_in, void* out, int64_t ld_out, gptq_dtype_t dtype,
+                                   int64_t rows, int64_t K, const int8_t* signs, void* stream) {
+    if (!in || !out || rows < 0 || K < 16 || K > 16384 || (K & (K - 1)) != 0) return GPTQ_ERR_ARG;
+    if (dtype != GPTQ_DTYPE_F32 && dtype != GPTQ_DTYPE_BF16) return GPTQ_ERR_ARG;
+    if (ld_in < K || ld_out < K || (in == out && ld_in != ld_out)) return GPTQ_ERR_ARG;
+    if (rows == 0) return GPTQ_OK;
+    int n = 0;
+    while ((int64_t(1) << n) < K) ++n;
+    return hadamard_rows(in, ld_in, out, ld_out, dtype == GPTQ_DTYPE_BF16, rows, n, signs,
+                         static_cast<hipStream_t>(stream)) == hipSuccess
+               ? GPTQ_OK
+               : GPTQ_ERR_HIP;
 }
 
 int64_t gptq_packed_words(int64_t K, int bits) {

@@ -137,3 +137,14 @@ def test_pack_validation(lib):
     assert un(FAKE, 8, 16, 8, 3, None, FAKE, 8, 1, FAKE, 0, 8, 1, None) == b.GPTQ_ERR_ARG  # W_hat without scales
     assert un(FAKE, 8, 16, 8, 3, FAKE, None, 0, 0, FAKE, 7, 8, 1, None) == b.GPTQ_ERR_ARG  # bad dtype
     assert un(FAKE, 8, 0, 8, 3, None, FAKE, 8, 1, None, 0, 0, 0, None) == b.GPTQ_ERR_ARG
+
+
+def test_hadamard_validation(lib):
+    h = lib.gptq_hadamard_rotate
+    assert h(FAKE, 64, FAKE, 64, 0, 4, 48, None, None) == b.GPTQ_ERR_ARG          # K not a power of two
+    assert h(FAKE, 16, FAKE, 16, 0, 4, 8, None, None) == b.GPTQ_ERR_ARG           # K < 16
+    assert h(FAKE, 32768, FAKE, 32768, 0, 4, 32768, None, None) == b.GPTQ_ERR_ARG  # K > 16384
+    assert h(FAKE, 32, FAKE, 64, 7, 4, 64, None, None) == b.GPTQ_ERR_ARG          # ld < K, bad dtype
+    assert h(FAKE, 64, FAKE, 128, 0, 4, 64, None, None) == b.GPTQ_ERR_ARG         # in place with different ld
+    assert h(None, 64, FAKE, 64, 0, 4, 64, None, None) == b.GPTQ_ERR_ARG
+    assert h(FAKE, 64, FAKE, 64, 0, 0, 64, None, None) == b.GPTQ_OK                # no rows: nothing to do

@@ -233,3 +233,24 @@ def test_c5_pack_codes_full_size(g):
     assert torch.equal(back["codes"], codes)
     print(f"c5 packing: {cfg.K}x{cfg.N} {cfg.bits}-bit codes -> {tuple(packed.shape)} words, round trip exact",
           flush=True)
+
+
+def test_c2_hadamard_rotation_full_size(g):
+    """The rotation step of the q_proj workload at full size (2,097,152 bf16 rows of K = 4096, in place) on
+    sampled rows against the exact rotation of the same unrotated rows."""
+    cfg = workloads.CONFIGS["c2_q_proj_8b"].scaled(hadamard=False)
+    X = torch.empty(cfg.M, cfg.K, dtype=torch.bfloat16, device=DEV)
+    workloads.ActivationSource(cfg, DEV).fill(X)
+    rows = np.sort(np.random.default_rng(61).choice(cfg.M, 64, replace=False))
+    R = torch.tensor(rows, device=DEV)
+    before = X.index_select(0, R).float().cpu().numpy().astype(np.float64)
+    d = workloads.hadamard_signs(workloads.CONFIGS["c2_q_proj_8b"]).astype(np.int8)
+    g.gptq_hadamard_rotate(X, torch.tensor(d, device=DEV), out=X)
+    after = X.index_select(0, R).float().cpu().numpy().astype(np.float64)
+    ref = O.hadamard_rotate_rows(before, d)
+    n = int(np.log2(cfg.K))
+    bound = 2.0 * (n + 2) * 2.0 ** -24 * np.abs(before).sum(axis=1, keepdims=True) / np.sqrt(cfg.K)
+    rel = np.abs(after - ref) - np.abs(ref) * 2.0 ** -8      # bf16 half-ulp of the result
+    assert (rel <= bound).all()
+    print(f"c2 rotation: {cfg.M} rows of {cfg.K} in place; 64 sampled rows within half a bf16 ulp + the fp32 bound",
+          flush=True)

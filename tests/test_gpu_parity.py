@@ -358,3 +358,63 @@ def test_pack_after_quantize_round_trip(g):
     back = g.gptq_unpack_codes(packed, cfg.K, cfg.bits, scales=out["scales"], W_hat=torch.empty_like(W))
     assert torch.equal(back["codes"], out["codes"])
     assert torch.equal(back["W_hat"], W_hat)
+
+
+# ------------------------------------------------------------------------------------------------ Hadamard rotation
+def _fwht_bound(x64, K):
+    """Rounding bound of an fp32 FWHT with n = log2 K butterfly stages and the final scaling, per row."""
+    n = int(np.log2(K))
+    return 2.0 * (n + 2) * 2.0 ** -24 * np.abs(x64).sum(axis=1, keepdims=True) / np.sqrt(K)
+
+
+@pytest.mark.parametrize("K,R,signed,inplace", [(16, 3, False, False), (32, 5, True, False), (64, 7, True, True),
+                                                (128, 33, True, False), (1024, 100, True, True),
+                                                (4096, 300, True, False), (8192, 17, False, False),
+                                                (16384, 9, True, True)])
+def test_hadamard_rotate_f32(g, K, R, signed, inplace):
+    rng = np.random.default_rng(K + R)
+    ld = K + 8
+    buf = rng.normal(size=(R, ld)).astype(np.float32)
+    x = buf[:, :K].astype(np.float64)
+    d = rng.choice([-1, 1], size=K).astype(np.int8) if signed else None
+    xt = torch.tensor(buf, device=DEV)[:, :K]
+    dt = torch.tensor(d, device=DEV) if signed else None
+    out = g.gptq_hadamard_rotate(xt, dt, out=xt if inplace else None)
+    ref = O.hadamard_rotate_rows(x, d)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - ref)
+    bound = _fwht_bound(x, K)
+    _print(f"hadamard f32 K={K} R={R}: max err / bound {float((err / bound).max()):.3f}")
+    assert (err <= bound).all()
+    if inplace:   # the padding beyond K is untouched
+        assert np.array_equal(torch.tensor(buf, device=DEV)[:, K:].cpu().numpy(), buf[:, K:])
+
+
+@pytest.mark.parametrize("K,R", [(64, 50), (4096, 200)])
+def test_hadamard_rotate_bf16(g, K, R):
+    """bf16 rows: the output is the nearest-even bf16 of the exact rotation, except where the exact value lies
+    within the fp32 rounding bound of a bf16 midpoint (then either neighbour is correct)."""
+    rng = np.random.default_rng(K)
+    x = torch.randn(R, K, generator=torch.Generator().manual_seed(K)).to(torch.bfloat16)
+    d = rng.choice([-1, 1], size=K).astype(np.int8)
+    out = g.gptq_hadamard_rotate(x.to(DEV), torch.tensor(d, device=DEV)).cpu().float().numpy().astype(np.float64)
+    x64 = x.float().numpy().astype(np.float64)
+    ref = O.hadamard_rotate_rows(x64, d)
+    rne = O.bf16_round(ref.astype(np.float32)).astype(np.float64)   # exact -> fp32 is within the bound too
+    bad = out != rne
+    bound = np.broadcast_to(_fwht_bound(x64, K), ref.shape) + np.abs(ref) * 2.0 ** -24
+    # where they differ, the exact value must sit within the bound of the midpoint between the two
+    mid = 0.5 * (out + rne)
+    assert (np.abs(ref - mid)[bad] <= bound[bad]).all()
+    _print(f"hadamard bf16 K={K}: {int(bad.sum())} of {bad.size} at a near-tie")
+
+
+def test_hadamard_rotation_keeps_products(g):
+    """Rotating X (M x K) and the nn.Linear-layout W (N x K) with the same signs keeps X W^T."""
+    rng = np.random.default_rng(5)
+    K = 1024
+    X = torch.tensor(rng.normal(size=(64, K)), dtype=torch.float32, device=DEV)
+    W = torch.tensor(rng.normal(size=(48, K)), dtype=torch.float32, device=DEV)
+    d = torch.tensor(rng.choice([-1, 1], size=K).astype(np.int8), device=DEV)
+    Y = g.gptq_hadamard_rotate(X, d) @ g.gptq_hadamard_rotate(W, d).T
+    ref = X.double().cpu() @ W.double().cpu().T
+    assert float((Y.double().cpu() - ref).abs().max() / ref.abs().max()) < 1e-5
