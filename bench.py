@@ -102,6 +102,9 @@ class Layer:
                  G.gptq_workspace_bytes(G.GPTQ_CALL_ASYM_CORRECTION, K),
                  G.gptq_workspace_bytes(G.GPTQ_CALL_QUANTIZE_LAYER, K, gs, 0, 2 if self.Xf is not None else 0))
         self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.ws_cae = torch.empty(G.gptq_workspace_bytes(G.GPTQ_CALL_QUANTIZE_LAYER, K, gs, 0,
+                                                         G.GPTQ_FLAG_CAE | (2 if self.Xf is not None else 0)),
+                                  dtype=torch.uint8, device=dev)
         self.ev = []
 
     def step(self, record: bool):
@@ -170,6 +173,55 @@ def cpu_baseline(layer: Layer, budget_s: float = 20.0) -> dict:
             "host_cores_visible": cores}
 
 
+def _time_ms(fn, reps: int = 3) -> float:
+    """Average HIP-event time of fn() on the current stream, after one untimed call."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def extras(layer: "Layer") -> dict:
+    """The rows beyond the layer path, on the same resident data: the CAE term in the column loop, packing the
+    layer's codes (and unpacking them with dequantisation), and the Hadamard rotation of the activations.
+    HBM-bound ones report bytes moved / time against the 8 TB/s peak."""
+    cfg, out = layer.cfg, {}
+    gs = layer.gs
+    sl = slice((cfg.groups - 1) * gs, cfg.groups * gs)          # H holds the last group's U after a step
+    Wg = layer.W[:, sl]
+
+    def quant(cae):
+        return lambda: G.gptq_quantize_layer(Wg, layer.H, cfg.bits, dead=layer.dead, P1=layer.P1 if layer.A is not None
+                                             else None, codes=layer.codes[:, sl], workspace=layer.ws_cae, cae=cae)
+    q_plain = _time_ms(quant(False))
+    q_cae = _time_ms(quant(True))
+    out["cae_term"] = {"quantize_ms": round(q_cae, 3), "quantize_ms_without": round(q_plain, 3),
+                       "channels": gs, "asymmetric": layer.A is not None}
+    K, N, b = cfg.K, cfg.N, cfg.bits
+    packed = G.gptq_pack_codes(layer.codes, b)
+    t_pack = _time_ms(lambda: G.gptq_pack_codes(layer.codes, b, packed=packed))
+    words = G.gptq_packed_words(K, b) * N * 4
+    W_hat = torch.empty(K, N, dtype=torch.bfloat16, device=layer.dev)
+    scales = torch.full((N,), 0.01, dtype=torch.float32, device=layer.dev)
+    t_unpack = _time_ms(lambda: G.gptq_unpack_codes(packed, K, b, scales=scales, codes=layer.codes, W_hat=W_hat))
+    for name, t, byt in (("pack_codes", t_pack, K * N + words), ("unpack_dequant_bf16", t_unpack, words + 3 * K * N)):
+        out[name] = {"ms": round(t, 4), "GB/s": round(byt / (t * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(byt / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 3), "bytes": byt}
+    if K & (K - 1) == 0 and 16 <= K <= 16384:
+        d = torch.tensor(workloads.hadamard_signs(cfg).astype("int8"), device=layer.dev)
+        t_rot = _time_ms(lambda: G.gptq_hadamard_rotate(layer.X, d, out=layer.X), reps=2)
+        byt = 2 * layer.X.numel() * layer.X.element_size()
+        out["hadamard_rotate_X"] = {"ms": round(t_rot, 3), "GB/s": round(byt / (t_rot * 1e-3) / 1e9, 1),
+                                    "frac_hbm": round(byt / (t_rot * 1e-3) / 1e9 / PEAK_HBM_GBS, 3), "bytes": byt,
+                                    "rows": layer.X.shape[0], "K": K, "dtype": str(layer.X.dtype)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +229,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="c2_q_proj_8b", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the timings of the rows beyond the layer path")
     ap.add_argument("--only", choices=["gram", "copy"], default=None,
                     help="profiling aids: run only the Gram launch per step, or a 1 GiB device copy (the "
                          "reference for scaling HBM byte counters)")
@@ -256,6 +309,9 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flop_per_launch": gram_flops(cfg), "launch_ms": round(gram_launch_ms, 3)},
     }
+    if not args.no_extras:
+        log("timing the CAE term, packing and the Hadamard rotation ...")
+        out["extras"] = extras(layer)
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(layer)
