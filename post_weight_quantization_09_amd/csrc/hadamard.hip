@@ -50,6 +50,9 @@ __global__ __launch_bounds__(1024) void fwht_rows_kernel(const void* in, int64_t
                                                          int64_t rows, int n, const int8_t* signs, float scale) {
     extern __shared__ float lds[];
     const int t = threadIdx.x;
+    float d[16];                      // this thread's signs, the same for every row
+#pragma unroll
+    for (int j = 0; j < 16; ++j) d[j] = signs ? (float)signs[16 * t + j] : 1.0f;
     for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
         float v[16];
         // pass 0: field at bit 0, the thread's 16 contiguous elements 16 t .. 16 t + 15
@@ -81,10 +84,8 @@ __global__ __launch_bounds__(1024) void fwht_rows_kernel(const void* in, int64_t
                 for (int j = 0; j < 16; ++j) v[j] = src[j];
             }
         }
-        if (signs) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) v[j] *= (float)signs[16 * t + j];
-        }
+        for (int j = 0; j < 16; ++j) v[j] *= d[j];
         butterflies(v, 0);
         int f = 0;
         for (int done = 4; done < n; done += 4) {
