@@ -52,7 +52,7 @@ import numpy as np
 __all__ = [
     "bf16_round", "gram", "gram_row_scaled", "cross_gram", "prepare", "channel_scales", "quantize_layer",
     "asym_correction", "asym_correction_by_definition", "cae_correction", "cae_correction_by_definition",
-    "pack_codes", "unpack_codes", "sylvester", "hadamard_rotate_rows", "layer_objective", "asym_objective",
+    "act_order_perm", "grid_scales", "MSE_SHRINK", "pack_codes", "unpack_codes", "sylvester", "hadamard_rotate_rows", "layer_objective", "asym_objective",
     "obq_sequential", "exhaustive_best", "fixed_grid_quantize", "dequantize_fp32",
 ]
 
@@ -170,13 +170,65 @@ def dequantize_fp32(codes: np.ndarray, scales: np.ndarray, bits: int) -> np.ndar
 # a6 + a7: the shared-order column loop.  [T3] one constrained compensation, [T4] its Cholesky form,
 # [T5] shared order for all channels and lazy block updates; [R]/[A] the asymmetric correction term.
 # ----------------------------------------------------------------------------------------------------------
+MSE_SHRINK = np.array([1.0 - i / 100.0 for i in range(21)], np.float32)   # clipping factors 1.00 .. 0.80
+
+
+def act_order_perm(H: np.ndarray) -> np.ndarray:
+    """[T6] act-order: the coordinates by descending Hessian diagonal, a processing-order heuristic.  Reading:
+    the dead fix comes first (a zero diagonal counts as 1), the sort is stable (equal diagonals keep their
+    natural order)."""
+    d = np.diag(np.asarray(H, np.float64)).copy()
+    d[d == 0.0] = 1.0
+    return np.argsort(-d, kind="stable")
+
+
+def grid_scales(Wg: np.ndarray, bits: int, mse: bool = False, choice: Optional[np.ndarray] = None,
+                band: float = 1e-4) -> np.ndarray:
+    """Symmetric grid scale per column of Wg (rows x N): s = fp32(2 max|w| / (2^b - 1)), 1 for an all-zero column.
+
+    mse=True (the weight-MSE clipping of [G]'s main experiments): candidates s_i = fp32(fp32(2 max|w| alpha_i)
+    / (2^b - 1)) for alpha_i = 1.00, 0.99, .., 0.80, and the one with the smallest sum of squared rounding
+    errors over the column is taken (the first on exact ties).  choice (N scales, optional): where another run
+    picked a different candidate whose error is within `band` (relative) of the smallest, that candidate is
+    taken (several results are correct when fp32 error sums decide).
+    """
+    Wf = np.asarray(Wg, np.float32)
+    N = Wf.shape[1]
+    amax = np.max(np.abs(Wf), axis=0) if Wf.shape[0] else np.zeros(N, np.float32)
+    qmax = np.float32(2 ** bits - 1)
+    base = np.float32(2.0) * amax
+    if not mse:
+        s = base / qmax
+    else:
+        z = 2 ** (bits - 1)
+        cand = (base[None, :] * MSE_SHRINK[:, None]) / qmax                   # fp32 products and quotients
+        w = Wf.astype(np.float64)
+        err = np.zeros(cand.shape)
+        for i in range(len(MSE_SHRINK)):
+            ci = cand[i].astype(np.float64)
+            safe = np.where(ci > 0, ci, 1.0)
+            q = ci * (np.clip(np.rint(w / safe) + z, 0, 2 ** bits - 1) - z)
+            err[i] = np.sum((w - q) ** 2, axis=0)
+        best = np.argmin(err, axis=0)
+        if choice is not None:
+            choice = np.asarray(choice, np.float32)
+            for n in range(N):
+                hit = np.flatnonzero(cand[:, n] == choice[n])
+                if hit.size and err[hit[0], n] <= err[best[n], n] * (1.0 + band):
+                    best[n] = hit[0]
+        s = cand[best, np.arange(N)]
+    return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+
+
 def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, dead: Optional[np.ndarray] = None,
                    scales: Optional[np.ndarray] = None, blocksize: Optional[int] = None,
                    P1: Optional[np.ndarray] = None, tie_codes: Optional[np.ndarray] = None,
-                   band: float = 1e-4, record_trace: bool = False, P2: Optional[np.ndarray] = None) -> dict:
-    """Quantise every output channel of W (K x N) in the natural coordinate order.
+                   band: float = 1e-4, record_trace: bool = False, P2: Optional[np.ndarray] = None,
+                   groupsize: Optional[int] = None, static_groups: bool = False, mse: bool = False,
+                   perm: Optional[np.ndarray] = None, scale_choice: Optional[np.ndarray] = None) -> dict:
+    """Quantise every output channel of W (K x N), all channels sharing one coordinate order.
 
-    For coordinate j (same j for every channel):
+    For coordinate j in processing order (same j for every channel), with s the scale in force at j:
         v = w_j / s;  c = clamp(round_half_even(v) + z, 0, 2^b - 1);  q = s (c - z)
         E_j = (w_j - q) / U_jj
         w_k -= U_jk E_j                      for every still-free k > j            [T3], [T4]
@@ -188,19 +240,52 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, dead: Optional[np.nd
     updates inside the current block at once and the rest for the whole block at its end (lazy batch,
     [T5]); the two are the same computation up to rounding order.
 
+    Scales ([T6]: groupsize changes the representation, blocksize only the computation):
+      groupsize=None   one scale per channel (grid_scales of W before dead rows are zeroed), or `scales`;
+      groupsize=G      one scale per channel and group of G coordinates.  Default ("re-estimated during
+                       compensation"): the groups are G consecutive coordinates of the processing order, and a
+                       group's scale is taken from the current, already compensated weights when the loop
+                       reaches its first coordinate.  static_groups=True: groups of G consecutive original
+                       coordinates with scales from W before the loop.
+      mse=True         weight-MSE clipping (grid_scales) of the scales that come from W before the loop
+                       (per channel or static groups); scale_choice gives another run's choice for ties.
+    perm (act-order, [T6]): processing order; U, P1 and P2 then belong to the permuted Hessian
+    (H[perm][:, perm]).  Inputs and outputs (codes, Q, E, V, W_pre, tie_codes) are in the original row
+    order; g_idx gives the group of each original coordinate.
+
     tie_codes (K x N ints, optional): where several results are correct - v within `band` of a rounding
     midpoint - take the given code if it is one of the two codes nearest to v, so that the remainder of a
     channel can be compared with a run that broke that tie the other way.  Anywhere else it is ignored.
     """
-    W0 = np.array(W, dtype=np.float64, copy=True)
-    K, N = W0.shape
+    W_in = np.asarray(W)
+    K, N = W_in.shape
+    order = np.arange(K) if perm is None else np.asarray(perm, np.int64)
+    assert sorted(order.tolist()) == list(range(K))
     U = np.asarray(U, np.float64)
     z = 2 ** (bits - 1)
     qmax = 2 ** bits - 1
-    s32 = channel_scales(W, bits) if scales is None else np.asarray(scales, np.float32)
-    s = s32.astype(np.float64)
+    if groupsize is None:
+        ng = 1
+        s32 = grid_scales(W_in, bits, mse, scale_choice) if scales is None else np.asarray(scales, np.float32)
+        S = s32[None, :]
+        grp = np.zeros(K, np.int64)                       # group of each processing position
+    else:
+        G = int(groupsize)
+        assert scales is None
+        ng = (K + G - 1) // G
+        S = np.zeros((ng, N), np.float32)
+        if static_groups:
+            for g in range(ng):
+                ch = None if scale_choice is None else np.asarray(scale_choice)[g]
+                S[g] = grid_scales(W_in[g * G:(g + 1) * G], bits, mse, ch)
+            grp = order // G
+        else:
+            assert not mse, "MSE clipping applies to scales taken from W before the loop"
+            grp = np.arange(K) // G
+    W0 = np.array(W_in, dtype=np.float64, copy=True)[order]
     if dead is not None:
-        W0[np.asarray(dead, bool), :] = 0.0
+        W0[np.asarray(dead, bool)[order], :] = 0.0
+    tie_p = None if tie_codes is None else np.asarray(tie_codes)[order]
     Wk = W0.copy()
     codes = np.zeros((K, N), np.int64)
     E = np.zeros((K, N))
@@ -214,6 +299,9 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, dead: Optional[np.nd
     for b0 in range(0, K, B):
         b1 = min(b0 + B, K)
         for j in range(b0, b1):
+            if groupsize is not None and not static_groups and j % G == 0:
+                S[j // G] = grid_scales(Wk[j:j + G], bits)   # current (compensated) weights of the group
+            s = S[grp[j]].astype(np.float64)
             w = Wk[j].copy()
             Wpre[j] = w
             v = w / s
@@ -221,10 +309,10 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, dead: Optional[np.nd
             fl = np.floor(v)
             inband = np.abs(v - fl - 0.5) < band
             n_inband += int(inband.sum())
-            if tie_codes is not None and inband.any():
+            if tie_p is not None and inband.any():
                 lo = np.clip(fl + z, 0, qmax)
                 hi = np.clip(fl + 1 + z, 0, qmax)
-                t = np.asarray(tie_codes[j], np.float64)
+                t = np.asarray(tie_p[j], np.float64)
                 take = inband & ((t == lo) | (t == hi)) & (t != c)
                 n_adopted += int(take.sum())
                 c = np.where(take, t, c)
@@ -254,9 +342,18 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, dead: Optional[np.nd
             if P2 is not None:
                 Wk[b1:] += P2[b0:b1, b1:].T @ (W0[b0:b1] - Wpre[b0:b1])
     losses = 0.5 * np.sum(E * E, axis=0)
+
+    def orig(a):                                           # processing order -> original row order
+        out = np.empty_like(a)
+        out[order] = a
+        return out
+
+    g_idx = orig(grp)
+    codes_o = orig(codes)
+    W_hat = (S[g_idx].astype(np.float32) * (codes_o.astype(np.float32) - np.float32(z))).astype(np.float32)
     return {
-        "codes": codes, "scales": s32, "Q": Q, "E": E, "V": V, "W_pre": Wpre, "W0": W0,
-        "losses": losses, "W_hat_fp32": dequantize_fp32(codes, s32, bits),
+        "codes": codes_o, "scales": S[0] if groupsize is None else S, "Q": orig(Q), "E": orig(E), "V": orig(V),
+        "W_pre": orig(Wpre), "W0": orig(W0), "losses": losses, "W_hat_fp32": W_hat, "g_idx": g_idx,
         "n_inband": n_inband, "n_adopted": n_adopted, "trace": trace,
     }
 
@@ -396,7 +493,8 @@ def fixed_grid_quantize(v: np.ndarray, lo: int = -8, hi: int = 7) -> np.ndarray:
 
 
 def obq_sequential(H: np.ndarray, w: np.ndarray, quant, order=None, A: Optional[np.ndarray] = None,
-                   damp: float = 0.0, X_free_basis: Optional[np.ndarray] = None, cae: bool = False) -> dict:
+                   damp: float = 0.0, X_free_basis: Optional[np.ndarray] = None, cae: bool = False,
+                   quant_at=None) -> dict:
     """Sequential constrained compensation with an explicit inverse of the free block at every step.
 
     [T3]: with free set F (current coordinate q first) and P_F = (H[F,F])^{-1}, fixing w_q to its grid
@@ -406,6 +504,8 @@ def obq_sequential(H: np.ndarray, w: np.ndarray, quant, order=None, A: Optional[
     ridge least squares; X_free_basis = (X, dX) pairs it is solved from directly (lstsq), independent of
     the P1 closed form.  cae=True adds the compensation-aware residual of coordinate q, (w0_q - w_q) X~_q with
     X~ = X + dX and w0 the starting weights, to the same least-squares right-hand side ([R] items 2, 3).
+    quant_at(i, w) (optional) returns the quantiser for step i given the current weights (grids that are
+    re-estimated during compensation).
     """
     H = np.asarray(H, np.float64)
     K = H.shape[0]
@@ -418,7 +518,7 @@ def obq_sequential(H: np.ndarray, w: np.ndarray, quant, order=None, A: Optional[
         F = order[i:]
         PF = np.linalg.inv(H[np.ix_(F, F)])
         pre = w[q]
-        target = quant(w[q])
+        target = (quant if quant_at is None else quant_at(i, w))(w[q])
         r = w[q] - target
         delta = -r * PF[:, 0] / PF[0, 0]
         added.append(r * r / (2.0 * PF[0, 0]))

@@ -447,3 +447,105 @@ def test_hadamard_rotation_properties():
     np.testing.assert_allclose(y @ O.hadamard_rotate_rows(W, d).T, x @ W.T, rtol=1e-10, atol=1e-10)
     # without signs the rotation is its own inverse
     np.testing.assert_allclose(O.hadamard_rotate_rows(O.hadamard_rotate_rows(x)), x, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------------ groups, act-order, MSE clipping
+def _sym_quant(s, bits):
+    z, qmax = 2 ** (bits - 1), 2 ** bits - 1
+    return lambda v: s * (np.clip(np.rint(v / s) + z, 0, qmax) - z)
+
+
+def test_act_order_perm_worked_example():
+    H = np.diag([3.0, 0.0, 5.0, 3.0])          # dead coordinate 1 counts as 1; equal diagonals keep their order
+    assert list(O.act_order_perm(H)) == [2, 0, 3, 1]
+
+
+def test_act_order_loop_equals_explicit_order():
+    """Loop over the permuted problem == sequential compensation with explicit inverses in that order."""
+    rng = np.random.default_rng(41)
+    K = 9
+    X = rng.normal(size=(40, K)) * np.exp(rng.normal(size=K))
+    prep = O.prepare(O.gram([X]), 0.01)
+    perm = O.act_order_perm(prep["Hd"])
+    assert not np.array_equal(perm, np.arange(K))
+    Up = O.prepare(O.gram([X[:, perm]]), 0.01)["U"]
+    w = rng.normal(0, 1.5, size=K)
+    one = np.array([1.0], np.float32)
+    r = O.quantize_layer(w[:, None], Up, bits=4, scales=one, perm=perm)
+    seq = O.obq_sequential(prep["Hd"], w, O.fixed_grid_quantize, order=perm)
+    np.testing.assert_allclose(r["Q"][:, 0], seq["w"], atol=1e-10)
+    rb = O.quantize_layer(w[:, None], Up, bits=4, scales=one, perm=perm, blocksize=4)
+    np.testing.assert_array_equal(rb["codes"], r["codes"])
+
+
+@pytest.mark.parametrize("G,act", [(4, False), (4, True), (8, False)])
+def test_dynamic_groups_equal_explicit_regrid(G, act):
+    """Re-estimated group scales == sequential compensation that recomputes the grid from the current weights
+    at every group start (explicit inverses, any order)."""
+    rng = np.random.default_rng(43 + G)
+    K, bits = 12, 3
+    X = rng.normal(size=(60, K)) * np.exp(rng.normal(size=K))
+    prep = O.prepare(O.gram([X]), 0.01)
+    perm = O.act_order_perm(prep["Hd"]) if act else np.arange(K)
+    Up = O.prepare(O.gram([X[:, perm]]), 0.01)["U"]
+    w = rng.normal(0, 0.05, size=K)
+    r = O.quantize_layer(w[:, None], Up, bits, groupsize=G, perm=perm)
+
+    state = {}
+
+    def quant_at(i, wc):
+        if i % G == 0:
+            grp = perm[i:i + G]
+            state["s"] = float(O.grid_scales(wc[grp][:, None], bits)[0])
+        return _sym_quant(state["s"], bits)
+
+    seq = O.obq_sequential(prep["Hd"], w, None, order=perm, quant_at=quant_at)
+    np.testing.assert_allclose(r["Q"][:, 0], seq["w"], atol=1e-10)
+    # group index of each original coordinate, and W_hat through it
+    np.testing.assert_array_equal(r["g_idx"][perm], np.arange(K) // G)
+    np.testing.assert_array_equal(r["W_hat_fp32"], (r["scales"][r["g_idx"]] * (r["codes"] - 4)).astype(np.float32))
+    rb = O.quantize_layer(w[:, None], Up, bits, groupsize=G, perm=perm, blocksize=G)
+    np.testing.assert_array_equal(rb["codes"], r["codes"])
+
+
+def test_group_scales_reduce_to_per_channel():
+    rng = np.random.default_rng(44)
+    K, N = 16, 5
+    W = rng.normal(size=(K, N))
+    W[3] = 0.0
+    U = O.prepare(O.gram([rng.normal(size=(50, K))]), 0.01)["U"]
+    ref = O.quantize_layer(W, U, 3)
+    np.testing.assert_array_equal(O.grid_scales(W, 3), O.channel_scales(W, 3))
+    for static in (False, True):
+        r = O.quantize_layer(W, U, 3, groupsize=K, static_groups=static)
+        np.testing.assert_array_equal(r["scales"][0], ref["scales"])
+        np.testing.assert_array_equal(r["codes"], ref["codes"])
+    # static groups take their scales from the original rows of their group
+    r = O.quantize_layer(W, U, 3, groupsize=4, static_groups=True)
+    for g in range(4):
+        np.testing.assert_array_equal(r["scales"][g], O.channel_scales(W[4 * g:4 * g + 4], 3))
+
+
+def test_mse_clipping():
+    bits = 3
+    # all |w| equal: the unclipped grid reproduces them exactly (zero error), so alpha = 1 is kept
+    W = np.array([[0.5, -1.0], [-0.5, 1.0], [0.5, 1.0]], np.float32)
+    np.testing.assert_array_equal(O.grid_scales(W, bits, mse=True), O.grid_scales(W, bits))
+    # one outlier among many small values: clipping lowers the squared error, never raises it
+    rng = np.random.default_rng(45)
+    W = rng.normal(0, 0.1, size=(128, 6)).astype(np.float32)
+    W[7] = 1.0
+    s1 = O.grid_scales(W, bits)
+    sm = O.grid_scales(W, bits, mse=True)
+    assert (sm <= s1).all() and (sm < s1).any()
+
+    def err(s):
+        q = s * (np.clip(np.rint(W / s) + 4, 0, 7) - 4)
+        return ((W.astype(np.float64) - q) ** 2).sum(axis=0)
+
+    assert (err(sm.astype(np.float64)) <= err(s1.astype(np.float64))).all()
+    # the chosen scale is one of the fp32 candidates, and no candidate has a smaller error
+    cands = (np.float32(2) * np.abs(W).max(axis=0))[None, :] * O.MSE_SHRINK[:, None] / np.float32(7)
+    for n in range(W.shape[1]):
+        assert sm[n] in cands[:, n]
+        assert err(sm.astype(np.float64))[n] <= min(err(np.full(6, c, np.float64))[n] for c in cands[:, n])
