@@ -62,12 +62,15 @@ typedef enum {
     GPTQ_CALL_ACCUMULATE_HESSIAN = 0,
     GPTQ_CALL_PREPARE = 1,
     GPTQ_CALL_ASYM_CORRECTION = 2,
-    GPTQ_CALL_QUANTIZE_LAYER = 3
+    GPTQ_CALL_QUANTIZE_LAYER = 3,
+    GPTQ_CALL_ACT_ORDER = 4
 } gptq_call_t;
 
 /* Flags of gptq_quantize_layer. */
 #define GPTQ_FLAG_SCALES_GIVEN 1u  /* `scales` is an input (e.g. the fixed teaching grid of [T] section 2) */
 #define GPTQ_FLAG_CAE 4u           /* add the compensation-aware error term of [R] items 2-3 (gptq_quantize_layer) */
+#define GPTQ_FLAG_STATIC_GROUPS 8u /* group scales fixed from W before the loop ([T] section 6 "static groups") */
+#define GPTQ_FLAG_MSE 16u          /* weight-MSE clipping of scales taken from W before the loop ([G]) */
 
 /*
  * gptq_workspace_bytes - bytes of `workspace` a call needs for the given sizes.
@@ -145,6 +148,22 @@ gptq_status_t gptq_asym_correction(const float* U, const float* A, float* P1, in
                                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gptq_act_order - act-order ([T] section 6): a processing order of the input coordinates by descending Hessian
+ * diagonal, a heuristic of the official implementation.  Reading: the dead fix comes first (a zero diagonal counts
+ * as 1), the order is stable (equal diagonals keep their natural order).
+ *
+ *   H      device, K x K fp32 from gptq_accumulate_hessian; permuted in place: H <- H[perm][:, perm].
+ *   A      NULL, or the cross Gram of asymmetric calibration, permuted the same way.
+ *   perm   device int32[K], written: processing position j handles original coordinate perm[j].
+ *   Then gptq_prepare (and gptq_asym_correction) on the permuted matrices, and gptq_quantize_layer with perm and
+ *   the returned dead mask (which is in processing order).
+ *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_ACT_ORDER, K, 0, 0, 0) (a K x K copy).
+ * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP.  Asynchronous.
+ */
+gptq_status_t gptq_act_order(float* H, float* A, int64_t K, int32_t* perm, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
  * gptq_quantize_layer - quantise every output channel of W in the natural (shared) input-coordinate order
  * ([T] sections 3-5; symmetric per-channel grid of [G]).
  *
@@ -156,6 +175,17 @@ gptq_status_t gptq_asym_correction(const float* U, const float* A, float* P1, in
  *     w_k -= U_jk E_j for the remaining k of the current block;  [P1: w_k += P1_jk * w_j(before rounding)]
  *     after each block of `blocksize` coordinates the same updates are applied to all later coordinates
  *     at once (lazy batch, [T] section 5).
+ *   Group-wise scales (groupsize 32, 64 or 128; [T] section 6: the group size changes the representation, the
+ *     block size only the computation): one scale per channel and group.  Default, re-estimated during the
+ *     loop: groups of `groupsize` consecutive processing positions, the scale taken from the current
+ *     (compensated) weights, s = fp32(2 max|w| / (2^bits - 1)) over the group, when the loop reaches the
+ *     group's first coordinate.  GPTQ_FLAG_STATIC_GROUPS: groups of consecutive original coordinates whose
+ *     scales come from W before the loop.  scales is then ceil(K / groupsize) x N (row g: group g).
+ *   GPTQ_FLAG_MSE: scales taken from W before the loop (per channel, or static groups) are clipped: among
+ *     fp32(fp32(2 max|w| a) / (2^bits - 1)) for a = 1.00, 0.99, .., 0.80 the one with the least sum of squared
+ *     rounding errors over the channel (group) is used.
+ *   perm (act-order): from gptq_act_order; U, dead and P1 then belong to the permuted Hessian; W, codes, W_hat
+ *     and g_idx stay in the original coordinate order (pre_round is in processing order).
  *   GPTQ_FLAG_CAE ([R] items 2-3): every step also aligns to the original float output, adding
  *     w_k += P2_jk (w0_j - w_j(before rounding)) with w0 the original weights (dead rows zeroed) and
  *     P2 = [((H + A) U^T) masked strictly upper] U (A = 0 without P1).  Because H_d U^T is upper triangular
@@ -168,13 +198,19 @@ gptq_status_t gptq_asym_correction(const float* U, const float* A, float* P1, in
  *   U          device, K x K fp32 from gptq_prepare.        dead: device uint8[K] from gptq_prepare or NULL.
  *   P1         NULL, or device K x K fp32 from gptq_asym_correction (asymmetric calibration).
  *   bits       2..8.   blocksize: 128 (the lazy-batch width; the only value this build accepts).
+ *   perm       NULL, or device int32[K] from gptq_act_order.
+ *   groupsize  0 (one scale per channel), 32, 64 or 128.
+ *   g_idx      NULL, or device int32[K]: the group of every original coordinate (0 without groups).
  *   codes      device uint8, code of (k, n) written at codes[k * c_rs + n * c_cs].
- *   scales     device fp32[N]: written, or read with GPTQ_FLAG_SCALES_GIVEN (then each > 0 and finite).
+ *   scales     device fp32[N] (groups: [ceil(K/groupsize) * N]): written, or read with GPTQ_FLAG_SCALES_GIVEN
+ *              (per channel only; then each > 0 and finite).
  *   W_hat      NULL, or device, dtype w_dtype, s (c - z) evaluated in fp32 then converted, written at
  *              W_hat[k * w_rs + n * w_cs] (same strides as W; may alias W).
  *   losses     NULL, or device fp32[N]: per channel sum_j 1/2 E_j^2 ([T] section 3: the added objective).
  *   pre_round  NULL, or device fp32, K x N row-major (ld = N): w_j / s just before rounding (diagnostic).
- *   flags      GPTQ_FLAG_SCALES_GIVEN | GPTQ_FLAG_CAE (others rejected).
+ *   flags      GPTQ_FLAG_SCALES_GIVEN | GPTQ_FLAG_CAE | GPTQ_FLAG_STATIC_GROUPS | GPTQ_FLAG_MSE (others rejected;
+ *              SCALES_GIVEN excludes groups and MSE, STATIC_GROUPS needs groupsize, MSE needs no groups or static
+ *              groups).
  *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, flags | (P1?2:0))
  *              (with GPTQ_FLAG_CAE it also holds a copy of the original weights, N x K fp32).
  * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_NONFINITE (NaN/Inf weight or given scale),
@@ -186,6 +222,7 @@ gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K
                                   int bits, int blocksize, unsigned flags,
                                   uint8_t* codes, int64_t c_rs, int64_t c_cs,
                                   float* scales, void* W_hat, float* losses, float* pre_round,
+                                  const int32_t* perm, int64_t groupsize, int32_t* g_idx,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -249,7 +249,7 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, dead: Optional[np.nd
                        coordinates with scales from W before the loop.
       mse=True         weight-MSE clipping (grid_scales) of the scales that come from W before the loop
                        (per channel or static groups); scale_choice gives another run's choice for ties.
-    perm (act-order, [T6]): processing order; U, P1 and P2 then belong to the permuted Hessian
+    perm (act-order, [T6]): processing order; U, P1, P2 and dead then belong to the permuted Hessian
     (H[perm][:, perm]).  Inputs and outputs (codes, Q, E, V, W_pre, tie_codes) are in the original row
     order; g_idx gives the group of each original coordinate.
 
@@ -283,8 +283,8 @@ def quantize_layer(W: np.ndarray, U: np.ndarray, bits: int, dead: Optional[np.nd
             assert not mse, "MSE clipping applies to scales taken from W before the loop"
             grp = np.arange(K) // G
     W0 = np.array(W_in, dtype=np.float64, copy=True)[order]
-    if dead is not None:
-        W0[np.asarray(dead, bool)[order], :] = 0.0
+    if dead is not None:                                  # like U, the dead mask is in processing order
+        W0[np.asarray(dead, bool), :] = 0.0
     tie_p = None if tie_codes is None else np.asarray(tie_codes)[order]
     Wk = W0.copy()
     codes = np.zeros((K, N), np.int64)

@@ -16,9 +16,11 @@ LIB_PATH = os.path.join(_PKG_DIR, "libgptq_hip.so")
 
 GPTQ_OK, GPTQ_ERR_ARG, GPTQ_ERR_NONFINITE, GPTQ_ERR_NOT_PD, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP = range(6)
 GPTQ_DTYPE_F32, GPTQ_DTYPE_BF16 = 0, 1
-GPTQ_CALL_ACCUMULATE_HESSIAN, GPTQ_CALL_PREPARE, GPTQ_CALL_ASYM_CORRECTION, GPTQ_CALL_QUANTIZE_LAYER = range(4)
+GPTQ_CALL_ACCUMULATE_HESSIAN, GPTQ_CALL_PREPARE, GPTQ_CALL_ASYM_CORRECTION, GPTQ_CALL_QUANTIZE_LAYER, GPTQ_CALL_ACT_ORDER = range(5)
 GPTQ_FLAG_SCALES_GIVEN = 1
 GPTQ_FLAG_CAE = 4
+GPTQ_FLAG_STATIC_GROUPS = 8
+GPTQ_FLAG_MSE = 16
 
 _i64, _f32, _u32, _ptr, _size = ctypes.c_int64, ctypes.c_float, ctypes.c_uint, ctypes.c_void_p, ctypes.c_size_t
 
@@ -33,7 +35,8 @@ _SIGNATURES = {
     "gptq_asym_correction": (ctypes.c_int, [_ptr, _ptr, _ptr, _i64, _ptr, _size, _ptr]),
     "gptq_quantize_layer": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
                                            ctypes.c_int, ctypes.c_int, _u32, _ptr, _i64, _i64, _ptr, _ptr, _ptr,
-                                           _ptr, _ptr, _size, _ptr]),
+                                           _ptr, _ptr, _i64, _ptr, _ptr, _size, _ptr]),
+    "gptq_act_order": (ctypes.c_int, [_ptr, _ptr, _i64, _ptr, _ptr, _size, _ptr]),
     "gptq_packed_words": (_i64, [_i64, ctypes.c_int]),
     "gptq_hadamard_rotate": (ctypes.c_int, [_ptr, _i64, _ptr, _i64, ctypes.c_int, _i64, _i64, _ptr, _ptr]),
     "gptq_pack_codes": (ctypes.c_int, [_ptr, _i64, _i64, _i64, _i64, ctypes.c_int, _ptr, _i64, _ptr]),
@@ -191,9 +194,12 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, dead: Optio
                         scales: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
                         W_hat: Optional[torch.Tensor] = None, losses: Optional[torch.Tensor] = None,
                         pre_round: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                        stream=None, cae: bool = False) -> dict:
+                        stream=None, cae: bool = False, perm: Optional[torch.Tensor] = None, groupsize: int = 0,
+                        static_groups: bool = False, mse: bool = False, g_idx: Optional[torch.Tensor] = None) -> dict:
     """Quantises W (K x N view, any strides) with U; given `scales` are used as the grid (fixed-grid mode);
-    cae=True adds the compensation-aware error term (GPTQ_FLAG_CAE).
+    cae=True adds the compensation-aware error term (GPTQ_FLAG_CAE); perm (from gptq_act_order) runs the loop in
+    act-order; groupsize > 0 gives group-wise scales (ceil(K/groupsize) x N), re-estimated during the loop or
+    static_groups; mse clips the scales taken from W before the loop.
 
     Returns dict(codes uint8 K x N, scales fp32[N], W_hat, losses, pre_round) with the tensors written.
     """
@@ -207,13 +213,20 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, dead: Optio
     _contig(dead, "dead", torch.uint8)
     _contig(scales, "scales", torch.float32)
     _contig(losses, "losses", torch.float32)
+    _contig(perm, "perm", torch.int32)
+    _contig(g_idx, "g_idx", torch.int32)
     flags = 0
+    ng = (K + groupsize - 1) // groupsize if groupsize > 0 else 0
     if scales is None:
-        scales = torch.empty(N, dtype=torch.float32, device=dev)
+        scales = torch.empty((ng, N) if ng else (N,), dtype=torch.float32, device=dev)
     else:
         flags |= GPTQ_FLAG_SCALES_GIVEN
     if cae:
         flags |= GPTQ_FLAG_CAE
+    if static_groups:
+        flags |= GPTQ_FLAG_STATIC_GROUPS
+    if mse:
+        flags |= GPTQ_FLAG_MSE
     if codes is None:
         codes = torch.empty(K, N, dtype=torch.uint8, device=dev)
     if W_hat is not None and (W_hat.shape != W.shape or W_hat.stride() != W.stride() or W_hat.dtype != W.dtype):
@@ -225,9 +238,10 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, dead: Optio
     st = load().gptq_quantize_layer(
         _dptr(W), _dtype_code(W), K, N, W.stride(0), W.stride(1), _dptr(U), _dptr(dead), _dptr(P1), int(bits),
         int(blocksize), flags, _dptr(codes), codes.stride(0), codes.stride(1), _dptr(scales), _dptr(W_hat),
-        _dptr(losses), _dptr(pre_round), wp, wb, _stream(dev, stream))
+        _dptr(losses), _dptr(pre_round), _dptr(perm), int(groupsize), _dptr(g_idx), wp, wb, _stream(dev, stream))
     _check(st, "gptq_quantize_layer")
-    return {"codes": codes, "scales": scales, "W_hat": W_hat, "losses": losses, "pre_round": pre_round}
+    return {"codes": codes, "scales": scales, "W_hat": W_hat, "losses": losses, "pre_round": pre_round,
+            "g_idx": g_idx}
 
 
 def gptq_packed_words(K: int, bits: int) -> int:
@@ -292,3 +306,21 @@ def gptq_hadamard_rotate(x: torch.Tensor, signs: Optional[torch.Tensor] = None, 
                                      _dptr(signs), _stream(x.device, stream))
     _check(st, "gptq_hadamard_rotate")
     return out
+
+
+def gptq_act_order(H: torch.Tensor, A: Optional[torch.Tensor] = None, perm: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Act-order: returns perm (int32[K]) and permutes H (and A) in place to H[perm][:, perm]."""
+    K = H.shape[0]
+    _square(H, "H", K)
+    _contig(H, "H", torch.float32)
+    if A is not None:
+        _square(A, "A", K)
+        _contig(A, "A", torch.float32)
+    if perm is None:
+        perm = torch.empty(K, dtype=torch.int32, device=H.device)
+    _contig(perm, "perm", torch.int32)
+    workspace, wp, wb = _workspace(GPTQ_CALL_ACT_ORDER, K, 0, 0, 0, H.device, workspace)
+    st = load().gptq_act_order(_dptr(H), _dptr(A), K, _dptr(perm), wp, wb, _stream(H.device, stream))
+    _check(st, "gptq_act_order")
+    return perm

@@ -8,6 +8,7 @@
 #include "quantize.hpp"
 #include "pack.hpp"
 #include "hadamard.hpp"
+#include "act_order.hpp"
 
 using namespace gptq;
 
@@ -66,6 +67,7 @@ size_t gptq_workspace_bytes(gptq_call_t call, int64_t K, int64_t N, int64_t M, u
         case GPTQ_CALL_ACCUMULATE_HESSIAN: return accumulate_ws(K, M, (flags & 1u) != 0, (flags & 2u) != 0);
         case GPTQ_CALL_PREPARE: return prepare_workspace_bytes(K);
         case GPTQ_CALL_ASYM_CORRECTION: return asym_ws(K);
+        case GPTQ_CALL_ACT_ORDER: return K > 0 ? act_order_workspace_bytes(K) : 0;
         case GPTQ_CALL_QUANTIZE_LAYER:
             return quantize_workspace_bytes(K, N, (flags & 2u) != 0, (flags & GPTQ_FLAG_CAE) != 0);
     }
@@ -151,12 +153,19 @@ gptq_status_t gptq_asym_correction(const float* U, const float* A, float* P1, in
 gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K, int64_t N, int64_t w_rs,
                                   int64_t w_cs, const float* U, const uint8_t* dead, const float* P1, int bits,
                                   int blocksize, unsigned flags, uint8_t* codes, int64_t c_rs, int64_t c_cs,
-                                  float* scales, void* W_hat, float* losses, float* pre_round, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+                                  float* scales, void* W_hat, float* losses, float* pre_round, const int32_t* perm,
+                                  int64_t groupsize, int32_t* g_idx, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
     if (!W || !U || !codes || !scales || K < 1 || N < 1) return GPTQ_ERR_ARG;
     if (w_dtype != GPTQ_DTYPE_F32 && w_dtype != GPTQ_DTYPE_BF16) return GPTQ_ERR_ARG;
     if (bits < 2 || bits > 8 || blocksize != 128) return GPTQ_ERR_ARG;
-    if ((flags & ~(GPTQ_FLAG_SCALES_GIVEN | GPTQ_FLAG_CAE)) != 0) return GPTQ_ERR_ARG;
+    const unsigned known = GPTQ_FLAG_SCALES_GIVEN | GPTQ_FLAG_CAE | GPTQ_FLAG_STATIC_GROUPS | GPTQ_FLAG_MSE;
+    if ((flags & ~known) != 0) return GPTQ_ERR_ARG;
+    if (groupsize != 0 && groupsize != 32 && groupsize != 64 && groupsize != 128) return GPTQ_ERR_ARG;
+    const bool stat = (flags & GPTQ_FLAG_STATIC_GROUPS) != 0, mse = (flags & GPTQ_FLAG_MSE) != 0;
+    if (stat && groupsize == 0) return GPTQ_ERR_ARG;
+    if (mse && groupsize != 0 && !stat) return GPTQ_ERR_ARG;
+    if ((flags & GPTQ_FLAG_SCALES_GIVEN) && (groupsize != 0 || mse)) return GPTQ_ERR_ARG;
     if (w_rs < 1 || w_cs < 1 || c_rs < 1 || c_cs < 1) return GPTQ_ERR_ARG;
     if (K > (int64_t)1 << 24 || N > (int64_t)1 << 28) return GPTQ_ERR_ARG;
     if (!ws_ok(workspace, workspace_bytes, quantize_workspace_bytes(K, N, P1 != nullptr, (flags & GPTQ_FLAG_CAE) != 0)))
@@ -165,9 +174,18 @@ gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K
     a.W = W; a.w_dtype = w_dtype; a.K = K; a.N = N; a.w_rs = w_rs; a.w_cs = w_cs;
     a.U = U; a.dead = dead; a.P1 = P1; a.bits = bits; a.scales_given = (flags & GPTQ_FLAG_SCALES_GIVEN) != 0;
     a.cae = (flags & GPTQ_FLAG_CAE) != 0;
+    a.perm = perm; a.groupsize = groupsize; a.static_groups = stat; a.mse = mse; a.g_idx = g_idx;
     a.codes = codes; a.c_rs = c_rs; a.c_cs = c_cs; a.scales = scales; a.W_hat = W_hat; a.losses = losses;
     a.pre_round = pre_round;
     return quantize_layer(a, workspace, static_cast<hipStream_t>(stream));
+}
+
+gptq_status_t gptq_act_order(float* H, float* A, int64_t K, int32_t* perm, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    if (!H || !perm || K < 1 || K > (int64_t)1 << 24) return GPTQ_ERR_ARG;
+    if (!ws_ok(workspace, workspace_bytes, act_order_workspace_bytes(K))) return GPTQ_ERR_WORKSPACE;
+    return act_order(H, A, K, perm, workspace, static_cast<hipStream_t>(stream)) == hipSuccess ? GPTQ_OK
+                                                                                                : GPTQ_ERR_HIP;
 }
 
 gptq_status_t gptq_hadamard_rotate(const void* in, int64_t ld_in, void* out, int64_t ld_out, gptq_dtype_t dtype,

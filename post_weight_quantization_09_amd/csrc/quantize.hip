@@ -38,10 +38,11 @@ __global__ void quant_init_kernel(DevStatus* st, uint32_t* amax_bits, float* los
 
 // W (K x N view with strides) -> Wt (N x ldt fp32, dead rows zeroed, padding zero) and per-channel max |w|
 // taken before dead rows are zeroed.  64 x 64 tiles transposed through LDS.
+// With act-order, processing position k reads original row perm[k]; `dead` is indexed by processing position.
 template <bool BF16>
 __global__ __launch_bounds__(256) void convert_kernel(const void* Wv, int64_t K, int64_t N, int64_t w_rs,
                                                      int64_t w_cs, const uint8_t* dead, float* Wt, int64_t ldt,
-                                                     uint32_t* amax_bits, DevStatus* st) {
+                                                     uint32_t* amax_bits, DevStatus* st, const int32_t* perm) {
     __shared__ float tile[64][65];
     const int tid = threadIdx.x;
     const int64_t k0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void convert_kernel(const void* Wv, int64_t K,
         const int64_t k = k0 + kk, n = n0 + nn;
         float v = 0.f;
         if (k < K && n < N) {
-            const int64_t off = k * w_rs + n * w_cs;
+            const int64_t off = (perm ? (int64_t)perm[k] : k) * w_rs + n * w_cs;
             if (BF16) v = __uint_as_float((uint32_t)(static_cast<const uint16_t*>(Wv)[off]) << 16);
             else v = static_cast<const float*>(Wv)[off];
             if (!isfinite(v)) bad = 1;
@@ -104,6 +105,58 @@ __global__ void scales_kernel(const uint32_t* amax_bits, float* scales, float* r
     rscale[n] = 1.0f / s;
 }
 
+// Scales from W before the loop, one per (group of G original rows, channel): static groups, and the
+// weight-MSE clipping of [G]'s main experiments (also for per-channel scales, G = K).  s = fp32(2 max|w| / qmax),
+// or with clipping the candidate fp32(fp32(2 max|w| alpha_i) / qmax), alpha_i = 1.00, 0.99, .., 0.80, with the
+// least sum of squared rounding errors over the group (first on ties).  One thread per (group, channel); the
+// rows are read twice (max, then all 21 candidate errors at once).
+constexpr int kShrink = 21;
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void group_scales_kernel(const void* Wv, int64_t K, int64_t N, int64_t w_rs,
+                                                          int64_t w_cs, int64_t G, int bits, bool mse,
+                                                          float* scales) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t g = blockIdx.y;
+    if (n >= N) return;
+    const int64_t k0 = g * G, k1 = min<int64_t>(K, k0 + G);
+    auto ld = [&](int64_t k) -> float {
+        const int64_t off = k * w_rs + n * w_cs;
+        return BF16 ? __uint_as_float((uint32_t)(static_cast<const uint16_t*>(Wv)[off]) << 16)
+                    : static_cast<const float*>(Wv)[off];
+    };
+    float amax = 0.f;
+    for (int64_t k = k0; k < k1; ++k) amax = fmaxf(amax, fabsf(ld(k)));
+    const float qmax = (float)((1 << bits) - 1), z = (float)(1 << (bits - 1));
+    const float base = 2.0f * amax;
+    float s = base / qmax;
+    if (mse && amax > 0.f) {
+        float cand[kShrink], rcand[kShrink], err[kShrink];
+#pragma unroll
+        for (int i = 0; i < kShrink; ++i) {
+            const float alpha = (float)(1.0 - i / 100.0);
+            cand[i] = (base * alpha) / qmax;
+            rcand[i] = 1.0f / cand[i];
+            err[i] = 0.f;
+        }
+        for (int64_t k = k0; k < k1; ++k) {
+            const float w = ld(k);
+#pragma unroll
+            for (int i = 0; i < kShrink; ++i) {
+                const float c = fminf(fmaxf(rintf(w * rcand[i]) + z, 0.f), qmax);
+                const float d = w - (c - z) * cand[i];
+                err[i] = fmaf(d, d, err[i]);
+            }
+        }
+        int best = 0;
+#pragma unroll
+        for (int i = 1; i < kShrink; ++i)
+            if (err[i] < err[best]) best = i;
+        s = cand[best];
+    }
+    scales[g * N + n] = amax > 0.f ? s : 1.0f;
+}
+
 // Broadcast lane `src` of each 16-lane row to the whole row (DPP row_newbcast, gfx90a+).
 __device__ inline float row_bcast(float x, int src) {
     const int xi = __float_as_int(x);
@@ -132,19 +185,30 @@ struct BlockArgs {
     float* loss_acc;                // N
     float* pre_round;               // optional, K x N
     const DevStatus* st;
+    int64_t G;                      // group size (group modes)
+    const int32_t* perm;            // act-order (static groups look up the original row's group)
+    float* gscales;                 // ng x N: written at group starts (re-estimated) or read (static)
 };
+
+// Scale modes of the block kernel: one scale per channel; groups re-estimated from the current weights at each
+// group start (processing order); static groups whose scales were computed from W before the loop.
+enum : int { kScalePerChannel = 0, kScaleDynamic = 1, kScaleStatic = 2 };
 
 // Per-lane state of the block kernel: 8 strided coordinates of one channel.
 struct LaneState {
     float w[8], e[8], pre[8], w0[8];
     uint32_t code[8];
     float loss;
+    float s, rs;                    // scale in force (and its reciprocal)
 };
 
 struct StepConst {
     const float* Up; const float* Pp; const float* rdiag;
-    float s, rs, z, qmax;
-    int l;
+    const float* Ts; const float* Trs;   // static groups: per-step scales of this workgroup's 16 channels
+    float z, qmax;
+    int l, ch;
+    int64_t G, b0;
+    float* gscales;
     float* pre_round; int64_t prow_off; int64_t N; bool live;
 };
 
@@ -152,12 +216,16 @@ struct StepConst {
 // reads the operands of step J + 1 while it runs, so no LDS latency sits on the chain of dependent steps.
 struct StepOps {
     f32x4 u0, u1, p0, p1;
-    float rd;
+    float rd, s, rs;
 };
 
-template <int J, bool ASYM>
+template <int J, bool ASYM, int SM>
 __device__ __forceinline__ void load_ops(StepOps& o, const StepConst& k) {
     if constexpr (J < kB) {
+        if constexpr (SM == kScaleStatic) {
+            o.s = k.Ts[J * 16 + k.ch];
+            o.rs = k.Trs[J * 16 + k.ch];
+        }
         const f32x4* urow = reinterpret_cast<const f32x4*>(k.Up + (J * 16 + k.l) * 8);
         o.u0 = urow[0];
         o.u1 = urow[1];
@@ -174,15 +242,40 @@ __device__ __forceinline__ void load_ops(StepOps& o, const StepConst& k) {
 // CAE: the step's update uses the original weight w0_j in place of the pre-rounding value, both in the
 // error that multiplies U (w0_j - q) / U_jj and in the P1 coefficient; the step error E_j itself still feeds
 // the loss.  This is the P2 = P1 + I - diag(U)^-1 U form of the CAE term.
-template <int J, bool ASYM, bool CAE, bool PRE>
+// Re-estimated groups: at a group's first coordinate J the scale becomes 2 max|w| / qmax over the group's
+// rows J .. J+G-1 of the current weights (registers m in [J/16, (J+G)/16) of the channel's 16 lanes).
+template <int J>
+__device__ __forceinline__ void regroup(LaneState& st, const StepConst& k) {
+    if ((J & (k.G - 1)) != 0) return;
+    constexpr int m0 = J >> 4;
+    const int m1 = m0 + (int)(k.G >> 4);
+    float mx = 0.f;
+#pragma unroll
+    for (int m = m0; m < 8; ++m)
+        if (m < m1) mx = fmaxf(mx, fabsf(st.w[m]));
+    mx = fmaxf(mx, __shfl_xor(mx, 8, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 4, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 2, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 1, 16));
+    st.s = mx > 0.f ? (2.0f * mx) / k.qmax : 1.0f;
+    st.rs = 1.0f / st.s;
+    if (k.l == 0 && k.live) k.gscales[((k.b0 + J) / k.G) * k.N + k.prow_off] = st.s;
+}
+
+template <int J, bool ASYM, bool CAE, bool PRE, int SM>
 __device__ __forceinline__ void loop_step(LaneState& st, const StepConst& k, StepOps (&ops)[2]) {
     constexpr int m = J >> 4, lj = J & 15;
     const StepOps& o = ops[J & 1];
-    load_ops<J + 1, ASYM>(ops[(J + 1) & 1], k);
+    if constexpr (SM == kScaleDynamic) regroup<J>(st, k);
+    if constexpr (SM == kScaleStatic) {
+        st.s = o.s;
+        st.rs = o.rs;
+    }
+    load_ops<J + 1, ASYM, SM>(ops[(J + 1) & 1], k);
     const float wj = row_bcast(st.w[m], lj);
-    const float v = wj * k.rs;
+    const float v = wj * st.rs;
     const float c = fminf(fmaxf(rintf(v) + k.z, 0.f), k.qmax);
-    const float q = (c - k.z) * k.s;
+    const float q = (c - k.z) * st.s;
     const float e = (wj - q) * o.rd;
     const float wu = CAE ? row_bcast(st.w0[m], lj) : wj;      // value the update is taken from
     const float eu = CAE ? (wu - q) * o.rd : e;
@@ -207,19 +300,21 @@ __device__ __forceinline__ void loop_step(LaneState& st, const StepConst& k, Ste
     }
 }
 
-template <bool ASYM, bool CAE, bool PRE, int... Js>
+template <bool ASYM, bool CAE, bool PRE, int SM, int... Js>
 __device__ __forceinline__ void run_steps(LaneState& st, const StepConst& k, int bs,
                                           std::integer_sequence<int, Js...>) {
     StepOps ops[2];
-    load_ops<0, ASYM>(ops[0], k);
-    ((Js < bs ? loop_step<Js, ASYM, CAE, PRE>(st, k, ops) : (void)0), ...);
+    load_ops<0, ASYM, SM>(ops[0], k);
+    ((Js < bs ? loop_step<Js, ASYM, CAE, PRE, SM>(st, k, ops) : (void)0), ...);
 }
 
-template <bool ASYM, bool CAE>
+template <bool ASYM, bool CAE, int SM>
 __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
     __shared__ __attribute__((aligned(16))) float Up[kB * kB];               // [row j][16 lanes][8 slots]
     __shared__ __attribute__((aligned(16))) float Pp[ASYM ? kB * kB : 4];    // same layout (asymmetric)
     __shared__ float rdiag[kB];
+    __shared__ float Ts[SM == kScaleStatic ? kB * kChPerWG : 1];           // [step][channel] static scales
+    __shared__ float Trs[SM == kScaleStatic ? kB * kChPerWG : 1];
 
     if (p.st->flags) return;   // an input was rejected earlier in this call
     const int tid = threadIdx.x;
@@ -260,6 +355,19 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
         }
     }
     for (int j = tid; j < kB; j += 256) rdiag[j] = (j < bs) ? 1.0f / p.U[(b0 + j) * p.K + b0 + j] : 0.f;
+    if constexpr (SM == kScaleStatic) {
+        for (int idx = tid; idx < kB * kChPerWG; idx += 256) {
+            const int j = idx >> 4;
+            const int64_t nc = (int64_t)blockIdx.x * kChPerWG + (idx & 15);
+            float sc = 1.0f;
+            if (j < bs && nc < p.N) {
+                const int64_t ko = p.perm ? (int64_t)p.perm[b0 + j] : b0 + j;
+                sc = p.gscales[(ko / p.G) * p.N + nc];
+            }
+            Ts[idx] = sc;
+            Trs[idx] = 1.0f / sc;
+        }
+    }
     __syncthreads();
 
     const int lane = tid & 63, l = lane & 15;
@@ -279,15 +387,23 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
     }
     st.loss = 0.f;
     StepConst k;
-    k.Up = Up; k.Pp = Pp; k.rdiag = rdiag;
-    k.s = p.scales[nn]; k.rs = p.rscale[nn];
+    k.Up = Up; k.Pp = Pp; k.rdiag = rdiag; k.Ts = Ts; k.Trs = Trs;
+    if constexpr (SM == kScalePerChannel) {
+        st.s = p.scales[nn];
+        st.rs = p.rscale[nn];
+    } else {
+        st.s = 1.0f;
+        st.rs = 1.0f;
+    }
     k.z = (float)(1 << (p.bits - 1));
     k.qmax = (float)((1 << p.bits) - 1);
     k.l = l;
+    k.ch = tid >> 4;
+    k.G = p.G; k.b0 = b0; k.gscales = p.gscales;
     k.pre_round = p.pre_round ? p.pre_round + b0 * p.N : nullptr;
     k.prow_off = n; k.N = p.N; k.live = live;
-    if (k.pre_round) run_steps<ASYM, CAE, true>(st, k, bs, std::make_integer_sequence<int, kB>{});
-    else run_steps<ASYM, CAE, false>(st, k, bs, std::make_integer_sequence<int, kB>{});
+    if (k.pre_round) run_steps<ASYM, CAE, true, SM>(st, k, bs, std::make_integer_sequence<int, kB>{});
+    else run_steps<ASYM, CAE, false, SM>(st, k, bs, std::make_integer_sequence<int, kB>{});
 
     if (!live) return;
     uint8_t* crow = p.codes_t + n * p.ldt + b0;
@@ -302,10 +418,13 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
 }
 
 // codes_t (N x ldt) -> codes (K x N view with strides); W_hat = s (c - z) in the weight dtype; losses copy.
+// Processing position k is written to original row perm[k]; its scale is scales[n] (per channel) or
+// scales[g N + n] with g = k / G (groups re-estimated in processing order) or perm[k] / G (static groups).
 template <bool BF16>
 __global__ __launch_bounds__(256) void finalize_kernel(const uint8_t* codes_t, int64_t ldt, int64_t K, int64_t N,
                                                       uint8_t* codes, int64_t c_rs, int64_t c_cs, void* W_hat,
-                                                      int64_t w_rs, int64_t w_cs, const float* scales, int bits) {
+                                                      int64_t w_rs, int64_t w_cs, const float* scales, int bits,
+                                                      const int32_t* perm, int64_t G, bool static_groups) {
     __shared__ uint8_t tile[64][65];
     const int tid = threadIdx.x;
     const int64_t k0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
@@ -325,15 +444,17 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint8_t* codes_t, i
         {
             const int kk = n_fast_c ? a : b, nn = n_fast_c ? b : a;
             const int64_t k = k0 + kk, n = n0 + nn;
-            if (k < K && n < N) codes[k * c_rs + n * c_cs] = tile[kk][nn];
+            if (k < K && n < N) codes[(perm ? (int64_t)perm[k] : k) * c_rs + n * c_cs] = tile[kk][nn];
         }
         if (W_hat) {
             const int kk = n_fast_w ? a : b, nn = n_fast_w ? b : a;
             const int64_t k = k0 + kk, n = n0 + nn;
             if (k < K && n < N) {
-                const float v = ((float)tile[kk][nn] - z) * scales[n];
-                if (BF16) static_cast<__bf16*>(W_hat)[k * w_rs + n * w_cs] = (__bf16)v;
-                else static_cast<float*>(W_hat)[k * w_rs + n * w_cs] = v;
+                const int64_t ko = perm ? (int64_t)perm[k] : k;
+                const float s = G > 0 ? scales[((static_groups ? ko : k) / G) * N + n] : scales[n];
+                const float v = ((float)tile[kk][nn] - z) * s;
+                if (BF16) static_cast<__bf16*>(W_hat)[ko * w_rs + n * w_cs] = (__bf16)v;
+                else static_cast<float*>(W_hat)[ko * w_rs + n * w_cs] = v;
             }
         }
     }
@@ -342,6 +463,15 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint8_t* codes_t, i
 __global__ void copy_losses_kernel(const float* src, float* dst, int64_t N) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < N) dst[i] = src[i];
+}
+
+// Group of every original row: processing position j (original row perm[j]) is in group j / G (re-estimated
+// groups) or perm[j] / G (static groups); 0 with one scale per channel.
+__global__ void g_idx_kernel(int32_t* g_idx, int64_t K, const int32_t* perm, int64_t G, bool static_groups) {
+    const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (j >= K) return;
+    const int64_t ko = perm ? (int64_t)perm[j] : j;
+    g_idx[ko] = G > 0 ? (int32_t)((static_groups ? ko : j) / G) : 0;
 }
 
 struct QuantLayout {
@@ -394,15 +524,35 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
         dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(ldt, 64));
         if (a.w_dtype == GPTQ_DTYPE_BF16)
             hipLaunchKernelGGL((convert_kernel<true>), grid, dim3(256), 0, stream, a.W, K, N, a.w_rs, a.w_cs, a.dead,
-                               L.Wt, ldt, L.amax, L.st);
+                               L.Wt, ldt, L.amax, L.st, a.perm);
         else
             hipLaunchKernelGGL((convert_kernel<false>), grid, dim3(256), 0, stream, a.W, K, N, a.w_rs, a.w_cs, a.dead,
-                               L.Wt, ldt, L.amax, L.st);
+                               L.Wt, ldt, L.amax, L.st, a.perm);
         GPTQ_LAUNCH_CHECK();
     }
-    hipLaunchKernelGGL(scales_kernel, grid1d(N, 256), dim3(256), 0, stream, L.amax, a.scales, L.rscale, N, a.bits,
-                       a.scales_given, L.st);
-    GPTQ_LAUNCH_CHECK();
+    const int64_t G = a.groupsize;
+    const int sm = G == 0 ? kScalePerChannel : (a.static_groups ? kScaleStatic : kScaleDynamic);
+    if (G == 0 && !a.mse) {
+        hipLaunchKernelGGL(scales_kernel, grid1d(N, 256), dim3(256), 0, stream, L.amax, a.scales, L.rscale, N, a.bits,
+                           a.scales_given, L.st);
+        GPTQ_LAUNCH_CHECK();
+    } else if (sm != kScaleDynamic) {
+        // scales from W before the loop: MSE-clipped per channel (one group of K rows) or static groups
+        const int64_t gsz = G == 0 ? K : G;
+        dim3 grid((unsigned)ceil_div(N, 256), (unsigned)ceil_div(K, gsz));
+        if (a.w_dtype == GPTQ_DTYPE_BF16)
+            hipLaunchKernelGGL((group_scales_kernel<true>), grid, dim3(256), 0, stream, a.W, K, N, a.w_rs, a.w_cs, gsz,
+                               a.bits, a.mse, a.scales);
+        else
+            hipLaunchKernelGGL((group_scales_kernel<false>), grid, dim3(256), 0, stream, a.W, K, N, a.w_rs, a.w_cs, gsz,
+                               a.bits, a.mse, a.scales);
+        GPTQ_LAUNCH_CHECK();
+        if (G == 0) {   // reciprocals for the per-channel loop
+            hipLaunchKernelGGL(scales_kernel, grid1d(N, 256), dim3(256), 0, stream, L.amax, a.scales, L.rscale, N,
+                               a.bits, true, L.st);
+            GPTQ_LAUNCH_CHECK();
+        }
+    }
     if (cae)   // the original weights (dead rows zeroed), read by every step and by the trailing updates
         GPTQ_HIP_CHECK(hipMemcpyAsync(L.W0t, L.Wt, sizeof(float) * (size_t)N * (size_t)ldt, hipMemcpyDeviceToDevice,
                                       stream));
@@ -413,11 +563,17 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
         p.Wt = L.Wt; p.ldt = ldt; p.U = a.U; p.P1 = a.P1; p.K = K; p.N = N; p.b0 = b0; p.bs = bs;
         p.scales = a.scales; p.rscale = L.rscale; p.bits = a.bits; p.codes_t = L.codes_t; p.E = L.E;
         p.Wpre = L.Wpre; p.W0t = L.W0t; p.loss_acc = L.loss_acc; p.pre_round = a.pre_round; p.st = L.st;
+        p.G = G; p.perm = a.perm; p.gscales = a.scales;
         dim3 grid((unsigned)ceil_div(N, kChPerWG));
-        if (asym && cae) hipLaunchKernelGGL((quant_block_kernel<true, true>), grid, dim3(256), 0, stream, p);
-        else if (asym) hipLaunchKernelGGL((quant_block_kernel<true, false>), grid, dim3(256), 0, stream, p);
-        else if (cae) hipLaunchKernelGGL((quant_block_kernel<false, true>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((quant_block_kernel<false, false>), grid, dim3(256), 0, stream, p);
+#define GPTQ_BLOCK(A_, C_)                                                                                        \
+    if (sm == kScaleDynamic) hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScaleDynamic>), grid, dim3(256), 0, stream, p); \
+    else if (sm == kScaleStatic) hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScaleStatic>), grid, dim3(256), 0, stream, p); \
+    else hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScalePerChannel>), grid, dim3(256), 0, stream, p);
+        if (asym && cae) { GPTQ_BLOCK(true, true) }
+        else if (asym) { GPTQ_BLOCK(true, false) }
+        else if (cae) { GPTQ_BLOCK(false, true) }
+        else { GPTQ_BLOCK(false, false) }
+#undef GPTQ_BLOCK
         GPTQ_LAUNCH_CHECK();
         const int64_t b1 = b0 + bs;
         if (b1 < K) {
@@ -443,10 +599,14 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
         dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(K, 64));
         if (a.w_dtype == GPTQ_DTYPE_BF16)
             hipLaunchKernelGGL((finalize_kernel<true>), grid, dim3(256), 0, stream, L.codes_t, ldt, K, N, a.codes, a.c_rs,
-                               a.c_cs, a.W_hat, a.w_rs, a.w_cs, a.scales, a.bits);
+                               a.c_cs, a.W_hat, a.w_rs, a.w_cs, a.scales, a.bits, a.perm, G, a.static_groups);
         else
             hipLaunchKernelGGL((finalize_kernel<false>), grid, dim3(256), 0, stream, L.codes_t, ldt, K, N, a.codes, a.c_rs,
-                               a.c_cs, a.W_hat, a.w_rs, a.w_cs, a.scales, a.bits);
+                               a.c_cs, a.W_hat, a.w_rs, a.w_cs, a.scales, a.bits, a.perm, G, a.static_groups);
+        GPTQ_LAUNCH_CHECK();
+    }
+    if (a.g_idx) {
+        hipLaunchKernelGGL(g_idx_kernel, grid1d(K, 256), dim3(256), 0, stream, a.g_idx, K, a.perm, G, a.static_groups);
         GPTQ_LAUNCH_CHECK();
     }
     if (a.losses) {

@@ -12,6 +12,11 @@ struct QuantizeArgs {
     int bits = 4;
     bool scales_given = false;
     bool cae = false;               // compensation-aware error term (P2 = P1 + I - diag(U)^-1 U)
+    const int32_t* perm = nullptr;  // act-order: processing position j handles original row perm[j]
+    int64_t groupsize = 0;          // 0: one scale per channel; 32, 64, 128: group-wise scales
+    bool static_groups = false;     // group scales from W before the loop (groups of original rows)
+    bool mse = false;               // weight-MSE clipping of the scales taken from W before the loop
+    int32_t* g_idx = nullptr;       // optional output: group of each original row
     uint8_t* codes = nullptr; int64_t c_rs = 0, c_cs = 0;
     float* scales = nullptr; void* W_hat = nullptr; float* losses = nullptr; float* pre_round = nullptr;
 };

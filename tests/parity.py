@@ -28,14 +28,29 @@ def rel_fro(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
 
 
+DYN_SCALE_TOL = 1e-4   # re-estimated group scales: max of fp32 vs float64 working weights
+
+
 def check_codes(gpu: dict, W: np.ndarray, U_ref: np.ndarray, bits: int, dead=None, P1=None, scales=None,
-                H_obj: np.ndarray | None = None, label: str = "", P2=None) -> dict:
-    """Runs the oracle loop with tie-following and asserts the GPU codes, scales, losses and objective."""
+                H_obj: np.ndarray | None = None, label: str = "", P2=None, **opts) -> dict:
+    """Runs the oracle loop with tie-following and asserts the GPU codes, scales, losses and objective.
+
+    opts go to the oracle loop (groupsize, static_groups, mse, perm).  Scales taken from W before the loop are
+    compared exactly (the oracle follows the GPU's pick among MSE candidates of equal error within the band);
+    scales re-estimated from the working weights within DYN_SCALE_TOL.
+    """
     codes = gpu["codes"].cpu().numpy().astype(np.int64)
     s_gpu = gpu["scales"].cpu().numpy()
+    dynamic = opts.get("groupsize") and not opts.get("static_groups")
+    if opts.get("mse"):
+        opts["scale_choice"] = s_gpu
     ref = O.quantize_layer(W, U_ref, bits, dead=dead, scales=scales, blocksize=128, P1=P1, tie_codes=codes,
-                           band=BAND, P2=P2)
-    assert np.array_equal(s_gpu, ref["scales"]), f"{label}: scales differ"
+                           band=BAND, P2=P2, **opts)
+    if dynamic:
+        rel = np.abs(s_gpu.astype(np.float64) - ref["scales"]) / ref["scales"]
+        assert rel.max() <= DYN_SCALE_TOL, f"{label}: re-estimated scales differ by {rel.max():.2e}"
+    else:
+        assert np.array_equal(s_gpu, ref["scales"]), f"{label}: scales differ"
     bad = codes != ref["codes"]
     n_bad = int(bad.sum())
     if n_bad:

@@ -94,7 +94,8 @@ def test_quantize_validation(lib):
         a.update(kw)
         return lib.gptq_quantize_layer(a["W"], a["dt"], a["K"], a["N"], a["wrs"], a["wcs"], a["U"], a["dead"],
                                        a["P1"], a["bits"], a["bsz"], a["flags"], a["codes"], a["crs"], a["ccs"],
-                                       a["scales"], None, None, None, a["ws"], a["wsb"], None)
+                                       a["scales"], None, None, None, a.get("perm"), a.get("G", 0), None, a["ws"],
+                                       a["wsb"], None)
 
     assert call(bits=1) == b.GPTQ_ERR_ARG
     assert call(bits=9) == b.GPTQ_ERR_ARG
@@ -110,6 +111,13 @@ def test_quantize_validation(lib):
     cae = lib.gptq_workspace_bytes(b.GPTQ_CALL_QUANTIZE_LAYER, 64, 64, 0, b.GPTQ_FLAG_CAE)
     assert cae >= plain + 64 * 128 * 4
     assert call(flags=b.GPTQ_FLAG_CAE, wsb=plain) == b.GPTQ_ERR_WORKSPACE
+    # group sizes and the flags that go with them
+    assert call(G=48) == b.GPTQ_ERR_ARG and call(G=256) == b.GPTQ_ERR_ARG
+    assert call(flags=b.GPTQ_FLAG_STATIC_GROUPS) == b.GPTQ_ERR_ARG              # static groups need a size
+    assert call(flags=b.GPTQ_FLAG_MSE, G=64) == b.GPTQ_ERR_ARG                  # MSE only on scales from W
+    assert call(flags=b.GPTQ_FLAG_SCALES_GIVEN, G=64) == b.GPTQ_ERR_ARG
+    assert call(flags=b.GPTQ_FLAG_SCALES_GIVEN | b.GPTQ_FLAG_MSE) == b.GPTQ_ERR_ARG
+    assert call(flags=32) == b.GPTQ_ERR_ARG
 
 
 def test_asym_validation(lib):
@@ -148,3 +156,13 @@ def test_hadamard_validation(lib):
     assert h(FAKE, 64, FAKE, 128, 0, 4, 64, None, None) == b.GPTQ_ERR_ARG         # in place with different ld
     assert h(None, 64, FAKE, 64, 0, 4, 64, None, None) == b.GPTQ_ERR_ARG
     assert h(FAKE, 64, FAKE, 64, 0, 0, 64, None, None) == b.GPTQ_OK                # no rows: nothing to do
+
+
+def test_act_order_validation(lib):
+    ws = ctypes.c_void_p(0x100000)
+    need = lib.gptq_workspace_bytes(b.GPTQ_CALL_ACT_ORDER, 64, 0, 0, 0)
+    assert need >= 64 * 64 * 4
+    assert lib.gptq_act_order(None, None, 64, FAKE, ws, need, None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_act_order(FAKE, None, 64, None, ws, need, None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_act_order(FAKE, None, 0, FAKE, ws, need, None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_act_order(FAKE, None, 64, FAKE, ws, need - 1, None) == b.GPTQ_ERR_WORKSPACE

@@ -418,3 +418,72 @@ def test_hadamard_rotation_keeps_products(g):
     Y = g.gptq_hadamard_rotate(X, d) @ g.gptq_hadamard_rotate(W, d).T
     ref = X.double().cpu() @ W.double().cpu().T
     assert float((Y.double().cpu() - ref).abs().max() / ref.abs().max()) < 1e-5
+
+
+# ------------------------------------------------------------------------------------------------ act-order, groups, MSE
+def _next2_case(g, K, N, M, seed, bits, act, groupsize=0, static=False, mse=False, asym=False, cae=False):
+    base = "c4_up_proj_8b_gptaq" if asym else "c5_down_proj_70b"
+    cfg, L = _bf16_layer(K, N, M, seed=seed, base=base, **({} if asym else {"dead_frac": 0.01}))
+    X, W = L["X"].to(DEV), L["W"].to(DEV)
+    Xf = L["X_float"].to(DEV) if asym else None
+    H = torch.zeros(K, K, device=DEV)
+    A = torch.zeros(K, K, device=DEV) if asym else None
+    g.gptq_accumulate_hessian(H, X, X_float=Xf, A=A)
+    H_before = np64(H)
+    perm = g.gptq_act_order(H, A) if act else None
+    dead, _, _ = g.gptq_prepare(H, cfg.percdamp)
+    P1 = g.gptq_asym_correction(H, A) if asym else None
+    g_idx = torch.empty(K, dtype=torch.int32, device=DEV)
+    out = g.gptq_quantize_layer(W, H, bits, dead=dead, P1=P1, losses=torch.empty(N, device=DEV), cae=cae, perm=perm,
+                                groupsize=groupsize, static_groups=static, mse=mse, g_idx=g_idx)
+    # oracle: its own Gram, the library's order (checked against the oracle's order of the same diagonal)
+    Xn = L["X"].float().numpy()
+    Href = O.gram([Xn])
+    p = np.arange(K)
+    if act:
+        p = perm.cpu().numpy().astype(np.int64)
+        assert np.array_equal(p, O.act_order_perm(H_before)), "act-order permutation"
+    ref = O.prepare(Href[np.ix_(p, p)], cfg.percdamp)
+    Aref = O.cross_gram(L["X_float"].float().numpy(), Xn)[np.ix_(p, p)] if asym else None
+    P1r = O.asym_correction(ref["U"], Aref) if asym else None
+    P2r = O.cae_correction(ref["U"], Href[np.ix_(p, p)], Aref) if cae else None
+    opts = dict(groupsize=groupsize or None, static_groups=static, mse=mse, perm=p if act else None)
+    info = check_codes(out, L["W"].float().numpy(), ref["U"], bits, dead=ref["dead"], P1=P1r, P2=P2r,
+                       label=f"K={K} act={act} G={groupsize} static={static} mse={mse}", **opts)
+    assert np.array_equal(g_idx.cpu().numpy(), info["ref"]["g_idx"])
+    return out, info
+
+
+def test_act_order_parity(g):
+    K = 300
+    cfg, L = _bf16_layer(K, 8, 2000, seed=70, base="c5_down_proj_70b")
+    H = torch.zeros(K, K, device=DEV)
+    g.gptq_accumulate_hessian(H, L["X"].to(DEV))
+    Hn = np64(H)
+    perm = g.gptq_act_order(H).cpu().numpy().astype(np.int64)
+    assert np.array_equal(perm, O.act_order_perm(Hn))
+    assert np.array_equal(np64(H), Hn[np.ix_(perm, perm)])
+    out, info = _next2_case(g, 300, 77, 3000, 71, 3, act=True)
+    _print(f"act-order K=300: inband={info['n_inband']} adopted={info['n_adopted']}")
+
+
+@pytest.mark.parametrize("G,static,act,bits", [(32, False, False, 3), (64, False, True, 4), (128, False, False, 2),
+                                               (128, True, False, 3), (64, True, True, 3), (32, True, True, 4)])
+def test_group_scales_parity(g, G, static, act, bits):
+    out, info = _next2_case(g, 300, 77, 3000, 72 + G, bits, act, groupsize=G, static=static)
+    assert out["scales"].shape == ((300 + G - 1) // G, 77)
+    _print(f"groups G={G} static={static} act={act}: inband={info['n_inband']} adopted={info['n_adopted']} "
+           f"loss rel max={info['loss_rel_max']:.2e}")
+
+
+@pytest.mark.parametrize("G,act", [(0, False), (0, True), (128, False), (64, True)])
+def test_mse_clipping_parity(g, G, act):
+    out, info = _next2_case(g, 300, 77, 3000, 80 + G, 3, act, groupsize=G, static=G > 0, mse=True)
+    _print(f"mse G={G} act={act}: inband={info['n_inband']} adopted={info['n_adopted']}")
+
+
+def test_groups_with_gptaq_cae_act_order(g):
+    """All options together: asymmetric calibration, the CAE term, act-order, re-estimated groups of 128."""
+    out, info = _next2_case(g, 384, 96, 4000, 90, 3, act=True, groupsize=128, asym=True, cae=True)
+    _print(f"gptaq+cae+act+G128: inband={info['n_inband']} adopted={info['n_adopted']} "
+           f"loss rel max={info['loss_rel_max']:.2e}")
