@@ -187,8 +187,9 @@ def _time_ms(fn, reps: int = 3) -> float:
 
 
 def extras(layer: "Layer") -> dict:
-    """The rows beyond the layer path, on the same resident data: the CAE term in the column loop, packing the
-    layer's codes (and unpacking them with dequantisation), and the Hadamard rotation of the activations.
+    """The rows beyond the layer path, on the same resident data: the CAE term in the column loop, act-order with
+    re-estimated groups, MSE-clipped scales, packing the layer's codes (and unpacking them with dequantisation),
+    and the Hadamard rotation of the activations.
     HBM-bound ones report bytes moved / time against the 8 TB/s peak."""
     cfg, out = layer.cfg, {}
     gs = layer.gs
@@ -202,6 +203,19 @@ def extras(layer: "Layer") -> dict:
     q_cae = _time_ms(quant(True))
     out["cae_term"] = {"quantize_ms": round(q_cae, 3), "quantize_ms_without": round(q_plain, 3),
                        "channels": gs, "asymmetric": layer.A is not None}
+    # act-order on a K x K matrix (here a copy of the factor), then the loop with its permutation and
+    # re-estimated groups of 128; per-channel weight-MSE clipping
+    Hc = layer.H.clone()
+    ws_ao = torch.empty(G.gptq_workspace_bytes(G.GPTQ_CALL_ACT_ORDER, cfg.K), dtype=torch.uint8, device=layer.dev)
+    perm = G.gptq_act_order(Hc, workspace=ws_ao)
+    t_ao = _time_ms(lambda: G.gptq_act_order(Hc, perm=perm, workspace=ws_ao))
+    q_grp = _time_ms(lambda: G.gptq_quantize_layer(Wg, layer.H, cfg.bits, dead=layer.dead, codes=layer.codes[:, sl],
+                                                   workspace=layer.ws_cae, perm=perm, groupsize=128))
+    q_mse = _time_ms(lambda: G.gptq_quantize_layer(Wg, layer.H, cfg.bits, dead=layer.dead, codes=layer.codes[:, sl],
+                                                   workspace=layer.ws_cae, mse=True))
+    out["act_order"] = {"ms": round(t_ao, 3), "K": cfg.K}
+    out["quantize_act_order_groups128_ms"] = round(q_grp, 3)
+    out["quantize_mse_clipped_ms"] = round(q_mse, 3)
     K, N, b = cfg.K, cfg.N, cfg.bits
     packed = G.gptq_pack_codes(layer.codes, b)
     t_pack = _time_ms(lambda: G.gptq_pack_codes(layer.codes, b, packed=packed))

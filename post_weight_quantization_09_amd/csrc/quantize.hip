@@ -108,29 +108,38 @@ __global__ void scales_kernel(const uint32_t* amax_bits, float* scales, float* r
 // Scales from W before the loop, one per (group of G original rows, channel): static groups, and the
 // weight-MSE clipping of [G]'s main experiments (also for per-channel scales, G = K).  s = fp32(2 max|w| / qmax),
 // or with clipping the candidate fp32(fp32(2 max|w| alpha_i) / qmax), alpha_i = 1.00, 0.99, .., 0.80, with the
-// least sum of squared rounding errors over the group (first on ties).  One thread per (group, channel); the
-// rows are read twice (max, then all 21 candidate errors at once).
+// least sum of squared rounding errors over the group (first on ties).  A workgroup takes 16 channels of one
+// group; 16 threads per channel split its rows and combine their maxima and error sums through LDS in a fixed
+// order; the rows are read twice (max, then all 21 candidate errors at once).
 constexpr int kShrink = 21;
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void group_scales_kernel(const void* Wv, int64_t K, int64_t N, int64_t w_rs,
                                                           int64_t w_cs, int64_t G, int bits, bool mse,
                                                           float* scales) {
-    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    __shared__ float part[16][kShrink][17];
+    const int c = threadIdx.x & 15, r = threadIdx.x >> 4;            // channel in the workgroup, row part
+    const int64_t n = (int64_t)blockIdx.x * 16 + c;
     const int64_t g = blockIdx.y;
-    if (n >= N) return;
     const int64_t k0 = g * G, k1 = min<int64_t>(K, k0 + G);
+    const bool live = n < N;
     auto ld = [&](int64_t k) -> float {
         const int64_t off = k * w_rs + n * w_cs;
         return BF16 ? __uint_as_float((uint32_t)(static_cast<const uint16_t*>(Wv)[off]) << 16)
                     : static_cast<const float*>(Wv)[off];
     };
     float amax = 0.f;
-    for (int64_t k = k0; k < k1; ++k) amax = fmaxf(amax, fabsf(ld(k)));
+    if (live)
+        for (int64_t k = k0 + r; k < k1; k += 16) amax = fmaxf(amax, fabsf(ld(k)));
+    part[r][0][c] = amax;
+    __syncthreads();
+    amax = 0.f;
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, part[i][0][c]);
+    __syncthreads();
     const float qmax = (float)((1 << bits) - 1), z = (float)(1 << (bits - 1));
     const float base = 2.0f * amax;
     float s = base / qmax;
-    if (mse && amax > 0.f) {
+    if (mse && amax > 0.f) {   // the same for a channel's 16 threads; the barrier below is outside it
         float cand[kShrink], rcand[kShrink], err[kShrink];
 #pragma unroll
         for (int i = 0; i < kShrink; ++i) {
@@ -139,22 +148,33 @@ __global__ __launch_bounds__(256) void group_scales_kernel(const void* Wv, int64
             rcand[i] = 1.0f / cand[i];
             err[i] = 0.f;
         }
-        for (int64_t k = k0; k < k1; ++k) {
+        for (int64_t k = k0 + r; k < k1; k += 16) {
             const float w = ld(k);
 #pragma unroll
             for (int i = 0; i < kShrink; ++i) {
-                const float c = fminf(fmaxf(rintf(w * rcand[i]) + z, 0.f), qmax);
-                const float d = w - (c - z) * cand[i];
+                const float cc = fminf(fmaxf(rintf(w * rcand[i]) + z, 0.f), qmax);
+                const float d = w - (cc - z) * cand[i];
                 err[i] = fmaf(d, d, err[i]);
             }
         }
-        int best = 0;
 #pragma unroll
-        for (int i = 1; i < kShrink; ++i)
-            if (err[i] < err[best]) best = i;
-        s = cand[best];
+        for (int i = 0; i < kShrink; ++i) part[r][i][c] = err[i];
     }
-    scales[g * N + n] = amax > 0.f ? s : 1.0f;
+    __syncthreads();
+    if (mse && amax > 0.f && r == 0) {
+        float best_e = 0.f;
+        int best = 0;
+        for (int i = 0; i < kShrink; ++i) {
+            float e = 0.f;
+            for (int j = 0; j < 16; ++j) e += part[j][i][c];
+            if (i == 0 || e < best_e) {
+                best_e = e;
+                best = i;
+            }
+        }
+        s = ((base * (float)(1.0 - best / 100.0)) / qmax);
+    }
+    if (r == 0 && live) scales[g * N + n] = amax > 0.f ? s : 1.0f;
 }
 
 // Broadcast lane `src` of each 16-lane row to the whole row (DPP row_newbcast, gfx90a+).
@@ -539,7 +559,7 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
     } else if (sm != kScaleDynamic) {
         // scales from W before the loop: MSE-clipped per channel (one group of K rows) or static groups
         const int64_t gsz = G == 0 ? K : G;
-        dim3 grid((unsigned)ceil_div(N, 256), (unsigned)ceil_div(K, gsz));
+        dim3 grid((unsigned)ceil_div(N, 16), (unsigned)ceil_div(K, gsz));
         if (a.w_dtype == GPTQ_DTYPE_BF16)
             hipLaunchKernelGGL((group_scales_kernel<true>), grid, dim3(256), 0, stream, a.W, K, N, a.w_rs, a.w_cs, gsz,
                                a.bits, a.mse, a.scales);
