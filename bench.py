@@ -323,12 +323,12 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flop_per_launch": gram_flops(cfg), "launch_ms": round(gram_launch_ms, 3)},
     }
-    if not args.no_extras:
-        log("timing the CAE term, packing and the Hadamard rotation ...")
-        out["extras"] = extras(layer)
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(layer)
+    if not args.no_extras:   # last: the rotation timing rotates the resident activations in place
+        log("timing the CAE term, act-order, groups, MSE clipping, packing and the Hadamard rotation ...")
+        out["extras"] = extras(layer)
     print(json.dumps(out), flush=True)
 
 
