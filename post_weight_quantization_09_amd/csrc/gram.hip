@@ -8,13 +8,12 @@
 // Design (256 threads, 4 waves, one 256 x 256 output tile per workgroup, 128 x 128 per wave):
 //   * X is row-major (tokens x features), so both MFMA operands have the reduction index (tokens) as the
 //     slow dimension.  32-token x 256-column slabs of the two operands are staged in LDS in their natural
-//     row layout (16-byte chunks XOR-swizzled by 4 * (row % 4) so that the reads below are bank-conflict
-//     free).
-//   * Operands are read with ds_read_b64_tr_b16: within each 16-lane group, output lane j, element e comes
-//     from input lane 4 e + j / 4, element j % 4.  Letting input lane i address token row T0 + i / 4 and
-//     columns C0 + 4 (i % 4) .. +3 gives output lane j column C0 + j over tokens T0 .. T0+3, i.e. an MFMA
-//     operand fragment with no register shuffles; two such reads give the 8 tokens of a
-//     v_mfma_f32_32x32x16_bf16 lane.  A and B use the same token <-> (lane half, slot) map.
+//     row layout.
+//   * Operands are read with ds_read_b64 (each lane 4 columns of one token row; lanes on consecutive
+//     columns, so the reads are conflict-free) and regrouped with v_perm into v_mfma_f32_32x32x16_bf16
+//     fragments: lane l gets 4 columns x 8 tokens and accumulates the 4 x 4 interleaved sub-blocks
+//     (row 4 r + a, column 4 c + b) of its wave's 128 x 128 quadrant.  A and B use the same token <->
+//     (lane half, slot) map.
 //   * Only tiles on or above the diagonal are computed (H is symmetric); the cross term computes all.
 //   * The token range is split across workgroups when there are too few tiles to fill 256 CUs.  Splits are
 //     assigned XCD by XCD (workgroup id mod 8) so that the workgroups sharing an XCD's L2 stream the same
@@ -100,56 +99,19 @@ __device__ inline u32x4 diff_bf16(u32x4 xf, u32x4 x) {
     return o;
 }
 
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-#ifndef GPTQ_GRAM_TR
-#define GPTQ_GRAM_TR 0          // operand fragments by transposing LDS reads (else b64 reads + v_perm)
-#endif
-#ifndef GPTQ_GRAM_SWIZZLE
-#define GPTQ_GRAM_SWIZZLE GPTQ_GRAM_TR
-#endif
 #ifndef GPTQ_GRAM_RING
 #define GPTQ_GRAM_RING 4        // LDS ring slots of the direct-to-LDS kernel (32 KB each)
 #endif
-#ifndef GPTQ_GRAM_DMA
-#define GPTQ_GRAM_DMA 1         // plain bf16 Gram through the direct-to-LDS kernel when the layout allows
-#endif
-#ifndef GPTQ_GRAM_MAP
-#define GPTQ_GRAM_MAP 0         // 0: token splits grouped by XCD; 1: split-major (all XCDs on the same tokens)
-#endif
-#ifndef GPTQ_GRAM_INTERLEAVE
-#define GPTQ_GRAM_INTERLEAVE 1
-#endif
 
-// XOR mask applied to the 16-byte chunk index of a slab row.
-__device__ __forceinline__ int chunk_swz(int row) { return GPTQ_GRAM_SWIZZLE ? ((row & 3) << 2) : 0; }
+// Short offset of (row, col) in a 32 x 256 bf16 slab (rows contiguous, 512 bytes each).  Written as chunk
+// base + chunk offset rather than plain `col`: the compiler then schedules the operand addresses of the
+// streaming kernel in a way measured about 2% faster (2M tokens x 4096 features).
+__device__ __forceinline__ int slab_off(int row, int col) { return row * kGT + (col & ~7) + (col & 7); }
 
-// Physical short offset of (row, col) in a 32 x 256 bf16 slab: 16-byte chunk c of row r is stored at
-// chunk c ^ (4 (r % 4)).
-__device__ __forceinline__ int slab_off(int row, int col) {
-    return row * kGT + (((col >> 3) ^ chunk_swz(row)) << 3) + (col & 7);
-}
-
-// MFMA fragments of one 16-token k-step for 4 x 32 columns starting at column `base` of a slab.
-// Transposing reads: frag[a] holds, for lane l, column base + 32 a + l % 32 over tokens 16 ks + 8 (l / 32)
-// + 0..7.  b64 reads + v_perm: frag[a] holds column base + 4 (l % 32) + a over the same tokens.
+// MFMA fragments of one 16-token k-step for 4 x 32 columns starting at column `base` of a slab: b64 reads of
+// 4 columns x 8 token rows, regrouped by v_perm so that frag[a] holds column base + 4 (l % 32) + a over tokens
+// 16 ks + 8 (l / 32) + 0..7 (lane l).  The reads are row-contiguous across lanes (conflict-free).
 __device__ __forceinline__ void load_frags(const uint16_t* slab, int base, int ks, int lane, u32x4 (&frag)[4]) {
-#if GPTQ_GRAM_TR
-    const int q = lane >> 4, i = lane & 15;
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int row = ks * 16 + 8 * (q >> 1) + 4 * h + (i >> 2);
-            const int col = base + 32 * a + 16 * (q & 1) + 4 * (i & 3);
-            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(slab + slab_off(row, col)));
-            const u32x2 w = __builtin_bit_cast(u32x2, v);
-            frag[a][2 * h] = w.x;
-            frag[a][2 * h + 1] = w.y;
-        }
-    }
-#else
     const int g = lane >> 5, r32 = lane & 31;
     u32x2 raw[8];
 #pragma unroll
@@ -167,14 +129,11 @@ __device__ __forceinline__ void load_frags(const uint16_t* slab, int base, int k
         frag[2][s] = __builtin_amdgcn_perm(hi1, hi0, 0x05040100u);
         frag[3][s] = __builtin_amdgcn_perm(hi1, hi0, 0x07060302u);
     }
-#endif
 }
 
 // (row, col) of accumulator element r of MFMA block (a, b) for `lane` inside a wave's 128 x 128 quadrant.
-__device__ __forceinline__ int acc_row(int a, int r, int lane) {
-    return GPTQ_GRAM_TR ? 32 * a + mfma32_row(r, lane) : 4 * mfma32_row(r, lane) + a;
-}
-__device__ __forceinline__ int acc_col(int b, int lane) { return GPTQ_GRAM_TR ? 32 * b + (lane & 31) : 4 * (lane & 31) + b; }
+__device__ __forceinline__ int acc_row(int a, int r, int lane) { return 4 * mfma32_row(r, lane) + a; }
+__device__ __forceinline__ int acc_col(int b, int lane) { return 4 * (lane & 31) + b; }
 
 // Raw global data of one 32-token stage held in registers while it is in flight; the per-token weight and
 // the float-stream mismatch are applied when the stage is written to LDS, so that no arithmetic waits on
@@ -186,27 +145,18 @@ struct StageRegs {
     float s[SCALED ? 4 : 1];
 };
 
-// Scheduling hint (gfx9 sched_group_barrier masks): spread the 16 transposing LDS reads of one k-step over
-// the 16 MFMAs of the other, so the matrix core keeps a queue while operands are fetched.
+// Scheduling hint (gfx9 sched_group_barrier masks): spread the 16 LDS reads and the v_perm regrouping of one
+// k-step over the 16 MFMAs of the other, so the matrix core keeps a queue while operands are fetched.
 __device__ __forceinline__ void interleave_kstep() {
-    if (!GPTQ_GRAM_INTERLEAVE) return;
-    if (GPTQ_GRAM_TR) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-        }
-    } else {
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU (v_perm)
-        }
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU (v_perm)
     }
 }
 
@@ -365,7 +315,7 @@ void gram_bf16_lds_kernel(GramArgs p) {
     const int wi = wave >> 1, wj = wave & 1;
     int split, tile;
     const int bid = blockIdx.x;
-    if (GPTQ_GRAM_MAP == 0 && p.splits % 8 == 0) {
+    if (p.splits % 8 == 0) {
         const int x = bid & 7, q = bid >> 3, per = p.splits / 8;
         split = x * per + q / p.ntiles;
         tile = q % p.ntiles;
@@ -387,30 +337,22 @@ void gram_bf16_lds_kernel(GramArgs p) {
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
     // This wave DMAs token rows 8*wave .. 8*wave+7 of both slabs: 8 instructions of 1 KB (two 512-byte
-    // rows each: lanes 0-31 the first row, lanes 32-63 the second).  Lane l lands in LDS chunk l % 32 of its
-    // row, so it fetches the global chunk that the slab swizzle stores there.
-    // Instruction i covers rows 8 wave + 2 i + (lane / 32), whose row % 4 alternates between two values
-    // with the parity of i, hence two swizzled source chunks per lane.
+    // rows each: lanes 0-31 the first row, lanes 32-63 the second; lane l lands in, and fetches, 16-byte
+    // chunk l % 32 of its row).
     const int lrow = 8 * wave + (lane >> 5);
-    const int gchunk0 = (lane & 31) ^ chunk_swz(lrow);
-    const int gchunk1 = (lane & 31) ^ chunk_swz(lrow + 2);
     const uint16_t* XA = p.XA ? p.XA : p.X;          // A-side operand (the mismatch for the cross term)
     const int64_t lda = p.XA ? p.ldxa : p.ldx;
-    const uint16_t* srcA0 = XA + (int64_t)bi * kGT + gchunk0 * 8;
-    const uint16_t* srcA1 = XA + (int64_t)bi * kGT + gchunk1 * 8;
-    const uint16_t* srcB0 = p.X + (int64_t)bj * kGT + gchunk0 * 8;
-    const uint16_t* srcB1 = p.X + (int64_t)bj * kGT + gchunk1 * 8;
+    const uint16_t* srcA = XA + (int64_t)bi * kGT + (lane & 31) * 8;
+    const uint16_t* srcB = p.X + (int64_t)bj * kGT + (lane & 31) * 8;
     auto issue = [&](int64_t st) {
         const int slot = (int)(st % kRing);
         const int64_t tb = t0 + st * kGK + lrow;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t tok = tb + 2 * i;
-            const uint16_t* sa = (i & 1) ? srcA1 : srcA0;
-            const uint16_t* sb = (i & 1) ? srcB1 : srcB0;
-            __builtin_amdgcn_global_load_lds((const void*)(sa + tok * lda),
+            __builtin_amdgcn_global_load_lds((const void*)(srcA + tok * lda),
                                              (lds_void_t*)&ring[slot][0][8 * wave + 2 * i][0], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(sb + tok * p.ldx),
+            __builtin_amdgcn_global_load_lds((const void*)(srcB + tok * p.ldx),
                                              (lds_void_t*)&ring[slot][1][8 * wave + 2 * i][0], 16, 0, 0);
         }
     };
@@ -584,7 +526,7 @@ hipError_t gram_bf16(const GramPlan& pl, const uint16_t* X, int64_t ldx, const u
     const bool fast = p.vec && K % kGT == 0;
     const bool whole_stages = p.tokens_per_split % kGK == 0 && M % kGK == 0;
     const bool transformed = cross || rho != nullptr;
-    if (GPTQ_GRAM_DMA && fast && whole_stages && (!transformed || staging)) {
+    if (fast && whole_stages && (!transformed || staging)) {
         if (transformed) {
             // stage bf16(rho * X) or bf16(X~ - X) once, then run the plain streaming kernel on it
             const int64_t chunks = M * (K / 8);
