@@ -99,9 +99,6 @@ __device__ inline u32x4 diff_bf16(u32x4 xf, u32x4 x) {
     return o;
 }
 
-#ifndef GPTQ_GRAM_RING
-#define GPTQ_GRAM_RING 4        // LDS ring slots of the direct-to-LDS kernel (32 KB each)
-#endif
 
 // Short offset of (row, col) in a 32 x 256 bf16 slab (rows contiguous, 512 bytes each).  Written as chunk
 // base + chunk offset rather than plain `col`: the compiler then schedules the operand addresses of the
@@ -287,14 +284,16 @@ void gram_bf16_kernel(GramArgs p) {
 }
 
 // Plain symmetric Gram, fast layout (K a multiple of 256, 16-byte aligned rows, every split a whole number
-// of 32-token stages): activations go straight from global memory into a 4-stage LDS ring with
-// global_load_lds_dwordx4 (no register staging), so three stages (~100 KB per CU) are in flight while one
-// is consumed.  Wait counts and barriers are explicit: the compiler cannot see that a DMA'd stage belongs
-// to a different ring slot than the one being read and would otherwise drain all loads at every barrier.
+// of 32-token stages): activations go straight from global memory into a RING-slot LDS ring (32 KB per
+// slot) with global_load_lds_dwordx4 (no register staging), so RING-1 stages are in flight while one is
+// consumed.  Wait counts and barriers are explicit: the compiler cannot see that a DMA'd stage belongs to a
+// different ring slot than the one being read and would otherwise drain all loads at every barrier.
 // Per stage st:  [MFMA (st, k-step 0) || LDS reads + v_perm of (st, k-step 1)]
-//                [wait for this wave's loads of st+1; barrier; issue loads of st+3 into the freed slot]
+//                [wait for this wave's loads of st+1; barrier; issue loads of st+RING-1 into the freed slot]
 //                [MFMA (st, k-step 1) || LDS reads + v_perm of (st+1, k-step 0)]
-constexpr int kRing = GPTQ_GRAM_RING;
+// Ring depth, measured on MI355X: 3 slots when the token range is split (few tiles, every XCD's 32
+// workgroups on the same tokens: 4% faster at 4096 features, a deeper ring only queues more requests in
+// the L2); 4 slots for unsplit launches (1.5% faster at 28672 features).
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Wait until at most `later` stages (8 DMA instructions each) of this wave are still in flight, then
@@ -306,10 +305,12 @@ __device__ __forceinline__ void wait_vm_and_barrier(int later) {
     else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <bool CROSS>
+template <bool CROSS, int RING>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gram_bf16_lds_kernel(GramArgs p) {
-    __shared__ __attribute__((aligned(1024))) uint16_t ring[kRing][2][kGK][kGT];   // 128 KB
+    constexpr int kRing = RING;
+    static_assert(kRing >= 3 && kRing <= 5, "ring slots: 3..5 (32 KB each, 160 KB of LDS)");
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[kRing][2][kGK][kGT];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int wi = wave >> 1, wj = wave & 1;
@@ -345,7 +346,7 @@ void gram_bf16_lds_kernel(GramArgs p) {
     const uint16_t* srcA = XA + (int64_t)bi * kGT + (lane & 31) * 8;
     const uint16_t* srcB = p.X + (int64_t)bj * kGT + (lane & 31) * 8;
     auto issue = [&](int64_t st) {
-        const int slot = (int)(st % kRing);
+        const int slot = (int)((uint32_t)st % (uint32_t)kRing);
         const int64_t tb = t0 + st * kGK + lrow;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -357,7 +358,7 @@ void gram_bf16_lds_kernel(GramArgs p) {
         }
     };
     auto prep = [&](int64_t st, int ks, u32x4 (&va)[4], u32x4 (&vb)[4]) {
-        const int slot = (int)(st % kRing);
+        const int slot = (int)((uint32_t)st % (uint32_t)kRing);
         load_frags(&ring[slot][0][0][0], wi * 128, ks, lane, va);
         load_frags(&ring[slot][1][0][0], wj * 128, ks, lane, vb);
     };
@@ -527,6 +528,8 @@ hipError_t gram_bf16(const GramPlan& pl, const uint16_t* X, int64_t ldx, const u
     const bool whole_stages = p.tokens_per_split % kGK == 0 && M % kGK == 0;
     const bool transformed = cross || rho != nullptr;
     if (fast && whole_stages && (!transformed || staging)) {
+        // stage indices are taken modulo the ring in 32 bits
+        if (p.tokens_per_split / kGK >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
         if (transformed) {
             // stage bf16(rho * X) or bf16(X~ - X) once, then run the plain streaming kernel on it
             const int64_t chunks = M * (K / 8);
@@ -542,8 +545,11 @@ hipError_t gram_bf16(const GramPlan& pl, const uint16_t* X, int64_t ldx, const u
             if (cross) { p.XA = staging; p.ldxa = K; }
             else { p.X = staging; p.ldx = K; }
         }
-        if (cross) hipLaunchKernelGGL(gram_bf16_lds_kernel<true>, dim3(nblk), dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL(gram_bf16_lds_kernel<false>, dim3(nblk), dim3(256), 0, stream, p);
+        const bool split = pl.splits > 1;
+        if (cross && split) hipLaunchKernelGGL((gram_bf16_lds_kernel<true, 3>), dim3(nblk), dim3(256), 0, stream, p);
+        else if (cross) hipLaunchKernelGGL((gram_bf16_lds_kernel<true, 4>), dim3(nblk), dim3(256), 0, stream, p);
+        else if (split) hipLaunchKernelGGL((gram_bf16_lds_kernel<false, 3>), dim3(nblk), dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((gram_bf16_lds_kernel<false, 4>), dim3(nblk), dim3(256), 0, stream, p);
     } else if (fast) {
         if (cross) hipLaunchKernelGGL((gram_bf16_kernel<true, false, true>), dim3(nblk), dim3(256), 0, stream, p);
         else if (rho) hipLaunchKernelGGL((gram_bf16_kernel<false, true, true>), dim3(nblk), dim3(256), 0, stream, p);
