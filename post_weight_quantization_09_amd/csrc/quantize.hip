@@ -3,8 +3,11 @@
 // [T] section 3: fixing coordinate q to its grid value moves the still-free weights along the OBS direction.
 // [T] section 4: with U the upper factor of H_d^{-1}, that move is w_k -= U_qk E_q with E_q = (w_q - Q(w_q)) / U_qq.
 // [T] section 5: every output channel uses the same coordinate order, so all channels share U; inside a
-// block of 128 coordinates the updates are applied at once, the rest of the matrix is updated once per
-// block by one matrix product (W[b1:] -= U[B, b1:]^T E_B), here an fp32 MFMA GEMM.
+// block of 128 coordinates the updates are applied at once, the rest of the matrix is updated by matrix
+// products (W[b1:] -= U[B, b1:]^T E_B), here fp32 MFMA GEMMs.  The products are applied in two levels:
+// after each block only the rows of its 512-coordinate super-block, and once per super-block the far rows
+// with the errors of all its blocks (depth 512), so the far part of W is read and written once per
+// super-block instead of once per block.  The sums are the same; only their grouping differs.
 // [R] item 3 / [A]: the asymmetric variant adds w_k += P1_qk * w_q(before rounding), in block and in the
 // lazy product (a second operand pair of the same GEMM).
 // [G] / [T] section 2: symmetric per-channel grid, codes 0..2^b-1, zero point 2^(b-1), value s (c - z).
@@ -28,6 +31,7 @@ namespace gptq {
 namespace {
 
 constexpr int kB = 128;          // block (lazy batch) width
+constexpr int kSB = 4 * kB;      // super-block: far rows are updated once per kSB coordinates
 constexpr int kChPerWG = 16;     // channels per workgroup of the block kernel
 
 __global__ void quant_init_kernel(DevStatus* st, uint32_t* amax_bits, float* loss_acc, int64_t N) {
@@ -199,8 +203,9 @@ struct BlockArgs {
     const float* scales; const float* rscale;
     int bits;
     uint8_t* codes_t;               // N x ldt
-    float* E;                       // N x 128
-    float* Wpre;                    // N x 128 (asymmetric without CAE)
+    float* E;                       // this block's errors: N rows, stride lde
+    float* Wpre;                    // this block's weights before rounding (asymmetric without CAE), stride lde
+    int64_t lde;                    // row stride of E and Wpre
     const float* W0t;               // N x ldt original weights (CAE only)
     float* loss_acc;                // N
     float* pre_round;               // optional, K x N
@@ -427,12 +432,12 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
 
     if (!live) return;
     uint8_t* crow = p.codes_t + n * p.ldt + b0;
-    float* erow = p.E + n * kB;
+    float* erow = p.E + n * p.lde;
     for (int m = 0; m < 8; ++m) {
         const int c = 16 * m + l;
         if (c < bs) crow[c] = (uint8_t)st.code[m];
         erow[c] = st.e[m];
-        if (ASYM && !CAE) p.Wpre[n * kB + c] = st.pre[m];
+        if (ASYM && !CAE) p.Wpre[n * p.lde + c] = st.pre[m];
     }
     if (l == 0) p.loss_acc[n] += 0.5f * st.loss;
 }
@@ -517,8 +522,8 @@ QuantLayout carve(void* ws, int64_t K, int64_t N, bool asym, bool cae) {
     L.loss_acc = c.take<float>((size_t)N);
     L.Wt = c.take<float>((size_t)N * ldt);
     L.codes_t = c.take<uint8_t>((size_t)N * ldt);
-    L.E = c.take<float>((size_t)N * kB);
-    L.Wpre = asym && !cae ? c.take<float>((size_t)N * kB) : nullptr;
+    L.E = c.take<float>((size_t)N * kSB);
+    L.Wpre = asym && !cae ? c.take<float>((size_t)N * kSB) : nullptr;
     L.W0t = cae ? c.take<float>((size_t)N * ldt) : nullptr;
     L.bytes = c.bytes();
     return L;
@@ -577,43 +582,55 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
         GPTQ_HIP_CHECK(hipMemcpyAsync(L.W0t, L.Wt, sizeof(float) * (size_t)N * (size_t)ldt, hipMemcpyDeviceToDevice,
                                       stream));
 
-    for (int64_t b0 = 0; b0 < K; b0 += kB) {
-        const int bs = (int)std::min<int64_t>(kB, K - b0);
-        BlockArgs p;
-        p.Wt = L.Wt; p.ldt = ldt; p.U = a.U; p.P1 = a.P1; p.K = K; p.N = N; p.b0 = b0; p.bs = bs;
-        p.scales = a.scales; p.rscale = L.rscale; p.bits = a.bits; p.codes_t = L.codes_t; p.E = L.E;
-        p.Wpre = L.Wpre; p.W0t = L.W0t; p.loss_acc = L.loss_acc; p.pre_round = a.pre_round; p.st = L.st;
-        p.G = G; p.perm = a.perm; p.gscales = a.scales;
-        dim3 grid((unsigned)ceil_div(N, kChPerWG));
+    // Wt[:, r0:r1] -= E U[k0:k0+depth, r0:r1] (+ Wpre P1[k0:k0+depth, r0:r1] for the asymmetric term; with CAE,
+    // E holds (w0 - q) / U_jj and the P1 term takes the original weights W0[:, k0:k0+depth]).  E and Wpre point
+    // at the errors / pre-rounding weights of coordinate k0 (row stride kSB).
+    auto trailing = [&](int64_t r0, int64_t r1, int64_t k0, int64_t depth, const float* Ek, const float* Wpk) {
+        GemmArgs g;
+        g.M = N; g.N = r1 - r0; g.K1 = depth;
+        g.A1 = Ek; g.lda1 = kSB;
+        g.B1 = a.U + k0 * K + r0; g.ldb1 = K;
+        if (asym) {
+            g.K2 = depth;
+            g.A2 = cae ? L.W0t + k0 : Wpk;
+            g.lda2 = cae ? ldt : kSB;
+            g.B2 = a.P1 + k0 * K + r0; g.ldb2 = K;
+            g.a2_scale = -1.f;
+        }
+        g.C = L.Wt + r0; g.ldc = ldt;
+        g.alpha = -1.f; g.beta = 1.f;
+        return gemm_f32(g, 1, stream) == hipSuccess;
+    };
+
+    for (int64_t sb0 = 0; sb0 < K; sb0 += kSB) {
+        const int64_t sb1 = std::min<int64_t>(K, sb0 + kSB);
+        for (int64_t b0 = sb0; b0 < sb1; b0 += kB) {
+            const int bs = (int)std::min<int64_t>(kB, K - b0);
+            float* Eb = L.E + (b0 - sb0);
+            float* Wpb = L.Wpre ? L.Wpre + (b0 - sb0) : nullptr;
+            BlockArgs p;
+            p.Wt = L.Wt; p.ldt = ldt; p.U = a.U; p.P1 = a.P1; p.K = K; p.N = N; p.b0 = b0; p.bs = bs;
+            p.scales = a.scales; p.rscale = L.rscale; p.bits = a.bits; p.codes_t = L.codes_t;
+            p.E = Eb; p.Wpre = Wpb; p.lde = kSB;
+            p.W0t = L.W0t; p.loss_acc = L.loss_acc; p.pre_round = a.pre_round; p.st = L.st;
+            p.G = G; p.perm = a.perm; p.gscales = a.scales;
+            dim3 grid((unsigned)ceil_div(N, kChPerWG));
 #define GPTQ_BLOCK(A_, C_)                                                                                        \
     if (sm == kScaleDynamic) hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScaleDynamic>), grid, dim3(256), 0, stream, p); \
     else if (sm == kScaleStatic) hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScaleStatic>), grid, dim3(256), 0, stream, p); \
     else hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScalePerChannel>), grid, dim3(256), 0, stream, p);
-        if (asym && cae) { GPTQ_BLOCK(true, true) }
-        else if (asym) { GPTQ_BLOCK(true, false) }
-        else if (cae) { GPTQ_BLOCK(false, true) }
-        else { GPTQ_BLOCK(false, false) }
+            if (asym && cae) { GPTQ_BLOCK(true, true) }
+            else if (asym) { GPTQ_BLOCK(true, false) }
+            else if (cae) { GPTQ_BLOCK(false, true) }
+            else { GPTQ_BLOCK(false, false) }
 #undef GPTQ_BLOCK
-        GPTQ_LAUNCH_CHECK();
-        const int64_t b1 = b0 + bs;
-        if (b1 < K) {
-            // Lazy batch: Wt[:, b1:] -= E_B U[B, b1:]  (+ Wpre_B P1[B, b1:] for the asymmetric term; with CAE,
-            // E holds (w0 - q) / U_jj and the P1 term takes the original weights W0_B)
-            GemmArgs g;
-            g.M = N; g.N = K - b1; g.K1 = bs;
-            g.A1 = L.E; g.lda1 = kB;
-            g.B1 = a.U + b0 * K + b1; g.ldb1 = K;
-            if (asym) {
-                g.K2 = bs;
-                g.A2 = cae ? L.W0t + b0 : L.Wpre;
-                g.lda2 = cae ? ldt : kB;
-                g.B2 = a.P1 + b0 * K + b1; g.ldb2 = K;
-                g.a2_scale = -1.f;
-            }
-            g.C = L.Wt + b1; g.ldc = ldt;
-            g.alpha = -1.f; g.beta = 1.f;
-            if (gemm_f32(g, 1, stream) != hipSuccess) return GPTQ_ERR_HIP;
+            GPTQ_LAUNCH_CHECK();
+            // near rows: the rest of this super-block
+            const int64_t b1 = b0 + bs;
+            if (b1 < sb1 && !trailing(b1, sb1, b0, bs, Eb, Wpb)) return GPTQ_ERR_HIP;
         }
+        // far rows: everything after the super-block, with the errors of all its blocks
+        if (sb1 < K && !trailing(sb1, K, sb0, sb1 - sb0, L.E, L.Wpre)) return GPTQ_ERR_HIP;
     }
     {
         dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(K, 64));
