@@ -262,10 +262,13 @@ hipError_t gemm_f32(GemmArgs p, int64_t batch, hipStream_t stream) {
     p.vecB1 = vec_ok(p.B1, p.ldb1, p.strideB1);
     p.vecA2 = vec_ok(p.A2, p.lda2, p.strideA2);
     p.vecB2 = vec_ok(p.B2, p.ldb2, p.strideB2);
-    // Tile shape, measured on gfx950: 64 x 64 matches 128 x 128 on large products and beats it on triangular
-    // ones (finer skipping), on the depth-128 trailing updates and on small products (more workgroups in
-    // flight); from about 12k x 12k outputs on, 128 x 128 is ~5% faster (half the L2 traffic per flop).
-    if (p.M >= 12288 && p.N >= 12288 && p.K1 >= 1024) return launch<128, 128, 16>(p, batch, stream);
+    // Tile shape, measured on gfx950 (random data): 64 x 64 matches 128 x 128 on general products up to ~7k and
+    // beats it on the depth-128 trailing updates and on small products (more workgroups in flight); from about
+    // 12k x 12k outputs on, 128 x 128 is faster (half the L2 traffic per flop: +20% at 14336).  Triangular
+    // products (the factorisation's) switch at 7168, where 128 x 128 is 2-8% faster and at 3584 up to 30% slower.
+    const bool tri = (p.flags & (kGemmBLower | kGemmBUpper | kGemmAUpper | kGemmCUpper)) != 0;
+    const int64_t big = tri ? 7168 : 12288;
+    if (p.M >= big && p.N >= big && p.K1 >= 1024) return launch<128, 128, 16>(p, batch, stream);
     return launch<64, 64, 16>(p, batch, stream);
 }
 
