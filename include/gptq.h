@@ -100,8 +100,11 @@ size_t gptq_workspace_bytes(gptq_call_t call, int64_t K, int64_t N, int64_t M, u
  *   A          device, K x K fp32 row-major, read-modify-written; required iff X_float != NULL.  Not
  *              symmetric.
  *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_ACCUMULATE_HESSIAN, K, 0, M, flags) with flags
- *              (X_float != 0) | 2 (row_scale != 0).  With a transformed operand (row_scale or X_float), K a
- *              multiple of 256 and M a multiple of 32 it includes M x K bf16 of staging for that operand.
+ *              (X_float != 0) | 2 (row_scale != 0).  It holds the per-token-range partial sums of the
+ *              256 x 256 tiles (up to 64 ranges for small K; 8 once there are >= 1024 tiles, i.e. K > 11264, or
+ *              K > 7936 for the cross term: about 16 K^2 bytes, 13 GB at K = 28672).  With a transformed
+ *              operand (row_scale or X_float), K a multiple of 256 and M a multiple of 32 it includes M x K
+ *              bf16 of staging for that operand.
  * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP.  Asynchronous.
  */
 gptq_status_t gptq_accumulate_hessian(float* H, int64_t K,

@@ -291,9 +291,9 @@ void gram_bf16_kernel(GramArgs p) {
 // Per stage st:  [MFMA (st, k-step 0) || LDS reads + v_perm of (st, k-step 1)]
 //                [wait for this wave's loads of st+1; barrier; issue loads of st+RING-1 into the freed slot]
 //                [MFMA (st, k-step 1) || LDS reads + v_perm of (st+1, k-step 0)]
-// Ring depth, measured on MI355X: 3 slots when the token range is split (few tiles, every XCD's 32
-// workgroups on the same tokens: 4% faster at 4096 features, a deeper ring only queues more requests in
-// the L2); 4 slots for unsplit launches (1.5% faster at 28672 features).
+// Ring depth, measured on MI355X: 3 slots when the token range is split (every XCD's 32 workgroups on the
+// same tokens: 4% faster at 4096 features, 1% at 28672; a deeper ring only queues more requests in the L2);
+// 4 slots for unsplit launches (short token ranges).
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Wait until at most `later` stages (8 DMA instructions each) of this wave are still in flight, then
@@ -487,7 +487,12 @@ GramPlan gram_plan(int64_t K, int64_t M, bool cross) {
     pl.ntiles = cross ? pl.nb * pl.nb : pl.nb * (pl.nb + 1) / 2;
     // One workgroup per CU (256 CUs).  With few tiles the token range is split so that the workgroup
     // count fills whole rounds of 256: the split count (a multiple of 8, so that splits map to XCDs)
-    // minimising the idle fraction of the last round, keeping >= 8192 tokens per split.
+    // minimising the idle fraction of the last round, keeping >= 8192 tokens per split.  With many tiles the
+    // range is still split 8 ways, one range per XCD: a workgroup then streams 1/8 of the tokens, and the 32
+    // co-resident workgroups of an XCD, which run consecutive tiles of the same range, stay close enough in
+    // step for their shared column slabs to hit in the XCD's L2 (unsplit, they drift apart over the whole
+    // range: 29% L2 hits and 79x the activation bytes fetched at 28672 features).  Measured: 488 -> 467 ms at
+    // 524288 x 28672, 66.4 -> 58.5 ms at 262144 x 14336, for 8 partial tile sums more.
     int64_t best = 1;
     if (pl.ntiles < 1024) {
         double best_eff = -1.0;
@@ -498,6 +503,8 @@ GramPlan gram_plan(int64_t K, int64_t M, bool cross) {
             if (eff > best_eff + 1e-9) { best_eff = eff; best = s; }
         }
         if (M < 8 * 4096) best = std::max<int64_t>(1, std::min<int64_t>(8, M / 4096));
+    } else if (M >= 8 * 8192) {
+        best = 8;
     }
     pl.splits = (int)best;
     pl.tokens_per_split = ceil_div(ceil_div(std::max<int64_t>(M, 1), pl.splits), kGK) * kGK;
