@@ -367,13 +367,17 @@ def _fwht_bound(x64, K):
     return 2.0 * (n + 2) * 2.0 ** -24 * np.abs(x64).sum(axis=1, keepdims=True) / np.sqrt(K)
 
 
-@pytest.mark.parametrize("K,R,signed,inplace", [(16, 3, False, False), (32, 5, True, False), (64, 7, True, True),
-                                                (128, 33, True, False), (1024, 100, True, True),
-                                                (4096, 300, True, False), (8192, 17, False, False),
-                                                (16384, 9, True, True)])
-def test_hadamard_rotate_f32(g, K, R, signed, inplace):
+@pytest.mark.parametrize("K,R,signed,inplace,ldpad", [(16, 3, False, False, 8), (32, 5, True, False, 8),
+                                                      (64, 7, True, True, 8), (128, 33, True, False, 8),
+                                                      (256, 20, True, False, 1), (512, 12, True, True, 8),
+                                                      (1024, 100, True, True, 8), (2048, 9, False, False, 3),
+                                                      (4096, 300, True, False, 8), (8192, 17, False, False, 8),
+                                                      (16384, 9, True, True, 8)])
+def test_hadamard_rotate_f32(g, K, R, signed, inplace, ldpad):
+    """Every supported length (16 .. 16384, each its own kernel instantiation), 16-byte vector rows and rows
+    whose stride is not a multiple of 4 floats (scalar loads)."""
     rng = np.random.default_rng(K + R)
-    ld = K + 8
+    ld = K + ldpad
     buf = rng.normal(size=(R, ld)).astype(np.float32)
     x = buf[:, :K].astype(np.float64)
     d = rng.choice([-1, 1], size=K).astype(np.int8) if signed else None
@@ -389,14 +393,22 @@ def test_hadamard_rotate_f32(g, K, R, signed, inplace):
         assert np.array_equal(torch.tensor(buf, device=DEV)[:, K:].cpu().numpy(), buf[:, K:])
 
 
-@pytest.mark.parametrize("K,R", [(64, 50), (4096, 200)])
-def test_hadamard_rotate_bf16(g, K, R):
+@pytest.mark.parametrize("K,R,ldpad,inplace", [(64, 50, 0, False), (4096, 200, 0, False), (16, 140000, 0, True),
+                                               (256, 40, 1, False), (512, 30, 8, True), (2048, 20, 3, False),
+                                               (8192, 10, 0, True), (16384, 6, 1, False)])
+def test_hadamard_rotate_bf16(g, K, R, ldpad, inplace):
     """bf16 rows: the output is the nearest-even bf16 of the exact rotation, except where the exact value lies
-    within the fp32 rounding bound of a bf16 midpoint (then either neighbour is correct)."""
+    within the fp32 rounding bound of a bf16 midpoint (then either neighbour is correct).  Includes more rows
+    than workgroups (each workgroup then loops, loading its next row while transforming the current one) and
+    rows whose stride is not a multiple of 8 elements (scalar loads)."""
     rng = np.random.default_rng(K)
     x = torch.randn(R, K, generator=torch.Generator().manual_seed(K)).to(torch.bfloat16)
     d = rng.choice([-1, 1], size=K).astype(np.int8)
-    out = g.gptq_hadamard_rotate(x.to(DEV), torch.tensor(d, device=DEV)).cpu().float().numpy().astype(np.float64)
+    buf = torch.zeros(R, K + ldpad, dtype=torch.bfloat16, device=DEV)
+    buf[:, :K] = x.to(DEV)
+    xv = buf[:, :K]
+    res = g.gptq_hadamard_rotate(xv, torch.tensor(d, device=DEV), out=xv if inplace else None)
+    out = res.cpu().float().numpy().astype(np.float64)
     x64 = x.float().numpy().astype(np.float64)
     ref = O.hadamard_rotate_rows(x64, d)
     rne = O.bf16_round(ref.astype(np.float32)).astype(np.float64)   # exact -> fp32 is within the bound too
