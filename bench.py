@@ -3,7 +3,8 @@
 One step = the whole hot path for one K x N linear layer with its calibration activations already resident
 in HBM:  H = 0;  H += 2 X^T X over all M tokens (gptq_accumulate_hessian);  dead/damp + U (gptq_prepare);
 [GPTAQ: P1 (gptq_asym_correction)];  shared-order column loop with lazy trailing GEMMs (gptq_quantize_layer).
-Output groups (G2PTQ-style workloads) repeat Gram/prepare/quantize per group.
+Output groups (G2PTQ-style workloads): one Gram and one column loop per group, the groups' Hessians factorised
+together (gptq_prepare_groups).
 
 Prints one JSON line: layer time (ms, lower is better) plus the Gram's MFMA roofline fraction and the float64
 oracle timed on a bounded sample of the same workload on the host cores.
@@ -87,10 +88,15 @@ class Layer:
         torch.cuda.synchronize()
         log(f"generated {cfg.name}: X {tuple(self.X.shape)} {self.X.dtype} in {time.time() - t0:.1f}s")
         K, N, M = cfg.K, cfg.N, cfg.M
-        self.H = torch.empty(K, K, dtype=torch.float32, device=dev)
+        # one Hessian per output-channel group (one for plain layers); self.H is the last group's
+        if cfg.groups > 1 and cfg.asym_noise > 0:
+            raise ValueError("asymmetric calibration with output groups is not a workload here")
+        self.Hs = torch.empty(cfg.groups, K, K, dtype=torch.float32, device=dev)
+        self.H = self.Hs[cfg.groups - 1]
         self.A = torch.empty(K, K, dtype=torch.float32, device=dev) if self.Xf is not None else None
         self.P1 = torch.empty(K, K, dtype=torch.float32, device=dev) if self.Xf is not None else None
-        self.dead = torch.empty(K, dtype=torch.uint8, device=dev)
+        self.deads = torch.empty(cfg.groups, K, dtype=torch.uint8, device=dev)
+        self.dead = self.deads[cfg.groups - 1]
         gs = N // cfg.groups
         self.gs = gs
         self.codes = torch.empty(K, N, dtype=torch.uint8, device=dev)
@@ -98,7 +104,7 @@ class Layer:
         self.losses = torch.empty(N, dtype=torch.float32, device=dev)
         flags = (1 if self.Xf is not None else 0) | (2 if self.rho is not None else 0)
         ws = max(G.gptq_workspace_bytes(G.GPTQ_CALL_ACCUMULATE_HESSIAN, K, 0, M, flags),
-                 G.gptq_workspace_bytes(G.GPTQ_CALL_PREPARE, K),
+                 G.gptq_workspace_bytes(G.GPTQ_CALL_PREPARE, K, cfg.groups),
                  G.gptq_workspace_bytes(G.GPTQ_CALL_ASYM_CORRECTION, K),
                  G.gptq_workspace_bytes(G.GPTQ_CALL_QUANTIZE_LAYER, K, gs, 0, 2 if self.Xf is not None else 0))
         self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
@@ -108,7 +114,8 @@ class Layer:
         self.ev = []
 
     def step(self, record: bool):
-        """One pass of the hot path; with record=True returns per-stage HIP events (current stream)."""
+        """One pass of the hot path; with record=True returns HIP events (current stream) at the starts and ends of
+        the three stages: every group's Gram, the factorisation(s), every group's column loop."""
         cfg = self.cfg
         evs = []
 
@@ -118,24 +125,31 @@ class Layer:
                 e.record()
                 evs.append(e)
 
+        mark()
         for gi in range(cfg.groups):
-            self.H.zero_()
+            Hg = self.Hs[gi]
+            Hg.zero_()
             if self.A is not None:
                 self.A.zero_()
             rs = self.rho[gi].contiguous() if self.rho is not None else None
-            mark()
-            G.gptq_accumulate_hessian(self.H, self.X, row_scale=rs, X_float=self.Xf, A=self.A, workspace=self.ws)
-            mark()
-            self.dead, self.damp, self.n_dead = G.gptq_prepare(self.H, cfg.percdamp, dead=self.dead,
+            G.gptq_accumulate_hessian(Hg, self.X, row_scale=rs, X_float=self.Xf, A=self.A, workspace=self.ws)
+        mark()
+        if cfg.groups == 1:
+            d, damp, nd = G.gptq_prepare(self.H, cfg.percdamp, dead=self.dead, workspace=self.ws)
+            self.damps, self.n_deads = [damp], [nd]
+        else:   # the groups' Hessians factorised together, every step one launch over all groups
+            _, self.damps, self.n_deads = G.gptq_prepare_groups(self.Hs, cfg.percdamp, dead=self.deads,
                                                                workspace=self.ws)
-            P1 = None
-            if self.A is not None:
-                P1 = G.gptq_asym_correction(self.H, self.A, self.P1, workspace=self.ws)
-            mark()
+        P1 = None
+        if self.A is not None:
+            P1 = G.gptq_asym_correction(self.H, self.A, self.P1, workspace=self.ws)
+        mark()
+        for gi in range(cfg.groups):
             sl = slice(gi * self.gs, (gi + 1) * self.gs)
-            G.gptq_quantize_layer(self.W[:, sl], self.H, cfg.bits, dead=self.dead, P1=P1, blocksize=cfg.blocksize,
-                                  scales=None, codes=self.codes[:, sl], losses=None, workspace=self.ws)
-            mark()
+            G.gptq_quantize_layer(self.W[:, sl], self.Hs[gi], cfg.bits, dead=self.deads[gi], P1=P1,
+                                  blocksize=cfg.blocksize, scales=None, codes=self.codes[:, sl], losses=None,
+                                  workspace=self.ws)
+        mark()
         return evs
 
 
@@ -284,12 +298,10 @@ def main():
         log(f"timed step {i} enqueued/done")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    for evs in ev_all:
-        for gi in range(cfg.groups):
-            e = evs[4 * gi: 4 * gi + 4]
-            stage["gram"] += e[0].elapsed_time(e[1])
-            stage["prepare"] += e[1].elapsed_time(e[2])
-            stage["quantize"] += e[2].elapsed_time(e[3])
+    for e in ev_all:
+        stage["gram"] += e[0].elapsed_time(e[1])
+        stage["prepare"] += e[1].elapsed_time(e[2])
+        stage["quantize"] += e[2].elapsed_time(e[3])
     for k in stage:
         stage[k] /= args.steps
     ms = 1e3 * wall / args.steps

@@ -2,11 +2,12 @@
  * gptq.h - C ABI of the MI355X (gfx950) GPTQ-family layer-quantisation library (libgptq_hip.so).
  *
  * The library implements the hot path of one linear layer's post-training quantisation:
- *   1. gptq_accumulate_hessian  H += 2 X^T X over calibration batches           (a1; [T] section 1)
- *                               [A += 2 (X~ - X)^T X for asymmetric calibration]  ([R] item 3, [A])
- *   2. gptq_prepare             dead coordinates, damping, U with H_d^{-1} = U^T U (a2, a3; [T] sections 4, 6)
- *   3. gptq_asym_correction     P1 = [(A U^T) masked strictly upper] U             (a4; [R] item 3)
- *   4. gptq_quantize_layer      shared-order column loop with lazy block updates   (a5-a8; [T] sections 3-5)
+ *   1. gptq_accumulate_hessian  H += 2 X^T X over calibration batches              ([T] section 1)
+ *                               [A += 2 (X~ - X)^T X for asymmetric calibration]     ([R] item 3, [A])
+ *   2. gptq_prepare             dead coordinates, damping, U with H_d^{-1} = U^T U   ([T] sections 4, 6)
+ *      gptq_prepare_groups      the same on the per-group Hessians of [G], all groups in each launch
+ *   3. gptq_asym_correction     P1 = [(A U^T) masked strictly upper] U               ([R] item 3)
+ *   4. gptq_quantize_layer      shared-order column loop with lazy block updates     ([T] sections 3-5)
  *
  * Sources, cited by page title and section:
  *   [T] GPTQ tutorial page "GPTQ：量化一个权重之后怎样补偿输出误差" (charlestar.github.io, 2026-10-15); its
@@ -126,7 +127,8 @@ gptq_status_t gptq_accumulate_hessian(float* H, int64_t K,
  *   percdamp   >= 0 and finite (0 disables damping).
  *   dead       device uint8[K], written.
  *   damp_out   NULL or host float*: receives damp.   n_dead_out: NULL or host int64_t*: number of dead.
- *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_PREPARE, K, 0, 0, 0).
+ *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_PREPARE, K, 0, 0, 0) (N counts the Hessians of
+ *              gptq_prepare_groups; 0 or 1 here).
  * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_NONFINITE (non-finite diagonal or pivot),
  * GPTQ_ERR_NOT_PD (a pivot <= 0; the contents of H_to_U are then unspecified), GPTQ_ERR_HIP.
  * Synchronises `stream` before returning.
@@ -134,6 +136,27 @@ gptq_status_t gptq_accumulate_hessian(float* H, int64_t K,
 gptq_status_t gptq_prepare(float* H_to_U, int64_t K, float percdamp,
                            uint8_t* dead, float* damp_out, int64_t* n_dead_out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gptq_prepare_groups - gptq_prepare on `groups` independent Hessians at once (the output-channel groups of
+ * [G], each with its own Hessian): every step of the factorisation runs as one launch over all groups,
+ * so the latency-bound small products and diagonal blocks of the recursion fill the GPU `groups` times better.
+ * Results are those of gptq_prepare on each Hessian.
+ *
+ *   H_to_U        device, groups K x K fp32 row-major matrices, Hessian g at H_to_U + g * group_stride.
+ *   K             >= 1.
+ *   groups        1 .. 65535.
+ *   group_stride  floats between consecutive Hessians, >= K * K (a multiple of 4 keeps the vector loads).
+ *   percdamp      as for gptq_prepare (the same for every group).
+ *   dead          device uint8[groups * K], dead[g * K + k] for coordinate k of group g.
+ *   damp_out      NULL or host float[groups].   n_dead_out: NULL or host int64_t[groups].
+ *   workspace     device scratch of gptq_workspace_bytes(GPTQ_CALL_PREPARE, K, groups, 0, 0).
+ * Errors: as gptq_prepare; GPTQ_ERR_NONFINITE or GPTQ_ERR_NOT_PD if any group fails (damp_out and n_dead_out
+ * are still written for every group).  Synchronises `stream` before returning.
+ */
+gptq_status_t gptq_prepare_groups(float* H_to_U, int64_t K, int64_t groups, int64_t group_stride, float percdamp,
+                                  uint8_t* dead, float* damp_out, int64_t* n_dead_out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gptq_asym_correction - GPTAQ correction matrix ([R] item 3; [A] closed form with channel

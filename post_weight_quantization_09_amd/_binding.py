@@ -32,6 +32,8 @@ _SIGNATURES = {
                                                _ptr, _size, _ptr]),
     "gptq_prepare": (ctypes.c_int, [_ptr, _i64, _f32, _ptr, ctypes.POINTER(_f32), ctypes.POINTER(_i64), _ptr,
                                     _size, _ptr]),
+    "gptq_prepare_groups": (ctypes.c_int, [_ptr, _i64, _i64, _i64, _f32, _ptr, ctypes.POINTER(_f32),
+                                           ctypes.POINTER(_i64), _ptr, _size, _ptr]),
     "gptq_asym_correction": (ctypes.c_int, [_ptr, _ptr, _ptr, _i64, _ptr, _size, _ptr]),
     "gptq_quantize_layer": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
                                            ctypes.c_int, ctypes.c_int, _u32, _ptr, _i64, _i64, _ptr, _ptr, _ptr,
@@ -170,6 +172,29 @@ def gptq_prepare(H: torch.Tensor, percdamp: float, dead: Optional[torch.Tensor] 
                              wb, _stream(H.device, stream))
     _check(st, "gptq_prepare")
     return dead, float(damp.value), int(n_dead.value)
+
+
+def gptq_prepare_groups(H: torch.Tensor, percdamp: float, dead: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None):
+    """In place H[g] -> U[g] for every group g of H (groups x K x K, each K x K matrix contiguous).
+    Returns (dead uint8[groups, K], damps list, n_dead list)."""
+    if H.dim() != 3 or H.shape[1] != H.shape[2]:
+        raise ValueError("H must be groups x K x K")
+    Gn, K = H.shape[0], H.shape[1]
+    if H.dtype != torch.float32 or H.stride(2) != 1 or H.stride(1) != K or H.stride(0) < K * K:
+        raise ValueError("H must be float32 with contiguous K x K matrices")
+    if dead is None:
+        dead = torch.empty(Gn, K, dtype=torch.uint8, device=H.device)
+    _contig(dead, "dead", torch.uint8)
+    if dead.numel() != Gn * K:
+        raise ValueError("dead must hold groups x K entries")
+    workspace, wp, wb = _workspace(GPTQ_CALL_PREPARE, K, Gn, 0, 0, H.device, workspace)
+    damps = (_f32 * Gn)()
+    n_dead = (_i64 * Gn)()
+    st = load().gptq_prepare_groups(_dptr(H), K, Gn, H.stride(0), float(percdamp), _dptr(dead), damps, n_dead, wp, wb,
+                                    _stream(H.device, stream))
+    _check(st, "gptq_prepare_groups")
+    return dead, [float(x) for x in damps], [int(x) for x in n_dead]
 
 
 def gptq_asym_correction(U: torch.Tensor, A: torch.Tensor, P1: Optional[torch.Tensor] = None,

@@ -65,7 +65,7 @@ size_t gptq_workspace_bytes(gptq_call_t call, int64_t K, int64_t N, int64_t M, u
     if (M < 0) M = 0;
     switch (call) {
         case GPTQ_CALL_ACCUMULATE_HESSIAN: return accumulate_ws(K, M, (flags & 1u) != 0, (flags & 2u) != 0);
-        case GPTQ_CALL_PREPARE: return prepare_workspace_bytes(K);
+        case GPTQ_CALL_PREPARE: return prepare_workspace_bytes(K, N);   // N: Hessians of gptq_prepare_groups
         case GPTQ_CALL_ASYM_CORRECTION: return asym_ws(K);
         case GPTQ_CALL_ACT_ORDER: return K > 0 ? act_order_workspace_bytes(K) : 0;
         case GPTQ_CALL_QUANTIZE_LAYER:
@@ -120,7 +120,18 @@ gptq_status_t gptq_prepare(float* H_to_U, int64_t K, float percdamp, uint8_t* de
     if (!H_to_U || K < 1 || !dead || !std::isfinite(percdamp) || percdamp < 0.f) return GPTQ_ERR_ARG;
     if (K > (int64_t)1 << 20) return GPTQ_ERR_ARG;
     if (!ws_ok(workspace, workspace_bytes, prepare_workspace_bytes(K))) return GPTQ_ERR_WORKSPACE;
-    return prepare(H_to_U, K, percdamp, dead, damp_out, n_dead_out, workspace, static_cast<hipStream_t>(stream));
+    return prepare(H_to_U, K, 1, K * K, percdamp, dead, damp_out, n_dead_out, workspace,
+                   static_cast<hipStream_t>(stream));
+}
+
+gptq_status_t gptq_prepare_groups(float* H_to_U, int64_t K, int64_t groups, int64_t group_stride, float percdamp,
+                                  uint8_t* dead, float* damp_out, int64_t* n_dead_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    if (!H_to_U || K < 1 || !dead || !std::isfinite(percdamp) || percdamp < 0.f) return GPTQ_ERR_ARG;
+    if (K > (int64_t)1 << 20 || groups < 1 || groups > 65535 || group_stride < K * K) return GPTQ_ERR_ARG;
+    if (!ws_ok(workspace, workspace_bytes, prepare_workspace_bytes(K, groups))) return GPTQ_ERR_WORKSPACE;
+    return prepare(H_to_U, K, groups, group_stride, percdamp, dead, damp_out, n_dead_out, workspace,
+                   static_cast<hipStream_t>(stream));
 }
 
 gptq_status_t gptq_asym_correction(const float* U, const float* A, float* P1, int64_t K, void* workspace,

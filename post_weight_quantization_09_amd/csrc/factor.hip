@@ -19,6 +19,7 @@
 // one LDS kernel factors and inverts.  Since the split points are multiples of 128 from the top, every
 // GEMM tile is aligned with the diagonal blocks.
 #include <algorithm>
+#include <vector>
 
 #include "factor.hpp"
 #include "gemm_f32.hpp"
@@ -29,8 +30,11 @@ namespace {
 
 constexpr int kNB = 128;
 
-__global__ __launch_bounds__(1024) void dead_damp_kernel(float* H, int64_t K, float percdamp, uint8_t* dead,
-                                                         DevStatus* st) {
+__global__ __launch_bounds__(1024) void dead_damp_kernel(float* H, int64_t K, int64_t strideH, float percdamp,
+                                                         uint8_t* dead, DevStatus* st) {
+    H += (int64_t)blockIdx.x * strideH;   // one workgroup per Hessian of the batch
+    dead += (int64_t)blockIdx.x * K;
+    st += blockIdx.x;
     __shared__ double ssum[1024];
     __shared__ unsigned scnt[1024];
     __shared__ unsigned sbad[1024];
@@ -86,7 +90,10 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
 //   Inverse by recursive doubling: the eight 16 x 16 diagonal blocks are inverted by back substitution, then
 //   adjacent blocks a (upper) and c are merged, U_ac = -U_aa (R_ac U_cc), for block sizes 16, 32 and 64,
 //   each product on v_mfma_f32_16x16x4_f32, one 16 x 16 tile per wave.
-__global__ __launch_bounds__(1024) void chol_ul_inv_kernel(float* D, int64_t ld, int n, DevStatus* st) {
+__global__ __launch_bounds__(1024) void chol_ul_inv_kernel(float* D, int64_t ld, int n, DevStatus* st,
+                                                           int64_t strideD) {
+    D += (int64_t)blockIdx.x * strideD;   // one workgroup per Hessian of the batch
+    st += blockIdx.x;
     __shared__ float S[kNB][kNB + 1];
     __shared__ float R[kNB][kNB + 1];
     __shared__ float Rinv[kNB];
@@ -219,16 +226,17 @@ __global__ __launch_bounds__(1024) void chol_ul_inv_kernel(float* D, int64_t ld,
     if (bad && tid == 0) atomicOr(&st->flags, bad);
 }
 
-__global__ void zero_lower_kernel(float* U, int64_t K) {
+__global__ void zero_lower_kernel(float* U, int64_t K, int64_t strideU) {
+    U += (int64_t)blockIdx.y * strideU;
     const int64_t row = blockIdx.x;
     for (int64_t c = threadIdx.x; c < row && c < K; c += blockDim.x) U[row * K + c] = 0.0f;
 }
 
-__global__ void clear_status_kernel(DevStatus* st) {
-    if (threadIdx.x == 0) {
-        st->flags = 0;
-        st->n_dead = 0;
-        st->damp = 0.f;
+__global__ void clear_status_kernel(DevStatus* st, int64_t n) {
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        st[i].flags = 0;
+        st[i].n_dead = 0;
+        st[i].damp = 0.f;
     }
 }
 
@@ -246,25 +254,41 @@ static size_t recursion_scratch_floats(int64_t n) {
     return std::max(recursion_scratch_floats(n2), x + std::max(x, recursion_scratch_floats(n1)));
 }
 
-size_t prepare_workspace_bytes(int64_t K) {
+// Per-Hessian scratch of a batch, rounded to 64 floats so that every batch element's operands stay 256-byte
+// aligned.
+static size_t batch_scratch_floats(int64_t K) {
+    return (std::max<size_t>(recursion_scratch_floats(K), 1) + 63) / 64 * 64;
+}
+
+size_t prepare_workspace_bytes(int64_t K, int64_t batch) {
+    batch = std::max<int64_t>(batch, 1);
     Carver c(nullptr);
-    c.take<DevStatus>(1);
-    c.take<float>(std::max<size_t>(recursion_scratch_floats(K), 1));
+    c.take<DevStatus>((size_t)batch);
+    c.take<float>(batch_scratch_floats(K) * (size_t)batch);
     return c.bytes();
 }
 
 namespace {
 
+// The recursion on `batch` Hessians at once (H + b strideH, scratch T + b Ts): the same splits for all, every
+// GEMM one batched launch and every diagonal block one launch with a workgroup per Hessian.
 struct Recursion {
     float* H;
     int64_t K;
     DevStatus* st;
     hipStream_t stream;
+    int64_t batch = 1, strideH = 0, Ts = 0;
+
+    hipError_t gemm(GemmArgs g, int64_t sa, int64_t sb, int64_t sc) const {
+        g.strideA1 = sa; g.strideB1 = sb; g.strideC = sc;
+        return gemm_f32(g, batch, stream);
+    }
 
     gptq_status_t run(int64_t o, int64_t n, float* T) {
         float* D = H + o * K + o;
         if (n <= kNB) {
-            hipLaunchKernelGGL(chol_ul_inv_kernel, dim3(1), dim3(1024), 0, stream, D, K, (int)n, st);
+            hipLaunchKernelGGL(chol_ul_inv_kernel, dim3((unsigned)batch), dim3(1024), 0, stream, D, K, (int)n, st,
+                               strideH);
             return hipGetLastError() == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
         }
         const int64_t n1 = split_top(n), n2 = n - n1;
@@ -281,7 +305,7 @@ struct Recursion {
             g.B1 = D22; g.ldb1 = K; g.transB = true;   // B(k, c) = U22[c][k], zero for k < c
             g.C = R12; g.ldc = n2;
             g.flags = kGemmBLower;
-            if (gemm_f32(g, 1, stream) != hipSuccess) return GPTQ_ERR_HIP;
+            if (gemm(g, strideH, strideH, Ts) != hipSuccess) return GPTQ_ERR_HIP;
         }
         {   // H11 -= R12 R12^T on the upper triangle
             GemmArgs g;
@@ -291,7 +315,7 @@ struct Recursion {
             g.C = D; g.ldc = K;
             g.alpha = -1.f; g.beta = 1.f;
             g.flags = kGemmCUpper;
-            if (gemm_f32(g, 1, stream) != hipSuccess) return GPTQ_ERR_HIP;
+            if (gemm(g, Ts, Ts, strideH) != hipSuccess) return GPTQ_ERR_HIP;
         }
         {   // X = R12 U22
             GemmArgs g;
@@ -300,7 +324,7 @@ struct Recursion {
             g.B1 = D22; g.ldb1 = K;
             g.C = X; g.ldc = n2;
             g.flags = kGemmBUpper;
-            if (gemm_f32(g, 1, stream) != hipSuccess) return GPTQ_ERR_HIP;
+            if (gemm(g, Ts, strideH, Ts) != hipSuccess) return GPTQ_ERR_HIP;
         }
         r = run(o, n1, T + n1 * n2);
         if (r != GPTQ_OK) return r;
@@ -312,7 +336,7 @@ struct Recursion {
             g.C = H12; g.ldc = K;
             g.alpha = -1.f; g.beta = 0.f;
             g.flags = kGemmAUpper;
-            if (gemm_f32(g, 1, stream) != hipSuccess) return GPTQ_ERR_HIP;
+            if (gemm(g, strideH, Ts, strideH) != hipSuccess) return GPTQ_ERR_HIP;
         }
         return GPTQ_OK;
     }
@@ -320,32 +344,38 @@ struct Recursion {
 
 }  // namespace
 
-gptq_status_t prepare(float* H, int64_t K, float percdamp, uint8_t* dead, float* damp_out, int64_t* n_dead_out,
-                      void* workspace, hipStream_t stream) {
+gptq_status_t prepare(float* H, int64_t K, int64_t batch, int64_t strideH, float percdamp, uint8_t* dead,
+                      float* damp_out, int64_t* n_dead_out, void* workspace, hipStream_t stream) {
     Carver c(workspace);
-    DevStatus* st = c.take<DevStatus>(1);
-    float* T = c.take<float>(std::max<size_t>(recursion_scratch_floats(K), 1));
+    DevStatus* st = c.take<DevStatus>((size_t)batch);
+    const int64_t Ts = (int64_t)batch_scratch_floats(K);
+    float* T = c.take<float>((size_t)Ts * (size_t)batch);
 
-    hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(64), 0, stream, st);
-    hipLaunchKernelGGL(dead_damp_kernel, dim3(1), dim3(1024), 0, stream, H, K, percdamp, dead, st);
+    hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(256), 0, stream, st, batch);
+    hipLaunchKernelGGL(dead_damp_kernel, dim3((unsigned)batch), dim3(1024), 0, stream, H, K, strideH, percdamp, dead,
+                       st);
     GPTQ_LAUNCH_CHECK();
     // Only the upper triangle of H is read.  The GEMMs treat the strictly lower parts of U blocks as stored
     // zeros, and no step writes below the diagonal outside the diagonal blocks (which the block kernel
     // clears), so clearing the lower triangle once keeps it zero throughout.
-    hipLaunchKernelGGL(zero_lower_kernel, dim3((unsigned)K), dim3(256), 0, stream, H, K);
+    hipLaunchKernelGGL(zero_lower_kernel, dim3((unsigned)K, (unsigned)batch), dim3(256), 0, stream, H, K, strideH);
     GPTQ_LAUNCH_CHECK();
 
-    Recursion rec{H, K, st, stream};
+    Recursion rec{H, K, st, stream, batch, strideH, Ts};
     gptq_status_t r = rec.run(0, K, T);
     if (r != GPTQ_OK) return r;
 
-    DevStatus hst;
-    GPTQ_HIP_CHECK(hipMemcpyAsync(&hst, st, sizeof(DevStatus), hipMemcpyDeviceToHost, stream));
+    std::vector<DevStatus> hst((size_t)batch);
+    GPTQ_HIP_CHECK(hipMemcpyAsync(hst.data(), st, sizeof(DevStatus) * (size_t)batch, hipMemcpyDeviceToHost, stream));
     GPTQ_HIP_CHECK(hipStreamSynchronize(stream));
-    if (damp_out) *damp_out = hst.damp;
-    if (n_dead_out) *n_dead_out = hst.n_dead;
-    if (hst.flags & kDevNonFinite) return GPTQ_ERR_NONFINITE;
-    if (hst.flags & kDevNotPD) return GPTQ_ERR_NOT_PD;
+    uint32_t flags = 0;
+    for (int64_t b = 0; b < batch; ++b) {
+        if (damp_out) damp_out[b] = hst[b].damp;
+        if (n_dead_out) n_dead_out[b] = hst[b].n_dead;
+        flags |= hst[b].flags;
+    }
+    if (flags & kDevNonFinite) return GPTQ_ERR_NONFINITE;
+    if (flags & kDevNotPD) return GPTQ_ERR_NOT_PD;
     return GPTQ_OK;
 }
 

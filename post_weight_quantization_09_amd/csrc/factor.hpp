@@ -5,10 +5,12 @@
 
 namespace gptq {
 
-size_t prepare_workspace_bytes(int64_t K);
+size_t prepare_workspace_bytes(int64_t K, int64_t batch = 1);
 
-// In place H -> U (upper, H_d^{-1} = U^T U, strictly lower part zero); writes dead[K]; synchronises.
-gptq_status_t prepare(float* H, int64_t K, float percdamp, uint8_t* dead, float* damp_out, int64_t* n_dead_out,
-                      void* workspace, hipStream_t stream);
+// In place on `batch` Hessians H + b strideH: H -> U (upper, H_d^{-1} = U^T U, strictly lower part zero);
+// writes dead[b K .. b K + K), damp_out[b] and n_dead_out[b] (host, nullable); synchronises.  The status words
+// of the batch are the first `batch` 256-byte headers of the workspace.
+gptq_status_t prepare(float* H, int64_t K, int64_t batch, int64_t strideH, float percdamp, uint8_t* dead,
+                      float* damp_out, int64_t* n_dead_out, void* workspace, hipStream_t stream);
 
 }  // namespace gptq

@@ -84,6 +84,22 @@ def test_prepare_validation(lib):
     assert lib.gptq_prepare(FAKE, 4096, 0.01, FAKE, None, None, ws, 1024, None) == b.GPTQ_ERR_WORKSPACE
 
 
+def test_prepare_groups_validation(lib):
+    ws = ctypes.c_void_p(0x100000)
+    big = 1 << 30
+    assert lib.gptq_prepare_groups(None, 8, 2, 64, 0.01, FAKE, None, None, ws, big, None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_prepare_groups(FAKE, 8, 0, 64, 0.01, FAKE, None, None, ws, big, None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_prepare_groups(FAKE, 8, 65536, 64, 0.01, FAKE, None, None, ws, big, None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_prepare_groups(FAKE, 8, 2, 63, 0.01, FAKE, None, None, ws, big, None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_prepare_groups(FAKE, 8, 2, 64, -1.0, FAKE, None, None, ws, big, None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_prepare_groups(FAKE, 8, 2, 64, 0.01, None, None, None, ws, big, None) == b.GPTQ_ERR_ARG
+    one = lib.gptq_workspace_bytes(b.GPTQ_CALL_PREPARE, 4096, 1, 0, 0)
+    four = lib.gptq_workspace_bytes(b.GPTQ_CALL_PREPARE, 4096, 4, 0, 0)
+    assert four > 3 * one and one == lib.gptq_workspace_bytes(b.GPTQ_CALL_PREPARE, 4096, 0, 0, 0)
+    assert lib.gptq_prepare_groups(FAKE, 4096, 4, 4096 * 4096, 0.01, FAKE, None, None, ws, four - 256,
+                                   None) == b.GPTQ_ERR_WORKSPACE
+
+
 def test_quantize_validation(lib):
     ws = ctypes.c_void_p(0x100000)
     big = 1 << 30

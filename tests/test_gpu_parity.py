@@ -129,6 +129,42 @@ def test_prepare(g, K):
     assert err <= 1e-4
 
 
+@pytest.mark.parametrize("K,groups,pad", [(300, 3, 0), (640, 4, 4), (1000, 2, 0), (129, 5, 1)])
+def test_prepare_groups(g, K, groups, pad):
+    """All groups in each launch give exactly the single-Hessian results (same kernels, same arithmetic per
+    group): U, dead flags, damp and dead counts, with different Hessians and dead sets per group and a group
+    stride with padding (pad = 1 makes it odd: scalar operand loads)."""
+    Hs = [_workload_H(K, seed=K + 7 * gi, dead_cols=[c for c in (gi, K // 2 + gi) if c < K]) for gi in range(groups)]
+    buf = torch.zeros(groups * (K * K + pad), dtype=torch.float32, device=DEV)
+    Hb = buf.as_strided((groups, K, K), (K * K + pad, K, 1))
+    for gi in range(groups):
+        Hb[gi].copy_(torch.tensor(Hs[gi], dtype=torch.float32))
+    dead, damps, n_dead = g.gptq_prepare_groups(Hb, 0.01)
+    for gi in range(groups):
+        Ht = torch.tensor(Hs[gi], dtype=torch.float32, device=DEV)
+        d1, damp1, nd1 = g.gptq_prepare(Ht, 0.01)
+        assert torch.equal(Hb[gi], Ht), f"group {gi}"
+        assert torch.equal(dead[gi], d1) and damps[gi] == damp1 and n_dead[gi] == nd1
+    ref = O.prepare(Hs[-1], 0.01)
+    err = np.abs(np64(Hb[groups - 1]) - ref["U"]).max() / np.abs(ref["U"]).max()
+    _print(f"prepare groups K={K} x{groups}: identical to single calls; last group U max rel err {err:.3e}")
+    assert err <= 1e-4
+    if pad:   # the padding between groups is untouched
+        gaps = torch.stack([buf[(gi + 1) * (K * K + pad) - pad:(gi + 1) * (K * K + pad)] for gi in range(groups)])
+        assert bool((gaps == 0).all())
+
+
+def test_prepare_groups_error_in_one_group(g):
+    """A non-positive-definite Hessian in one of three groups makes the call report it."""
+    H = torch.zeros(3, 2, 2, device=DEV)
+    H[0] = torch.tensor([[2.0, 1.0], [1.0, 2.0]])
+    H[1] = torch.tensor([[1.0, 2.0], [2.0, 1.0]])
+    H[2] = torch.tensor([[4.0, 0.0], [0.0, 4.0]])
+    with pytest.raises(g.GptqError) as e:
+        g.gptq_prepare_groups(H, 0.0)
+    assert e.value.status == g.GPTQ_ERR_NOT_PD
+
+
 def test_prepare_errors(g):
     H = torch.tensor([[1.0, 2.0], [2.0, 1.0]], device=DEV)
     with pytest.raises(g.GptqError) as e:
