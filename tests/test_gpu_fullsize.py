@@ -170,6 +170,26 @@ def test_c3_group_gram_prepare_loop(g):
                 "c3 group 2")
 
 
+def test_c3_prepare_groups_full_size(g):
+    """The four group Hessians of the down_proj workload (K = 14336) factorised in one grouped call, as the
+    bench's groups driver does: bit-identical to one gptq_prepare per group (the batched launches include the
+    128 x 128-tile triangular products of the two top levels)."""
+    cfg = workloads.CONFIGS["c3_down_proj_8b_g4"]
+    _, X, _, rho = _make(cfg)
+    Hs = torch.zeros(cfg.groups, cfg.K, cfg.K, device=DEV)
+    for gi in range(cfg.groups):
+        g.gptq_accumulate_hessian(Hs[gi], X, row_scale=rho[gi].contiguous())
+    del X
+    torch.cuda.empty_cache()
+    single = Hs.clone()
+    dead, damps, n_dead = g.gptq_prepare_groups(Hs, cfg.percdamp)
+    for gi in range(cfg.groups):
+        d1, damp1, nd1 = g.gptq_prepare(single[gi], cfg.percdamp)
+        assert torch.equal(Hs[gi], single[gi]), f"group {gi}: U differs from the single-Hessian call"
+        assert torch.equal(dead[gi], d1) and damps[gi] == damp1 and n_dead[gi] == nd1
+    print(f"c3 grouped prepare: {cfg.groups} x K={cfg.K} identical to single calls; damps {damps}", flush=True)
+
+
 def test_c4_gptaq_gram_prepare_asym_loop(g):
     cfg = workloads.CONFIGS["c4_up_proj_8b_gptaq"]
     W, X, Xf, _ = _make(cfg)
