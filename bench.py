@@ -3,8 +3,8 @@
 One step = the whole hot path for one K x N linear layer with its calibration activations already resident
 in HBM:  H = 0;  H += 2 X^T X over all M tokens (gptq_accumulate_hessian);  dead/damp + U (gptq_prepare);
 [GPTAQ: P1 (gptq_asym_correction)];  shared-order column loop with lazy trailing GEMMs (gptq_quantize_layer).
-Output groups (G2PTQ-style workloads): one Gram and one column loop per group, the groups' Hessians factorised
-together (gptq_prepare_groups).
+Output groups (G2PTQ-style workloads): one Gram per group, then the groups' factorisations and column loops
+together (gptq_prepare_groups, gptq_quantize_layer_groups).
 
 Prints one JSON line: layer time (ms, lower is better) plus the Gram's MFMA roofline fraction and the float64
 oracle timed on a bounded sample of the same workload on the host cores.
@@ -106,7 +106,7 @@ class Layer:
         ws = max(G.gptq_workspace_bytes(G.GPTQ_CALL_ACCUMULATE_HESSIAN, K, 0, M, flags),
                  G.gptq_workspace_bytes(G.GPTQ_CALL_PREPARE, K, cfg.groups),
                  G.gptq_workspace_bytes(G.GPTQ_CALL_ASYM_CORRECTION, K),
-                 G.gptq_workspace_bytes(G.GPTQ_CALL_QUANTIZE_LAYER, K, gs, 0, 2 if self.Xf is not None else 0))
+                 G.gptq_workspace_bytes(G.GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, 2 if self.Xf is not None else 0))
         self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
         self.ws_cae = torch.empty(G.gptq_workspace_bytes(G.GPTQ_CALL_QUANTIZE_LAYER, K, gs, 0,
                                                          G.GPTQ_FLAG_CAE | (2 if self.Xf is not None else 0)),
@@ -144,11 +144,12 @@ class Layer:
         if self.A is not None:
             P1 = G.gptq_asym_correction(self.H, self.A, self.P1, workspace=self.ws)
         mark()
-        for gi in range(cfg.groups):
-            sl = slice(gi * self.gs, (gi + 1) * self.gs)
-            G.gptq_quantize_layer(self.W[:, sl], self.Hs[gi], cfg.bits, dead=self.deads[gi], P1=P1,
-                                  blocksize=cfg.blocksize, scales=None, codes=self.codes[:, sl], losses=None,
-                                  workspace=self.ws)
+        if cfg.groups == 1:
+            G.gptq_quantize_layer(self.W, self.H, cfg.bits, dead=self.dead, P1=P1, blocksize=cfg.blocksize,
+                                  scales=None, codes=self.codes, losses=None, workspace=self.ws)
+        else:   # every group's column loop in the same launches
+            G.gptq_quantize_layer_groups(self.W, self.Hs, cfg.bits, dead=self.deads, blocksize=cfg.blocksize,
+                                         scales=None, codes=self.codes, losses=None, workspace=self.ws)
         mark()
         return evs
 

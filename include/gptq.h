@@ -8,6 +8,7 @@
  *      gptq_prepare_groups      the same on the per-group Hessians of [G], all groups in each launch
  *   3. gptq_asym_correction     P1 = [(A U^T) masked strictly upper] U               ([R] item 3)
  *   4. gptq_quantize_layer      shared-order column loop with lazy block updates     ([T] sections 3-5)
+ *      gptq_quantize_layer_groups  the same for output-channel groups with a Hessian each ([G])
  *
  * Sources, cited by page title and section:
  *   [T] GPTQ tutorial page "GPTQ：量化一个权重之后怎样补偿输出误差" (charlestar.github.io, 2026-10-15); its
@@ -250,6 +251,35 @@ gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K
                                   float* scales, void* W_hat, float* losses, float* pre_round,
                                   const int32_t* perm, int64_t groupsize, int32_t* g_idx,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * gptq_quantize_layer_groups - gptq_quantize_layer on a layer whose N output channels form `groups` equal
+ * contiguous groups, each quantised against its own Hessian ([G]: output-channel groups with a Hessian each).
+ * Channel n belongs to group g = n / (N / groups) and uses U + g * u_stride, P1 + g * u_stride (if given),
+ * dead + g * K and perm + g * K (if given), and its act-order rows go to g_idx + g * K.  Every launch covers
+ * all groups (the column loop of every channel at once, the trailing products batched over the groups), so a
+ * layer with small groups fills the GPU like one large layer.  Codes, scales, W_hat, losses and pre_round are
+ * per channel as for gptq_quantize_layer, whose results this equals group by group.
+ *
+ *   groups     >= 1, dividing N; with groups > 1, N / groups must be a multiple of 16.
+ *   U, P1      device, groups K x K fp32 matrices, u_stride floats apart (u_stride >= K * K when groups > 1;
+ *              a multiple of 4 keeps the trailing products' vector loads).
+ *   dead       NULL or device uint8[groups * K].   perm: NULL or device int32[groups * K], one act-order
+ *              permutation per group (from gptq_act_order on that group's Hessian).
+ *   g_idx      NULL or device int32[groups * K] (written).
+ *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, flags | (P1?2:0)),
+ *              the same as one call over all N channels.
+ *   All other arguments as for gptq_quantize_layer.
+ * Errors: as gptq_quantize_layer.  Synchronises `stream` before returning.
+ */
+gptq_status_t gptq_quantize_layer_groups(const void* W, gptq_dtype_t w_dtype, int64_t K, int64_t N,
+                                         int64_t w_rs, int64_t w_cs, int64_t groups,
+                                         const float* U, int64_t u_stride, const uint8_t* dead, const float* P1,
+                                         int bits, int blocksize, unsigned flags,
+                                         uint8_t* codes, int64_t c_rs, int64_t c_cs,
+                                         float* scales, void* W_hat, float* losses, float* pre_round,
+                                         const int32_t* perm, int64_t groupsize, int32_t* g_idx,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * gptq_hadamard_rotate - randomised Hadamard rotation of rows, the step before quantisation in [G] (setup

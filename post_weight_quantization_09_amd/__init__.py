@@ -2,7 +2,8 @@
 
 The entry points carry the C names of include/gptq.h:
     gptq_accumulate_hessian, gptq_prepare, gptq_asym_correction, gptq_quantize_layer (the layer path),
-    gptq_prepare_groups (the per-group Hessians of output-channel groups, all groups per launch),
+    gptq_prepare_groups, gptq_quantize_layer_groups (output-channel groups with a Hessian each, all groups per
+    launch),
     gptq_act_order (act-order),
     gptq_pack_codes, gptq_unpack_codes (storing the codes), gptq_hadamard_rotate (the rotation before it)
 """
@@ -11,5 +12,5 @@ from ._binding import (  # noqa: F401
     GPTQ_CALL_QUANTIZE_LAYER,
     GPTQ_ERR_ARG, GPTQ_FLAG_CAE, GPTQ_FLAG_MSE, GPTQ_FLAG_SCALES_GIVEN, GPTQ_FLAG_STATIC_GROUPS, GPTQ_ERR_HIP, GPTQ_ERR_NONFINITE, GPTQ_ERR_NOT_PD, GPTQ_ERR_WORKSPACE, GPTQ_OK, LIB_PATH,
     GptqError, gptq_accumulate_hessian, gptq_act_order, gptq_asym_correction, gptq_hadamard_rotate, gptq_pack_codes, gptq_packed_words, gptq_prepare, gptq_prepare_groups,
-    gptq_quantize_layer, gptq_unpack_codes, gptq_workspace_bytes, load, status_string, version,
+    gptq_quantize_layer, gptq_quantize_layer_groups, gptq_unpack_codes, gptq_workspace_bytes, load, status_string, version,
 )

@@ -38,6 +38,9 @@ _SIGNATURES = {
     "gptq_quantize_layer": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
                                            ctypes.c_int, ctypes.c_int, _u32, _ptr, _i64, _i64, _ptr, _ptr, _ptr,
                                            _ptr, _ptr, _i64, _ptr, _ptr, _size, _ptr]),
+    "gptq_quantize_layer_groups": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _ptr, _i64, _ptr,
+                                                  _ptr, ctypes.c_int, ctypes.c_int, _u32, _ptr, _i64, _i64, _ptr,
+                                                  _ptr, _ptr, _ptr, _ptr, _i64, _ptr, _ptr, _size, _ptr]),
     "gptq_act_order": (ctypes.c_int, [_ptr, _ptr, _i64, _ptr, _ptr, _size, _ptr]),
     "gptq_packed_words": (_i64, [_i64, ctypes.c_int]),
     "gptq_hadamard_rotate": (ctypes.c_int, [_ptr, _i64, _ptr, _i64, ctypes.c_int, _i64, _i64, _ptr, _ptr]),
@@ -228,18 +231,52 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, dead: Optio
 
     Returns dict(codes uint8 K x N, scales fp32[N], W_hat, losses, pre_round) with the tensors written.
     """
-    K, N = W.shape
-    dev = W.device
+    K = W.shape[0]
     _square(U, "U", K)
     if P1 is not None:
         _square(P1, "P1", K)
     _contig(U, "U", torch.float32)
     _contig(P1, "P1", torch.float32)
     _contig(dead, "dead", torch.uint8)
-    _contig(scales, "scales", torch.float32)
-    _contig(losses, "losses", torch.float32)
     _contig(perm, "perm", torch.int32)
     _contig(g_idx, "g_idx", torch.int32)
+    return _quantize(W, 1, U, 0, bits, dead, P1, blocksize, scales, codes, W_hat, losses, pre_round, workspace,
+                     stream, cae, perm, groupsize, static_groups, mse, g_idx)
+
+
+def gptq_quantize_layer_groups(W: torch.Tensor, U: torch.Tensor, bits: int, dead: Optional[torch.Tensor] = None,
+                               P1: Optional[torch.Tensor] = None, blocksize: int = 128,
+                               scales: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
+                               W_hat: Optional[torch.Tensor] = None, losses: Optional[torch.Tensor] = None,
+                               pre_round: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                               stream=None, cae: bool = False, perm: Optional[torch.Tensor] = None,
+                               groupsize: int = 0, static_groups: bool = False, mse: bool = False,
+                               g_idx: Optional[torch.Tensor] = None) -> dict:
+    """gptq_quantize_layer for output-channel groups: U (and P1) are groups x K x K (each K x K contiguous, the same
+    group stride), dead, perm and g_idx groups x K; the N channels of W split into `groups` equal contiguous
+    groups, group g quantised against U[g].  Same outputs as gptq_quantize_layer."""
+    if U.dim() != 3 or U.shape[1] != U.shape[2]:
+        raise ValueError("U must be groups x K x K")
+    Gn, K = U.shape[0], U.shape[1]
+    if W.shape[0] != K:
+        raise ValueError("W must be K x N")
+    for t, nm in ((U, "U"), (P1, "P1")):
+        if t is not None and (t.shape != U.shape or t.dtype != torch.float32 or t.stride(2) != 1 or t.stride(1) != K
+                              or t.stride(0) != U.stride(0)):
+            raise ValueError(f"{nm} must be float32 groups x K x K with contiguous matrices and U's group stride")
+    for t, nm, dt in ((dead, "dead", torch.uint8), (perm, "perm", torch.int32), (g_idx, "g_idx", torch.int32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous() or t.numel() != Gn * K):
+            raise ValueError(f"{nm} must be a contiguous {dt} tensor of groups x K entries")
+    return _quantize(W, Gn, U, U.stride(0), bits, dead, P1, blocksize, scales, codes, W_hat, losses, pre_round,
+                     workspace, stream, cae, perm, groupsize, static_groups, mse, g_idx)
+
+
+def _quantize(W, groups, U, u_stride, bits, dead, P1, blocksize, scales, codes, W_hat, losses, pre_round, workspace,
+              stream, cae, perm, groupsize, static_groups, mse, g_idx) -> dict:
+    K, N = W.shape
+    dev = W.device
+    _contig(scales, "scales", torch.float32)
+    _contig(losses, "losses", torch.float32)
     flags = 0
     ng = (K + groupsize - 1) // groupsize if groupsize > 0 else 0
     if scales is None:
@@ -260,11 +297,17 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, dead: Optio
         raise ValueError("pre_round must be a contiguous K x N fp32 tensor")
     ws_flags = flags | (2 if P1 is not None else 0)
     workspace, wp, wb = _workspace(GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, ws_flags, dev, workspace)
-    st = load().gptq_quantize_layer(
-        _dptr(W), _dtype_code(W), K, N, W.stride(0), W.stride(1), _dptr(U), _dptr(dead), _dptr(P1), int(bits),
-        int(blocksize), flags, _dptr(codes), codes.stride(0), codes.stride(1), _dptr(scales), _dptr(W_hat),
-        _dptr(losses), _dptr(pre_round), _dptr(perm), int(groupsize), _dptr(g_idx), wp, wb, _stream(dev, stream))
-    _check(st, "gptq_quantize_layer")
+    common = (int(bits), int(blocksize), flags, _dptr(codes), codes.stride(0), codes.stride(1), _dptr(scales),
+              _dptr(W_hat), _dptr(losses), _dptr(pre_round), _dptr(perm), int(groupsize), _dptr(g_idx), wp, wb,
+              _stream(dev, stream))
+    if groups == 1:
+        st = load().gptq_quantize_layer(_dptr(W), _dtype_code(W), K, N, W.stride(0), W.stride(1), _dptr(U),
+                                        _dptr(dead), _dptr(P1), *common)
+        _check(st, "gptq_quantize_layer")
+    else:
+        st = load().gptq_quantize_layer_groups(_dptr(W), _dtype_code(W), K, N, W.stride(0), W.stride(1), int(groups),
+                                               _dptr(U), int(u_stride), _dptr(dead), _dptr(P1), *common)
+        _check(st, "gptq_quantize_layer_groups")
     return {"codes": codes, "scales": scales, "W_hat": W_hat, "losses": losses, "pre_round": pre_round,
             "g_idx": g_idx}
 

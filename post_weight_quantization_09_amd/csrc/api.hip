@@ -41,6 +41,39 @@ size_t asym_ws(int64_t K) {
     return c.bytes();
 }
 
+gptq_status_t quantize_common(const void* W, gptq_dtype_t w_dtype, int64_t K, int64_t N, int64_t w_rs, int64_t w_cs,
+                              int64_t groups, const float* U, int64_t u_stride, const uint8_t* dead, const float* P1,
+                              int bits, int blocksize, unsigned flags, uint8_t* codes, int64_t c_rs, int64_t c_cs,
+                              float* scales, void* W_hat, float* losses, float* pre_round, const int32_t* perm,
+                              int64_t groupsize, int32_t* g_idx, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    if (!W || !U || !codes || !scales || K < 1 || N < 1) return GPTQ_ERR_ARG;
+    if (w_dtype != GPTQ_DTYPE_F32 && w_dtype != GPTQ_DTYPE_BF16) return GPTQ_ERR_ARG;
+    if (bits < 2 || bits > 8 || blocksize != 128) return GPTQ_ERR_ARG;
+    const unsigned known = GPTQ_FLAG_SCALES_GIVEN | GPTQ_FLAG_CAE | GPTQ_FLAG_STATIC_GROUPS | GPTQ_FLAG_MSE;
+    if ((flags & ~known) != 0) return GPTQ_ERR_ARG;
+    if (groupsize != 0 && groupsize != 32 && groupsize != 64 && groupsize != 128) return GPTQ_ERR_ARG;
+    const bool stat = (flags & GPTQ_FLAG_STATIC_GROUPS) != 0, mse = (flags & GPTQ_FLAG_MSE) != 0;
+    if (stat && groupsize == 0) return GPTQ_ERR_ARG;
+    if (mse && groupsize != 0 && !stat) return GPTQ_ERR_ARG;
+    if ((flags & GPTQ_FLAG_SCALES_GIVEN) && (groupsize != 0 || mse)) return GPTQ_ERR_ARG;
+    if (w_rs < 1 || w_cs < 1 || c_rs < 1 || c_cs < 1) return GPTQ_ERR_ARG;
+    if (K > (int64_t)1 << 24 || N > (int64_t)1 << 28) return GPTQ_ERR_ARG;
+    if (groups < 1 || groups > 65535 || N % groups != 0) return GPTQ_ERR_ARG;
+    if (groups > 1 && ((N / groups) % 16 != 0 || u_stride < K * K)) return GPTQ_ERR_ARG;
+    if (!ws_ok(workspace, workspace_bytes, quantize_workspace_bytes(K, N, P1 != nullptr, (flags & GPTQ_FLAG_CAE) != 0)))
+        return GPTQ_ERR_WORKSPACE;
+    QuantizeArgs a;
+    a.W = W; a.w_dtype = w_dtype; a.K = K; a.N = N; a.w_rs = w_rs; a.w_cs = w_cs;
+    a.U = U; a.dead = dead; a.P1 = P1; a.bits = bits; a.scales_given = (flags & GPTQ_FLAG_SCALES_GIVEN) != 0;
+    a.cae = (flags & GPTQ_FLAG_CAE) != 0;
+    a.perm = perm; a.groupsize = groupsize; a.static_groups = stat; a.mse = mse; a.g_idx = g_idx;
+    a.groups = groups; a.u_stride = groups > 1 ? u_stride : 0;
+    a.codes = codes; a.c_rs = c_rs; a.c_cs = c_cs; a.scales = scales; a.W_hat = W_hat; a.losses = losses;
+    a.pre_round = pre_round;
+    return quantize_layer(a, workspace, static_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -167,28 +200,21 @@ gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K
                                   float* scales, void* W_hat, float* losses, float* pre_round, const int32_t* perm,
                                   int64_t groupsize, int32_t* g_idx, void* workspace, size_t workspace_bytes,
                                   void* stream) {
-    if (!W || !U || !codes || !scales || K < 1 || N < 1) return GPTQ_ERR_ARG;
-    if (w_dtype != GPTQ_DTYPE_F32 && w_dtype != GPTQ_DTYPE_BF16) return GPTQ_ERR_ARG;
-    if (bits < 2 || bits > 8 || blocksize != 128) return GPTQ_ERR_ARG;
-    const unsigned known = GPTQ_FLAG_SCALES_GIVEN | GPTQ_FLAG_CAE | GPTQ_FLAG_STATIC_GROUPS | GPTQ_FLAG_MSE;
-    if ((flags & ~known) != 0) return GPTQ_ERR_ARG;
-    if (groupsize != 0 && groupsize != 32 && groupsize != 64 && groupsize != 128) return GPTQ_ERR_ARG;
-    const bool stat = (flags & GPTQ_FLAG_STATIC_GROUPS) != 0, mse = (flags & GPTQ_FLAG_MSE) != 0;
-    if (stat && groupsize == 0) return GPTQ_ERR_ARG;
-    if (mse && groupsize != 0 && !stat) return GPTQ_ERR_ARG;
-    if ((flags & GPTQ_FLAG_SCALES_GIVEN) && (groupsize != 0 || mse)) return GPTQ_ERR_ARG;
-    if (w_rs < 1 || w_cs < 1 || c_rs < 1 || c_cs < 1) return GPTQ_ERR_ARG;
-    if (K > (int64_t)1 << 24 || N > (int64_t)1 << 28) return GPTQ_ERR_ARG;
-    if (!ws_ok(workspace, workspace_bytes, quantize_workspace_bytes(K, N, P1 != nullptr, (flags & GPTQ_FLAG_CAE) != 0)))
-        return GPTQ_ERR_WORKSPACE;
-    QuantizeArgs a;
-    a.W = W; a.w_dtype = w_dtype; a.K = K; a.N = N; a.w_rs = w_rs; a.w_cs = w_cs;
-    a.U = U; a.dead = dead; a.P1 = P1; a.bits = bits; a.scales_given = (flags & GPTQ_FLAG_SCALES_GIVEN) != 0;
-    a.cae = (flags & GPTQ_FLAG_CAE) != 0;
-    a.perm = perm; a.groupsize = groupsize; a.static_groups = stat; a.mse = mse; a.g_idx = g_idx;
-    a.codes = codes; a.c_rs = c_rs; a.c_cs = c_cs; a.scales = scales; a.W_hat = W_hat; a.losses = losses;
-    a.pre_round = pre_round;
-    return quantize_layer(a, workspace, static_cast<hipStream_t>(stream));
+    return quantize_common(W, w_dtype, K, N, w_rs, w_cs, 1, U, 0, dead, P1, bits, blocksize, flags, codes, c_rs, c_cs,
+                           scales, W_hat, losses, pre_round, perm, groupsize, g_idx, workspace, workspace_bytes,
+                           stream);
+}
+
+gptq_status_t gptq_quantize_layer_groups(const void* W, gptq_dtype_t w_dtype, int64_t K, int64_t N, int64_t w_rs,
+                                         int64_t w_cs, int64_t groups, const float* U, int64_t u_stride,
+                                         const uint8_t* dead, const float* P1, int bits, int blocksize,
+                                         unsigned flags, uint8_t* codes, int64_t c_rs, int64_t c_cs, float* scales,
+                                         void* W_hat, float* losses, float* pre_round, const int32_t* perm,
+                                         int64_t groupsize, int32_t* g_idx, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+    return quantize_common(W, w_dtype, K, N, w_rs, w_cs, groups, U, u_stride, dead, P1, bits, blocksize, flags, codes,
+                           c_rs, c_cs, scales, W_hat, losses, pre_round, perm, groupsize, g_idx, workspace,
+                           workspace_bytes, stream);
 }
 
 gptq_status_t gptq_act_order(float* H, float* A, int64_t K, int32_t* perm, void* workspace, size_t workspace_bytes,

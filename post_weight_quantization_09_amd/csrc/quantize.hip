@@ -43,10 +43,13 @@ __global__ void quant_init_kernel(DevStatus* st, uint32_t* amax_bits, float* los
 // W (K x N view with strides) -> Wt (N x ldt fp32, dead rows zeroed, padding zero) and per-channel max |w|
 // taken before dead rows are zeroed.  64 x 64 tiles transposed through LDS.
 // With act-order, processing position k reads original row perm[k]; `dead` is indexed by processing position.
+// Output-channel groups of gs channels: channel n uses the dead flags and permutation of group n / gs
+// (dead + g K, perm + g K).
 template <bool BF16>
 __global__ __launch_bounds__(256) void convert_kernel(const void* Wv, int64_t K, int64_t N, int64_t w_rs,
                                                      int64_t w_cs, const uint8_t* dead, float* Wt, int64_t ldt,
-                                                     uint32_t* amax_bits, DevStatus* st, const int32_t* perm) {
+                                                     uint32_t* amax_bits, DevStatus* st, const int32_t* perm,
+                                                     int64_t gs) {
     __shared__ float tile[64][65];
     const int tid = threadIdx.x;
     const int64_t k0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
@@ -59,7 +62,8 @@ __global__ __launch_bounds__(256) void convert_kernel(const void* Wv, int64_t K,
         const int64_t k = k0 + kk, n = n0 + nn;
         float v = 0.f;
         if (k < K && n < N) {
-            const int64_t off = (perm ? (int64_t)perm[k] : k) * w_rs + n * w_cs;
+            const int64_t gK = (int64_t)((uint32_t)n / (uint32_t)gs) * K;
+            const int64_t off = (perm ? (int64_t)perm[gK + k] : k) * w_rs + n * w_cs;
             if (BF16) v = __uint_as_float((uint32_t)(static_cast<const uint16_t*>(Wv)[off]) << 16);
             else v = static_cast<const float*>(Wv)[off];
             if (!isfinite(v)) bad = 1;
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(256) void convert_kernel(const void* Wv, int64_t K,
         const int64_t k = k0 + kk, n = n0 + nn;
         if (n < N && k < ldt) {
             float v = (k < K) ? tile[kk][nn] : 0.f;
-            if (k < K && dead && dead[k]) v = 0.f;
+            if (k < K && dead && dead[(int64_t)((uint32_t)n / (uint32_t)gs) * K + k]) v = 0.f;
             Wt[n * ldt + k] = v;
         }
     }
@@ -211,6 +215,7 @@ struct BlockArgs {
     float* pre_round;               // optional, K x N
     const DevStatus* st;
     int64_t G;                      // group size (group modes)
+    int64_t gs, u_stride;           // output-channel groups: gs channels each, U and P1 of group g at + g u_stride
     const int32_t* perm;            // act-order (static groups look up the original row's group)
     float* gscales;                 // ng x N: written at group starts (re-estimated) or read (static)
 };
@@ -342,6 +347,12 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
     __shared__ float Trs[SM == kScaleStatic ? kB * kChPerWG : 1];
 
     if (p.st->flags) return;   // an input was rejected earlier in this call
+    {   // output-channel groups: the workgroup's channels all belong to one group (gs is a multiple of 16)
+        const int64_t g = (int64_t)blockIdx.x * kChPerWG / p.gs;
+        p.U += g * p.u_stride;
+        if (p.P1) p.P1 += g * p.u_stride;
+        if (p.perm) p.perm += g * p.K;
+    }
     const int tid = threadIdx.x;
     const int64_t b0 = p.b0;
     const int bs = p.bs;
@@ -449,7 +460,8 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void finalize_kernel(const uint8_t* codes_t, int64_t ldt, int64_t K, int64_t N,
                                                       uint8_t* codes, int64_t c_rs, int64_t c_cs, void* W_hat,
                                                       int64_t w_rs, int64_t w_cs, const float* scales, int bits,
-                                                      const int32_t* perm, int64_t G, bool static_groups) {
+                                                      const int32_t* perm, int64_t G, bool static_groups,
+                                                      int64_t gs) {
     __shared__ uint8_t tile[64][65];
     const int tid = threadIdx.x;
     const int64_t k0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
@@ -469,13 +481,17 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint8_t* codes_t, i
         {
             const int kk = n_fast_c ? a : b, nn = n_fast_c ? b : a;
             const int64_t k = k0 + kk, n = n0 + nn;
-            if (k < K && n < N) codes[(perm ? (int64_t)perm[k] : k) * c_rs + n * c_cs] = tile[kk][nn];
+            if (k < K && n < N) {
+                const int64_t gK = (int64_t)((uint32_t)n / (uint32_t)gs) * K;
+                codes[(perm ? (int64_t)perm[gK + k] : k) * c_rs + n * c_cs] = tile[kk][nn];
+            }
         }
         if (W_hat) {
             const int kk = n_fast_w ? a : b, nn = n_fast_w ? b : a;
             const int64_t k = k0 + kk, n = n0 + nn;
             if (k < K && n < N) {
-                const int64_t ko = perm ? (int64_t)perm[k] : k;
+                const int64_t gK = (int64_t)((uint32_t)n / (uint32_t)gs) * K;
+                const int64_t ko = perm ? (int64_t)perm[gK + k] : k;
                 const float s = G > 0 ? scales[((static_groups ? ko : k) / G) * N + n] : scales[n];
                 const float v = ((float)tile[kk][nn] - z) * s;
                 if (BF16) static_cast<__bf16*>(W_hat)[ko * w_rs + n * w_cs] = (__bf16)v;
@@ -495,6 +511,8 @@ __global__ void copy_losses_kernel(const float* src, float* dst, int64_t N) {
 __global__ void g_idx_kernel(int32_t* g_idx, int64_t K, const int32_t* perm, int64_t G, bool static_groups) {
     const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= K) return;
+    g_idx += (int64_t)blockIdx.y * K;   // one row of K per output-channel group
+    if (perm) perm += (int64_t)blockIdx.y * K;
     const int64_t ko = perm ? (int64_t)perm[j] : j;
     g_idx[ko] = G > 0 ? (int32_t)((static_groups ? ko : j) / G) : 0;
 }
@@ -541,6 +559,7 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
     const int64_t ldt = ceil_div(std::max<int64_t>(K, 1), kB) * kB;
     const bool cae = a.cae;
     QuantLayout L = carve(workspace, K, N, asym, cae);
+    const int64_t groups = std::max<int64_t>(a.groups, 1), gs = N / groups;   // output-channel groups
 
     hipLaunchKernelGGL(quant_init_kernel, grid1d(std::max<int64_t>(N, 1), 256), dim3(256), 0, stream, L.st, L.amax,
                        L.loss_acc, N);
@@ -549,10 +568,10 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
         dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(ldt, 64));
         if (a.w_dtype == GPTQ_DTYPE_BF16)
             hipLaunchKernelGGL((convert_kernel<true>), grid, dim3(256), 0, stream, a.W, K, N, a.w_rs, a.w_cs, a.dead,
-                               L.Wt, ldt, L.amax, L.st, a.perm);
+                               L.Wt, ldt, L.amax, L.st, a.perm, gs);
         else
             hipLaunchKernelGGL((convert_kernel<false>), grid, dim3(256), 0, stream, a.W, K, N, a.w_rs, a.w_cs, a.dead,
-                               L.Wt, ldt, L.amax, L.st, a.perm);
+                               L.Wt, ldt, L.amax, L.st, a.perm, gs);
         GPTQ_LAUNCH_CHECK();
     }
     const int64_t G = a.groupsize;
@@ -585,21 +604,24 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
     // Wt[:, r0:r1] -= E U[k0:k0+depth, r0:r1] (+ Wpre P1[k0:k0+depth, r0:r1] for the asymmetric term; with CAE,
     // E holds (w0 - q) / U_jj and the P1 term takes the original weights W0[:, k0:k0+depth]).  E and Wpre point
     // at the errors / pre-rounding weights of coordinate k0 (row stride kSB).
+    // With output-channel groups the product runs batched over the groups: group g's gs channels (rows of E, Wt)
+    // with its own U and P1.
     auto trailing = [&](int64_t r0, int64_t r1, int64_t k0, int64_t depth, const float* Ek, const float* Wpk) {
         GemmArgs g;
-        g.M = N; g.N = r1 - r0; g.K1 = depth;
-        g.A1 = Ek; g.lda1 = kSB;
-        g.B1 = a.U + k0 * K + r0; g.ldb1 = K;
+        g.M = gs; g.N = r1 - r0; g.K1 = depth;
+        g.A1 = Ek; g.lda1 = kSB; g.strideA1 = gs * kSB;
+        g.B1 = a.U + k0 * K + r0; g.ldb1 = K; g.strideB1 = a.u_stride;
         if (asym) {
             g.K2 = depth;
             g.A2 = cae ? L.W0t + k0 : Wpk;
             g.lda2 = cae ? ldt : kSB;
-            g.B2 = a.P1 + k0 * K + r0; g.ldb2 = K;
+            g.strideA2 = gs * (cae ? ldt : kSB);
+            g.B2 = a.P1 + k0 * K + r0; g.ldb2 = K; g.strideB2 = a.u_stride;
             g.a2_scale = -1.f;
         }
-        g.C = L.Wt + r0; g.ldc = ldt;
+        g.C = L.Wt + r0; g.ldc = ldt; g.strideC = gs * ldt;
         g.alpha = -1.f; g.beta = 1.f;
-        return gemm_f32(g, 1, stream) == hipSuccess;
+        return gemm_f32(g, groups, stream) == hipSuccess;
     };
 
     for (int64_t sb0 = 0; sb0 < K; sb0 += kSB) {
@@ -614,6 +636,7 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
             p.E = Eb; p.Wpre = Wpb; p.lde = kSB;
             p.W0t = L.W0t; p.loss_acc = L.loss_acc; p.pre_round = a.pre_round; p.st = L.st;
             p.G = G; p.perm = a.perm; p.gscales = a.scales;
+            p.gs = gs; p.u_stride = a.u_stride;
             dim3 grid((unsigned)ceil_div(N, kChPerWG));
 #define GPTQ_BLOCK(A_, C_)                                                                                        \
     if (sm == kScaleDynamic) hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScaleDynamic>), grid, dim3(256), 0, stream, p); \
@@ -636,14 +659,16 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
         dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(K, 64));
         if (a.w_dtype == GPTQ_DTYPE_BF16)
             hipLaunchKernelGGL((finalize_kernel<true>), grid, dim3(256), 0, stream, L.codes_t, ldt, K, N, a.codes, a.c_rs,
-                               a.c_cs, a.W_hat, a.w_rs, a.w_cs, a.scales, a.bits, a.perm, G, a.static_groups);
+                               a.c_cs, a.W_hat, a.w_rs, a.w_cs, a.scales, a.bits, a.perm, G, a.static_groups, gs);
         else
             hipLaunchKernelGGL((finalize_kernel<false>), grid, dim3(256), 0, stream, L.codes_t, ldt, K, N, a.codes, a.c_rs,
-                               a.c_cs, a.W_hat, a.w_rs, a.w_cs, a.scales, a.bits, a.perm, G, a.static_groups);
+                               a.c_cs, a.W_hat, a.w_rs, a.w_cs, a.scales, a.bits, a.perm, G, a.static_groups, gs);
         GPTQ_LAUNCH_CHECK();
     }
     if (a.g_idx) {
-        hipLaunchKernelGGL(g_idx_kernel, grid1d(K, 256), dim3(256), 0, stream, a.g_idx, K, a.perm, G, a.static_groups);
+        dim3 gi = grid1d(K, 256);
+        gi.y = (unsigned)groups;
+        hipLaunchKernelGGL(g_idx_kernel, gi, dim3(256), 0, stream, a.g_idx, K, a.perm, G, a.static_groups);
         GPTQ_LAUNCH_CHECK();
     }
     if (a.losses) {

@@ -17,6 +17,8 @@ struct QuantizeArgs {
     bool static_groups = false;     // group scales from W before the loop (groups of original rows)
     bool mse = false;               // weight-MSE clipping of the scales taken from W before the loop
     int32_t* g_idx = nullptr;       // optional output: group of each original row
+    int64_t groups = 1;             // output-channel groups: channel n uses U, P1, dead, perm (and g_idx) of group
+    int64_t u_stride = 0;           //   g = n / (N / groups); U, P1 of group g at + g u_stride, the rest at + g K
     uint8_t* codes = nullptr; int64_t c_rs = 0, c_cs = 0;
     float* scales = nullptr; void* W_hat = nullptr; float* losses = nullptr; float* pre_round = nullptr;
 };

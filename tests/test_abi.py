@@ -136,6 +136,27 @@ def test_quantize_validation(lib):
     assert call(flags=32) == b.GPTQ_ERR_ARG
 
 
+def test_quantize_groups_validation(lib):
+    ws = ctypes.c_void_p(0x100000)
+    big = 1 << 30
+
+    def call(**kw):
+        a = dict(K=64, N=64, groups=2, u_stride=64 * 64)
+        a.update(kw)
+        return lib.gptq_quantize_layer_groups(FAKE, 1, a["K"], a["N"], a["N"], 1, a["groups"], FAKE, a["u_stride"],
+                                              None, None, 4, 128, 0, FAKE, a["N"], 1, FAKE, None, None, None, None, 0,
+                                              None, ws, big, None)
+
+    assert call(groups=0) == b.GPTQ_ERR_ARG
+    assert call(groups=65536) == b.GPTQ_ERR_ARG
+    assert call(groups=3) == b.GPTQ_ERR_ARG                 # 64 channels do not split into 3 equal groups
+    assert call(N=96, groups=4) == b.GPTQ_ERR_ARG           # 24 channels per group: not a multiple of 16
+    assert call(u_stride=64 * 64 - 1) == b.GPTQ_ERR_ARG
+    assert call(K=0) == b.GPTQ_ERR_ARG
+    assert lib.gptq_quantize_layer_groups(FAKE, 1, 64, 64, 64, 1, 2, FAKE, 4096, None, None, 4, 128, 0, FAKE, 64, 1,
+                                          FAKE, None, None, None, None, 0, None, ws, 100, None) == b.GPTQ_ERR_WORKSPACE
+
+
 def test_asym_validation(lib):
     ws = ctypes.c_void_p(0x100000)
     assert lib.gptq_asym_correction(None, FAKE, FAKE, 8, ws, 1 << 20, None) == b.GPTQ_ERR_ARG

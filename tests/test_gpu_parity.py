@@ -468,6 +468,56 @@ def test_hadamard_rotation_keeps_products(g):
     assert float((Y.double().cpu() - ref).abs().max() / ref.abs().max()) < 1e-5
 
 
+@pytest.mark.parametrize("K,gs,groups,wdt,opts", [
+    (300, 32, 3, torch.float32, {}),
+    (640, 16, 4, torch.bfloat16, {"act": True, "groupsize": 64}),
+    (256, 48, 2, torch.bfloat16, {"act": True, "groupsize": 32, "static_groups": True, "W_hat": True}),
+    (200, 32, 2, torch.float32, {"mse": True}),
+    (384, 32, 2, torch.float32, {"asym": True}),
+    (384, 32, 2, torch.float32, {"asym": True, "cae": True}),
+])
+def test_quantize_layer_groups(g, K, gs, groups, wdt, opts):
+    """Output-channel groups quantised in one call equal one gptq_quantize_layer call per group on its slice of
+    W (codes, scales, losses, W_hat and g_idx bit for bit): every launch covers all groups, the column loop of each
+    channel uses its group's U (and P1, dead flags, act-order), the trailing products are batched over the groups."""
+    N = gs * groups
+    rng = np.random.default_rng(K + gs)
+    Us, deads, perms, P1s = [], [], [], []
+    for gi in range(groups):
+        H = torch.tensor(_workload_H(K, seed=100 * gi + K, dead_cols=[gi + 1]), dtype=torch.float32, device=DEV)
+        perm = g.gptq_act_order(H) if opts.get("act") else None
+        d, _, _ = g.gptq_prepare(H, 0.01)
+        Us.append(H); deads.append(d); perms.append(perm)
+        if opts.get("asym"):
+            A = torch.tensor(rng.normal(size=(K, K)) * 0.05, dtype=torch.float32, device=DEV)
+            P1s.append(g.gptq_asym_correction(H, A))
+    U = torch.stack(Us)
+    dead = torch.stack(deads)
+    perm = torch.stack(perms) if opts.get("act") else None
+    P1 = torch.stack(P1s) if opts.get("asym") else None
+    W = torch.tensor(rng.normal(size=(K, N)) * 0.02, dtype=torch.float32).to(wdt).to(DEV)
+    kw = dict(groupsize=opts.get("groupsize", 0), static_groups=opts.get("static_groups", False),
+              mse=opts.get("mse", False), cae=opts.get("cae", False))
+    g_idx = torch.empty(groups, K, dtype=torch.int32, device=DEV) if opts.get("act") else None
+    W_hat = torch.empty_like(W) if opts.get("W_hat") else None
+    out = g.gptq_quantize_layer_groups(W, U, 3, dead=dead, P1=P1, perm=perm, g_idx=g_idx, W_hat=W_hat,
+                                       losses=torch.empty(N, device=DEV), **kw)
+    for gi in range(groups):
+        sl = slice(gi * gs, (gi + 1) * gs)
+        gi_idx = torch.empty(K, dtype=torch.int32, device=DEV) if opts.get("act") else None
+        wh = torch.empty_like(W)[:, sl] if opts.get("W_hat") else None   # W's strides, as the binding requires
+        ref = g.gptq_quantize_layer(W[:, sl], Us[gi], 3, dead=deads[gi], P1=P1s[gi] if P1 is not None else None,
+                                    perm=perms[gi], g_idx=gi_idx, W_hat=wh, losses=torch.empty(gs, device=DEV), **kw)
+        assert torch.equal(out["codes"][:, sl], ref["codes"]), f"group {gi} codes"
+        assert torch.equal(out["scales"][..., sl], ref["scales"]), f"group {gi} scales"
+        assert torch.equal(out["losses"][sl], ref["losses"]), f"group {gi} losses"
+        if gi_idx is not None:
+            assert torch.equal(g_idx[gi], gi_idx)
+        if wh is not None:
+            assert torch.equal(W_hat[:, sl], wh)
+    _print(f"quantize groups K={K} {groups}x{gs} {opts}: identical to per-group calls")
+
+
 # ------------------------------------------------------------------------------------------------ act-order, groups, MSE
 def _next2_case(g, K, N, M, seed, bits, act, groupsize=0, static=False, mse=False, asym=False, cae=False):
     base = "c4_up_proj_8b_gptaq" if asym else "c5_down_proj_70b"
