@@ -17,7 +17,8 @@
 //   6. U12 = -U11 X                                (U R = I gives U11 R12 + U12 R22 = 0)
 // Steps 2, 3, 4 and 6 are fp32 MFMA GEMMs; the recursion ends in 128 x 128 (or smaller) diagonal blocks that
 // one LDS kernel factors and inverts.  Since the split points are multiples of 128 from the top, every
-// GEMM tile is aligned with the diagonal blocks.
+// GEMM tile is aligned with the diagonal blocks.  A batch of Hessians ([G]: one per output-channel group)
+// runs the same recursion with every GEMM batched and every diagonal block one launch over the batch.
 #include <algorithm>
 #include <vector>
 

@@ -15,9 +15,9 @@
 //     (row 4 r + a, column 4 c + b) of its wave's 128 x 128 quadrant.  A and B use the same token <->
 //     (lane half, slot) map.
 //   * Only tiles on or above the diagonal are computed (H is symmetric); the cross term computes all.
-//   * The token range is split across workgroups when there are too few tiles to fill 256 CUs.  Splits are
-//     assigned XCD by XCD (workgroup id mod 8) so that the workgroups sharing an XCD's L2 stream the same
-//     tokens.  Each split writes its fp32 partial tile in register order (coalesced); a second kernel sums
+//   * The token range is split across workgroups: enough ways to fill whole rounds of 256 CUs when there
+//     are few tiles, 8 ways (one range per XCD) when there are many.  Splits are assigned XCD by XCD
+//     (workgroup id mod 8) so that the workgroups sharing an XCD's L2 stream the same tokens in step.  Each split writes its fp32 partial tile in register order (coalesced); a second kernel sums
 //     the partials in a fixed order (deterministic, no float atomics), scales by 2, adds into H and writes
 //     the mirrored lower triangle.
 #include "gram.hpp"
