@@ -57,10 +57,15 @@ def trailing_flops(cfg) -> float:
 
 
 def source_hash(*names) -> str:
+    """Hash of the code of the named sources (line comments and blank lines dropped, so that a comment edit
+    does not disown the traffic measured on the same kernel)."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "post_weight_quantization_09_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "post_weight_quantization_09_amd", "csrc", n)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
