@@ -9,7 +9,7 @@ together (gptq_prepare_groups, gptq_quantize_layer_groups).
 Prints one JSON line: layer time (ms, lower is better) plus the Gram's MFMA roofline fraction and the float64
 oracle timed on a bounded sample of the same workload on the host cores.
 
-    python bench.py [--gpus 1] [--steps 3] [--warmup 1] [--config c2_q_proj_8b] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 5] [--warmup 1] [--config c2_q_proj_8b] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -259,7 +259,7 @@ def extras(layer: "Layer") -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", default="c2_q_proj_8b", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
