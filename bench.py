@@ -264,9 +264,10 @@ def main():
     ap.add_argument("--config", default="c2_q_proj_8b", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the timings of the rows beyond the layer path")
-    ap.add_argument("--only", choices=["gram", "copy"], default=None,
-                    help="profiling aids: run only the Gram launch per step, or a 1 GiB device copy (the "
-                         "reference for scaling HBM byte counters)")
+    ap.add_argument("--only", choices=["gram", "copy", "hadamard"], default=None,
+                    help="profiling aids: run only the Gram launch per step, only the in-place Hadamard rotation of "
+                         "the activations per step, or a 1 GiB device copy (the reference for scaling HBM byte "
+                         "counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer path is single-GPU here",
@@ -291,6 +292,13 @@ def main():
             G.gptq_accumulate_hessian(layer.H, layer.X, workspace=layer.ws)
         torch.cuda.synchronize()
         log(f"gram-only: {args.warmup + args.steps} launches")
+        return
+    if args.only == "hadamard":
+        d = torch.tensor(workloads.hadamard_signs(cfg).astype("int8"), device=dev)
+        for i in range(args.warmup + args.steps):
+            G.gptq_hadamard_rotate(layer.X, d, out=layer.X)
+        torch.cuda.synchronize()
+        log(f"hadamard-only: {args.warmup + args.steps} rotations of {tuple(layer.X.shape)}")
         return
     for i in range(args.warmup):
         layer.step(record=False)
