@@ -335,7 +335,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 MFMA Gram (fp32 accumulate) + fp32 factor/loop",
+        "dtype": "bf16+f32",   # bf16 MFMA products with fp32 accumulation (Gram); fp32 factorisation and loop
         "data": "synthetic",
         "config": {"workload": cfg.name, "K": cfg.K, "N": cfg.N, "M": cfg.M, "x_dtype": cfg.x_dtype,
                    "w_dtype": cfg.w_dtype, "bits": cfg.bits, "blocksize": cfg.blocksize, "percdamp": cfg.percdamp,
