@@ -103,6 +103,21 @@ def test_gram_deterministic(g):
     assert torch.equal(H1, H2)
 
 
+def test_gram_many_splits_partial_round(g):
+    # 1536 features, 196608 tokens: 21 upper tiles x 24 token splits = 504 workgroups, i.e. one whole round of
+    # 256 in the chip-wide (split, tile) order used above 8 splits and a partial round of 248 in identity order.
+    cfg, L = _bf16_layer(1536, 8, 196608, seed=3)
+    X = L["X"].to(DEV)
+    H = torch.zeros(cfg.K, cfg.K, device=DEV)
+    g.gptq_accumulate_hessian(H, X)
+    ref = O.gram([L["X"].float().numpy()], K=cfg.K)
+    err = rel_fro(np64(H), ref)
+    _print(f"gram bf16 K={cfg.K} M={cfg.M} (24 splits, 504 workgroups) rel={err:.3e}")
+    assert err <= H_TOL
+    Hn = np64(H)
+    assert np.array_equal(Hn, Hn.T)
+
+
 # ------------------------------------------------------------------------------------------------ prepare
 def _workload_H(K, M=None, seed=0, dead_cols=()):
     cfg, L = _bf16_layer(K, 8, M or max(4 * K, 2048), seed=seed)
