@@ -224,7 +224,7 @@ gptq_status_t gptq_act_order(float* H, float* A, int64_t K, int32_t* perm, void*
  *              (row-major K x N: w_rs = ldw, w_cs = 1; an N x K nn.Linear weight: w_rs = 1, w_cs = K).
  *   U          device, K x K fp32 from gptq_prepare.        dead: device uint8[K] from gptq_prepare or NULL.
  *   P1         NULL, or device K x K fp32 from gptq_asym_correction (asymmetric calibration).
- *   bits       2..8.   blocksize: 128 (the lazy-batch width; the only value this build accepts).
+ *   bits       2..8.   blocksize: 128 (the lazy-batch width; other values are rejected with GPTQ_ERR_ARG).
  *   perm       NULL, or device int32[K] from gptq_act_order.
  *   groupsize  0 (one scale per channel), 32, 64 or 128.
  *   g_idx      NULL, or device int32[K]: the group of every original coordinate (0 without groups).
