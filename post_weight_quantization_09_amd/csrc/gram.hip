@@ -73,8 +73,9 @@ __device__ inline void tile_coords(int t, int nb, bool full, int& bi, int& bj) {
 }
 
 // Workgroup -> (token split, tile).  Workgroup b runs on XCD b % 8, and each XCD runs its workgroups in rounds
-// of 32 (one per CU), in order.  Up to 8 splits (many tiles): XCD x streams its own splits, consecutive tiles
-// at a time, so the co-resident workgroups of an XCD read the same tokens and share column slabs in its L2.
+// of 32 (one per CU), in order.  8 splits (many tiles): XCD x streams split x, consecutive tiles at a time, so
+// the co-resident workgroups of an XCD read the same tokens and share column slabs in its L2.  Fewer splits
+// (short token ranges): split-major order.
 // More splits (few tiles, short token ranges): the 256 co-resident workgroups of the chip take 256 consecutive
 // (split, tile) items, XCD x the x-th 32 of them, so that all XCDs sweep the same few splits together and the
 // slabs one XCD misses in its L2 have mostly just been fetched by another (hits in the memory-side cache):
