@@ -118,6 +118,19 @@ def test_gram_many_splits_partial_round(g):
     assert np.array_equal(Hn, Hn.T)
 
 
+def test_gram_cross_many_splits(g):
+    # cross term at 1280 features, 327680 tokens: 25 tiles x 40 token splits = 1000 workgroups, three whole rounds
+    # in the chip-wide order and a partial round of 232.
+    cfg, L = _bf16_layer(1280, 8, 327680, seed=5, base="c4_up_proj_8b_gptaq")
+    X, Xf = L["X"].to(DEV), L["X_float"].to(DEV)
+    H = torch.zeros(cfg.K, cfg.K, device=DEV)
+    A = torch.zeros(cfg.K, cfg.K, device=DEV)
+    g.gptq_accumulate_hessian(H, X, X_float=Xf, A=A)
+    ea = rel_fro(np64(A), O.cross_gram(L["X_float"].float().numpy(), L["X"].float().numpy()))
+    _print(f"gram cross K={cfg.K} M={cfg.M} (40 splits, 1000 workgroups): A rel={ea:.3e}")
+    assert ea <= H_TOL
+
+
 # ------------------------------------------------------------------------------------------------ prepare
 def _workload_H(K, M=None, seed=0, dead_cols=()):
     cfg, L = _bf16_layer(K, 8, M or max(4 * K, 2048), seed=seed)
