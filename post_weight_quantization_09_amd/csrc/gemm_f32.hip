@@ -5,10 +5,10 @@
 // after a block, the far weights are updated with one matrix product) and the two products of the GPTAQ
 // correction ([R] item 3).
 //
-// Tiling: 256 threads = 4 waves in 2 x 2, a TM x TN tile of C per workgroup (64 x 64, or 128 x 128 for large
-// products), each wave (TM/2) x (TN/2) as 32 x 32 v_mfma_f32_32x32x2_f32 accumulators.  k advances TK = 16 at a
-// time through double-buffered LDS tiles stored k-major (As[k][m], Bs[k][n]) so that every MFMA operand read
-// is a conflict-free ds_read_b32.
+// Tiling: 256 threads = 4 waves in 2 x 2, a 64 x 64 tile of C per workgroup, each wave 32 x 32 as a
+// v_mfma_f32_32x32x2_f32 accumulator.  k advances TK = 16 at a time through double-buffered LDS tiles stored
+// k-major (As[k][m], Bs[k][n]) so that every MFMA operand read is a conflict-free ds_read_b32.  Large products
+// with a long reduction take the split-bf16 kernel below (128 x 128 tiles, same structure flags and epilogue).
 #include "gemm_f32.hpp"
 
 namespace gptq {
@@ -238,6 +238,233 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
     }
 }
 
+// ---- fp32-accurate products on the bf16 MFMA: every fp32 operand is split into three bf16 parts
+// (v = h0 + h1 + h2 + O(2^-24 |v|), each part the round-to-nearest-even bf16 of the remainder), and the six
+// part products of order <= 2 are accumulated in fp32 by v_mfma_f32_32x32x16_bf16.  Part planes are stored
+// k-contiguous (row pitch 24 bf16 = 48 bytes), so a lane's 8 k-values are one conflict-free 16-byte LDS read.
+constexpr int kXP = 24;
+__device__ inline void split3(float v, uint16_t& h0, uint16_t& h1, uint16_t& h2) {
+    const __bf16 b0 = (__bf16)v;
+    const float r1 = v - (float)b0;
+    const __bf16 b1 = (__bf16)r1;
+    const float r2 = r1 - (float)b1;
+    const __bf16 b2 = (__bf16)r2;
+    h0 = __builtin_bit_cast(uint16_t, b0);
+    h1 = __builtin_bit_cast(uint16_t, b1);
+    h2 = __builtin_bit_cast(uint16_t, b2);
+}
+
+template <int TM, int TN, int TK, bool TA, bool TB, bool FULL>
+__global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
+    using T = Tile<TM, TN, TK>;
+    static_assert(TK == 16, "one 32x32x16 MFMA k-step per stage");
+    static_assert(TM % 128 == 0 && TN % 128 == 0, "strided operands are loaded 128 rows per pass");
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][3][TM][kXP];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][3][TN][kXP];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;
+    int64_t tx = blockIdx.x, ty = blockIdx.y;
+    if (p.flags & (kGemmBLower | kGemmBUpper)) {
+        const int64_t id = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        tx = id / gridDim.y;
+        ty = id % gridDim.y;
+        if (p.flags & kGemmBUpper) tx = gridDim.x - 1 - tx;
+    }
+    const int64_t m0 = ty * TM;
+    const int64_t n0 = tx * TN;
+    const int64_t bz = blockIdx.z;
+    if (m0 >= p.M || n0 >= p.N) return;
+    if ((p.flags & kGemmCUpper) && m0 >= n0 + TN) return;
+
+    const float* A1 = p.A1 + bz * p.strideA1;
+    const float* B1 = p.B1 + bz * p.strideB1;
+    const float* A2 = p.A2 ? p.A2 + bz * p.strideA2 : nullptr;
+    const float* B2 = p.B2 ? p.B2 + bz * p.strideB2 : nullptr;
+    float* C = p.C + bz * p.strideC;
+
+    int64_t klo = 0, khi = p.K1;
+    if (p.flags & (kGemmAUpper | kGemmAStrictUpperMask)) klo = max<int64_t>(klo, m0);
+    if (p.flags & kGemmBLower) klo = max<int64_t>(klo, n0);
+    if (p.flags & kGemmBUpper) khi = min<int64_t>(khi, n0 + TN);
+    klo = (klo / TK) * TK;
+    const int64_t nt1 = khi > klo ? ceil_div(khi - klo, TK) : 0;
+    const int64_t nt2 = (A2 && p.K2 > 0) ? ceil_div(p.K2, TK) : 0;
+    const int64_t nt = nt1 + nt2;
+    const bool mask = (p.flags & kGemmAStrictUpperMask) != 0;
+
+    f32x16 acc[T::MA][T::NB];
+    for (int a = 0; a < T::MA; ++a)
+        for (int b = 0; b < T::NB; ++b)
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+    TileIO<TM, TN, TK, TA, TB, FULL> io;
+    // Operands whose k index is strided in memory (A with TA, B without TB) are loaded as single floats: thread
+    // t takes row/column t % T and the 8 consecutive k of group t / T (T = 128 rows per 256 threads; a 256-row
+    // tile takes two such passes), so each load instruction is coalesced along the contiguous index and each
+    // thread ends with k-contiguous values for its planes.
+    constexpr int SA = TA ? TM / 128 : 1, SB = TB ? 1 : TN / 128;
+    float sa[TA ? SA : 1][8], sb[TB ? 1 : SB][8];
+    float sa_scale = 1.f;
+    auto load_strided = [&](const float* X, int64_t ldx, int64_t rows, int64_t kEnd, int64_t r0, int64_t k0, int passes,
+                            bool strict_upper, float (*dst)[8]) {
+        const int r = tid & 127, kq = tid >> 7;
+        for (int ps = 0; ps < passes; ++ps) {
+            const int64_t row = r0 + 128 * ps + r;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int64_t kk = k0 + 8 * kq + e;
+                float v = (FULL || (row < rows && kk < kEnd)) ? X[kk * ldx + row] : 0.f;
+                if (strict_upper && kk <= row) v = 0.f;
+                dst[ps][e] = v;
+            }
+        }
+    };
+    auto load = [&](int64_t t) {
+        const bool second = t >= nt1;
+        const int64_t k0 = second ? (t - nt1) * TK : klo + t * TK;
+        const float* Ap = second ? A2 : A1; const float* Bp = second ? B2 : B1;
+        const int64_t ldA = second ? p.lda2 : p.lda1, ldB = second ? p.ldb2 : p.ldb1;
+        const int64_t kEnd = second ? p.K2 : p.K1;
+        if constexpr (TA) {
+            load_strided(Ap, ldA, p.M, kEnd, m0, k0, SA, second ? false : mask, sa);
+            sa_scale = second ? p.a2_scale : 1.f;
+        } else {
+            io.load_a(Ap, ldA, p.M, kEnd, m0, k0, second ? p.vecA2 : p.vecA1, second ? p.a2_scale : 1.0f,
+                      second ? false : mask, tid);
+        }
+        if constexpr (TB) io.load_b(Bp, ldB, p.N, kEnd, n0, k0, second ? p.vecB2 : p.vecB1, tid);
+        else load_strided(Bp, ldB, p.N, kEnd, n0, k0, SB, false, sb);
+    };
+    auto store = [&](int buf) {
+        if constexpr (TA) {
+            const int r = tid & 127, kq = tid >> 7;
+            for (int ps = 0; ps < SA; ++ps) {
+                uint16_t h[3][8];
+                for (int e = 0; e < 8; ++e) split3(sa[ps][e] * sa_scale, h[0][e], h[1][e], h[2][e]);
+                for (int q = 0; q < 3; ++q) {
+                    u32x4 w = {(uint32_t)h[q][0] | ((uint32_t)h[q][1] << 16), (uint32_t)h[q][2] | ((uint32_t)h[q][3] << 16),
+                               (uint32_t)h[q][4] | ((uint32_t)h[q][5] << 16), (uint32_t)h[q][6] | ((uint32_t)h[q][7] << 16)};
+                    *reinterpret_cast<u32x4*>(&As[buf][q][128 * ps + r][8 * kq]) = w;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < T::NVA; ++i) {
+                int mi, ki;
+                io.a_pos(i, tid, mi, ki);
+                f32x4 va = io.a[i] * io.a_scale;
+                if (io.a_mask) {
+                    for (int e = 0; e < 4; ++e) {
+                        const int64_t me = io.am0 + mi, ke = io.ak0 + ki + e;
+                        if (ke <= me) va[e] = 0.f;
+                    }
+                }
+                uint16_t h[3][4];
+                for (int e = 0; e < 4; ++e) split3(va[e], h[0][e], h[1][e], h[2][e]);
+                for (int q = 0; q < 3; ++q) {
+                    u32x2 w = {(uint32_t)h[q][0] | ((uint32_t)h[q][1] << 16), (uint32_t)h[q][2] | ((uint32_t)h[q][3] << 16)};
+                    *reinterpret_cast<u32x2*>(&As[buf][q][mi][ki]) = w;
+                }
+            }
+        }
+        if constexpr (TB) {
+#pragma unroll
+            for (int i = 0; i < T::NVB; ++i) {
+                int ni, ki;
+                io.b_pos(i, tid, ni, ki);
+                const f32x4 vb = io.b[i];
+                uint16_t h[3][4];
+                for (int e = 0; e < 4; ++e) split3(vb[e], h[0][e], h[1][e], h[2][e]);
+                for (int q = 0; q < 3; ++q) {
+                    u32x2 w = {(uint32_t)h[q][0] | ((uint32_t)h[q][1] << 16), (uint32_t)h[q][2] | ((uint32_t)h[q][3] << 16)};
+                    *reinterpret_cast<u32x2*>(&Bs[buf][q][ni][ki]) = w;
+                }
+            }
+        } else {
+            const int r = tid & 127, kq = tid >> 7;
+            for (int ps = 0; ps < SB; ++ps) {
+                uint16_t h[3][8];
+                for (int e = 0; e < 8; ++e) split3(sb[ps][e], h[0][e], h[1][e], h[2][e]);
+                for (int q = 0; q < 3; ++q) {
+                    u32x4 w = {(uint32_t)h[q][0] | ((uint32_t)h[q][1] << 16), (uint32_t)h[q][2] | ((uint32_t)h[q][3] << 16),
+                               (uint32_t)h[q][4] | ((uint32_t)h[q][5] << 16), (uint32_t)h[q][6] | ((uint32_t)h[q][7] << 16)};
+                    *reinterpret_cast<u32x4*>(&Bs[buf][q][128 * ps + r][8 * kq]) = w;
+                }
+            }
+        }
+    };
+
+    if (nt > 0) {
+        load(0);
+        store(0);
+    }
+    __syncthreads();
+    for (int64_t t = 0; t < nt; ++t) {
+        const int buf = (int)(t & 1);
+        if (t + 1 < nt) load(t + 1);
+        const int kk = 8 * (lane >> 5);
+        u32x4 fa[3][T::MA], fb[3][T::NB];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+#pragma unroll
+            for (int a = 0; a < T::MA; ++a)
+                fa[q][a] = *reinterpret_cast<const u32x4*>(&As[buf][q][wm * (TM / 2) + 32 * a + (lane & 31)][kk]);
+#pragma unroll
+            for (int b = 0; b < T::NB; ++b)
+                fb[q][b] = *reinterpret_cast<const u32x4*>(&Bs[buf][q][wn * (TN / 2) + 32 * b + (lane & 31)][kk]);
+        }
+#pragma unroll
+        for (int a = 0; a < T::MA; ++a)
+#pragma unroll
+            for (int b = 0; b < T::NB; ++b) {
+                // small parts first
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[2][a]), __builtin_bit_cast(bf16x8, fb[0][b]), acc[a][b], 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[1][a]), __builtin_bit_cast(bf16x8, fb[1][b]), acc[a][b], 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[0][a]), __builtin_bit_cast(bf16x8, fb[2][b]), acc[a][b], 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[1][a]), __builtin_bit_cast(bf16x8, fb[0][b]), acc[a][b], 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[0][a]), __builtin_bit_cast(bf16x8, fb[1][b]), acc[a][b], 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[0][a]), __builtin_bit_cast(bf16x8, fb[0][b]), acc[a][b], 0, 0, 0);
+            }
+        if (t + 1 < nt) store(buf ^ 1);
+        __syncthreads();
+    }
+
+    for (int a = 0; a < T::MA; ++a) {
+        for (int b = 0; b < T::NB; ++b) {
+            const int64_t col = n0 + wn * (TN / 2) + 32 * b + (lane & 31);
+            if (col >= p.N) continue;
+            for (int r = 0; r < 16; ++r) {
+                const int64_t row = m0 + wm * (TM / 2) + 32 * a + mfma32_row(r, lane);
+                if (row >= p.M) continue;
+                float* cp = C + row * p.ldc + col;
+                float v = p.alpha * acc[a][b][r];
+                if (p.beta != 0.f) v += p.beta * *cp;
+                *cp = v;
+            }
+        }
+    }
+}
+
+template <int TM, int TN>
+hipError_t launch_x6(const GemmArgs& p, int64_t batch, hipStream_t stream) {
+    constexpr int TK = 16;
+    dim3 grid((unsigned)ceil_div(p.N, TN), (unsigned)ceil_div(p.M, TM), (unsigned)batch);
+    if (grid.y > 65535u || grid.z > 65535u) return hipErrorInvalidValue;
+    const bool full = p.M % TM == 0 && p.N % TN == 0 && p.K1 % TK == 0 && p.vecA1 && p.vecB1 &&
+                      (!p.A2 || (p.K2 % TK == 0 && p.vecA2 && p.vecB2));
+#define GPTQ_X6_LAUNCH(TA_, TB_)                                                                              \
+    if (full) hipLaunchKernelGGL((gemm_x6_kernel<TM, TN, TK, TA_, TB_, true>), grid, dim3(256), 0, stream, p);  \
+    else hipLaunchKernelGGL((gemm_x6_kernel<TM, TN, TK, TA_, TB_, false>), grid, dim3(256), 0, stream, p);
+    if (!p.transA && !p.transB) { GPTQ_X6_LAUNCH(false, false) }
+    else if (!p.transA && p.transB) { GPTQ_X6_LAUNCH(false, true) }
+    else if (p.transA && !p.transB) { GPTQ_X6_LAUNCH(true, false) }
+    else { GPTQ_X6_LAUNCH(true, true) }
+#undef GPTQ_X6_LAUNCH
+    return hipGetLastError();
+}
+
 inline bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
 
 
@@ -276,9 +503,10 @@ hipError_t gemm_f32(GemmArgs p, int64_t batch, hipStream_t stream) {
     // beats it on the depth-128 trailing updates and on small products (more workgroups in flight); from about
     // 12k x 12k outputs on, 128 x 128 is faster (half the L2 traffic per flop: +20% at 14336).  Triangular
     // products (the factorisation's) switch at 7168, where 128 x 128 is 2-8% faster and at 3584 up to 30% slower.
-    const bool tri = (p.flags & (kGemmBLower | kGemmBUpper | kGemmAUpper | kGemmCUpper)) != 0;
-    const int64_t big = tri ? 7168 : 12288;
-    if (p.M >= big && p.N >= big && p.K1 >= 1024) return launch<128, 128, 16>(p, batch, stream);
+    // Large products with a long reduction run on the bf16 MFMA with three-part operand splits (fp32 accuracy):
+    // 156-167 TFLOP/s against 87-122 for the fp32 MFMA at 3584-14336 (the fp32 MFMA peak is 157.3), equal at depth
+    // 512, slower below ~3000 outputs per side (fewer workgroups) and at depth <= 256 (per-stage overhead).
+    if (p.M >= 3584 && p.N >= 3584 && p.K1 >= 1024) return launch_x6<128, 128>(p, batch, stream);
     return launch<64, 64, 16>(p, batch, stream);
 }
 

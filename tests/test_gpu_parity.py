@@ -68,6 +68,17 @@ def test_gram_f32(g):
     assert err <= H_TOL
 
 
+def test_gram_f32_large(g):
+    # fp32 activations at 4096 features: the product runs on the split-bf16 GEMM with a transposed A operand
+    rng = np.random.default_rng(11)
+    X = (rng.standard_normal((4096, 4096)) * np.exp(rng.standard_normal(4096))).astype(np.float32)
+    H = torch.zeros(4096, 4096, device=DEV)
+    g.gptq_accumulate_hessian(H, torch.tensor(X, device=DEV))
+    err = rel_fro(np64(H), O.gram([X.astype(np.float64)]))
+    _print(f"gram f32 K=4096 M=4096 rel={err:.3e}")
+    assert err <= H_TOL
+
+
 @pytest.mark.parametrize("K,M", [(300, 3000), (512, 4096)])
 def test_gram_row_scaled(g, K, M):
     cfg, L = _bf16_layer(K, 8, M, base="c3_down_proj_8b_g4", groups=4)
@@ -151,6 +162,22 @@ def test_prepare(g, K):
     assert np.array_equal(dead.cpu().numpy().astype(bool), ref["dead"])
     assert n_dead == int(ref["dead"].sum())
     assert abs(damp - ref["damp"]) <= 1e-6 * ref["damp"]
+    assert np.count_nonzero(np.tril(U, -1)) == 0
+    err = np.abs(U - ref["U"]).max() / np.abs(ref["U"]).max()
+    _print(f"prepare K={K} U max rel err={err:.3e}")
+    assert err <= 1e-4
+
+
+@pytest.mark.parametrize("K", [7168, 7300])
+def test_prepare_split_bf16_products(g, K):
+    """Factorisations whose top-level products (>= 3584 per side, depth >= 1024) run on the split-bf16 GEMM:
+    whole tiles (7168) and ragged ones (7300), with dead coordinates."""
+    H = _workload_H(K, M=8192, seed=K, dead_cols=(0, K // 3, K - 1))
+    Ht = torch.tensor(H, dtype=torch.float32, device=DEV)
+    dead, damp, n_dead = g.gptq_prepare(Ht, 0.01)
+    ref = O.prepare(H, 0.01)
+    U = np64(Ht)
+    assert np.array_equal(dead.cpu().numpy().astype(bool), ref["dead"])
     assert np.count_nonzero(np.tril(U, -1)) == 0
     err = np.abs(U - ref["U"]).max() / np.abs(ref["U"]).max()
     _print(f"prepare K={K} U max rel err={err:.3e}")
