@@ -506,7 +506,8 @@ hipError_t gemm_f32(GemmArgs p, int64_t batch, hipStream_t stream) {
     // Large products with a long reduction run on the bf16 MFMA with three-part operand splits (fp32 accuracy):
     // 156-167 TFLOP/s against 87-122 for the fp32 MFMA at 3584-14336 (the fp32 MFMA peak is 157.3), equal at depth
     // 512, slower below ~3000 outputs per side (fewer workgroups) and at depth <= 256 (per-stage overhead).
-    if (p.M >= 3584 && p.N >= 3584 && p.K1 >= 1024) return launch_x6<128, 128>(p, batch, stream);
+    // A batch counts like more rows (the grouped factorisation and trailing updates of output-channel groups).
+    if (p.M >= 1024 && p.M * batch >= 3584 && p.N >= 3584 && p.K1 >= 1024) return launch_x6<128, 128>(p, batch, stream);
     return launch<64, 64, 16>(p, batch, stream);
 }
 

@@ -4,10 +4,11 @@
 // [T] section 4: with U the upper factor of H_d^{-1}, that move is w_k -= U_qk E_q with E_q = (w_q - Q(w_q)) / U_qq.
 // [T] section 5: every output channel uses the same coordinate order, so all channels share U; inside a
 // block of 128 coordinates the updates are applied at once, the rest of the matrix is updated by matrix
-// products (W[b1:] -= U[B, b1:]^T E_B), here fp32 MFMA GEMMs.  The products are applied in two levels:
-// after each block only the rows of its 512-coordinate super-block, and once per super-block the far rows
-// with the errors of all its blocks (depth 512), so the far part of W is read and written once per
-// super-block instead of once per block.  The sums are the same; only their grouping differs.
+// products (W[b1:] -= U[B, b1:]^T E_B), here fp32-accurate MFMA GEMMs.  The products are applied in two
+// levels: after each block only the rows of its 1024-coordinate super-block, and once per super-block the far
+// rows with the errors of all its blocks (depth 1024), so the far part of W is read and written once per
+// super-block instead of once per block, and the far product is deep enough for the split-bf16 GEMM.  The sums
+// are the same; only their grouping differs.
 // [R] item 3 / [A]: the asymmetric variant adds w_k += P1_qk * w_q(before rounding), in block and in the
 // lazy product (a second operand pair of the same GEMM).
 // [G] / [T] section 2: symmetric per-channel grid, codes 0..2^b-1, zero point 2^(b-1), value s (c - z).
@@ -31,7 +32,7 @@ namespace gptq {
 namespace {
 
 constexpr int kB = 128;          // block (lazy batch) width
-constexpr int kSB = 4 * kB;      // super-block: far rows are updated once per kSB coordinates
+constexpr int kSB = 8 * kB;      // super-block: far rows are updated once per kSB coordinates
 constexpr int kChPerWG = 16;     // channels per workgroup of the block kernel
 
 __global__ void quant_init_kernel(DevStatus* st, uint32_t* amax_bits, float* loss_acc, int64_t N) {
