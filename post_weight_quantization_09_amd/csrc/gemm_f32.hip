@@ -503,11 +503,14 @@ hipError_t gemm_f32(GemmArgs p, int64_t batch, hipStream_t stream) {
     // beats it on the depth-128 trailing updates and on small products (more workgroups in flight); from about
     // 12k x 12k outputs on, 128 x 128 is faster (half the L2 traffic per flop: +20% at 14336).  Triangular
     // products (the factorisation's) switch at 7168, where 128 x 128 is 2-8% faster and at 3584 up to 30% slower.
-    // Large products with a long reduction run on the bf16 MFMA with three-part operand splits (fp32 accuracy):
-    // 156-167 TFLOP/s against 87-122 for the fp32 MFMA at 3584-14336 (the fp32 MFMA peak is 157.3), equal at depth
-    // 512, slower below ~3000 outputs per side (fewer workgroups) and at depth <= 256 (per-stage overhead).
-    // A batch counts like more rows (the grouped factorisation and trailing updates of output-channel groups).
-    if (p.M >= 1024 && p.M * batch >= 3584 && p.N >= 3584 && p.K1 >= 1024) return launch_x6<128, 128>(p, batch, stream);
+    // Products with a long reduction and enough 128 x 128 tiles run on the bf16 MFMA with three-part operand
+    // splits (fp32 accuracy).  Measured at depth >= 1024: 156-167 TFLOP/s against 87-122 for the fp32 MFMA on
+    // 3584-14336 squares (the fp32 MFMA peak is 157.3), 118-136 against 87-106 on the 1024-3072-wide trailing
+    // updates; equal at 256 tiles, slower on the 2048 squares and at depth <= 512 (per-stage overhead).  The choice
+    // depends on one batch element's shape only, so a batched call (all output-channel groups at once) does the
+    // same arithmetic as one call per element, bit for bit.
+    const int64_t tiles128 = ceil_div(p.M, 128) * ceil_div(p.N, 128);
+    if (p.K1 >= 1024 && p.M >= 1024 && p.N >= 1024 && tiles128 >= 512) return launch_x6<128, 128>(p, batch, stream);
     return launch<64, 64, 16>(p, batch, stream);
 }
 

@@ -573,6 +573,29 @@ def test_quantize_layer_groups(g, K, gs, groups, wdt, opts):
     _print(f"quantize groups K={K} {groups}x{gs} {opts}: identical to per-group calls")
 
 
+def test_quantize_layer_groups_split_bf16_trailing(g):
+    """Groups of 1024 channels at 9216 coordinates: the first far trailing update (8192 x 1024 per group, depth
+    1024) runs on the split-bf16 GEMM; the batched call still equals one call per group bit for bit.  U is a
+    synthetic well-conditioned upper factor (this checks the batching, not the factorisation)."""
+    K, gs, groups = 9216, 1024, 2
+    gen = torch.Generator(device=DEV)
+    Us = []
+    for gi in range(groups):
+        gen.manual_seed(17 + gi)
+        Us.append(torch.triu(torch.randn(K, K, device=DEV, generator=gen) * 0.01, 1) + 2.0 * torch.eye(K, device=DEV))
+    U = torch.stack(Us)
+    dead = torch.zeros(groups, K, dtype=torch.uint8, device=DEV)
+    gen.manual_seed(5)
+    W = (torch.randn(K, gs * groups, device=DEV, generator=gen) * 0.02).contiguous()
+    out = g.gptq_quantize_layer_groups(W, U, 4, dead=dead, losses=torch.empty(gs * groups, device=DEV))
+    for gi in range(groups):
+        sl = slice(gi * gs, (gi + 1) * gs)
+        ref = g.gptq_quantize_layer(W[:, sl], Us[gi], 4, dead=dead[gi], losses=torch.empty(gs, device=DEV))
+        assert torch.equal(out["codes"][:, sl], ref["codes"]), f"group {gi} codes"
+        assert torch.equal(out["losses"][sl], ref["losses"]), f"group {gi} losses"
+    _print(f"quantize groups K={K} {groups}x{gs}: identical to per-group calls")
+
+
 # ------------------------------------------------------------------------------------------------ act-order, groups, MSE
 def _next2_case(g, K, N, M, seed, bits, act, groupsize=0, static=False, mse=False, asym=False, cae=False):
     base = "c4_up_proj_8b_gptaq" if asym else "c5_down_proj_70b"
