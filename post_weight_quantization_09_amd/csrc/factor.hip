@@ -80,6 +80,48 @@ __device__ __forceinline__ float readlane_f(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }
 
+// Wave 0's factorisation of the 16-column panel p0 .. p0 + 15 of chol_ul_inv_kernel.  Lane l holds rows l and
+// l + 64 of the panel in two register halves.  HI (p0 >= 64): every row of half 0 lies above the panel, so its
+// entries are only scaled; otherwise every row of half 1 lies below the panel, is zero in R and is not held.
+template <bool HI>
+__device__ __forceinline__ void factor_panel(float (*S)[kNB + 1], float (*R)[kNB + 1], float* Rinv, int p0,
+                                             int lane, unsigned& bad) {
+    constexpr int NH = HI ? 2 : 1;   // register halves holding rows at or above the panel
+    float pn[NH][16];
+#pragma unroll
+    for (int s2 = 0; s2 < NH; ++s2)
+#pragma unroll
+        for (int c = 0; c < 16; ++c) pn[s2][c] = S[lane + 64 * s2][p0 + c];
+#pragma unroll
+    for (int c = 15; c >= 0; --c) {
+        const int j = p0 + c;
+        float d = readlane_f(pn[NH - 1][c], j & 63);
+        if (!(d > 0.0f)) {
+            bad |= isfinite(d) ? kDevNotPD : kDevNonFinite;
+            d = 1.0f;
+        }
+        float rinv = __builtin_amdgcn_rsqf(d);
+        rinv = rinv * fmaf(-0.5f * d * rinv, rinv, 1.5f);   // one Newton step on 1/sqrt(d)
+        const float r = d * rinv;
+        float cj[NH];
+#pragma unroll
+        for (int s2 = 0; s2 < NH; ++s2) {
+            const int row = lane + 64 * s2;
+            if (HI && s2 == 0) cj[s2] = pn[s2][c] * rinv;   // row < 64 <= j
+            else cj[s2] = row < j ? pn[s2][c] * rinv : (row == j ? r : 0.f);
+            R[row][j] = cj[s2];
+        }
+        if (!HI) R[lane + 64][j] = 0.f;
+        if (lane == 0) Rinv[j] = rinv;
+#pragma unroll
+        for (int cc = 0; cc < c; ++cc) {
+            const float ck = readlane_f(cj[NH - 1], (p0 + cc) & 63);
+#pragma unroll
+            for (int s2 = 0; s2 < NH; ++s2) pn[s2][cc] = fmaf(-cj[s2], ck, pn[s2][cc]);
+        }
+    }
+}
+
 // In place on the n x n diagonal block D (ld, n <= 128): reads its upper triangle (a symmetric block S),
 // factors S = R R^T with R upper and writes U = R^{-1} (upper, strictly lower part zeroed).
 //   The block sits in the bottom-right corner of a 128 x 128 frame whose top-left is the identity, so every
@@ -112,38 +154,8 @@ __global__ __launch_bounds__(1024) void chol_ul_inv_kernel(float* D, int64_t ld,
     for (int P = kNB / 16 - 1; P >= 0; --P) {
         const int p0 = 16 * P;
         if (wave == 0) {
-            const bool hi = p0 >= 64;   // the panel's rows p0..p0+15 sit in register half 1
-            float pn[2][16];
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                for (int c = 0; c < 16; ++c) pn[s2][c] = S[lane + 64 * s2][p0 + c];
-#pragma unroll
-            for (int c = 15; c >= 0; --c) {
-                const int j = p0 + c;
-                float d = readlane_f(hi ? pn[1][c] : pn[0][c], j & 63);
-                if (!(d > 0.0f)) {
-                    bad |= isfinite(d) ? kDevNotPD : kDevNonFinite;
-                    d = 1.0f;
-                }
-                float rinv = __builtin_amdgcn_rsqf(d);
-                rinv = rinv * fmaf(-0.5f * d * rinv, rinv, 1.5f);   // one Newton step on 1/sqrt(d)
-                const float r = d * rinv;
-                float cj[2];
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const int row = lane + 64 * s2;
-                    cj[s2] = row < j ? pn[s2][c] * rinv : (row == j ? r : 0.f);
-                    R[row][j] = cj[s2];
-                }
-                if (lane == 0) Rinv[j] = rinv;
-#pragma unroll
-                for (int cc = 0; cc < c; ++cc) {
-                    const float ck = readlane_f(hi ? cj[1] : cj[0], (p0 + cc) & 63);
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2) pn[s2][cc] = fmaf(-cj[s2], ck, pn[s2][cc]);
-                }
-            }
+            if (p0 >= 64) factor_panel<true>(S, R, Rinv, p0, lane, bad);
+            else factor_panel<false>(S, R, Rinv, p0, lane, bad);
         }
         __syncthreads();
         if (p0 > 0) {

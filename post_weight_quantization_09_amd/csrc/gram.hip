@@ -454,40 +454,61 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(GramArgs p, float* Out
     const int64_t R0 = (int64_t)bi * kGT + wi * 128, C0 = (int64_t)bj * kGT + wj * 128;
 
     // The partial of (split, tile, wave) is 256 registers x 64 lanes, contiguous.  Thread t sums elements
-    // 4 (t + 256 i) .. +3 over the splits in split order (the order of the original sequential sum), with
-    // eight splits' 16-byte loads in flight at a time.
+    // 4 (t + 256 i) .. +3 over the splits in split order (the order of the original sequential sum), two
+    // element groups at a time with eight splits each: sixteen 16-byte loads in flight per thread.
     const int64_t qstride = (int64_t)p.ntiles * 4 * 256 * 64;
     const float* base = p.partial + ((int64_t)tile * 4 + wave) * (256 * 64);
     constexpr int kInFlight = 8;
-    for (int i = 0; i < 16; ++i) {
-        const int e = (tid + 256 * i) * 4;            // element (ri, lane0 .. lane0+3)
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 16; i += 2) {
+        const int e0 = (tid + 256 * i) * 4, e1 = e0 + 256 * 4;   // elements (ri, lane0 .. lane0+3)
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
         int sp = 0;
         for (; sp + kInFlight <= p.splits; sp += kInFlight) {
-            f32x4 v[kInFlight];
+            f32x4 v0[kInFlight], v1[kInFlight];
 #pragma unroll
-            for (int u = 0; u < kInFlight; ++u)
-                v[u] = *reinterpret_cast<const f32x4*>(base + (int64_t)(sp + u) * qstride + e);
+            for (int u = 0; u < kInFlight; ++u) {
+                const float* q = base + (int64_t)(sp + u) * qstride;
+                v0[u] = *reinterpret_cast<const f32x4*>(q + e0);
+                v1[u] = *reinterpret_cast<const f32x4*>(q + e1);
+            }
 #pragma unroll
-            for (int u = 0; u < kInFlight; ++u) s += v[u];
+            for (int u = 0; u < kInFlight; ++u) { s0 += v0[u]; s1 += v1[u]; }
         }
-        for (; sp < p.splits; ++sp) s += *reinterpret_cast<const f32x4*>(base + (int64_t)sp * qstride + e);
-        const int ri = e >> 6, lane0 = e & 63;
-        const int a = ri >> 6, b = (ri >> 4) & 3, r = ri & 15;
+        for (; sp < p.splits; ++sp) {
+            const float* q = base + (int64_t)sp * qstride;
+            s0 += *reinterpret_cast<const f32x4*>(q + e0);
+            s1 += *reinterpret_cast<const f32x4*>(q + e1);
+        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) T[acc_row(a, r, lane0 + q)][acc_col(b, lane0 + q)] = 2.0f * s[q];
+        for (int h = 0; h < 2; ++h) {
+            const int e = h ? e1 : e0;
+            const f32x4 s = h ? s1 : s0;
+            const int ri = e >> 6, lane0 = e & 63;
+            const int a = ri >> 6, b = (ri >> 4) & 3, r = ri & 15;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) T[acc_row(a, r, lane0 + q)][acc_col(b, lane0 + q)] = 2.0f * s[q];
+        }
     }
     __syncthreads();
-    for (int i = 0; i < 64; ++i) {
-        const int idx = tid + 256 * i;
-        const int row = idx >> 7, col = idx & 127;
-        if (R0 + row < p.K && C0 + col < p.K) {
-            float* o = Out + (R0 + row) * p.K + C0 + col;
-            *o += T[row][col];
+    // Out += the quadrant (and its mirror).  The two blocks a workgroup updates are disjoint, and disjoint from
+    // every other workgroup's, so sixteen rows' reads are issued before their writes instead of one
+    // read-modify-write round trip at a time.
+    constexpr int kRows = 16;
+    for (int i0 = 0; i0 < 64; i0 += kRows) {
+        float dv[kRows], mv[kRows];
+#pragma unroll
+        for (int u = 0; u < kRows; ++u) {
+            const int idx = tid + 256 * (i0 + u);
+            const int row = idx >> 7, col = idx & 127;
+            dv[u] = (R0 + row < p.K && C0 + col < p.K) ? Out[(R0 + row) * p.K + C0 + col] : 0.f;
+            mv[u] = (mirror && C0 + row < p.K && R0 + col < p.K) ? Out[(C0 + row) * p.K + R0 + col] : 0.f;
         }
-        if (mirror && C0 + row < p.K && R0 + col < p.K) {
-            float* o = Out + (C0 + row) * p.K + R0 + col;
-            *o += T[col][row];
+#pragma unroll
+        for (int u = 0; u < kRows; ++u) {
+            const int idx = tid + 256 * (i0 + u);
+            const int row = idx >> 7, col = idx & 127;
+            if (R0 + row < p.K && C0 + col < p.K) Out[(R0 + row) * p.K + C0 + col] = dv[u] + T[row][col];
+            if (mirror && C0 + row < p.K && R0 + col < p.K) Out[(C0 + row) * p.K + R0 + col] = mv[u] + T[col][row];
         }
     }
 }
