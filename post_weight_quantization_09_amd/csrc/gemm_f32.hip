@@ -186,39 +186,51 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
         for (int b = 0; b < T::NB; ++b)
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    TileIO<TM, TN, TK, TA, TB, FULL> io;
-    auto load = [&](int64_t t) {
+    // Stage t (TK values of k) is loaded into registers kD - 1 stages ahead of its product, written to the LDS
+    // buffer t & 1 one stage ahead, and multiplied after a barrier.  The loop is unrolled by kD so that every
+    // register slot index is a constant; loads past the last stage re-read it (never stored), which keeps the
+    // loop free of branches around loads.
+    constexpr int kD = 4;
+    using IO = TileIO<TM, TN, TK, TA, TB, FULL>;
+    IO io[kD];
+    auto load = [&](IO& x, int64_t t) {
         if (t < nt1) {
             int64_t k0 = klo + t * TK;
-            io.load_a(A1, p.lda1, p.M, p.K1, m0, k0, p.vecA1, 1.0f, mask, tid);
-            io.load_b(B1, p.ldb1, p.N, p.K1, n0, k0, p.vecB1, tid);
+            x.load_a(A1, p.lda1, p.M, p.K1, m0, k0, p.vecA1, 1.0f, mask, tid);
+            x.load_b(B1, p.ldb1, p.N, p.K1, n0, k0, p.vecB1, tid);
         } else {
             int64_t k0 = (t - nt1) * TK;
-            io.load_a(A2, p.lda2, p.M, p.K2, m0, k0, p.vecA2, p.a2_scale, false, tid);
-            io.load_b(B2, p.ldb2, p.N, p.K2, n0, k0, p.vecB2, tid);
+            x.load_a(A2, p.lda2, p.M, p.K2, m0, k0, p.vecA2, p.a2_scale, false, tid);
+            x.load_b(B2, p.ldb2, p.N, p.K2, n0, k0, p.vecB2, tid);
         }
     };
 
     if (nt > 0) {
-        load(0);
-        io.store(As[0], Bs[0], tid);
+#pragma unroll
+        for (int s = 0; s < kD - 1; ++s) load(io[s], min<int64_t>(s, nt - 1));
+        io[0].store(As[0], Bs[0], tid);
     }
     __syncthreads();
-    for (int64_t t = 0; t < nt; ++t) {
-        const int buf = (int)(t & 1);
-        if (t + 1 < nt) load(t + 1);
+    for (int64_t t0 = 0; t0 < nt; t0 += kD) {
 #pragma unroll
-        for (int kk = 0; kk < TK / 2; ++kk) {
-            const int k = 2 * kk + (lane >> 5);
-            float av[T::MA], bv[T::NB];
-            for (int a = 0; a < T::MA; ++a) av[a] = As[buf][k][wm * (TM / 2) + 32 * a + (lane & 31)];
-            for (int b = 0; b < T::NB; ++b) bv[b] = Bs[buf][k][wn * (TN / 2) + 32 * b + (lane & 31)];
-            for (int a = 0; a < T::MA; ++a)
-                for (int b = 0; b < T::NB; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
+        for (int u = 0; u < kD; ++u) {
+            const int64_t t = t0 + u;
+            if (t >= nt) break;
+            const int buf = u & 1;   // t0 is even
+            load(io[(u + kD - 1) % kD], min<int64_t>(t + kD - 1, nt - 1));
+#pragma unroll
+            for (int kk = 0; kk < TK / 2; ++kk) {
+                const int k = 2 * kk + (lane >> 5);
+                float av[T::MA], bv[T::NB];
+                for (int a = 0; a < T::MA; ++a) av[a] = As[buf][k][wm * (TM / 2) + 32 * a + (lane & 31)];
+                for (int b = 0; b < T::NB; ++b) bv[b] = Bs[buf][k][wn * (TN / 2) + 32 * b + (lane & 31)];
+                for (int a = 0; a < T::MA; ++a)
+                    for (int b = 0; b < T::NB; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
+            }
+            if (t + 1 < nt) io[(u + 1) % kD].store(As[buf ^ 1], Bs[buf ^ 1], tid);
+            __syncthreads();
         }
-        if (t + 1 < nt) io.store(As[buf ^ 1], Bs[buf ^ 1], tid);
-        __syncthreads();
     }
 
     // Epilogue: C = alpha * acc + beta * C.
