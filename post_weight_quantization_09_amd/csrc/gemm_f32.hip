@@ -255,15 +255,20 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 // part products of order <= 2 are accumulated in fp32 by v_mfma_f32_32x32x16_bf16.  Part planes are stored
 // k-contiguous (row pitch 24 bf16 = 48 bytes), so a lane's 8 k-values are one conflict-free 16-byte LDS read.
 constexpr int kXP = 24;
-__device__ inline void split3(float v, uint16_t& h0, uint16_t& h1, uint16_t& h2) {
-    const __bf16 b0 = (__bf16)v;
-    const float r1 = v - (float)b0;
-    const __bf16 b1 = (__bf16)r1;
-    const float r2 = r1 - (float)b1;
-    const __bf16 b2 = (__bf16)r2;
-    h0 = __builtin_bit_cast(uint16_t, b0);
-    h1 = __builtin_bit_cast(uint16_t, b1);
-    h2 = __builtin_bit_cast(uint16_t, b2);
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+// The parts of two consecutive k-values at once (one packed conversion per part); word q holds part q of
+// `lo` in its low half and of `hi` in its high half.
+__device__ inline void split3x2(float lo, float hi, uint32_t& w0, uint32_t& w1, uint32_t& w2) {
+    const f32x2_t v = {lo, hi};
+    const bf16x2_t b0 = __builtin_convertvector(v, bf16x2_t);
+    const f32x2_t r1 = v - __builtin_convertvector(b0, f32x2_t);
+    const bf16x2_t b1 = __builtin_convertvector(r1, bf16x2_t);
+    const f32x2_t r2 = r1 - __builtin_convertvector(b1, f32x2_t);
+    const bf16x2_t b2 = __builtin_convertvector(r2, bf16x2_t);
+    w0 = __builtin_bit_cast(uint32_t, b0);
+    w1 = __builtin_bit_cast(uint32_t, b1);
+    w2 = __builtin_bit_cast(uint32_t, b2);
 }
 
 template <int TM, int TN, int TK, bool TA, bool TB, bool FULL>
@@ -353,13 +358,11 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
         if constexpr (TA) {
             const int r = tid & 127, kq = tid >> 7;
             for (int ps = 0; ps < SA; ++ps) {
-                uint16_t h[3][8];
-                for (int e = 0; e < 8; ++e) split3(sa[ps][e] * sa_scale, h[0][e], h[1][e], h[2][e]);
-                for (int q = 0; q < 3; ++q) {
-                    u32x4 w = {(uint32_t)h[q][0] | ((uint32_t)h[q][1] << 16), (uint32_t)h[q][2] | ((uint32_t)h[q][3] << 16),
-                               (uint32_t)h[q][4] | ((uint32_t)h[q][5] << 16), (uint32_t)h[q][6] | ((uint32_t)h[q][7] << 16)};
-                    *reinterpret_cast<u32x4*>(&As[buf][q][128 * ps + r][8 * kq]) = w;
-                }
+                uint32_t w[3][4];
+                for (int e = 0; e < 4; ++e)
+                    split3x2(sa[ps][2 * e] * sa_scale, sa[ps][2 * e + 1] * sa_scale, w[0][e], w[1][e], w[2][e]);
+                for (int q = 0; q < 3; ++q)
+                    *reinterpret_cast<u32x4*>(&As[buf][q][128 * ps + r][8 * kq]) = u32x4{w[q][0], w[q][1], w[q][2], w[q][3]};
             }
         } else {
 #pragma unroll
@@ -373,12 +376,9 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
                         if (ke <= me) va[e] = 0.f;
                     }
                 }
-                uint16_t h[3][4];
-                for (int e = 0; e < 4; ++e) split3(va[e], h[0][e], h[1][e], h[2][e]);
-                for (int q = 0; q < 3; ++q) {
-                    u32x2 w = {(uint32_t)h[q][0] | ((uint32_t)h[q][1] << 16), (uint32_t)h[q][2] | ((uint32_t)h[q][3] << 16)};
-                    *reinterpret_cast<u32x2*>(&As[buf][q][mi][ki]) = w;
-                }
+                uint32_t w[3][2];
+                for (int e = 0; e < 2; ++e) split3x2(va[2 * e], va[2 * e + 1], w[0][e], w[1][e], w[2][e]);
+                for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x2*>(&As[buf][q][mi][ki]) = u32x2{w[q][0], w[q][1]};
             }
         }
         if constexpr (TB) {
@@ -387,23 +387,17 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
                 int ni, ki;
                 io.b_pos(i, tid, ni, ki);
                 const f32x4 vb = io.b[i];
-                uint16_t h[3][4];
-                for (int e = 0; e < 4; ++e) split3(vb[e], h[0][e], h[1][e], h[2][e]);
-                for (int q = 0; q < 3; ++q) {
-                    u32x2 w = {(uint32_t)h[q][0] | ((uint32_t)h[q][1] << 16), (uint32_t)h[q][2] | ((uint32_t)h[q][3] << 16)};
-                    *reinterpret_cast<u32x2*>(&Bs[buf][q][ni][ki]) = w;
-                }
+                uint32_t w[3][2];
+                for (int e = 0; e < 2; ++e) split3x2(vb[2 * e], vb[2 * e + 1], w[0][e], w[1][e], w[2][e]);
+                for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x2*>(&Bs[buf][q][ni][ki]) = u32x2{w[q][0], w[q][1]};
             }
         } else {
             const int r = tid & 127, kq = tid >> 7;
             for (int ps = 0; ps < SB; ++ps) {
-                uint16_t h[3][8];
-                for (int e = 0; e < 8; ++e) split3(sb[ps][e], h[0][e], h[1][e], h[2][e]);
-                for (int q = 0; q < 3; ++q) {
-                    u32x4 w = {(uint32_t)h[q][0] | ((uint32_t)h[q][1] << 16), (uint32_t)h[q][2] | ((uint32_t)h[q][3] << 16),
-                               (uint32_t)h[q][4] | ((uint32_t)h[q][5] << 16), (uint32_t)h[q][6] | ((uint32_t)h[q][7] << 16)};
-                    *reinterpret_cast<u32x4*>(&Bs[buf][q][128 * ps + r][8 * kq]) = w;
-                }
+                uint32_t w[3][4];
+                for (int e = 0; e < 4; ++e) split3x2(sb[ps][2 * e], sb[ps][2 * e + 1], w[0][e], w[1][e], w[2][e]);
+                for (int q = 0; q < 3; ++q)
+                    *reinterpret_cast<u32x4*>(&Bs[buf][q][128 * ps + r][8 * kq]) = u32x4{w[q][0], w[q][1], w[q][2], w[q][3]};
             }
         }
     };
