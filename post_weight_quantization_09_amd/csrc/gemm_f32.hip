@@ -371,10 +371,9 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
                 io.a_pos(i, tid, mi, ki);
                 f32x4 va = io.a[i] * io.a_scale;
                 if (io.a_mask) {
-                    for (int e = 0; e < 4; ++e) {
-                        const int64_t me = io.am0 + mi, ke = io.ak0 + ki + e;
-                        if (ke <= me) va[e] = 0.f;
-                    }
+                    const int d = (int)(io.ak0 - io.am0) + ki - mi;   // k - m of element 0 (|k - m| < 2^31)
+                    for (int e = 0; e < 4; ++e)
+                        if (d + e <= 0) va[e] = 0.f;
                 }
                 uint32_t w[3][2];
                 for (int e = 0; e < 2; ++e) split3x2(va[2 * e], va[2 * e + 1], w[0][e], w[1][e], w[2][e]);
