@@ -320,24 +320,23 @@ struct Recursion {
             g.flags = kGemmBLower;
             if (gemm(g, strideH, strideH, Ts) != hipSuccess) return GPTQ_ERR_HIP;
         }
-        {   // H11 -= R12 R12^T on the upper triangle
-            GemmArgs g;
-            g.M = n1; g.N = n1; g.K1 = n2;
-            g.A1 = R12; g.lda1 = n2;
-            g.B1 = R12; g.ldb1 = n2; g.transB = true;
-            g.C = D; g.ldc = K;
-            g.alpha = -1.f; g.beta = 1.f;
-            g.flags = kGemmCUpper;
-            if (gemm(g, Ts, Ts, strideH) != hipSuccess) return GPTQ_ERR_HIP;
-        }
-        {   // X = R12 U22
-            GemmArgs g;
-            g.M = n1; g.N = n2; g.K1 = n2;
-            g.A1 = R12; g.lda1 = n2;
-            g.B1 = D22; g.ldb1 = K;
-            g.C = X; g.ldc = n2;
-            g.flags = kGemmBUpper;
-            if (gemm(g, Ts, strideH, Ts) != hipSuccess) return GPTQ_ERR_HIP;
+        {   // H11 -= R12 R12^T on the upper triangle, and X = R12 U22: independent, one launch where both fit it
+            GemmArgs s;
+            s.M = n1; s.N = n1; s.K1 = n2;
+            s.A1 = R12; s.lda1 = n2;
+            s.B1 = R12; s.ldb1 = n2; s.transB = true;
+            s.C = D; s.ldc = K;
+            s.alpha = -1.f; s.beta = 1.f;
+            s.flags = kGemmCUpper;
+            s.strideA1 = Ts; s.strideB1 = Ts; s.strideC = strideH;
+            GemmArgs x;
+            x.M = n1; x.N = n2; x.K1 = n2;
+            x.A1 = R12; x.lda1 = n2;
+            x.B1 = D22; x.ldb1 = K;
+            x.C = X; x.ldc = n2;
+            x.flags = kGemmBUpper;
+            x.strideA1 = Ts; x.strideB1 = strideH; x.strideC = Ts;
+            if (gemm_f32_pair(s, x, batch, stream) != hipSuccess) return GPTQ_ERR_HIP;
         }
         r = run(o, n1, T + n1 * n2);
         if (r != GPTQ_OK) return r;

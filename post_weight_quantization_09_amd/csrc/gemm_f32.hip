@@ -140,28 +140,27 @@ struct TileIO {
     }
 };
 
+// One output tile of a product: block (bx, by) of a gx x gy tile grid, batch element bz, with the workgroup's
+// LDS tiles passed in.
 template <int TM, int TN, int TK, bool TA, bool TB, bool FULL>
-__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
+__device__ __forceinline__ void gemm_f32_tile(const GemmArgs& p, int64_t bx, int64_t by, int64_t gx, int64_t gy,
+                                              int64_t bz, float (*As)[TK][TM + kPad], float (*Bs)[TK][TN + kPad]) {
     using T = Tile<TM, TN, TK>;
-    __shared__ __attribute__((aligned(16))) float As[2][TK][TM + kPad];
-    __shared__ __attribute__((aligned(16))) float Bs[2][TK][TN + kPad];
-
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
     // Tile order.  With a triangular B the work of a tile depends on its column only (k from n0 for B lower, up
     // to n0 + TN for B upper): tiles are dispatched column by column, heaviest column first, so that the last
     // workgroups to start are the shortest (25-35% faster than row order on these products).
-    int64_t tx = blockIdx.x, ty = blockIdx.y;
+    int64_t tx = bx, ty = by;
     if (p.flags & (kGemmBLower | kGemmBUpper)) {
-        const int64_t id = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-        tx = id / gridDim.y;
-        ty = id % gridDim.y;
-        if (p.flags & kGemmBUpper) tx = gridDim.x - 1 - tx;
+        const int64_t id = by * gx + bx;
+        tx = id / gy;
+        ty = id % gy;
+        if (p.flags & kGemmBUpper) tx = gx - 1 - tx;
     }
     const int64_t m0 = ty * TM;
     const int64_t n0 = tx * TN;
-    const int64_t bz = blockIdx.z;
     if (m0 >= p.M || n0 >= p.N) return;
     if ((p.flags & kGemmCUpper) && m0 >= n0 + TN) return;
 
@@ -247,6 +246,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
                 *cp = v;
             }
         }
+    }
+}
+
+template <int TM, int TN, int TK, bool TA, bool TB, bool FULL>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
+    __shared__ __attribute__((aligned(16))) float As[2][TK][TM + kPad];
+    __shared__ __attribute__((aligned(16))) float Bs[2][TK][TN + kPad];
+    gemm_f32_tile<TM, TN, TK, TA, TB, FULL>(p, blockIdx.x, blockIdx.y, gridDim.x, gridDim.y, blockIdx.z, As, Bs);
+}
+
+// Two independent products in one launch (64 x 64 tiles): the first gx1 * gy1 workgroups of each batch element
+// take the tiles of p1 (B transposed), the rest those of p2 (neither transposed).  Each tile is computed
+// exactly as by gemm_f32_kernel.
+template <bool FULL1, bool FULL2>
+__global__ __launch_bounds__(256) void gemm_f32_pair_kernel(GemmArgs p1, GemmArgs p2, int gx1, int gy1, int gx2,
+                                                            int gy2) {
+    __shared__ __attribute__((aligned(16))) float As[2][16][64 + kPad];
+    __shared__ __attribute__((aligned(16))) float Bs[2][16][64 + kPad];
+    const int64_t id = blockIdx.x, n1 = (int64_t)gx1 * gy1;
+    if (id < n1) {
+        gemm_f32_tile<64, 64, 16, false, true, FULL1>(p1, id % gx1, id / gx1, gx1, gy1, blockIdx.z, As, Bs);
+    } else {
+        const int64_t j = id - n1;
+        gemm_f32_tile<64, 64, 16, false, false, FULL2>(p2, j % gx2, j / gx2, gx2, gy2, blockIdx.z, As, Bs);
     }
 }
 
@@ -473,13 +496,17 @@ hipError_t launch_x6(const GemmArgs& p, int64_t batch, hipStream_t stream) {
 inline bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
 
 
+// Whole tiles only, every operand 16-byte vectorisable: no per-element guards in the k-loop.
+bool full_tiles(const GemmArgs& p, int TM, int TN, int TK) {
+    return p.M % TM == 0 && p.N % TN == 0 && p.K1 % TK == 0 && p.vecA1 && p.vecB1 &&
+           (!p.A2 || (p.K2 % TK == 0 && p.vecA2 && p.vecB2));
+}
+
 template <int TM, int TN, int TK>
 hipError_t launch(const GemmArgs& p, int64_t batch, hipStream_t stream) {
     dim3 grid((unsigned)ceil_div(p.N, TN), (unsigned)ceil_div(p.M, TM), (unsigned)batch);
     if (grid.y > 65535u || grid.z > 65535u) return hipErrorInvalidValue;
-    // Whole tiles only, every operand 16-byte vectorisable: no per-element guards in the k-loop.
-    const bool full = p.M % TM == 0 && p.N % TN == 0 && p.K1 % TK == 0 && p.vecA1 && p.vecB1 &&
-                      (!p.A2 || (p.K2 % TK == 0 && p.vecA2 && p.vecB2));
+    const bool full = full_tiles(p, TM, TN, TK);
 #define GPTQ_GEMM_LAUNCH(TA_, TB_)                                                                          \
     if (full) hipLaunchKernelGGL((gemm_f32_kernel<TM, TN, TK, TA_, TB_, true>), grid, dim3(256), 0, stream, p); \
     else hipLaunchKernelGGL((gemm_f32_kernel<TM, TN, TK, TA_, TB_, false>), grid, dim3(256), 0, stream, p);
@@ -491,12 +518,9 @@ hipError_t launch(const GemmArgs& p, int64_t batch, hipStream_t stream) {
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t gemm_f32(GemmArgs p, int64_t batch, hipStream_t stream) {
-    if (p.M <= 0 || p.N <= 0 || batch <= 0) return hipSuccess;
-    // 16-byte vector loads need an aligned base, a leading dimension (and batch stride) that is a multiple
-    // of 4 floats; otherwise the tile loads fall back to scalar accesses.
+// 16-byte vector loads need an aligned base, a leading dimension (and batch stride) that is a multiple of 4
+// floats; otherwise the tile loads fall back to scalar accesses.
+void set_vector_flags(GemmArgs& p, int64_t batch) {
     auto vec_ok = [&](const float* ptr, int64_t ld, int64_t stride) {
         return ptr && aligned16(ptr) && ld % 4 == 0 && (batch == 1 || stride % 4 == 0);
     };
@@ -504,6 +528,18 @@ hipError_t gemm_f32(GemmArgs p, int64_t batch, hipStream_t stream) {
     p.vecB1 = vec_ok(p.B1, p.ldb1, p.strideB1);
     p.vecA2 = vec_ok(p.A2, p.lda2, p.strideA2);
     p.vecB2 = vec_ok(p.B2, p.ldb2, p.strideB2);
+}
+
+bool use_split_bf16(const GemmArgs& p) {
+    const int64_t tiles128 = ceil_div(p.M, 128) * ceil_div(p.N, 128);
+    return p.K1 >= 1024 && p.M >= 1024 && p.N >= 1024 && tiles128 >= 512;
+}
+
+}  // namespace
+
+hipError_t gemm_f32(GemmArgs p, int64_t batch, hipStream_t stream) {
+    if (p.M <= 0 || p.N <= 0 || batch <= 0) return hipSuccess;
+    set_vector_flags(p, batch);
     // Tile shape, measured on gfx950 (random data): 64 x 64 matches 128 x 128 on general products up to ~7k and
     // beats it on the depth-128 trailing updates and on small products (more workgroups in flight); from about
     // 12k x 12k outputs on, 128 x 128 is faster (half the L2 traffic per flop: +20% at 14336).  Triangular
@@ -514,9 +550,30 @@ hipError_t gemm_f32(GemmArgs p, int64_t batch, hipStream_t stream) {
     // updates; equal at 256 tiles, slower on the 2048 squares and at depth <= 512 (per-stage overhead).  The choice
     // depends on one batch element's shape only, so a batched call (all output-channel groups at once) does the
     // same arithmetic as one call per element, bit for bit.
-    const int64_t tiles128 = ceil_div(p.M, 128) * ceil_div(p.N, 128);
-    if (p.K1 >= 1024 && p.M >= 1024 && p.N >= 1024 && tiles128 >= 512) return launch_x6<128, 128>(p, batch, stream);
+    if (use_split_bf16(p)) return launch_x6<128, 128>(p, batch, stream);
     return launch<64, 64, 16>(p, batch, stream);
+}
+
+hipError_t gemm_f32_pair(GemmArgs a, GemmArgs b, int64_t batch, hipStream_t stream) {
+    if (batch <= 0) return hipSuccess;
+    const bool pairable = a.M > 0 && a.N > 0 && b.M > 0 && b.N > 0 && !use_split_bf16(a) && !use_split_bf16(b) &&
+                          !a.transA && a.transB && !b.transA && !b.transB && batch <= 65535;
+    const int64_t gx1 = ceil_div(a.N, 64), gy1 = ceil_div(a.M, 64), gx2 = ceil_div(b.N, 64), gy2 = ceil_div(b.M, 64);
+    const int64_t n = gx1 * gy1 + gx2 * gy2;
+    if (!pairable || n > 0x7fffffff) {
+        const hipError_t e = gemm_f32(a, batch, stream);
+        return e != hipSuccess ? e : gemm_f32(b, batch, stream);
+    }
+    set_vector_flags(a, batch);
+    set_vector_flags(b, batch);
+    const bool f1 = full_tiles(a, 64, 64, 16), f2 = full_tiles(b, 64, 64, 16);
+    const dim3 grid((unsigned)n, 1, (unsigned)batch);
+    const int g[4] = {(int)gx1, (int)gy1, (int)gx2, (int)gy2};
+    if (f1 && f2) hipLaunchKernelGGL((gemm_f32_pair_kernel<true, true>), grid, dim3(256), 0, stream, a, b, g[0], g[1], g[2], g[3]);
+    else if (f1) hipLaunchKernelGGL((gemm_f32_pair_kernel<true, false>), grid, dim3(256), 0, stream, a, b, g[0], g[1], g[2], g[3]);
+    else if (f2) hipLaunchKernelGGL((gemm_f32_pair_kernel<false, true>), grid, dim3(256), 0, stream, a, b, g[0], g[1], g[2], g[3]);
+    else hipLaunchKernelGGL((gemm_f32_pair_kernel<false, false>), grid, dim3(256), 0, stream, a, b, g[0], g[1], g[2], g[3]);
+    return hipGetLastError();
 }
 
 }  // namespace gptq

@@ -35,4 +35,8 @@ struct GemmArgs {
 
 hipError_t gemm_f32(GemmArgs p, int64_t batch, hipStream_t stream);
 
+// Two independent products, each exactly as gemm_f32 computes it: one launch when both run on the 64 x 64 fp32
+// kernel with B transposed in `a` only (the recursion's SYRK and its X = R12 U22), otherwise two launches.
+hipError_t gemm_f32_pair(GemmArgs a, GemmArgs b, int64_t batch, hipStream_t stream);
+
 }  // namespace gptq
