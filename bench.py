@@ -6,10 +6,12 @@ in HBM:  H = 0;  H += 2 X^T X over all M tokens (gptq_accumulate_hessian);  dead
 Output groups (G2PTQ-style workloads): one Gram per group, then the groups' factorisations and column loops
 together (gptq_prepare_groups, gptq_quantize_layer_groups).
 
-Prints one JSON line: layer time (ms, lower is better) plus the Gram's MFMA roofline fraction and the float64
-oracle timed on a bounded sample of the same workload on the host cores.
+Prints one JSON line: layer time (ms, lower is better) plus the Gram's MFMA roofline fraction, the trailing
+products' fp32 MFMA fraction and the column loop's HBM fraction, and the float64 oracle timed on a bounded sample
+of the same workload on the host cores.  The default workload is the largest that fits one GPU: the 70B-shaped
+down_proj layer (K = 28672, N = 8192, 524,288 calibration tokens).
 
-    python bench.py [--gpus 1] [--steps 5] [--warmup 1] [--config c2_q_proj_8b] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 5] [--warmup 1] [--config c5_down_proj_70b] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -56,6 +58,18 @@ def trailing_flops(cfg) -> float:
     return f * (2 if cfg.asym_noise > 0 else 1)
 
 
+def loop_bytes(cfg) -> float:
+    """Algorithmic HBM bytes of the column loop (every block kernel of one layer): the working weights read and
+    written once in fp32 (8 bytes per coordinate and channel), the codes written (1 byte); 4 more bytes per
+    coordinate and channel for the pre-rounding values the asymmetric term keeps."""
+    return (13.0 if cfg.asym_noise > 0 else 9.0) * cfg.K * cfg.N
+
+
+def factor_flops(cfg) -> float:
+    """Cholesky factorisation plus triangular inverse: 2 K^3 / 3 per Hessian (x groups)."""
+    return 2.0 * cfg.K ** 3 / 3.0 * cfg.groups
+
+
 def source_hash(*names) -> str:
     """Hash of the code of the named sources (line comments and blank lines dropped, so that a comment edit
     does not disown the traffic measured on the same kernel)."""
@@ -69,14 +83,15 @@ def source_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, src_hash: str):
-    """HBM bytes per launch from committed rocprofv3 --pmc summaries, if taken on the current source."""
-    p = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+def measured_traffic(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary of this kernel on this workload, if it was
+    taken on the current source (else None)."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("source_hash") != src_hash:
+    if d.get("source_hash") != src_hash or d.get("workload") != workload:
         return None
     return d.get("bytes_per_launch")
 
@@ -118,7 +133,7 @@ class Layer:
                                   dtype=torch.uint8, device=dev)
         self.ev = []
 
-    def step(self, record: bool):
+    def step(self, record: bool, sync_prepare: bool = False):
         """One pass of the hot path; with record=True returns HIP events (current stream) at the starts and ends of
         the three stages: every group's Gram, the factorisation(s), every group's column loop."""
         cfg = self.cfg
@@ -139,28 +154,35 @@ class Layer:
             rs = self.rho[gi].contiguous() if self.rho is not None else None
             G.gptq_accumulate_hessian(Hg, self.X, row_scale=rs, X_float=self.Xf, A=self.A, workspace=self.ws)
         mark()
+        # stream-ordered unless sync_prepare (then damping and dead counts come back to the host, one
+        # synchronisation after the factorisation); device errors are read from the latch after the timed steps
         if cfg.groups == 1:
-            d, damp, nd = G.gptq_prepare(self.H, cfg.percdamp, dead=self.dead, workspace=self.ws)
+            d, damp, nd = G.gptq_prepare(self.H, cfg.percdamp, dead=self.dead, workspace=self.ws, sync=sync_prepare)
             self.damps, self.n_deads = [damp], [nd]
         else:   # the groups' Hessians factorised together, every step one launch over all groups
             _, self.damps, self.n_deads = G.gptq_prepare_groups(self.Hs, cfg.percdamp, dead=self.deads,
-                                                               workspace=self.ws)
+                                                               workspace=self.ws, sync=sync_prepare)
         P1 = None
         if self.A is not None:
             P1 = G.gptq_asym_correction(self.H, self.A, self.P1, workspace=self.ws)
         mark()
+        # stream-ordered: no host synchronisation; the latched status is read after the timed steps
         if cfg.groups == 1:
             G.gptq_quantize_layer(self.W, self.H, cfg.bits, dead=self.dead, P1=P1, blocksize=cfg.blocksize,
-                                  scales=None, codes=self.codes, losses=None, workspace=self.ws)
+                                  scales=None, codes=self.codes, losses=None, workspace=self.ws, check=False)
         else:   # every group's column loop in the same launches
             G.gptq_quantize_layer_groups(self.W, self.Hs, cfg.bits, dead=self.deads, blocksize=cfg.blocksize,
-                                         scales=None, codes=self.codes, losses=None, workspace=self.ws)
+                                         scales=None, codes=self.codes, losses=None, workspace=self.ws,
+                                         check=False)
         mark()
         return evs
 
 
-def cpu_baseline(layer: Layer, budget_s: float = 20.0) -> dict:
-    """The float64 oracle on a bounded sample of the same workload, projected to the full layer."""
+def cpu_baseline(layer: Layer) -> dict:
+    """The float64 oracle on a bounded sample of the same workload (about 10-20 s of host time), projected to the
+    full layer: the Gram on Ms tokens of all K features (scaled by M / Ms); prepare on the leading Ks x Ks block of
+    that Hessian (scaled by (K / Ks)^3); the blocked loop on Ks coordinates x Ns channels with that factor (scaled
+    by (K / Ks)^2 x gs / Ns).  Per output-channel group, times the groups."""
     import oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -169,28 +191,70 @@ def cpu_baseline(layer: Layer, budget_s: float = 20.0) -> dict:
         threads = os.cpu_count()
     cfg = layer.cfg
     cores = len(os.sched_getaffinity(0))
-    Ms = min(cfg.M, 8192 if cfg.K > 8192 else 16384)
+    Ms = min(cfg.M, max(1024, (16384 * 4096 * 4096) // (cfg.K * cfg.K) // 1024 * 1024))
+    Ks = min(cfg.K, 4096)
     Xs = layer.X[:Ms].float().cpu().numpy()
     t0 = time.perf_counter()
     H = O.gram([Xs])
     if layer.Xf is not None:
         O.cross_gram(layer.Xf[:Ms].float().cpu().numpy(), Xs)
     t_gram = (time.perf_counter() - t0) * (cfg.M / Ms)
+    Hk = H[:Ks, :Ks]
+    del H
     t0 = time.perf_counter()
-    prep = O.prepare(H, cfg.percdamp)
-    t_prep = time.perf_counter() - t0
+    prep = O.prepare(Hk, cfg.percdamp)
+    t_prep = (time.perf_counter() - t0) * (cfg.K / Ks) ** 3
     Ns = min(layer.gs, 128)
-    Wsub = layer.W[:, :Ns].float().cpu().numpy()
+    Wsub = layer.W[:Ks, :Ns].float().cpu().numpy()
     t0 = time.perf_counter()
     O.quantize_layer(Wsub, prep["U"], cfg.bits, dead=prep["dead"], blocksize=cfg.blocksize)
-    t_loop = (time.perf_counter() - t0) * (layer.gs / Ns)
+    t_loop = (time.perf_counter() - t0) * (cfg.K / Ks) ** 2 * (layer.gs / Ns)
     per_group = t_gram + t_prep + t_loop
     total_ms = 1e3 * per_group * cfg.groups
     return {"value": round(total_ms, 1), "unit": "ms", "cores": int(min(cores, threads or cores)), "kind": "oracle",
-            "sample": f"float64 numpy/BLAS oracle: Gram on {Ms} of {cfg.M} tokens (scaled x{cfg.M / Ms:.0f}), full "
-                      f"{cfg.K}x{cfg.K} prepare, blocked loop on {Ns} of {layer.gs} channels (scaled); "
-                      f"stage seconds gram={t_gram:.1f} prepare={t_prep:.1f} loop={t_loop:.1f} per group",
+            "sample": f"float64 numpy/BLAS oracle on a bounded sample, projected: Gram on {Ms} of {cfg.M} tokens x "
+                      f"{cfg.K} features (x{cfg.M / Ms:.0f}); prepare on the leading {Ks}x{Ks} block "
+                      f"(x(K/{Ks})^3); blocked loop on {Ks} coordinates x {Ns} of {layer.gs} channels "
+                      f"(x(K/{Ks})^2 x {layer.gs / Ns:.0f}); projected stage seconds gram={t_gram:.1f} "
+                      f"prepare={t_prep:.1f} loop={t_loop:.1f} per group, x{cfg.groups} groups",
             "host_cores_visible": cores}
+
+
+def kernel_breakdown(layer: Layer) -> dict:
+    """One more step of the path with the library's kernel timer on (HIP events around every launch, on the
+    stream the kernel runs on): GPU time per kernel class, and the rates of the classes the metric names."""
+    cfg = layer.cfg
+    G.gptq_timer_enable(True)
+    try:
+        layer.step(record=False)
+        t = G.gptq_timer_read()
+    finally:
+        G.gptq_timer_enable(False)
+    ms = {k: round(v[0], 3) for k, v in t.items()}
+    launches = {k: v[1] for k, v in t.items()}
+    tf = trailing_flops(cfg)
+    lb = loop_bytes(cfg)
+    ff = factor_flops(cfg)
+    loop_ms, tr_ms = t["loop"][0], t["trailing"][0]
+    steps = cfg.K   # dependent coordinate steps of every channel (the loop's latency chain)
+    out = {
+        "ms": ms, "launches": launches,
+        "trailing_gemm": {"ms": round(tr_ms, 3), "flop": tf,
+                          "TFLOP/s": round(tf / (tr_ms * 1e-3) / 1e12, 1) if tr_ms > 0 else None,
+                          "peak": PEAK_FP32_MFMA_TFLOPS,
+                          "frac": round(tf / (tr_ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4) if tr_ms > 0 else None,
+                          "floor_ms": round(tf / (PEAK_FP32_MFMA_TFLOPS * 1e12) * 1e3, 3)},
+        "column_loop": {"ms": round(loop_ms, 3), "bytes": lb,
+                        "GB/s": round(lb / (loop_ms * 1e-3) / 1e9, 1) if loop_ms > 0 else None,
+                        "peak": PEAK_HBM_GBS,
+                        "frac": round(lb / (loop_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if loop_ms > 0 else None,
+                        "hbm_floor_ms": round(lb / (PEAK_HBM_GBS * 1e9) * 1e3, 3),
+                        "ns_per_step": round(loop_ms * 1e6 / steps, 1) if loop_ms > 0 else None},
+        "factorisation": {"ms": round(t["factor_diag"][0] + t["factor_gemm"][0], 3), "flop": ff,
+                          "TFLOP/s": round(ff / ((t["factor_diag"][0] + t["factor_gemm"][0]) * 1e-3) / 1e12, 1)
+                          if t["factor_gemm"][0] > 0 else None},
+    }
+    return out
 
 
 def _time_ms(fn, reps: int = 3) -> float:
@@ -218,7 +282,8 @@ def extras(layer: "Layer") -> dict:
 
     def quant(cae):
         return lambda: G.gptq_quantize_layer(Wg, layer.H, cfg.bits, dead=layer.dead, P1=layer.P1 if layer.A is not None
-                                             else None, codes=layer.codes[:, sl], workspace=layer.ws_cae, cae=cae)
+                                             else None, codes=layer.codes[:, sl], workspace=layer.ws_cae, cae=cae,
+                                             check=False)
     q_plain = _time_ms(quant(False))
     q_cae = _time_ms(quant(True))
     out["cae_term"] = {"quantize_ms": round(q_cae, 3), "quantize_ms_without": round(q_plain, 3),
@@ -230,9 +295,9 @@ def extras(layer: "Layer") -> dict:
     perm = G.gptq_act_order(Hc, workspace=ws_ao)
     t_ao = _time_ms(lambda: G.gptq_act_order(Hc, perm=perm, workspace=ws_ao))
     q_grp = _time_ms(lambda: G.gptq_quantize_layer(Wg, layer.H, cfg.bits, dead=layer.dead, codes=layer.codes[:, sl],
-                                                   workspace=layer.ws_cae, perm=perm, groupsize=128))
+                                                   workspace=layer.ws_cae, perm=perm, groupsize=128, check=False))
     q_mse = _time_ms(lambda: G.gptq_quantize_layer(Wg, layer.H, cfg.bits, dead=layer.dead, codes=layer.codes[:, sl],
-                                                   workspace=layer.ws_cae, mse=True))
+                                                   workspace=layer.ws_cae, mse=True, check=False))
     out["act_order"] = {"ms": round(t_ao, 3), "K": cfg.K}
     out["quantize_act_order_groups128_ms"] = round(q_grp, 3)
     out["quantize_mse_clipped_ms"] = round(q_mse, 3)
@@ -261,7 +326,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", default="c2_q_proj_8b", choices=sorted(workloads.CONFIGS))
+    ap.add_argument("--config", default="c5_down_proj_70b", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the timings of the rows beyond the layer path")
     ap.add_argument("--only", choices=["gram", "copy", "hadamard"], default=None,
@@ -312,6 +377,9 @@ def main():
         log(f"timed step {i} enqueued/done")
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    status = G.gptq_device_status(layer.ws)   # the latched device status of the last step's calls
+    if status != G.GPTQ_OK:
+        raise G.GptqError(status, "bench step")
     for e in ev_all:
         stage["gram"] += e[0].elapsed_time(e[1])
         stage["prepare"] += e[1].elapsed_time(e[2])
@@ -323,7 +391,7 @@ def main():
     gram_launch_ms = stage["gram"] / cfg.groups
     achieved = gram_flops(cfg) / (gram_launch_ms * 1e-3) / 1e12
     src = source_hash("gram.hip")
-    traffic = measured_traffic("gram_bf16", src)
+    traffic = measured_traffic("gram_bf16", cfg.name, src)
     out = {
         "metric": "layer quantize time (ms) + Gram/trailing TFLOP/s vs MFMA peak, KxN layer",
         "value": round(ms, 3),
@@ -343,12 +411,13 @@ def main():
                    "dead_frac": cfg.dead_frac},
         "stages_ms": {k: round(v, 3) for k, v in stage.items()},
         "gram_tflops": round(gflop / (stage["gram"] * 1e-3) / 1e12, 1),
-        "trailing_gemm_gflop": round(trailing_flops(cfg) * 1e-9, 1),
         "roofline": {"bound": "mfma", "kernel": "gram_bf16_lds_kernel + gram_reduce_kernel (one accumulate call)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flop_per_launch": gram_flops(cfg), "launch_ms": round(gram_launch_ms, 3)},
     }
+    log("kernel classes: one more step with the kernel timer on ...")
+    out["kernels"] = kernel_breakdown(layer)
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(layer)

@@ -24,12 +24,19 @@
  *   - Layout follows [T]: X is M x K (tokens x input features), W is K x N (input features x output
  *     channels).  Matrices are row-major with an explicit leading dimension unless strides are given.
  *   - Every pointer named as "device" must point to device memory (hipMalloc / a torch CUDA tensor) of the
- *     current HIP device.  The caller owns every buffer; the library never allocates or frees memory and
- *     keeps no state between calls.  Scratch memory is passed in as `workspace` (device, 256-byte aligned,
+ *     current HIP device.  The caller owns every buffer; the library never allocates or frees device memory
+ *     and keeps no state between calls (the optional kernel timer below aside).  Scratch memory is passed in as `workspace` (device, 256-byte aligned,
  *     size from gptq_workspace_bytes); its contents need not be initialised and are clobbered.
- *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued on it in order.  Calls return
- *     after enqueueing, except gptq_prepare and gptq_quantize_layer, which synchronise `stream` at their end
- *     to report device-detected errors (non-positive pivot, non-finite input).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued on it in order and every call
+ *     returns after enqueueing, so a caller can queue the layers of a model back to back on one stream.  The
+ *     one exception is gptq_prepare(_groups) asked for its host-side outputs (damp_out, n_dead_out), which
+ *     synchronises `stream` to fill them.
+ *   - Errors found on the device (a non-finite input, a non-positive pivot) are latched in a status word at
+ *     the head of `workspace`: gptq_prepare(_groups) and gptq_quantize_layer(_groups) clear it when their work
+ *     starts on the stream and set bits in it as their kernels find problems; the kernels of the same call
+ *     skip their remaining work once it is set.  gptq_device_status reads it (after synchronising `stream`).
+ *     This follows the refusal convention of the worked 2-D check of [T] section 7: non-finite values and
+ *     non-positive pivots are reported as errors, never repaired.
  *   - Arguments are validated on the host before any HIP call; an invalid call returns GPTQ_ERR_ARG and
  *     enqueues nothing.  No input is ever silently repaired, except by the two documented rules of [T]
  *     section 6: dead coordinates and damping.
@@ -116,6 +123,16 @@ gptq_status_t gptq_accumulate_hessian(float* H, int64_t K,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gptq_gram_plan - how gptq_accumulate_hessian splits its work for K features and M tokens (host-side query; no
+ * device work).  out[0] = 256-column blocks nb, out[1] = 256 x 256 tiles (nb (nb + 1) / 2 upper tiles, or nb^2 for
+ * the cross term), out[2] = token splits, out[3] = tokens per split (a multiple of 32), out[4] = floats of split
+ * partials the launch writes (splits x tiles x 65536), out[5] = bf16 elements of staging for a transformed
+ * operand (0 if the operand is not staged).  cross: 0 symmetric, 1 cross term; transformed: 1 if row_scale or
+ * X_float is given.  Errors: GPTQ_ERR_ARG (K < 1, M < 0, out NULL).
+ */
+gptq_status_t gptq_gram_plan(int64_t K, int64_t M, int cross, int transformed, int64_t* out);
+
+/*
  * gptq_prepare - in place H -> U ([T] sections 4 and 6).
  *   1. dead coordinates: every k with H_kk == 0 gets H_kk := 1 and dead[k] = 1 (else 0);
  *   2. damping: damp = percdamp * mean_k(H_kk) (after step 1), H_d = H + damp * I;
@@ -130,9 +147,11 @@ gptq_status_t gptq_accumulate_hessian(float* H, int64_t K,
  *   damp_out   NULL or host float*: receives damp.   n_dead_out: NULL or host int64_t*: number of dead.
  *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_PREPARE, K, 0, 0, 0) (N counts the Hessians of
  *              gptq_prepare_groups; 0 or 1 here).
- * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_NONFINITE (non-finite diagonal or pivot),
- * GPTQ_ERR_NOT_PD (a pivot <= 0; the contents of H_to_U are then unspecified), GPTQ_ERR_HIP.
- * Synchronises `stream` before returning.
+ * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP on return.  The device-side errors GPTQ_ERR_NONFINITE
+ * (non-finite diagonal or pivot) and GPTQ_ERR_NOT_PD (a pivot <= 0; the contents of H_to_U are then unspecified)
+ * are latched in the workspace status word.  If damp_out or n_dead_out is given, the call synchronises `stream`,
+ * fills them and returns the latched status as well; with both NULL it returns after enqueueing, and the status
+ * is read with gptq_device_status(workspace, stream).
  */
 gptq_status_t gptq_prepare(float* H_to_U, int64_t K, float percdamp,
                            uint8_t* dead, float* damp_out, int64_t* n_dead_out,
@@ -153,7 +172,8 @@ gptq_status_t gptq_prepare(float* H_to_U, int64_t K, float percdamp,
  *   damp_out      NULL or host float[groups].   n_dead_out: NULL or host int64_t[groups].
  *   workspace     device scratch of gptq_workspace_bytes(GPTQ_CALL_PREPARE, K, groups, 0, 0).
  * Errors: as gptq_prepare; GPTQ_ERR_NONFINITE or GPTQ_ERR_NOT_PD if any group fails (damp_out and n_dead_out
- * are still written for every group).  Synchronises `stream` before returning.
+ * are still written for every group).  Synchronises `stream` only if damp_out or n_dead_out is given; the
+ * latched status of all groups together is read with gptq_device_status.
  */
 gptq_status_t gptq_prepare_groups(float* H_to_U, int64_t K, int64_t groups, int64_t group_stride, float percdamp,
                                   uint8_t* dead, float* damp_out, int64_t* n_dead_out,
@@ -240,8 +260,9 @@ gptq_status_t gptq_act_order(float* H, float* A, int64_t K, int32_t* perm, void*
  *              groups).
  *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, flags | (P1?2:0))
  *              (with GPTQ_FLAG_CAE it also holds a copy of the original weights, N x K fp32).
- * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_NONFINITE (NaN/Inf weight or given scale),
- * GPTQ_ERR_HIP.  Synchronises `stream` before returning.
+ * Errors: GPTQ_ERR_ARG, GPTQ_ERR_WORKSPACE, GPTQ_ERR_HIP on return (asynchronous: the call returns after
+ * enqueueing).  A NaN/Inf weight or given scale latches GPTQ_ERR_NONFINITE in the workspace status word (the
+ * loop is then skipped and the outputs are unspecified); read it with gptq_device_status.
  */
 gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K, int64_t N,
                                   int64_t w_rs, int64_t w_cs,
@@ -270,7 +291,7 @@ gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K
  *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, flags | (P1?2:0)),
  *              the same as one call over all N channels.
  *   All other arguments as for gptq_quantize_layer.
- * Errors: as gptq_quantize_layer.  Synchronises `stream` before returning.
+ * Errors: as gptq_quantize_layer (asynchronous; device-side errors through gptq_device_status).
  */
 gptq_status_t gptq_quantize_layer_groups(const void* W, gptq_dtype_t w_dtype, int64_t K, int64_t N,
                                          int64_t w_rs, int64_t w_cs, int64_t groups,
@@ -323,6 +344,46 @@ int64_t gptq_packed_words(int64_t K, int bits);
 gptq_status_t gptq_unpack_codes(const uint32_t* packed, int64_t ldp, int64_t K, int64_t N, int bits,
                                 const float* scales, uint8_t* codes, int64_t c_rs, int64_t c_cs,
                                 void* W_hat, gptq_dtype_t w_dtype, int64_t w_rs, int64_t w_cs, void* stream);
+
+/*
+ * gptq_device_status - the error latched on the device by the latest gptq_prepare, gptq_prepare_groups,
+ * gptq_quantize_layer or gptq_quantize_layer_groups call that used `workspace` (the refusal convention of [T]
+ * section 7: a non-finite input or a non-positive pivot is an error, reported and not repaired).
+ *
+ *   workspace  the device workspace given to that call (its 256-byte head holds the status word).
+ *   stream     the stream that call was enqueued on; it is synchronised before the word is read.
+ * Returns GPTQ_OK, GPTQ_ERR_NONFINITE or GPTQ_ERR_NOT_PD (the latter two as latched), GPTQ_ERR_ARG for a NULL
+ * or misaligned workspace, GPTQ_ERR_HIP if the synchronisation or the read fails.  Does not clear the word:
+ * the next latching call on the same workspace does.  Read it before reusing the workspace for such a call
+ * if both calls' errors matter.
+ */
+gptq_status_t gptq_device_status(const void* workspace, void* stream);
+
+/*
+ * Kernel timer: a measurement aid, off by default.  While it is on, every kernel launch of the library is
+ * bracketed by two HIP events on its stream and attributed to one class; gptq_timer_read synchronises the
+ * recorded events and returns the summed GPU time per class.  The timer is process-wide state of the library
+ * (events are created on first use and kept); enabling or disabling it drops unread records.  Event records
+ * add a few microseconds per launch, so timed runs leave it off.
+ */
+typedef enum {
+    GPTQ_TIMER_GRAM = 0,          /* Gram kernels (including the staging of a transformed operand) */
+    GPTQ_TIMER_GRAM_REDUCE = 1,   /* fixed-order sum of the token-split partials into H (or A) */
+    GPTQ_TIMER_FACTOR_DIAG = 2,   /* 128 x 128 diagonal blocks of the factorisation */
+    GPTQ_TIMER_FACTOR_GEMM = 3,   /* matrix products of the factorisation and of gptq_asym_correction */
+    GPTQ_TIMER_LOOP = 4,          /* the column-loop kernel (quantise and compensate inside a block) */
+    GPTQ_TIMER_TRAILING = 5,      /* lazy trailing products of the column loop */
+    GPTQ_TIMER_OTHER = 6,         /* everything else (conversions, scales, dead/damp, outputs, ...) */
+    GPTQ_TIMER_CLASSES = 7
+} gptq_timer_class_t;
+
+/* on != 0 turns the timer on, 0 off; either way unread records are dropped.  Errors: GPTQ_ERR_HIP. */
+gptq_status_t gptq_timer_enable(int on);
+
+/* ms[c] = summed GPU milliseconds and launches[c] (nullable) = launches of class c recorded since the last
+ * enable or read, for c < GPTQ_TIMER_CLASSES; clears the records.  Synchronises the recorded events.
+ * Errors: GPTQ_ERR_ARG (ms NULL), GPTQ_ERR_HIP. */
+gptq_status_t gptq_timer_read(double* ms, int64_t* launches);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* gptq_status_string(gptq_status_t status);

@@ -47,7 +47,13 @@ _SIGNATURES = {
     "gptq_pack_codes": (ctypes.c_int, [_ptr, _i64, _i64, _i64, _i64, ctypes.c_int, _ptr, _i64, _ptr]),
     "gptq_unpack_codes": (ctypes.c_int, [_ptr, _i64, _i64, _i64, ctypes.c_int, _ptr, _ptr, _i64, _i64, _ptr,
                                          ctypes.c_int, _i64, _i64, _ptr]),
+    "gptq_device_status": (ctypes.c_int, [_ptr, _ptr]),
+    "gptq_gram_plan": (ctypes.c_int, [_i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(_i64)]),
+    "gptq_timer_enable": (ctypes.c_int, [ctypes.c_int]),
+    "gptq_timer_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),
 }
+
+GPTQ_TIMER_CLASSES = ("gram", "gram_reduce", "factor_diag", "factor_gemm", "loop", "trailing", "other")
 
 _lib = None
 
@@ -137,6 +143,38 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+def gptq_device_status(workspace: torch.Tensor, stream=None, check: bool = False) -> int:
+    """Synchronises the stream and returns the status latched in `workspace` by the latest prepare / quantize call
+    that used it (GPTQ_OK, GPTQ_ERR_NONFINITE or GPTQ_ERR_NOT_PD); check=True raises GptqError instead of
+    returning an error status."""
+    st = load().gptq_device_status(_dptr(workspace), _stream(workspace.device, stream))
+    if check:
+        _check(st, "gptq_device_status")
+    return int(st)
+
+
+def gptq_gram_plan(K: int, M: int, cross: bool = False, transformed: bool = False) -> dict:
+    """How gptq_accumulate_hessian splits K features x M tokens (host-side query)."""
+    out = (_i64 * 6)()
+    _check(load().gptq_gram_plan(int(K), int(M), int(cross), int(transformed), out), "gptq_gram_plan")
+    keys = ("nb", "ntiles", "splits", "tokens_per_split", "partial_floats", "staging_elems")
+    return {k: int(out[i]) for i, k in enumerate(keys)}
+
+
+def gptq_timer_enable(on: bool = True) -> None:
+    """Turns the library's per-class kernel timer on or off (drops unread records)."""
+    _check(load().gptq_timer_enable(1 if on else 0), "gptq_timer_enable")
+
+
+def gptq_timer_read() -> dict:
+    """{class: (ms, launches)} for the launches recorded since the last enable or read."""
+    n = len(GPTQ_TIMER_CLASSES)
+    ms = (ctypes.c_double * n)()
+    cnt = (_i64 * n)()
+    _check(load().gptq_timer_read(ms, cnt), "gptq_timer_read")
+    return {c: (float(ms[i]), int(cnt[i])) for i, c in enumerate(GPTQ_TIMER_CLASSES)}
+
+
 def gptq_accumulate_hessian(H: torch.Tensor, X: torch.Tensor, row_scale: Optional[torch.Tensor] = None,
                             X_float: Optional[torch.Tensor] = None, A: Optional[torch.Tensor] = None,
                             workspace: Optional[torch.Tensor] = None, stream=None) -> None:
@@ -160,8 +198,9 @@ def gptq_accumulate_hessian(H: torch.Tensor, X: torch.Tensor, row_scale: Optiona
 
 
 def gptq_prepare(H: torch.Tensor, percdamp: float, dead: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None, stream=None):
-    """In place H -> U.  Returns (dead uint8[K], damp, n_dead)."""
+                 workspace: Optional[torch.Tensor] = None, stream=None, sync: bool = True):
+    """In place H -> U.  Returns (dead uint8[K], damp, n_dead).  sync=False passes no host outputs: the call then
+    returns after enqueueing with damp and n_dead None, and device errors are read with gptq_device_status."""
     K = H.shape[0]
     _square(H, "H")
     _contig(H, "H", torch.float32)
@@ -171,16 +210,18 @@ def gptq_prepare(H: torch.Tensor, percdamp: float, dead: Optional[torch.Tensor] 
     workspace, wp, wb = _workspace(GPTQ_CALL_PREPARE, K, 0, 0, 0, H.device, workspace)
     damp = _f32(0.0)
     n_dead = _i64(0)
-    st = load().gptq_prepare(_dptr(H), K, float(percdamp), _dptr(dead), ctypes.byref(damp), ctypes.byref(n_dead), wp,
-                             wb, _stream(H.device, stream))
+    st = load().gptq_prepare(_dptr(H), K, float(percdamp), _dptr(dead), ctypes.byref(damp) if sync else None,
+                             ctypes.byref(n_dead) if sync else None, wp, wb, _stream(H.device, stream))
     _check(st, "gptq_prepare")
+    if not sync:
+        return dead, None, None
     return dead, float(damp.value), int(n_dead.value)
 
 
 def gptq_prepare_groups(H: torch.Tensor, percdamp: float, dead: Optional[torch.Tensor] = None,
-                        workspace: Optional[torch.Tensor] = None, stream=None):
+                        workspace: Optional[torch.Tensor] = None, stream=None, sync: bool = True):
     """In place H[g] -> U[g] for every group g of H (groups x K x K, each K x K matrix contiguous).
-    Returns (dead uint8[groups, K], damps list, n_dead list)."""
+    Returns (dead uint8[groups, K], damps list, n_dead list); sync=False as for gptq_prepare (lists None)."""
     if H.dim() != 3 or H.shape[1] != H.shape[2]:
         raise ValueError("H must be groups x K x K")
     Gn, K = H.shape[0], H.shape[1]
@@ -194,9 +235,12 @@ def gptq_prepare_groups(H: torch.Tensor, percdamp: float, dead: Optional[torch.T
     workspace, wp, wb = _workspace(GPTQ_CALL_PREPARE, K, Gn, 0, 0, H.device, workspace)
     damps = (_f32 * Gn)()
     n_dead = (_i64 * Gn)()
-    st = load().gptq_prepare_groups(_dptr(H), K, Gn, H.stride(0), float(percdamp), _dptr(dead), damps, n_dead, wp, wb,
+    st = load().gptq_prepare_groups(_dptr(H), K, Gn, H.stride(0), float(percdamp), _dptr(dead),
+                                    damps if sync else None, n_dead if sync else None, wp, wb,
                                     _stream(H.device, stream))
     _check(st, "gptq_prepare_groups")
+    if not sync:
+        return dead, None, None
     return dead, [float(x) for x in damps], [int(x) for x in n_dead]
 
 
@@ -223,11 +267,14 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, dead: Optio
                         W_hat: Optional[torch.Tensor] = None, losses: Optional[torch.Tensor] = None,
                         pre_round: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                         stream=None, cae: bool = False, perm: Optional[torch.Tensor] = None, groupsize: int = 0,
-                        static_groups: bool = False, mse: bool = False, g_idx: Optional[torch.Tensor] = None) -> dict:
+                        static_groups: bool = False, mse: bool = False, g_idx: Optional[torch.Tensor] = None,
+                        check: bool = True) -> dict:
     """Quantises W (K x N view, any strides) with U; given `scales` are used as the grid (fixed-grid mode);
     cae=True adds the compensation-aware error term (GPTQ_FLAG_CAE); perm (from gptq_act_order) runs the loop in
     act-order; groupsize > 0 gives group-wise scales (ceil(K/groupsize) x N), re-estimated during the loop or
     static_groups; mse clips the scales taken from W before the loop.
+    The C call is stream-ordered; check=True then reads the latched device status (gptq_device_status, which
+    synchronises) and raises on an error, check=False leaves that to the caller.
 
     Returns dict(codes uint8 K x N, scales fp32[N], W_hat, losses, pre_round) with the tensors written.
     """
@@ -241,7 +288,7 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, bits: int, dead: Optio
     _contig(perm, "perm", torch.int32)
     _contig(g_idx, "g_idx", torch.int32)
     return _quantize(W, 1, U, 0, bits, dead, P1, blocksize, scales, codes, W_hat, losses, pre_round, workspace,
-                     stream, cae, perm, groupsize, static_groups, mse, g_idx)
+                     stream, cae, perm, groupsize, static_groups, mse, g_idx, check)
 
 
 def gptq_quantize_layer_groups(W: torch.Tensor, U: torch.Tensor, bits: int, dead: Optional[torch.Tensor] = None,
@@ -251,7 +298,7 @@ def gptq_quantize_layer_groups(W: torch.Tensor, U: torch.Tensor, bits: int, dead
                                pre_round: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                                stream=None, cae: bool = False, perm: Optional[torch.Tensor] = None,
                                groupsize: int = 0, static_groups: bool = False, mse: bool = False,
-                               g_idx: Optional[torch.Tensor] = None) -> dict:
+                               g_idx: Optional[torch.Tensor] = None, check: bool = True) -> dict:
     """gptq_quantize_layer for output-channel groups: U (and P1) are groups x K x K (each K x K contiguous, the same
     group stride), dead, perm and g_idx groups x K; the N channels of W split into `groups` equal contiguous
     groups, group g quantised against U[g].  Same outputs as gptq_quantize_layer."""
@@ -268,11 +315,11 @@ def gptq_quantize_layer_groups(W: torch.Tensor, U: torch.Tensor, bits: int, dead
         if t is not None and (t.dtype != dt or not t.is_contiguous() or t.numel() != Gn * K):
             raise ValueError(f"{nm} must be a contiguous {dt} tensor of groups x K entries")
     return _quantize(W, Gn, U, U.stride(0), bits, dead, P1, blocksize, scales, codes, W_hat, losses, pre_round,
-                     workspace, stream, cae, perm, groupsize, static_groups, mse, g_idx)
+                     workspace, stream, cae, perm, groupsize, static_groups, mse, g_idx, check)
 
 
 def _quantize(W, groups, U, u_stride, bits, dead, P1, blocksize, scales, codes, W_hat, losses, pre_round, workspace,
-              stream, cae, perm, groupsize, static_groups, mse, g_idx) -> dict:
+              stream, cae, perm, groupsize, static_groups, mse, g_idx, check) -> dict:
     K, N = W.shape
     dev = W.device
     _contig(scales, "scales", torch.float32)
@@ -308,6 +355,9 @@ def _quantize(W, groups, U, u_stride, bits, dead, P1, blocksize, scales, codes, 
         st = load().gptq_quantize_layer_groups(_dptr(W), _dtype_code(W), K, N, W.stride(0), W.stride(1), int(groups),
                                                _dptr(U), int(u_stride), _dptr(dead), _dptr(P1), *common)
         _check(st, "gptq_quantize_layer_groups")
+    if check:
+        _check(load().gptq_device_status(wp, _stream(dev, stream)),
+               "gptq_quantize_layer" if groups == 1 else "gptq_quantize_layer_groups")
     return {"codes": codes, "scales": scales, "W_hat": W_hat, "losses": losses, "pre_round": pre_round,
             "g_idx": g_idx}
 

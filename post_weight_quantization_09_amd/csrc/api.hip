@@ -9,6 +9,7 @@
 #include "pack.hpp"
 #include "hadamard.hpp"
 #include "act_order.hpp"
+#include "timer.hpp"
 
 using namespace gptq;
 
@@ -92,6 +93,18 @@ const char* gptq_status_string(gptq_status_t s) {
     return "unknown status";
 }
 
+gptq_status_t gptq_device_status(const void* workspace, void* stream) {
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return GPTQ_ERR_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t flags = 0;
+    // the read is ordered after the stream's work; the copy into pageable memory returns once it is done
+    if (hipMemcpyAsync(&flags, workspace, sizeof(flags), hipMemcpyDeviceToHost, st) != hipSuccess) return GPTQ_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return GPTQ_ERR_HIP;
+    if (flags & kDevNonFinite) return GPTQ_ERR_NONFINITE;
+    if (flags & kDevNotPD) return GPTQ_ERR_NOT_PD;
+    return GPTQ_OK;
+}
+
 size_t gptq_workspace_bytes(gptq_call_t call, int64_t K, int64_t N, int64_t M, unsigned flags) {
     if (K < 1) K = 1;
     if (N < 1) N = 1;
@@ -105,6 +118,18 @@ size_t gptq_workspace_bytes(gptq_call_t call, int64_t K, int64_t N, int64_t M, u
             return quantize_workspace_bytes(K, N, (flags & 2u) != 0, (flags & GPTQ_FLAG_CAE) != 0);
     }
     return 0;
+}
+
+gptq_status_t gptq_gram_plan(int64_t K, int64_t M, int cross, int transformed, int64_t* out) {
+    if (K < 1 || M < 0 || !out) return GPTQ_ERR_ARG;
+    const GramPlan pl = gram_plan(K, M, cross != 0);
+    out[0] = pl.nb;
+    out[1] = pl.ntiles;
+    out[2] = pl.splits;
+    out[3] = pl.tokens_per_split;
+    out[4] = (int64_t)pl.partial_floats;
+    out[5] = (int64_t)gram_staging_elems(K, M, transformed != 0);
+    return GPTQ_OK;
 }
 
 gptq_status_t gptq_accumulate_hessian(float* H, int64_t K, const void* X, gptq_dtype_t x_dtype, int64_t M,
@@ -128,6 +153,7 @@ gptq_status_t gptq_accumulate_hessian(float* H, int64_t K, const void* X, gptq_d
         g.B1 = static_cast<const float*>(X); g.ldb1 = ldx;
         g.C = H; g.ldc = K;
         g.alpha = 2.f; g.beta = 1.f;
+        TimerScope ts(st, GPTQ_TIMER_GRAM);
         return gemm_f32(g, 1, st) == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
     }
     Carver c(workspace);
@@ -175,6 +201,7 @@ gptq_status_t gptq_asym_correction(const float* U, const float* A, float* P1, in
     Carver c(workspace);
     c.take<DevStatus>(1);
     float* T = c.take<float>((size_t)K * (size_t)K);
+    TimerScope ts(st, GPTQ_TIMER_FACTOR_GEMM);
     // T = A U^T  (only the part on or above the diagonal is used)
     GemmArgs g1;
     g1.M = K; g1.N = K; g1.K1 = K;
@@ -221,6 +248,7 @@ gptq_status_t gptq_act_order(float* H, float* A, int64_t K, int32_t* perm, void*
                              void* stream) {
     if (!H || !perm || K < 1 || K > (int64_t)1 << 24) return GPTQ_ERR_ARG;
     if (!ws_ok(workspace, workspace_bytes, act_order_workspace_bytes(K))) return GPTQ_ERR_WORKSPACE;
+    TimerScope ts(static_cast<hipStream_t>(stream), GPTQ_TIMER_OTHER);
     return act_order(H, A, K, perm, workspace, static_cast<hipStream_t>(stream)) == hipSuccess ? GPTQ_OK
                                                                                                 : GPTQ_ERR_HIP;
 }
@@ -233,6 +261,7 @@ gptq_status_t gptq_hadamard_rotate(const void* in, int64_t ld_in, void* out, int
     if (rows == 0) return GPTQ_OK;
     int n = 0;
     while ((int64_t(1) << n) < K) ++n;
+    TimerScope ts(static_cast<hipStream_t>(stream), GPTQ_TIMER_OTHER);
     return hadamard_rows(in, ld_in, out, ld_out, dtype == GPTQ_DTYPE_BF16, rows, n, signs,
                          static_cast<hipStream_t>(stream)) == hipSuccess
                ? GPTQ_OK
@@ -248,6 +277,7 @@ gptq_status_t gptq_pack_codes(const uint8_t* codes, int64_t c_rs, int64_t c_cs, 
                               uint32_t* packed, int64_t ldp, void* stream) {
     if (!codes || !packed || K < 1 || N < 1 || bits < 1 || bits > 8) return GPTQ_ERR_ARG;
     if (c_rs < 1 || c_cs < 1 || ldp < N) return GPTQ_ERR_ARG;
+    TimerScope ts(static_cast<hipStream_t>(stream), GPTQ_TIMER_OTHER);
     return pack_codes(codes, c_rs, c_cs, K, N, bits, packed, ldp, static_cast<hipStream_t>(stream)) == hipSuccess
                ? GPTQ_OK
                : GPTQ_ERR_HIP;
@@ -260,6 +290,7 @@ gptq_status_t gptq_unpack_codes(const uint32_t* packed, int64_t ldp, int64_t K, 
     if (codes && (c_rs < 1 || c_cs < 1)) return GPTQ_ERR_ARG;
     if (W_hat && (!scales || w_rs < 1 || w_cs < 1)) return GPTQ_ERR_ARG;
     if (W_hat && w_dtype != GPTQ_DTYPE_F32 && w_dtype != GPTQ_DTYPE_BF16) return GPTQ_ERR_ARG;
+    TimerScope ts(static_cast<hipStream_t>(stream), GPTQ_TIMER_OTHER);
     return unpack_codes(packed, ldp, K, N, bits, scales, codes, c_rs, c_cs, W_hat, w_dtype == GPTQ_DTYPE_BF16, w_rs,
                         w_cs, static_cast<hipStream_t>(stream)) == hipSuccess
                ? GPTQ_OK

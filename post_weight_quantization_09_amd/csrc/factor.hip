@@ -24,6 +24,7 @@
 
 #include "factor.hpp"
 #include "gemm_f32.hpp"
+#include "timer.hpp"
 
 namespace gptq {
 
@@ -253,6 +254,13 @@ __global__ void clear_status_kernel(DevStatus* st, int64_t n) {
     }
 }
 
+// st[0].flags |= st[b].flags for every b: the first status word then reports the whole batch.
+__global__ void merge_status_kernel(DevStatus* st, int64_t n) {
+    uint32_t f = 0;
+    for (int64_t i = 1 + threadIdx.x; i < n; i += blockDim.x) f |= st[i].flags;
+    if (f) atomicOr(&st[0].flags, f);
+}
+
 }  // namespace
 
 // Split of an n-block (n > 128): the top part n1 is a multiple of 128, the bottom part n2 = n - n1 > 0.
@@ -294,12 +302,14 @@ struct Recursion {
 
     hipError_t gemm(GemmArgs g, int64_t sa, int64_t sb, int64_t sc) const {
         g.strideA1 = sa; g.strideB1 = sb; g.strideC = sc;
+        TimerScope ts(stream, GPTQ_TIMER_FACTOR_GEMM);
         return gemm_f32(g, batch, stream);
     }
 
     gptq_status_t run(int64_t o, int64_t n, float* T) {
         float* D = H + o * K + o;
         if (n <= kNB) {
+            TimerScope ts(stream, GPTQ_TIMER_FACTOR_DIAG);
             hipLaunchKernelGGL(chol_ul_inv_kernel, dim3((unsigned)batch), dim3(1024), 0, stream, D, K, (int)n, st,
                                strideH);
             return hipGetLastError() == hipSuccess ? GPTQ_OK : GPTQ_ERR_HIP;
@@ -336,6 +346,7 @@ struct Recursion {
             x.C = X; x.ldc = n2;
             x.flags = kGemmBUpper;
             x.strideA1 = Ts; x.strideB1 = strideH; x.strideC = Ts;
+            TimerScope ts(stream, GPTQ_TIMER_FACTOR_GEMM);
             if (gemm_f32_pair(s, x, batch, stream) != hipSuccess) return GPTQ_ERR_HIP;
         }
         r = run(o, n1, T + n1 * n2);
@@ -363,6 +374,8 @@ gptq_status_t prepare(float* H, int64_t K, int64_t batch, int64_t strideH, float
     const int64_t Ts = (int64_t)batch_scratch_floats(K);
     float* T = c.take<float>((size_t)Ts * (size_t)batch);
 
+    {
+    TimerScope ts(stream, GPTQ_TIMER_OTHER);
     hipLaunchKernelGGL(clear_status_kernel, dim3(1), dim3(256), 0, stream, st, batch);
     hipLaunchKernelGGL(dead_damp_kernel, dim3((unsigned)batch), dim3(1024), 0, stream, H, K, strideH, percdamp, dead,
                        st);
@@ -372,10 +385,17 @@ gptq_status_t prepare(float* H, int64_t K, int64_t batch, int64_t strideH, float
     // clears), so clearing the lower triangle once keeps it zero throughout.
     hipLaunchKernelGGL(zero_lower_kernel, dim3((unsigned)K, (unsigned)batch), dim3(256), 0, stream, H, K, strideH);
     GPTQ_LAUNCH_CHECK();
+    }
 
     Recursion rec{H, K, st, stream, batch, strideH, Ts};
     gptq_status_t r = rec.run(0, K, T);
     if (r != GPTQ_OK) return r;
+    if (batch > 1) {   // the first status word reports every Hessian's errors (what gptq_device_status reads)
+        TimerScope ts(stream, GPTQ_TIMER_OTHER);
+        hipLaunchKernelGGL(merge_status_kernel, dim3(1), dim3(64), 0, stream, st, batch);
+        GPTQ_LAUNCH_CHECK();
+    }
+    if (!damp_out && !n_dead_out) return GPTQ_OK;   // stream-ordered: errors stay latched for gptq_device_status
 
     std::vector<DevStatus> hst((size_t)batch);
     GPTQ_HIP_CHECK(hipMemcpyAsync(hst.data(), st, sizeof(DevStatus) * (size_t)batch, hipMemcpyDeviceToHost, stream));

@@ -24,6 +24,8 @@
 
 #include <algorithm>
 
+#include "timer.hpp"
+
 namespace gptq {
 
 namespace {
@@ -569,6 +571,8 @@ hipError_t gram_bf16(const GramPlan& pl, const uint16_t* X, int64_t ldx, const u
     const bool fast = p.vec && K % kGT == 0;
     const bool whole_stages = p.tokens_per_split % kGK == 0 && M % kGK == 0;
     const bool transformed = cross || rho != nullptr;
+    {
+    TimerScope ts(stream, GPTQ_TIMER_GRAM);
     if (fast && whole_stages && (!transformed || staging)) {
         // stage indices are taken modulo the ring in 32 bits
         if (p.tokens_per_split / kGK >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
@@ -603,6 +607,8 @@ hipError_t gram_bf16(const GramPlan& pl, const uint16_t* X, int64_t ldx, const u
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    }
+    TimerScope ts(stream, GPTQ_TIMER_GRAM_REDUCE);
     const unsigned nred = (unsigned)(pl.ntiles * 4);
     if (cross) hipLaunchKernelGGL((gram_reduce_kernel<true>), dim3(nred), dim3(256), 0, stream, p, Out);
     else hipLaunchKernelGGL((gram_reduce_kernel<false>), dim3(nred), dim3(256), 0, stream, p, Out);

@@ -26,6 +26,7 @@
 
 #include "gemm_f32.hpp"
 #include "quantize.hpp"
+#include "timer.hpp"
 
 namespace gptq {
 
@@ -562,6 +563,10 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
     QuantLayout L = carve(workspace, K, N, asym, cae);
     const int64_t groups = std::max<int64_t>(a.groups, 1), gs = N / groups;   // output-channel groups
 
+    const int64_t G = a.groupsize;
+    const int sm = G == 0 ? kScalePerChannel : (a.static_groups ? kScaleStatic : kScaleDynamic);
+    {
+    TimerScope ts(stream, GPTQ_TIMER_OTHER);
     hipLaunchKernelGGL(quant_init_kernel, grid1d(std::max<int64_t>(N, 1), 256), dim3(256), 0, stream, L.st, L.amax,
                        L.loss_acc, N);
     GPTQ_LAUNCH_CHECK();
@@ -575,8 +580,6 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
                                L.Wt, ldt, L.amax, L.st, a.perm, gs);
         GPTQ_LAUNCH_CHECK();
     }
-    const int64_t G = a.groupsize;
-    const int sm = G == 0 ? kScalePerChannel : (a.static_groups ? kScaleStatic : kScaleDynamic);
     if (G == 0 && !a.mse) {
         hipLaunchKernelGGL(scales_kernel, grid1d(N, 256), dim3(256), 0, stream, L.amax, a.scales, L.rscale, N, a.bits,
                            a.scales_given, L.st);
@@ -601,6 +604,7 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
     if (cae)   // the original weights (dead rows zeroed), read by every step and by the trailing updates
         GPTQ_HIP_CHECK(hipMemcpyAsync(L.W0t, L.Wt, sizeof(float) * (size_t)N * (size_t)ldt, hipMemcpyDeviceToDevice,
                                       stream));
+    }
 
     // Wt[:, r0:r1] -= E U[k0:k0+depth, r0:r1] (+ Wpre P1[k0:k0+depth, r0:r1] for the asymmetric term; with CAE,
     // E holds (w0 - q) / U_jj and the P1 term takes the original weights W0[:, k0:k0+depth]).  E and Wpre point
@@ -622,6 +626,7 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
         }
         g.C = L.Wt + r0; g.ldc = ldt; g.strideC = gs * ldt;
         g.alpha = -1.f; g.beta = 1.f;
+        TimerScope ts(stream, GPTQ_TIMER_TRAILING);
         return gemm_f32(g, groups, stream) == hipSuccess;
     };
 
@@ -639,6 +644,8 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
             p.G = G; p.perm = a.perm; p.gscales = a.scales;
             p.gs = gs; p.u_stride = a.u_stride;
             dim3 grid((unsigned)ceil_div(N, kChPerWG));
+            {
+            TimerScope ts(stream, GPTQ_TIMER_LOOP);
 #define GPTQ_BLOCK(A_, C_)                                                                                        \
     if (sm == kScaleDynamic) hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScaleDynamic>), grid, dim3(256), 0, stream, p); \
     else if (sm == kScaleStatic) hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScaleStatic>), grid, dim3(256), 0, stream, p); \
@@ -649,6 +656,7 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
             else { GPTQ_BLOCK(false, false) }
 #undef GPTQ_BLOCK
             GPTQ_LAUNCH_CHECK();
+            }
             // near rows: the rest of this super-block
             const int64_t b1 = b0 + bs;
             if (b1 < sb1 && !trailing(b1, sb1, b0, bs, Eb, Wpb)) return GPTQ_ERR_HIP;
@@ -656,6 +664,7 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
         // far rows: everything after the super-block, with the errors of all its blocks
         if (sb1 < K && !trailing(sb1, K, sb0, sb1 - sb0, L.E, L.Wpre)) return GPTQ_ERR_HIP;
     }
+    TimerScope ts(stream, GPTQ_TIMER_OTHER);
     {
         dim3 grid((unsigned)ceil_div(N, 64), (unsigned)ceil_div(K, 64));
         if (a.w_dtype == GPTQ_DTYPE_BF16)
@@ -676,10 +685,6 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
         hipLaunchKernelGGL(copy_losses_kernel, grid1d(N, 256), dim3(256), 0, stream, L.loss_acc, a.losses, N);
         GPTQ_LAUNCH_CHECK();
     }
-    DevStatus hst;
-    GPTQ_HIP_CHECK(hipMemcpyAsync(&hst, L.st, sizeof(DevStatus), hipMemcpyDeviceToHost, stream));
-    GPTQ_HIP_CHECK(hipStreamSynchronize(stream));
-    if (hst.flags & kDevNonFinite) return GPTQ_ERR_NONFINITE;
     return GPTQ_OK;
 }
 

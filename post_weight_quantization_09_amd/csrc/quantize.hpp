@@ -25,7 +25,7 @@ struct QuantizeArgs {
 
 size_t quantize_workspace_bytes(int64_t K, int64_t N, bool asym, bool cae);
 
-// Runs the whole loop on `stream` and synchronises it; returns GPTQ_ERR_NONFINITE for rejected inputs.
+// Enqueues the whole loop on `stream`; rejected inputs latch kDevNonFinite in the workspace status word.
 gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t stream);
 
 }  // namespace gptq

@@ -67,13 +67,30 @@ def check_codes(gpu: dict, W: np.ndarray, U_ref: np.ndarray, bits: int, dead=Non
         assert (err[live] <= OBJ_TOL).all(), f"{label}: loss rel err max {err[live].max():.3e}"
         info["loss_rel_max"] = float(err[live].max()) if live.any() else 0.0
     if H_obj is not None:
+        # the layer objective 1/2 tr(D^T H D) and, since it splits into one quadratic per output channel, each
+        # channel's 1/2 d_n^T H d_n, both within OBJ_TOL of the oracle's
         z = 2 ** (bits - 1)
-        W_hat = s_gpu.astype(np.float64)[None, :] * (codes - z)
-        Jg = O.layer_objective(H_obj, W, W_hat)
-        Jr = O.layer_objective(H_obj, W, ref["Q"])
+        W_hat = _gpu_values(codes, s_gpu, bits, ref)
+        jg = O.layer_objective_per_channel(H_obj, W, W_hat)
+        jr = O.layer_objective_per_channel(H_obj, W, ref["Q"])
+        Jg, Jr = float(jg.sum()), float(jr.sum())
         assert abs(Jg - Jr) <= OBJ_TOL * abs(Jr), f"{label}: objective {Jg} vs {Jr}"
+        live = jr > 1e-30 * max(1.0, float(jr.max()))
+        cerr = np.abs(jg - jr)[live] / jr[live]
+        assert (cerr <= OBJ_TOL).all(), f"{label}: per-channel objective rel err max {cerr.max():.3e}"
         info["J_gpu"], info["J_ref"] = Jg, Jr
+        info["J_channel_rel_max"] = float(cerr.max()) if cerr.size else 0.0
     return info
+
+
+def _gpu_values(codes: np.ndarray, s_gpu: np.ndarray, bits: int, ref: dict) -> np.ndarray:
+    """Grid values s (c - z) of the GPU's codes in float64, with the scale in force at each original row
+    (per channel, or per group through the oracle's group index of every row)."""
+    z = 2 ** (bits - 1)
+    s = np.asarray(s_gpu, np.float64)
+    if s.ndim == 1:
+        return s[None, :] * (codes - z)
+    return s[ref["g_idx"]] * (codes - z)
 
 
 def inverse_factor_residual(H32: np.ndarray, U_rows: np.ndarray, rows: np.ndarray, dead: np.ndarray,

@@ -203,3 +203,57 @@ def test_act_order_validation(lib):
     assert lib.gptq_act_order(FAKE, None, 64, None, ws, need, None) == b.GPTQ_ERR_ARG
     assert lib.gptq_act_order(FAKE, None, 0, FAKE, ws, need, None) == b.GPTQ_ERR_ARG
     assert lib.gptq_act_order(FAKE, None, 64, FAKE, ws, need - 1, None) == b.GPTQ_ERR_WORKSPACE
+
+
+def test_device_status_and_timer_host_paths(lib):
+    """gptq_device_status refuses a NULL or misaligned workspace before any HIP call; the kernel timer turns on and
+    off and reads zeros when nothing was launched (no device work is needed for either)."""
+    assert lib.gptq_device_status(None, None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_device_status(ctypes.c_void_p(0x100010), None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_timer_read(None, None) == b.GPTQ_ERR_ARG
+    assert lib.gptq_timer_enable(1) == b.GPTQ_OK
+    t = g.gptq_timer_read()
+    assert set(t) == set(g.GPTQ_TIMER_CLASSES) and all(v == (0.0, 0) for v in t.values())
+    assert lib.gptq_timer_enable(0) == b.GPTQ_OK
+
+
+def _al(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("K", [1, 8, 255, 256, 257, 300, 520, 1000, 1024, 4096, 7936, 7937, 11264, 11265, 14336,
+                               28672])
+def test_gram_plans_fit_the_workspace(lib, K):
+    """Host-side check of every Gram plan against the workspace gptq_workspace_bytes sizes (symmetric, row-weighted
+    and cross term, ragged K and M, every split count the planner picks): the split partials the launches write
+    (split, tile, wave) for the symmetric plan and, with X_float, the cross plan that reuses the same region; the
+    staging of a transformed operand; the token ranges of the splits (inside [0, M), covering every token)."""
+    for M in (0, 1, 31, 32, 33, 1000, 2500, 4096, 8200, 20000, 65536, 65537, 196608, 327680, 524288, 2097152):
+        for cross, scaled in ((False, False), (False, True), (True, False)):
+            flags = (1 if cross else 0) | (2 if scaled else 0)
+            ws = g.gptq_workspace_bytes(g.GPTQ_CALL_ACCUMULATE_HESSIAN, K, 0, M, flags)
+            plans = [g.gptq_gram_plan(K, M, False, cross or scaled)]
+            if cross:
+                plans.append(g.gptq_gram_plan(K, M, True, True))
+            region = 0
+            for c, pl in zip((False, True), plans):
+                nb = -(-K // 256)
+                assert pl["nb"] == nb
+                assert pl["ntiles"] == (nb * nb if c else nb * (nb + 1) // 2)
+                assert pl["tokens_per_split"] % 32 == 0 and pl["splits"] >= 1
+                assert pl["splits"] * pl["tokens_per_split"] >= M, (K, M, c, pl)
+                # highest float a workgroup writes: ((split * ntiles + tile) * 4 + wave) * 16384 + 16383
+                top = ((pl["splits"] - 1) * pl["ntiles"] + pl["ntiles"] - 1) * 4 + 3
+                assert (top + 1) * 16384 == pl["partial_floats"]
+                region = max(region, pl["partial_floats"])
+                for s in range(pl["splits"]):
+                    t0 = s * pl["tokens_per_split"]
+                    t1 = min(M, t0 + pl["tokens_per_split"])
+                    assert t0 >= 0 and (t1 <= t0 or t1 <= M)
+            staging = plans[0]["staging_elems"]
+            if (cross or scaled) and K % 256 == 0 and M % 32 == 0:
+                assert staging == M * K
+            else:
+                assert staging == 0
+            need = 256 + _al(4 * region) + _al(2 * staging)
+            assert ws >= need, (K, M, cross, scaled, ws, need)

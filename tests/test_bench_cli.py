@@ -29,3 +29,19 @@ def test_source_hash_ignores_comments(tmp_path, monkeypatch):
     assert bench.source_hash("k.hip") == h1
     (csrc / "k.hip").write_text("int f() { return 2; }\nint g();\n")
     assert bench.source_hash("k.hip") != h1
+
+
+def test_traffic_is_keyed_by_workload(tmp_path, monkeypatch):
+    """The HBM traffic of a kernel is read only from the summary of the same workload and source."""
+    import json
+    sys.path.insert(0, ROOT)
+    import bench
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    rec = {"workload": "c5_down_proj_70b", "source_hash": "abc", "bytes_per_launch": 123.0}
+    (tmp_path / "profiles" / "gram_bf16_c5_down_proj_70b_traffic.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("gram_bf16", "c5_down_proj_70b", "abc") == 123.0
+    assert bench.measured_traffic("gram_bf16", "c5_down_proj_70b", "other") is None
+    assert bench.measured_traffic("gram_bf16", "c2_q_proj_8b", "abc") is None
+    (tmp_path / "profiles" / "gram_bf16_c2_q_proj_8b_traffic.json").write_text(json.dumps(rec))
+    assert bench.measured_traffic("gram_bf16", "c2_q_proj_8b", "abc") is None   # a file naming another workload

@@ -9,7 +9,7 @@ import torch
 
 import oracle as O
 import workloads
-from tests.parity import H_TOL, check_codes, inverse_factor_residual, np64, rel_fro
+from tests.parity import BAND, H_TOL, check_codes, inverse_factor_residual, np64, rel_fro
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -57,34 +57,33 @@ def test_c2_gram_sampled_block(g, c2):
 
 
 def test_c2_prepare_and_quantize_sampled_channels(g, c2):
+    """The whole q_proj layer as the bench runs it: the GPU Gram over all 2,097,152 tokens, prepare and the column
+    loop over all 4096 channels; the oracle factorises the same Hessian in float64 (its own U) and runs its loop on
+    64 sampled channels: codes, per-channel and layer objectives, and the pre-rounding drift."""
     cfg, X, W = c2
-    Ms = 16384
-    Hs = O.gram([X[:Ms].float().cpu().numpy()]).astype(np.float32).astype(np.float64)
-    Ht = torch.tensor(Hs, dtype=torch.float32, device=DEV)
-    dead, damp, n_dead = g.gptq_prepare(Ht, cfg.percdamp)
-    ref = O.prepare(Hs, cfg.percdamp)
-    Ug = np64(Ht)
+    H = torch.zeros(cfg.K, cfg.K, device=DEV)
+    g.gptq_accumulate_hessian(H, X)
+    H32 = H.cpu().numpy()
+    H64 = H32.astype(np.float64)
+    ref = O.prepare(H64, cfg.percdamp)
+    dead, damp, n_dead = g.gptq_prepare(H, cfg.percdamp)
+    Ug = np64(H)
     uerr = float(np.abs(Ug - ref["U"]).max() / np.abs(ref["U"]).max())
     print(f"c2 prepare K={cfg.K}: U max rel err {uerr:.3e}, damp {damp:.6e} vs {ref['damp']:.6e}", flush=True)
     assert uerr <= 1e-3
-    out = g.gptq_quantize_layer(W, Ht, cfg.bits, dead=dead, losses=torch.empty(cfg.N, device=DEV))
-    rng = np.random.default_rng(7)
-    C = np.sort(rng.choice(cfg.N, size=64, replace=False))
-    sub = {"codes": out["codes"][:, torch.tensor(C, device=DEV)], "scales": out["scales"][torch.tensor(C, device=DEV)],
-           "losses": out["losses"][torch.tensor(C, device=DEV)]}
-    Wn = W.float().cpu().numpy()[:, C]
-    info = check_codes(sub, Wn, ref["U"], cfg.bits, dead=ref["dead"], H_obj=Hs, label="c2 full-size")
-    print(f"c2 quantize (64 sampled channels of {cfg.N}): inband={info['n_inband']} adopted={info['n_adopted']} "
-          f"loss rel max={info['loss_rel_max']:.2e} J={info['J_gpu']:.6e}/{info['J_ref']:.6e}", flush=True)
+    chans = np.sort(np.random.default_rng(7).choice(cfg.N, size=64, replace=False))
+    _loop_check(g, W, H, dead, cfg.bits, chans, "c2 full layer (oracle's own U)", U_ref=ref["U"],
+                dead_ref=ref["dead"], H_obj=H64)
 
 
 # ------------------------------------------------------------------------------------------------------------
 # The other layer workloads at full size: C3 (down_proj 8B, K = 14336, four output-channel groups with their
 # own token-weighted Hessians), C4 (up_proj 8B with asymmetric calibration), C5 (70B down_proj, K = 28672, with
 # 287 dead input channels).  Gram blocks are checked exactly on sampled coordinates; U through the
-# U H_d U^T = I property on sampled rows (no full-size reference factorisation is needed); the column loop on
-# sampled channels against the oracle run with the library's own U (and P1), so that each stage is checked
-# on its own inputs.
+# U H_d U^T = I property on sampled rows; the column loop on sampled channels against the oracle, with the
+# oracle's own float64 factor wherever the host finishes it in about a minute (K = 4096, 14336) and with the
+# library's U at K = 28672 (the float64 inverse and two Cholesky factorisations of a 28672 x 28672 matrix take
+# several minutes of host time), every time with the layer objective of the full-size Hessian.
 # ------------------------------------------------------------------------------------------------------------
 RESID_TOL = 1e-4   # |U H_d U^T - I| on sampled rows: fp32 rounding gives ~1e-6 here; a 1% damping error gives ~1e-2
 
@@ -117,57 +116,104 @@ def _block_err(Hg, ref, S, label):
     return err
 
 
-def _prepare_and_check(g, H, cfg, label, rows_seed):
-    """Full-size prepare on the GPU; checks dead set, damping and the factor property on sampled rows."""
-    H32 = H.cpu().numpy()
+def _factor_check(U, H32, dead, damp, percdamp, label, rows_seed):
+    """Dead set and damping exactly, and U H_d U^T = I on sampled rows of the library's U (device, in place of H)."""
+    K = H32.shape[0]
     diag = np.diag(H32).astype(np.float64)
     dead_ref = diag == 0.0
-    damp_ref = cfg.percdamp * np.where(dead_ref, 1.0, diag).mean()
-    dead, damp, n_dead = g.gptq_prepare(H, cfg.percdamp)
+    damp_ref = percdamp * np.where(dead_ref, 1.0, diag).mean()
     assert np.array_equal(dead.cpu().numpy().astype(bool), dead_ref)
-    assert n_dead == int(dead_ref.sum())
     assert abs(damp - damp_ref) <= 1e-6 * damp_ref
-    rows = _sample(cfg.K, 24, rows_seed, extra=np.flatnonzero(dead_ref)[:2])
-    Ur = H.index_select(0, torch.tensor(rows, device=H.device)).cpu().numpy()
+    rows = _sample(K, 24, rows_seed, extra=np.flatnonzero(dead_ref)[:2])
+    Ur = U.index_select(0, torch.tensor(rows, device=U.device)).cpu().numpy()
     for i, r in enumerate(rows):
         assert np.count_nonzero(Ur[i, :r]) == 0, f"{label}: row {r} of U not upper triangular"
     R = inverse_factor_residual(H32, Ur, rows, dead_ref, damp)
-    print(f"{label}: prepare n_dead={n_dead} damp={damp:.6e} |U H_d U^T - I| max on {len(rows)} rows "
+    print(f"{label}: prepare n_dead={int(dead_ref.sum())} damp={damp:.6e} |U H_d U^T - I| max on {len(rows)} rows "
           f"{np.abs(R).max():.3e}", flush=True)
     assert np.abs(R).max() <= RESID_TOL
-    return dead, dead_ref
+    return dead_ref
 
 
-def _loop_check(g, W, U, dead, bits, chans, label, P1=None, P2=None):
-    """P2 given: the loop runs with GPTQ_FLAG_CAE and the oracle with that P2."""
-    out = g.gptq_quantize_layer(W, U, bits, dead=dead, P1=P1, losses=torch.empty(W.shape[1], device=DEV),
+def _prepare_and_check(g, H, cfg, label, rows_seed):
+    """Full-size prepare on the GPU; returns (dead device mask, dead reference, fp32 Hessian copied before)."""
+    H32 = H.cpu().numpy()
+    dead, damp, n_dead = g.gptq_prepare(H, cfg.percdamp)
+    dead_ref = _factor_check(H, H32, dead, damp, cfg.percdamp, label, rows_seed)
+    assert n_dead == int(dead_ref.sum())
+    return dead, dead_ref, H32
+
+
+def _drift_and_print(label, info, pre_sub, extra=""):
+    drift = float(np.abs(pre_sub - info["ref"]["V"]).max())
+    print(f"{label}: {info['ref']['V'].shape[1]} channels: codes equal outside the band; inband={info['n_inband']} "
+          f"adopted={info['n_adopted']} pre_round drift max={drift:.2e} loss rel max={info.get('loss_rel_max', 0):.2e}"
+          f" objective rel max per channel={info.get('J_channel_rel_max', 0):.2e} "
+          f"J={info.get('J_gpu', 0):.6e}/{info.get('J_ref', 0):.6e}{extra}", flush=True)
+    assert drift < BAND
+    return drift
+
+
+def _loop_check(g, W, U, dead, bits, chans, label, U_ref=None, dead_ref=None, P1=None, P1_ref=None, P2=None,
+                H_obj=None):
+    """The column loop over all of W's channels (the bench's launch), checked on `chans` against the oracle with
+    U_ref (default: the library's U) and P1_ref (default: the library's P1).  P2 given: the loop runs with
+    GPTQ_FLAG_CAE and the oracle with that P2.  Returns the check info and the pre-rounding drift."""
+    K, N = W.shape
+    pre = torch.empty(K, N, device=DEV)
+    out = g.gptq_quantize_layer(W, U, bits, dead=dead, P1=P1, losses=torch.empty(N, device=DEV), pre_round=pre,
                                 cae=P2 is not None)
     C = torch.tensor(chans, device=DEV)
     sub = {"codes": out["codes"][:, C], "scales": out["scales"][C], "losses": out["losses"][C]}
-    U64 = np64(U)
-    P64 = np64(P1) if P1 is not None else None
-    info = check_codes(sub, W.float().cpu().numpy()[:, chans], U64, bits, dead=dead.cpu().numpy().astype(bool),
-                       P1=P64, P2=P2, label=label)
-    print(f"{label}: column loop on {len(chans)} sampled channels: inband={info['n_inband']} "
-          f"adopted={info['n_adopted']} loss rel max={info['loss_rel_max']:.2e}", flush=True)
+    U64 = np64(U) if U_ref is None else U_ref
+    P64 = (np64(P1) if P1 is not None else None) if P1_ref is None else P1_ref
+    dref = dead.cpu().numpy().astype(bool) if dead_ref is None else dead_ref
+    info = check_codes(sub, W.float().cpu().numpy()[:, chans], U64, bits, dead=dref, P1=P64, P2=P2, H_obj=H_obj,
+                       label=label)
+    drift = _drift_and_print(label, info, pre[:, C].cpu().double().numpy())
+    return info, drift
 
 
-def test_c3_group_gram_prepare_loop(g):
+def test_c3_groups_full_size_end_to_end(g):
+    """The down_proj layer with four output-channel groups as the bench runs it: four token-weighted Grams,
+    gptq_prepare_groups and gptq_quantize_layer_groups over all 4096 channels.  Group 2 against the oracle's own
+    float64 factor of its Hessian (32 sampled channels); every group's factor by the U H_d U^T = I property and
+    8 channels of each group against the oracle fed that group's library U; objectives of each group's Hessian."""
     cfg = workloads.CONFIGS["c3_down_proj_8b_g4"]
     W, X, _, rho = _make(cfg)
-    gi = 2
-    H = torch.zeros(cfg.K, cfg.K, device=DEV)
-    g.gptq_accumulate_hessian(H, X, row_scale=rho[gi].contiguous())
+    Hs = torch.zeros(cfg.groups, cfg.K, cfg.K, device=DEV)
+    for gi in range(cfg.groups):
+        g.gptq_accumulate_hessian(Hs[gi], X, row_scale=rho[gi].contiguous())
     S = _sample(cfg.K, 40, 31)
-    ref = O.gram_row_scaled(_cols(X, S), rho[gi].cpu().numpy())
-    assert _block_err(H, ref, S, "c3 group 2 Gram") <= H_TOL
+    ref_blk = O.gram_row_scaled(_cols(X, S), rho[2].cpu().numpy())
+    assert _block_err(Hs[2], ref_blk, S, "c3 group 2 Gram") <= H_TOL
     del X
     torch.cuda.empty_cache()
-    dead, _ = _prepare_and_check(g, H, cfg, "c3 group 2", 32)
-    gs = cfg.N // cfg.groups
-    Wg = W[:, gi * gs:(gi + 1) * gs]
-    _loop_check(g, Wg, H, dead, cfg.bits, np.sort(np.random.default_rng(33).choice(gs, 16, replace=False)),
-                "c3 group 2")
+    H32 = [Hs[gi].cpu().numpy() for gi in range(cfg.groups)]
+    dead, damps, n_dead = g.gptq_prepare_groups(Hs, cfg.percdamp)
+    for gi in range(cfg.groups):
+        _factor_check(Hs[gi], H32[gi], dead[gi], damps[gi], cfg.percdamp, f"c3 group {gi}", 32 + gi)
+    K, N, gs = cfg.K, cfg.N, cfg.N // cfg.groups
+    pre = torch.empty(K, N, device=DEV)
+    out = g.gptq_quantize_layer_groups(W, Hs, cfg.bits, dead=dead, losses=torch.empty(N, device=DEV), pre_round=pre)
+    Wn = W.float().cpu().numpy()
+
+    def check(gi, chans, U_ref, dead_ref, label):
+        cols = gi * gs + chans
+        C = torch.tensor(cols, device=DEV)
+        sub = {"codes": out["codes"][:, C], "scales": out["scales"][C], "losses": out["losses"][C]}
+        H64 = H32[gi].astype(np.float64)
+        info = check_codes(sub, Wn[:, cols], U_ref, cfg.bits, dead=dead_ref, H_obj=H64, label=label)
+        _drift_and_print(label, info, pre[:, C].cpu().double().numpy())
+
+    rng = np.random.default_rng(33)
+    for gi in range(cfg.groups):
+        chans = np.sort(rng.choice(gs, 8, replace=False))
+        check(gi, chans, np64(Hs[gi]), dead[gi].cpu().numpy().astype(bool), f"c3 group {gi} (library U)")
+    ref = O.prepare(H32[2].astype(np.float64), cfg.percdamp)
+    uerr = float(np.abs(np64(Hs[2]) - ref["U"]).max() / np.abs(ref["U"]).max())
+    print(f"c3 group 2: float64 factor K={K}; library U max rel err {uerr:.3e}", flush=True)
+    check(2, np.sort(rng.choice(gs, 32, replace=False)), ref["U"], ref["dead"], "c3 group 2 (oracle's own U)")
 
 
 def test_c3_prepare_groups_full_size(g):
@@ -203,6 +249,7 @@ def test_c4_gptaq_gram_prepare_asym_loop(g):
     del X, Xf
     torch.cuda.empty_cache()
     H64 = np64(H)
+    A64 = np64(A)
     dead, damp, n_dead = g.gptq_prepare(H, cfg.percdamp)
     ref = O.prepare(H64, cfg.percdamp)
     U64 = np64(H)
@@ -210,14 +257,17 @@ def test_c4_gptaq_gram_prepare_asym_loop(g):
     print(f"c4 prepare K={cfg.K}: U max rel err {uerr:.3e}", flush=True)
     assert uerr <= 1e-3
     P1 = g.gptq_asym_correction(H, A)
-    P1_ref = O.asym_correction(U64, np64(A))
-    perr = rel_fro(np64(P1), P1_ref)
+    P1_lib = O.asym_correction(U64, A64)
+    perr = rel_fro(np64(P1), P1_lib)
     print(f"c4 P1 (full {cfg.K}x{cfg.K}) rel fro {perr:.3e}", flush=True)
     assert perr <= 1e-4
-    chans = np.sort(np.random.default_rng(43).choice(cfg.N, 16, replace=False))
-    _loop_check(g, W, H, dead, cfg.bits, chans, "c4", P1=P1)
-    P2 = O.cae_correction(U64, H64, np64(A))      # the CAE term from the same U, H and A
-    _loop_check(g, W, H, dead, cfg.bits, chans, "c4 with the CAE term", P1=P1, P2=P2)
+    P1_ref = O.asym_correction(ref["U"], A64)          # from the oracle's own factor
+    chans = np.sort(np.random.default_rng(43).choice(cfg.N, 32, replace=False))
+    _loop_check(g, W, H, dead, cfg.bits, chans, "c4 (oracle's own U and P1)", U_ref=ref["U"], dead_ref=ref["dead"],
+                P1=P1, P1_ref=P1_ref, H_obj=H64)
+    P2 = O.cae_correction(ref["U"], H64, A64)           # the CAE term from the oracle's U, H and A
+    _loop_check(g, W, H, dead, cfg.bits, chans, "c4 with the CAE term (oracle's own U, P1, P2)", U_ref=ref["U"],
+                dead_ref=ref["dead"], P1=P1, P1_ref=P1_ref, P2=P2, H_obj=H64)
 
 
 def test_c5_gram_prepare_loop(g):
@@ -231,9 +281,10 @@ def test_c5_gram_prepare_loop(g):
     assert _block_err(H, O.gram([_cols(X, S)]), S, "c5 Gram") <= H_TOL
     del X
     torch.cuda.empty_cache()
-    dead, dead_ref = _prepare_and_check(g, H, cfg, "c5", 52)
+    dead, dead_ref, H32 = _prepare_and_check(g, H, cfg, "c5", 52)
     assert np.array_equal(np.flatnonzero(dead_ref), dead_idx)
-    _loop_check(g, W, H, dead, cfg.bits, np.sort(np.random.default_rng(53).choice(cfg.N, 16, replace=False)), "c5")
+    chans = np.sort(np.random.default_rng(53).choice(cfg.N, 32, replace=False))
+    _loop_check(g, W, H, dead, cfg.bits, chans, "c5 (library U)", dead_ref=dead_ref, H_obj=H32.astype(np.float64))
 
 
 def test_c5_pack_codes_full_size(g):

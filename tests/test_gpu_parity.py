@@ -372,6 +372,58 @@ def test_end_to_end_groups(g):
         _print(f"group {gi}: inband={info['n_inband']} adopted={info['n_adopted']}")
 
 
+@pytest.mark.parametrize("K,gs,groups,bits", [(512, 64, 4, 2), (300, 48, 3, 4)])
+def test_grouped_entry_points_against_oracle(g, K, gs, groups, bits):
+    """The groups driver as the bench runs it (one row-weighted Gram per group, gptq_prepare_groups,
+    gptq_quantize_layer_groups over all channels in each launch) against the oracle directly: every group's
+    Hessian, float64 factor, loop and objective ([G]: output channels in groups, each with its own Hessian)."""
+    cfg, L = _bf16_layer(K, gs * groups, 4096, seed=21 + K, base="c3_down_proj_8b_g4", groups=groups, bits=bits)
+    X = L["X"].to(DEV)
+    W = L["W"].to(DEV)
+    Hs = torch.zeros(groups, K, K, device=DEV)
+    for gi in range(groups):
+        g.gptq_accumulate_hessian(Hs[gi], X, row_scale=L["rho"][gi].to(DEV).contiguous())
+    dead, damps, n_dead = g.gptq_prepare_groups(Hs, cfg.percdamp)
+    N = gs * groups
+    out = g.gptq_quantize_layer_groups(W, Hs, bits, dead=dead, losses=torch.empty(N, device=DEV),
+                                       pre_round=torch.empty(K, N, device=DEV))
+    Xn, Wn = L["X"].float().numpy(), L["W"].float().numpy()
+    for gi in range(groups):
+        H = O.gram_row_scaled(Xn, L["rho"][gi].numpy())
+        ref = O.prepare(H, cfg.percdamp)
+        assert abs(damps[gi] - ref["damp"]) <= 1e-5 * ref["damp"]
+        sl = slice(gi * gs, (gi + 1) * gs)
+        sub = {"codes": out["codes"][:, sl], "scales": out["scales"][sl], "losses": out["losses"][sl]}
+        info = check_codes(sub, Wn[:, sl], ref["U"], bits, dead=ref["dead"], H_obj=H, label=f"grouped {gi}")
+        drift = np.abs(out["pre_round"][:, sl].cpu().double().numpy() - info["ref"]["V"]).max()
+        _print(f"grouped entry points K={K} group {gi}/{groups}: inband={info['n_inband']} "
+               f"adopted={info['n_adopted']} drift={drift:.2e} J={info['J_gpu']:.6e}/{info['J_ref']:.6e}")
+        assert drift < BAND
+
+
+@pytest.mark.parametrize("K,N,bits", [(4096, 64, 8), (4096, 64, 6), (4096, 64, 5)])
+def test_quantize_many_bits_large_K(g, K, N, bits):
+    """Wide grids at a realistic depth: the oracle's own float64 factor, fp32 U on the GPU; codes equal outside the
+    1e-4 band and the pre-rounding drift inside it."""
+    cfg, L = _bf16_layer(K, N, 8192, seed=5 + bits, hadamard=False)
+    X = L["X"].to(DEV)
+    H = torch.zeros(K, K, device=DEV)
+    g.gptq_accumulate_hessian(H, X)
+    H64 = np64(H)
+    ref = O.prepare(H64, cfg.percdamp)
+    W = L["W"].to(DEV)
+    pre = torch.empty(K, N, device=DEV)
+    out = g.gptq_quantize_layer(W, torch.tensor(np.ascontiguousarray(ref["U"]), dtype=torch.float32, device=DEV), bits,
+                                dead=torch.tensor(ref["dead"].astype(np.uint8), device=DEV),
+                                losses=torch.empty(N, device=DEV), pre_round=pre)
+    U32 = np.ascontiguousarray(ref["U"], dtype=np.float32).astype(np.float64)   # the factor the GPU was given
+    info = check_codes(out, L["W"].float().numpy(), U32, bits, dead=ref["dead"], H_obj=H64,
+                       label=f"{bits}-bit K={K}")
+    drift = np.abs(pre.cpu().double().numpy() - info["ref"]["V"]).max()
+    _print(f"{bits}-bit K={K} N={N}: inband={info['n_inband']} adopted={info['n_adopted']} pre_round drift={drift:.2e}")
+    assert drift < BAND
+
+
 def test_end_to_end_gptaq(g):
     cfg, L = _bf16_layer(256, 192, 4096, seed=9, base="c4_up_proj_8b_gptaq")
     out = _pipeline(g, L["X"].to(DEV), L["W"].to(DEV), cfg.bits, X_float=L["X_float"].to(DEV))
