@@ -49,7 +49,7 @@ def test_quantize_nonfinite_weight_latched(g):
     rng = np.random.default_rng(11)
     W = torch.tensor(rng.normal(0, 0.02, size=(K, N)).astype(np.float32), device=DEV)
     H = O.gram([rng.normal(size=(1024, K))])
-    U = torch.tensor(O.prepare(H, 0.01)["U"], dtype=torch.float32, device=DEV)
+    U = torch.tensor(np.ascontiguousarray(O.prepare(H, 0.01)["U"]), dtype=torch.float32, device=DEV)
     codes = torch.empty(K, N, dtype=torch.uint8, device=DEV)
     scales = torch.empty(N, device=DEV)
     ws = torch.empty(g.gptq_workspace_bytes(g.GPTQ_CALL_QUANTIZE_LAYER, K, N), dtype=torch.uint8, device=DEV)

@@ -214,6 +214,19 @@ def test_c3_groups_full_size_end_to_end(g):
     uerr = float(np.abs(np64(Hs[2]) - ref["U"]).max() / np.abs(ref["U"]).max())
     print(f"c3 group 2: float64 factor K={K}; library U max rel err {uerr:.3e}", flush=True)
     check(2, np.sort(rng.choice(gs, 32, replace=False)), ref["U"], ref["dead"], "c3 group 2 (oracle's own U)")
+    # wider grids on the same factor: 5 and 6 bits (the band is relatively tighter as |w / s| grows)
+    chans = np.sort(rng.choice(gs, 16, replace=False))
+    for bits in (5, 6):
+        Wg = W[:, 2 * gs:3 * gs]
+        pre_b = torch.empty(K, gs, device=DEV)
+        out_b = g.gptq_quantize_layer(Wg, Hs[2], bits, dead=dead[2], losses=torch.empty(gs, device=DEV),
+                                      pre_round=pre_b)
+        C = torch.tensor(chans, device=DEV)
+        sub = {"codes": out_b["codes"][:, C], "scales": out_b["scales"][C], "losses": out_b["losses"][C]}
+        label = f"c3 group 2 at {bits} bits (oracle's own U)"
+        info = check_codes(sub, Wn[:, 2 * gs + chans], ref["U"], bits, dead=ref["dead"],
+                           H_obj=H32[2].astype(np.float64), label=label)
+        _drift_and_print(label, info, pre_b[:, C].cpu().double().numpy())
 
 
 def test_c3_prepare_groups_full_size(g):
@@ -284,7 +297,9 @@ def test_c5_gram_prepare_loop(g):
     dead, dead_ref, H32 = _prepare_and_check(g, H, cfg, "c5", 52)
     assert np.array_equal(np.flatnonzero(dead_ref), dead_idx)
     chans = np.sort(np.random.default_rng(53).choice(cfg.N, 32, replace=False))
-    _loop_check(g, W, H, dead, cfg.bits, chans, "c5 (library U)", dead_ref=dead_ref, H_obj=H32.astype(np.float64))
+    H64 = H32.astype(np.float64)
+    _loop_check(g, W, H, dead, cfg.bits, chans, "c5 (library U)", dead_ref=dead_ref, H_obj=H64)
+    _loop_check(g, W, H, dead, 6, chans[::2], "c5 at 6 bits (library U)", dead_ref=dead_ref, H_obj=H64)
 
 
 def test_c5_pack_codes_full_size(g):
