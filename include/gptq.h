@@ -274,6 +274,30 @@ gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * gptq_quantize_layer_noalloc - gptq_quantize_layer for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It takes no workspace: its scratch is a static
+ * device array of the library, 64 MiB (67,108,864 bytes), one per GPU, held from the first call on that GPU until the
+ * process ends.  It calls no hipMalloc, hipFree or other allocating routine (the kernel timer records nothing
+ * during it).
+ *
+ *   Arguments, results and errors: as gptq_quantize_layer (same kernels, same outputs), without workspace.
+ *   The layer must fit the array: gptq_workspace_bytes(GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, flags | (P1 ? 2 : 0))
+ *   <= 67,108,864 (e.g. K = 4096 with up to 2560 channels), else GPTQ_ERR_WORKSPACE and nothing is enqueued; wider
+ *   layers can be quantised in channel slices (W, codes, scales and the other outputs offset by the slice).
+ *   Every call on a GPU uses that GPU's one array, which keeps the previous call's contents (each call clears what
+ *   must start at zero): calls that overlap on one GPU (other streams, other threads) race and must be ordered by
+ *   the caller.  Device-side errors are latched in the array's status word: gptq_device_status(NULL, stream) reads
+ *   it for the current device.
+ */
+gptq_status_t gptq_quantize_layer_noalloc(const void* W, gptq_dtype_t w_dtype, int64_t K, int64_t N,
+                                          int64_t w_rs, int64_t w_cs,
+                                          const float* U, const uint8_t* dead, const float* P1,
+                                          int bits, int blocksize, unsigned flags,
+                                          uint8_t* codes, int64_t c_rs, int64_t c_cs,
+                                          float* scales, void* W_hat, float* losses, float* pre_round,
+                                          const int32_t* perm, int64_t groupsize, int32_t* g_idx, void* stream);
+
+/*
  * gptq_quantize_layer_groups - gptq_quantize_layer on a layer whose N output channels form `groups` equal
  * contiguous groups, each quantised against its own Hessian ([G]: output-channel groups with a Hessian each).
  * Channel n belongs to group g = n / (N / groups) and uses U + g * u_stride, P1 + g * u_stride (if given),
@@ -350,10 +374,12 @@ gptq_status_t gptq_unpack_codes(const uint32_t* packed, int64_t ldp, int64_t K, 
  * gptq_quantize_layer or gptq_quantize_layer_groups call that used `workspace` (the refusal convention of [T]
  * section 7: a non-finite input or a non-positive pivot is an error, reported and not repaired).
  *
- *   workspace  the device workspace given to that call (its 256-byte head holds the status word).
+ *   workspace  the device workspace given to that call (its 256-byte head holds the status word), or NULL for
+ *              the static scratch of gptq_quantize_layer_noalloc on the current device.
  *   stream     the stream that call was enqueued on; it is synchronised before the word is read.
- * Returns GPTQ_OK, GPTQ_ERR_NONFINITE or GPTQ_ERR_NOT_PD (the latter two as latched), GPTQ_ERR_ARG for a NULL
- * or misaligned workspace, GPTQ_ERR_HIP if the synchronisation or the read fails.  Does not clear the word:
+ * Returns GPTQ_OK, GPTQ_ERR_NONFINITE or GPTQ_ERR_NOT_PD (the latter two as latched), GPTQ_ERR_ARG for a
+ * misaligned workspace (or NULL before any gptq_quantize_layer_noalloc call on the current device), GPTQ_ERR_HIP if
+ * the synchronisation or the read fails.  Does not clear the word:
  * the next latching call on the same workspace does.  Read it before reusing the workspace for such a call
  * if both calls' errors matter.
  */

@@ -48,6 +48,9 @@ _SIGNATURES = {
     "gptq_unpack_codes": (ctypes.c_int, [_ptr, _i64, _i64, _i64, ctypes.c_int, _ptr, _ptr, _i64, _i64, _ptr,
                                          ctypes.c_int, _i64, _i64, _ptr]),
     "gptq_device_status": (ctypes.c_int, [_ptr, _ptr]),
+    "gptq_quantize_layer_noalloc": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _i64, _ptr, _ptr, _ptr,
+                                                   ctypes.c_int, ctypes.c_int, _u32, _ptr, _i64, _i64, _ptr, _ptr, _ptr,
+                                                   _ptr, _ptr, _i64, _ptr, _ptr]),
     "gptq_gram_plan": (ctypes.c_int, [_i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.POINTER(_i64)]),
     "gptq_timer_enable": (ctypes.c_int, [ctypes.c_int]),
     "gptq_timer_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i64)]),

@@ -1,6 +1,7 @@
 // C ABI of libgptq_hip.so: argument validation, workspace sizing and launch order (see include/gptq.h).
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "factor.hpp"
 #include "gemm_f32.hpp"
@@ -75,6 +76,33 @@ gptq_status_t quantize_common(const void* W, gptq_dtype_t w_dtype, int64_t K, in
     return quantize_layer(a, workspace, static_cast<hipStream_t>(stream));
 }
 
+// Scratch of gptq_quantize_layer_noalloc: a static device array, one copy per device, kept until the process ends.
+// Host code uses it only through the device address hipGetSymbolAddress returns for the current device (the array's
+// name is a host-side stand-in, not a device address).
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's scratch address, looked up on the first call on the device (with it current) and cached.
+// lookup = false only reads the cache (null if no call has run on the current device).
+gptq_status_t static_scratch(void** out, bool lookup) {
+    *out = nullptr;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return lookup ? GPTQ_ERR_HIP : GPTQ_ERR_ARG;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (!lookup) return GPTQ_ERR_ARG;
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GPTQ_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GPTQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -94,7 +122,13 @@ const char* gptq_status_string(gptq_status_t s) {
 }
 
 gptq_status_t gptq_device_status(const void* workspace, void* stream) {
-    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return GPTQ_ERR_ARG;
+    if (!workspace) {   // the static scratch of gptq_quantize_layer_noalloc on the current device
+        void* p = nullptr;
+        const gptq_status_t r = static_scratch(&p, false);
+        if (r != GPTQ_OK) return r;
+        workspace = p;
+    }
+    if ((reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0) return GPTQ_ERR_ARG;
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint32_t flags = 0;
     // the read is ordered after the stream's work; the copy into pageable memory returns once it is done
@@ -230,6 +264,24 @@ gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K
     return quantize_common(W, w_dtype, K, N, w_rs, w_cs, 1, U, 0, dead, P1, bits, blocksize, flags, codes, c_rs, c_cs,
                            scales, W_hat, losses, pre_round, perm, groupsize, g_idx, workspace, workspace_bytes,
                            stream);
+}
+
+gptq_status_t gptq_quantize_layer_noalloc(const void* W, gptq_dtype_t w_dtype, int64_t K, int64_t N, int64_t w_rs,
+                                          int64_t w_cs, const float* U, const uint8_t* dead, const float* P1, int bits,
+                                          int blocksize, unsigned flags, uint8_t* codes, int64_t c_rs, int64_t c_cs,
+                                          float* scales, void* W_hat, float* losses, float* pre_round,
+                                          const int32_t* perm, int64_t groupsize, int32_t* g_idx, void* stream) {
+    // The size check comes before any HIP call; the argument checks are those of gptq_quantize_layer, which runs
+    // unchanged on the static scratch (the kernel timer is kept off so that no event is created).
+    if (K < 1 || N < 1 || K > (int64_t)1 << 24 || N > (int64_t)1 << 28) return GPTQ_ERR_ARG;
+    if (quantize_workspace_bytes(K, N, P1 != nullptr, (flags & GPTQ_FLAG_CAE) != 0) > kStaticScratchBytes)
+        return GPTQ_ERR_WORKSPACE;
+    void* ws = nullptr;
+    const gptq_status_t r = static_scratch(&ws, true);
+    if (r != GPTQ_OK) return r;
+    TimerSuppress quiet;
+    return quantize_common(W, w_dtype, K, N, w_rs, w_cs, 1, U, 0, dead, P1, bits, blocksize, flags, codes, c_rs, c_cs,
+                           scales, W_hat, losses, pre_round, perm, groupsize, g_idx, ws, kStaticScratchBytes, stream);
 }
 
 gptq_status_t gptq_quantize_layer_groups(const void* W, gptq_dtype_t w_dtype, int64_t K, int64_t N, int64_t w_rs,

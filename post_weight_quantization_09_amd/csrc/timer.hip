@@ -43,9 +43,15 @@ TimerState& state() {
     return s;
 }
 
+thread_local bool t_suppressed = false;
+
 }  // namespace
 
+TimerSuppress::TimerSuppress() : prev_(t_suppressed) { t_suppressed = true; }
+TimerSuppress::~TimerSuppress() { t_suppressed = prev_; }
+
 TimerScope::TimerScope(hipStream_t stream, int cls) : stream_(stream), cls_(cls), start_(nullptr) {
+    if (t_suppressed) return;
     TimerState& s = state();
     std::lock_guard<std::mutex> g(s.mu);
     if (!s.on) return;

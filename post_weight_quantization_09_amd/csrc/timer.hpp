@@ -20,4 +20,17 @@ private:
     hipEvent_t start_;
 };
 
+// While one exists on a thread, TimerScope records nothing on that thread (no events are created): used by the
+// entry point that must not allocate.
+class TimerSuppress {
+public:
+    TimerSuppress();
+    ~TimerSuppress();
+    TimerSuppress(const TimerSuppress&) = delete;
+    TimerSuppress& operator=(const TimerSuppress&) = delete;
+
+private:
+    bool prev_;
+};
+
 }  // namespace gptq
