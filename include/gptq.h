@@ -244,7 +244,11 @@ gptq_status_t gptq_act_order(float* H, float* A, int64_t K, int32_t* perm, void*
  *              (row-major K x N: w_rs = ldw, w_cs = 1; an N x K nn.Linear weight: w_rs = 1, w_cs = K).
  *   U          device, K x K fp32 from gptq_prepare.        dead: device uint8[K] from gptq_prepare or NULL.
  *   P1         NULL, or device K x K fp32 from gptq_asym_correction (asymmetric calibration).
- *   bits       2..8.   blocksize: 128 (the lazy-batch width; other values are rejected with GPTQ_ERR_ARG).
+ *   bits       2..6 (7 and 8 are rejected with GPTQ_ERR_ARG: with |w / s| up to 2^(bits-1) the fp32 working weights
+ *              drift past a 1e-4 s band around the rounding midpoints over a few thousand coordinates, so the codes
+ *              would no longer be those of an exact-arithmetic loop; measured 2.6e-4 s at 8 bits and 3.4e-5 s at
+ *              6 bits for K = 4096).
+ *   blocksize  128 (the lazy-batch width; other values are rejected with GPTQ_ERR_ARG).
  *   perm       NULL, or device int32[K] from gptq_act_order.
  *   groupsize  0 (one scale per channel), 32, 64 or 128.
  *   g_idx      NULL, or device int32[K]: the group of every original coordinate (0 without groups).

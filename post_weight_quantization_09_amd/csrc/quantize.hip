@@ -187,18 +187,11 @@ __global__ __launch_bounds__(256) void group_scales_kernel(const void* Wv, int64
     if (r == 0 && live) scales[g * N + n] = amax > 0.f ? s : 1.0f;
 }
 
-// Broadcast lane `src` of each 16-lane row to the whole row (DPP row_newbcast, gfx90a+).
-__device__ inline float row_bcast(float x, int src) {
-    const int xi = __float_as_int(x);
-    int r;
-    switch (src) {
-#define GPTQ_BC(i) case i: r = __builtin_amdgcn_update_dpp(0, xi, 0x150 + i, 0xF, 0xF, false); break;
-        GPTQ_BC(0) GPTQ_BC(1) GPTQ_BC(2) GPTQ_BC(3) GPTQ_BC(4) GPTQ_BC(5) GPTQ_BC(6) GPTQ_BC(7)
-        GPTQ_BC(8) GPTQ_BC(9) GPTQ_BC(10) GPTQ_BC(11) GPTQ_BC(12) GPTQ_BC(13) GPTQ_BC(14) GPTQ_BC(15)
-#undef GPTQ_BC
-        default: r = xi;
-    }
-    return __int_as_float(r);
+// Broadcast lane SRC of each 16-lane row to the whole row (DPP row_newbcast, gfx90a+).  Every lane reads a lane
+// of its own row, so the destination's previous value does not matter.
+template <int SRC>
+__device__ __forceinline__ float row_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + SRC, 0xF, 0xF, true));
 }
 
 struct BlockArgs {
@@ -226,30 +219,33 @@ struct BlockArgs {
 // group start (processing order); static groups whose scales were computed from W before the loop.
 enum : int { kScalePerChannel = 0, kScaleDynamic = 1, kScaleStatic = 2 };
 
-// Per-lane state of the block kernel: 8 strided coordinates of one channel.
+// Per-lane state of the block kernel: 8 strided coordinates of one channel.  A coordinate's slot keeps its value
+// just before rounding: the step that fixes coordinate j leaves slot j alone (the panel's entry (j, j) is zero), and
+// later steps add zero to it (U is upper triangular), so codes, errors and losses are evaluated once at the end of
+// the block from the kept values, with the same arithmetic as inside the step.
 struct LaneState {
-    float w[8], e[8], pre[8], w0[8];
-    uint32_t code[8];
-    float loss;
+    float w[8], w0[8];
     float s, rs;                    // scale in force (and its reciprocal)
+    float qs[4], qrs[4];            // re-estimated groups: the scale of each 32-coordinate quarter of the block
 };
 
 struct StepConst {
-    const float* Up; const float* Pp; const float* rdiag;
+    const float* Up; const float* Pp;
     const float* Ts; const float* Trs;   // static groups: per-step scales of this workgroup's 16 channels
-    float z, qmax;
+    float clo, chi, qmax;                // signed code range -z .. qmax - z
     int l, ch;
     int64_t G, b0;
     float* gscales;
-    float* pre_round; int64_t prow_off; int64_t N; bool live;
+    int64_t N, n; bool live;
 };
 
-// Per-step operands read from LDS: this lane's 8 entries of U row J (and of P1 row J), 1 / U_JJ.  Step J
-// reads the operands of step J + 1 while it runs, so no LDS latency sits on the chain of dependent steps.
+// Per-step operands read from LDS: this lane's 8 entries of row J of the scaled panel U_Jk / U_JJ (and of P1).
+// They are read kLook - 1 steps ahead, so no LDS latency sits on the chain of dependent steps.
 struct StepOps {
     f32x4 u0, u1, p0, p1;
-    float rd, s, rs;
+    float s, rs;
 };
+constexpr int kLook = 4;
 
 template <int J, bool ASYM, int SM>
 __device__ __forceinline__ void load_ops(StepOps& o, const StepConst& k) {
@@ -266,14 +262,9 @@ __device__ __forceinline__ void load_ops(StepOps& o, const StepConst& k) {
             o.p0 = prow[0];
             o.p1 = prow[1];
         }
-        o.rd = k.rdiag[J];
     }
 }
 
-// One step j of the loop (j compile-time so that slots, DPP lane and LDS offsets are immediates).
-// CAE: the step's update uses the original weight w0_j in place of the pre-rounding value, both in the
-// error that multiplies U (w0_j - q) / U_jj and in the P1 coefficient; the step error E_j itself still feeds
-// the loss.  This is the P2 = P1 + I - diag(U)^-1 U form of the CAE term.
 // Re-estimated groups: at a group's first coordinate J the scale becomes 2 max|w| / qmax over the group's
 // rows J .. J+G-1 of the current weights (registers m in [J/16, (J+G)/16) of the channel's 16 lanes).
 template <int J>
@@ -291,56 +282,69 @@ __device__ __forceinline__ void regroup(LaneState& st, const StepConst& k) {
     mx = fmaxf(mx, __shfl_xor(mx, 1, 16));
     st.s = mx > 0.f ? (2.0f * mx) / k.qmax : 1.0f;
     st.rs = 1.0f / st.s;
-    if (k.l == 0 && k.live) k.gscales[((k.b0 + J) / k.G) * k.N + k.prow_off] = st.s;
+    if (k.l == 0 && k.live) k.gscales[((k.b0 + J) / k.G) * k.N + k.n] = st.s;
 }
 
-template <int J, bool ASYM, bool CAE, bool PRE, int SM>
-__device__ __forceinline__ void loop_step(LaneState& st, const StepConst& k, StepOps (&ops)[2]) {
+// Signed code of v: round half to even, clamp to -z .. qmax - z.
+__device__ __forceinline__ float signed_code(float v, const StepConst& k) {
+    return __builtin_amdgcn_fmed3f(rintf(v), k.clo, k.chi);
+}
+
+// One step j of the loop (j compile-time so that slots, DPP lane and LDS offsets are immediates).  The chain
+// from one step to the next is: broadcast w_j, scale, round, clamp, d = w_j - c s, then the update of the slot
+// holding coordinate j + 1.  With the panel holding U_jk / U_jj, w_k -= (U_jk / U_jj) d is the update
+// w_k -= U_jk E_j with E_j = d / U_jj; slot j itself has a zero entry and keeps its pre-rounding value.
+// CAE: the update is taken from the original weight, d = w0_j - c s (the P2 = P1 + I - diag(U)^-1 U form), and the
+// P1 coefficient is w0_j.
+template <int J, bool ASYM, bool CAE, int SM>
+__device__ __forceinline__ void loop_step(LaneState& st, const StepConst& k, StepOps (&ops)[kLook]) {
     constexpr int m = J >> 4, lj = J & 15;
-    const StepOps& o = ops[J & 1];
-    if constexpr (SM == kScaleDynamic) regroup<J>(st, k);
+    const StepOps& o = ops[J % kLook];
+    // Steps stay in program order: the scheduler would otherwise sink the look-ahead reads to their uses.
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SM == kScaleDynamic && (J & 31) == 0) {
+        regroup<J>(st, k);
+        st.qs[J >> 5] = st.s;
+        st.qrs[J >> 5] = st.rs;
+    }
     if constexpr (SM == kScaleStatic) {
         st.s = o.s;
         st.rs = o.rs;
     }
-    load_ops<J + 1, ASYM, SM>(ops[(J + 1) & 1], k);
-    const float wj = row_bcast(st.w[m], lj);
-    const float v = wj * st.rs;
-    const float c = fminf(fmaxf(rintf(v) + k.z, 0.f), k.qmax);
-    const float q = (c - k.z) * st.s;
-    const float e = (wj - q) * o.rd;
-    const float wu = CAE ? row_bcast(st.w0[m], lj) : wj;      // value the update is taken from
-    const float eu = CAE ? (wu - q) * o.rd : e;
+    load_ops<J + kLook - 1, ASYM, SM>(ops[(J + kLook - 1) % kLook], k);
+    const float wj = row_bcast<lj>(st.w[m]);
+    const float c = signed_code(wj * st.rs, k);
+    const float wu = CAE ? row_bcast<lj>(st.w0[m]) : wj;     // value the update is taken from
+    const float d = fmaf(-c, st.s, wu);
     const float uu[8] = {o.u0.x, o.u0.y, o.u0.z, o.u0.w, o.u1.x, o.u1.y, o.u1.z, o.u1.w};
-    const bool owner = (k.l == lj);
     if constexpr (ASYM) {
         const float pp[8] = {o.p0.x, o.p0.y, o.p0.z, o.p0.w, o.p1.x, o.p1.y, o.p1.z, o.p1.w};
-        st.w[m] = owner ? q : fmaf(pp[m], wu, fmaf(-uu[m], eu, st.w[m]));
 #pragma unroll
-        for (int mm = m + 1; mm < 8; ++mm) st.w[mm] = fmaf(pp[mm], wu, fmaf(-uu[mm], eu, st.w[mm]));
+        for (int mm = m; mm < 8; ++mm) st.w[mm] = fmaf(pp[mm], wu, fmaf(-uu[mm], d, st.w[mm]));
+        asm volatile("" ::"v"(o.p0), "v"(o.p1));
     } else {
-        st.w[m] = owner ? q : fmaf(-uu[m], eu, st.w[m]);
 #pragma unroll
-        for (int mm = m + 1; mm < 8; ++mm) st.w[mm] = fmaf(-uu[mm], eu, st.w[mm]);
+        for (int mm = m; mm < 8; ++mm) st.w[mm] = fmaf(-uu[mm], d, st.w[mm]);
     }
-    st.loss = fmaf(e, e, st.loss);
-    st.code[m] = owner ? (uint32_t)c : st.code[m];
-    st.e[m] = owner ? eu : st.e[m];
-    if constexpr (ASYM) st.pre[m] = owner ? wj : st.pre[m];
-    if constexpr (PRE) {
-        if (owner && k.live) k.pre_round[(int64_t)J * k.N + k.prow_off] = v;
-    }
+    // The entries of slots below m are not needed, but their registers are the destinations of this step's LDS
+    // read; keeping them live until here stops the allocator from reusing one while the read is in flight (which
+    // would make the next instruction wait for the read).
+    asm volatile("" ::"v"(o.u0), "v"(o.u1));
 }
 
-template <bool ASYM, bool CAE, bool PRE, int SM, int... Js>
+template <bool ASYM, bool CAE, int SM, bool WHOLE, int... Js>
 __device__ __forceinline__ void run_steps(LaneState& st, const StepConst& k, int bs,
                                           std::integer_sequence<int, Js...>) {
-    StepOps ops[2];
+    StepOps ops[kLook];
     load_ops<0, ASYM, SM>(ops[0], k);
-    ((Js < bs ? loop_step<Js, ASYM, CAE, PRE, SM>(st, k, ops) : (void)0), ...);
+    load_ops<1, ASYM, SM>(ops[1], k);
+    load_ops<2, ASYM, SM>(ops[2], k);
+    static_assert(kLook == 4, "prologue loads kLook - 1 steps");
+    ((WHOLE || Js < bs ? loop_step<Js, ASYM, CAE, SM>(st, k, ops) : (void)0), ...);
 }
 
-template <bool ASYM, bool CAE, int SM>
+// WHOLE: the block has all 128 coordinates (every block but a ragged last one), so the steps carry no bounds test.
+template <bool ASYM, bool CAE, int SM, bool WHOLE>
 __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
     __shared__ __attribute__((aligned(16))) float Up[kB * kB];               // [row j][16 lanes][8 slots]
     __shared__ __attribute__((aligned(16))) float Pp[ASYM ? kB * kB : 4];    // same layout (asymmetric)
@@ -357,27 +361,32 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
     }
     const int tid = threadIdx.x;
     const int64_t b0 = p.b0;
-    const int bs = p.bs;
-    // Stage the U (and P1) panel rows b0..b0+bs-1, columns b0..b0+127 (zero beyond the block) as
-    // [row j][lane l][slot m] for column 16 m + l.  All global loads are issued before the LDS stores.
+    const int bs = WHOLE ? kB : p.bs;
+    // Stage the panel rows b0..b0+bs-1, columns b0..b0+127 as [row j][lane l][slot m] for column 16 m + l: U_jk / U_jj
+    // for k > j (zero on and below the diagonal and beyond the block), P1 as it is (strictly upper).  All global loads
+    // are issued before the LDS stores.
     {
         constexpr int kV = kB * kB / 4 / 256;     // 16-byte vectors per thread
-        const bool vec = p.bs == kB && (p.K % 4) == 0 && (b0 % 4) == 0;
+        const bool vec = bs == kB && (p.K % 4) == 0 && (b0 % 4) == 0;
         f32x4 uv[kV], pv[ASYM ? kV : 1];
+        float rd[kV];
 #pragma unroll
         for (int i = 0; i < kV; ++i) {
             const int idx = tid + 256 * i, j = idx >> 5, c = (idx & 31) * 4;
             const int64_t off = (b0 + j) * p.K + b0 + c;
             f32x4 u = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
+            rd[i] = 0.f;
             if (vec) {
                 u = *reinterpret_cast<const f32x4*>(p.U + off);
                 if constexpr (ASYM) q = *reinterpret_cast<const f32x4*>(p.P1 + off);
+                rd[i] = p.U[(b0 + j) * p.K + b0 + j];
             } else if (j < bs) {
                 for (int e = 0; e < 4; ++e)
                     if (c + e < bs) {
                         u[e] = p.U[off + e];
                         if constexpr (ASYM) q[e] = p.P1[off + e];
                     }
+                rd[i] = p.U[(b0 + j) * p.K + b0 + j];
             }
             uv[i] = u;
             if constexpr (ASYM) pv[i] = q;
@@ -385,14 +394,15 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
 #pragma unroll
         for (int i = 0; i < kV; ++i) {
             const int idx = tid + 256 * i, j = idx >> 5, c = (idx & 31) * 4;
+            const float r = j < bs ? 1.0f / rd[i] : 0.f;
+            if ((idx & 31) == 0) rdiag[j] = r;
             for (int e = 0; e < 4; ++e) {
                 const int l = (c + e) & 15, m = (c + e) >> 4;
-                Up[(j * 16 + l) * 8 + m] = uv[i][e];
+                Up[(j * 16 + l) * 8 + m] = c + e > j ? uv[i][e] * r : 0.f;
                 if constexpr (ASYM) Pp[(j * 16 + l) * 8 + m] = pv[i][e];
             }
         }
     }
-    for (int j = tid; j < kB; j += 256) rdiag[j] = (j < bs) ? 1.0f / p.U[(b0 + j) * p.K + b0 + j] : 0.f;
     if constexpr (SM == kScaleStatic) {
         for (int idx = tid; idx < kB * kChPerWG; idx += 256) {
             const int j = idx >> 4;
@@ -414,18 +424,20 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
     const int64_t nn = live ? n : 0;
 
     LaneState st;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        st.qs[q] = 1.0f;
+        st.qrs[q] = 1.0f;
+    }
     const float* wrow = p.Wt + nn * p.ldt + b0;
     const float* w0row = CAE ? p.W0t + nn * p.ldt + b0 : nullptr;
+#pragma unroll
     for (int m = 0; m < 8; ++m) {
         st.w[m] = wrow[16 * m + l];
         if constexpr (CAE) st.w0[m] = w0row[16 * m + l];
-        st.e[m] = 0.f;
-        st.pre[m] = 0.f;
-        st.code[m] = 0;
     }
-    st.loss = 0.f;
     StepConst k;
-    k.Up = Up; k.Pp = Pp; k.rdiag = rdiag; k.Ts = Ts; k.Trs = Trs;
+    k.Up = Up; k.Pp = Pp; k.Ts = Ts; k.Trs = Trs;
     if constexpr (SM == kScalePerChannel) {
         st.s = p.scales[nn];
         st.rs = p.rscale[nn];
@@ -433,26 +445,55 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
         st.s = 1.0f;
         st.rs = 1.0f;
     }
-    k.z = (float)(1 << (p.bits - 1));
+    const float z = (float)(1 << (p.bits - 1));
     k.qmax = (float)((1 << p.bits) - 1);
+    k.clo = -z;
+    k.chi = k.qmax - z;
     k.l = l;
     k.ch = tid >> 4;
     k.G = p.G; k.b0 = b0; k.gscales = p.gscales;
-    k.pre_round = p.pre_round ? p.pre_round + b0 * p.N : nullptr;
-    k.prow_off = n; k.N = p.N; k.live = live;
-    if (k.pre_round) run_steps<ASYM, CAE, true, SM>(st, k, bs, std::make_integer_sequence<int, kB>{});
-    else run_steps<ASYM, CAE, false, SM>(st, k, bs, std::make_integer_sequence<int, kB>{});
+    k.N = p.N; k.n = n; k.live = live;
+    run_steps<ASYM, CAE, SM, WHOLE>(st, k, bs, std::make_integer_sequence<int, kB>{});
 
-    if (!live) return;
-    uint8_t* crow = p.codes_t + n * p.ldt + b0;
-    float* erow = p.E + n * p.lde;
+    // Codes, errors, pre-rounding values and the loss from the kept pre-rounding values, with the step's arithmetic.
+    float loss = 0.f;
+    uint8_t* crow = p.codes_t + nn * p.ldt + b0;
+    float* erow = p.E + nn * p.lde;
+#pragma unroll
     for (int m = 0; m < 8; ++m) {
-        const int c = 16 * m + l;
-        if (c < bs) crow[c] = (uint8_t)st.code[m];
-        erow[c] = st.e[m];
-        if (ASYM && !CAE) p.Wpre[n * p.lde + c] = st.pre[m];
+        const int j = 16 * m + l;
+        float s = st.s, rs = st.rs;
+        if constexpr (SM == kScaleDynamic) {
+            s = st.qs[m >> 1];
+            rs = st.qrs[m >> 1];
+        }
+        if constexpr (SM == kScaleStatic) {
+            s = Ts[j * 16 + k.ch];
+            rs = Trs[j * 16 + k.ch];
+        }
+        if (WHOLE || j < bs) {
+            const float v = st.w[m] * rs;
+            const float c = signed_code(v, k);
+            const float r = rdiag[j];
+            const float e = fmaf(-c, s, st.w[m]) * r;
+            loss = fmaf(e, e, loss);
+            if (live) {
+                crow[j] = (uint8_t)(uint32_t)(c + z);
+                erow[j] = CAE ? fmaf(-c, s, st.w0[m]) * r : e;
+                if (ASYM && !CAE) p.Wpre[n * p.lde + j] = st.w[m];
+                if (p.pre_round) p.pre_round[(b0 + j) * p.N + n] = v;
+            }
+        } else if (live) {
+            erow[j] = 0.f;
+            if (ASYM && !CAE) p.Wpre[n * p.lde + j] = 0.f;
+        }
     }
-    if (l == 0) p.loss_acc[n] += 0.5f * st.loss;
+    // the channel's loss: sum over its 16 lanes
+    loss += __shfl_xor(loss, 8, 16);
+    loss += __shfl_xor(loss, 4, 16);
+    loss += __shfl_xor(loss, 2, 16);
+    loss += __shfl_xor(loss, 1, 16);
+    if (l == 0 && live) p.loss_acc[n] += 0.5f * loss;
 }
 
 // codes_t (N x ldt) -> codes (K x N view with strides); W_hat = s (c - z) in the weight dtype; losses copy.
@@ -646,15 +687,18 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
             dim3 grid((unsigned)ceil_div(N, kChPerWG));
             {
             TimerScope ts(stream, GPTQ_TIMER_LOOP);
+#define GPTQ_BLOCK_W(A_, C_, W_)                                                                                  \
+    if (sm == kScaleDynamic) hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScaleDynamic, W_>), grid, dim3(256), 0, stream, p); \
+    else if (sm == kScaleStatic) hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScaleStatic, W_>), grid, dim3(256), 0, stream, p); \
+    else hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScalePerChannel, W_>), grid, dim3(256), 0, stream, p);
 #define GPTQ_BLOCK(A_, C_)                                                                                        \
-    if (sm == kScaleDynamic) hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScaleDynamic>), grid, dim3(256), 0, stream, p); \
-    else if (sm == kScaleStatic) hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScaleStatic>), grid, dim3(256), 0, stream, p); \
-    else hipLaunchKernelGGL((quant_block_kernel<A_, C_, kScalePerChannel>), grid, dim3(256), 0, stream, p);
+    if (bs == kB) { GPTQ_BLOCK_W(A_, C_, true) } else { GPTQ_BLOCK_W(A_, C_, false) }
             if (asym && cae) { GPTQ_BLOCK(true, true) }
             else if (asym) { GPTQ_BLOCK(true, false) }
             else if (cae) { GPTQ_BLOCK(false, true) }
             else { GPTQ_BLOCK(false, false) }
 #undef GPTQ_BLOCK
+#undef GPTQ_BLOCK_W
             GPTQ_LAUNCH_CHECK();
             }
             // near rows: the rest of this super-block

@@ -115,6 +115,7 @@ def test_quantize_validation(lib):
 
     assert call(bits=1) == b.GPTQ_ERR_ARG
     assert call(bits=9) == b.GPTQ_ERR_ARG
+    assert call(bits=7) == b.GPTQ_ERR_ARG and call(bits=8) == b.GPTQ_ERR_ARG   # beyond the fp32 drift bound
     assert call(bsz=64) == b.GPTQ_ERR_ARG
     assert call(W=None) == b.GPTQ_ERR_ARG
     assert call(dt=7) == b.GPTQ_ERR_ARG

@@ -249,7 +249,7 @@ def test_page_examples_on_gpu(g, golden_dir):
 # ------------------------------------------------------------------------------------------------ column loop
 @pytest.mark.parametrize("K,N,bits,layout,wdt", [
     (256, 96, 4, "KN", "bf16"), (300, 77, 3, "KN", "bf16"), (640, 130, 2, "NK", "bf16"),
-    (512, 512, 4, "KN", "f32"), (129, 33, 8, "NK", "f32"), (1, 5, 4, "KN", "f32")])
+    (512, 512, 4, "KN", "f32"), (129, 33, 6, "NK", "f32"), (1, 5, 4, "KN", "f32")])
 def test_quantize_stage(g, K, N, bits, layout, wdt):
     H = _workload_H(K, seed=K + N)
     ref = O.prepare(H, 0.01)
@@ -401,7 +401,7 @@ def test_grouped_entry_points_against_oracle(g, K, gs, groups, bits):
         assert drift < BAND
 
 
-@pytest.mark.parametrize("K,N,bits", [(4096, 64, 8), (4096, 64, 6), (4096, 64, 5)])
+@pytest.mark.parametrize("K,N,bits", [(4096, 64, 6), (4096, 64, 5)])
 def test_quantize_many_bits_large_K(g, K, N, bits):
     """Wide grids at a realistic depth: the oracle's own float64 factor, fp32 U on the GPU; codes equal outside the
     1e-4 band and the pre-rounding drift inside it."""
