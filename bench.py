@@ -126,7 +126,7 @@ class Layer:
         ws = max(G.gptq_workspace_bytes(G.GPTQ_CALL_ACCUMULATE_HESSIAN, K, 0, M, flags),
                  G.gptq_workspace_bytes(G.GPTQ_CALL_PREPARE, K, cfg.groups),
                  G.gptq_workspace_bytes(G.GPTQ_CALL_ASYM_CORRECTION, K),
-                 G.gptq_workspace_bytes(G.GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, 2 if self.Xf is not None else 0))
+                 G.gptq_workspace_bytes(G.GPTQ_CALL_QUANTIZE_LAYER, K, N, cfg.groups, 2 if self.Xf is not None else 0))
         self.ws = torch.empty(ws, dtype=torch.uint8, device=dev)
         self.ws_cae = torch.empty(G.gptq_workspace_bytes(G.GPTQ_CALL_QUANTIZE_LAYER, K, gs, 0,
                                                          G.GPTQ_FLAG_CAE | (2 if self.Xf is not None else 0)),

@@ -83,7 +83,9 @@ typedef enum {
 
 /*
  * gptq_workspace_bytes - bytes of `workspace` a call needs for the given sizes.
- *   call: which entry point; K, N, M: sizes as in that call (unused ones are ignored); flags: for
+ *   call: which entry point; K, N, M: sizes as in that call (unused ones are ignored; for
+ *   GPTQ_CALL_QUANTIZE_LAYER, M is the number of output-channel groups of gptq_quantize_layer_groups, 0 or 1 for
+ *   gptq_quantize_layer); flags: for
  *   gptq_accumulate_hessian 1 if X_float will be given | 2 if row_scale will be given; for
  *   gptq_quantize_layer its flags (GPTQ_FLAG_CAE matters) | 2 if P1 will be given; else 0.
  * Returns 0 for an unknown call.  Never fails otherwise.
@@ -316,8 +318,8 @@ gptq_status_t gptq_quantize_layer_noalloc(const void* W, gptq_dtype_t w_dtype, i
  *   dead       NULL or device uint8[groups * K].   perm: NULL or device int32[groups * K], one act-order
  *              permutation per group (from gptq_act_order on that group's Hessian).
  *   g_idx      NULL or device int32[groups * K] (written).
- *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, flags | (P1?2:0)),
- *              the same as one call over all N channels.
+ *   workspace  device scratch of gptq_workspace_bytes(GPTQ_CALL_QUANTIZE_LAYER, K, N, groups, flags | (P1?2:0))
+ *              (one call over all N channels, plus per group the split diagonal blocks of its U).
  *   All other arguments as for gptq_quantize_layer.
  * Errors: as gptq_quantize_layer (asynchronous; device-side errors through gptq_device_status).
  */

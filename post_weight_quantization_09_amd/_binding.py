@@ -346,7 +346,7 @@ def _quantize(W, groups, U, u_stride, bits, dead, P1, blocksize, scales, codes, 
     if pre_round is not None and (pre_round.shape != (K, N) or not pre_round.is_contiguous()):
         raise ValueError("pre_round must be a contiguous K x N fp32 tensor")
     ws_flags = flags | (2 if P1 is not None else 0)
-    workspace, wp, wb = _workspace(GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, ws_flags, dev, workspace)
+    workspace, wp, wb = _workspace(GPTQ_CALL_QUANTIZE_LAYER, K, N, groups, ws_flags, dev, workspace)
     common = (int(bits), int(blocksize), flags, _dptr(codes), codes.stride(0), codes.stride(1), _dptr(scales),
               _dptr(W_hat), _dptr(losses), _dptr(pre_round), _dptr(perm), int(groupsize), _dptr(g_idx), wp, wb,
               _stream(dev, stream))

@@ -65,7 +65,8 @@ gptq_status_t quantize_common(const void* W, gptq_dtype_t w_dtype, int64_t K, in
     if (K > (int64_t)1 << 24 || N > (int64_t)1 << 28) return GPTQ_ERR_ARG;
     if (groups < 1 || groups > 65535 || N % groups != 0) return GPTQ_ERR_ARG;
     if (groups > 1 && ((N / groups) % 16 != 0 || u_stride < K * K)) return GPTQ_ERR_ARG;
-    if (!ws_ok(workspace, workspace_bytes, quantize_workspace_bytes(K, N, P1 != nullptr, (flags & GPTQ_FLAG_CAE) != 0)))
+    if (!ws_ok(workspace, workspace_bytes,
+               quantize_workspace_bytes(K, N, P1 != nullptr, (flags & GPTQ_FLAG_CAE) != 0, groups)))
         return GPTQ_ERR_WORKSPACE;
     QuantizeArgs a;
     a.W = W; a.w_dtype = w_dtype; a.K = K; a.N = N; a.w_rs = w_rs; a.w_cs = w_cs;
@@ -151,7 +152,8 @@ size_t gptq_workspace_bytes(gptq_call_t call, int64_t K, int64_t N, int64_t M, u
         case GPTQ_CALL_ASYM_CORRECTION: return asym_ws(K);
         case GPTQ_CALL_ACT_ORDER: return K > 0 ? act_order_workspace_bytes(K) : 0;
         case GPTQ_CALL_QUANTIZE_LAYER:
-            return quantize_workspace_bytes(K, N, (flags & 2u) != 0, (flags & GPTQ_FLAG_CAE) != 0);
+            // M: the output-channel groups of gptq_quantize_layer_groups (0 or 1: one)
+            return quantize_workspace_bytes(K, N, (flags & 2u) != 0, (flags & GPTQ_FLAG_CAE) != 0, std::max<int64_t>(M, 1));
     }
     return 0;
 }

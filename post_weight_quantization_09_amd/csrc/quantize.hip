@@ -343,7 +343,188 @@ __device__ __forceinline__ void run_steps(LaneState& st, const StepConst& k, int
     ((WHOLE || Js < bs ? loop_step<Js, ASYM, CAE, SM>(st, k, ops) : (void)0), ...);
 }
 
-// WHOLE: the block has all 128 coordinates (every block but a ragged last one), so the steps carry no bounds test.
+// The panel of the block at b0 (bs rows) for one output-channel group's U (and P1): rows b0..b0+bs-1, columns
+// b0..b0+127, staged in LDS as [row j][lane l][slot m] for column 16 m + l.  U is stored as U_jk / U_jj for k > j
+// (zero on and below the diagonal and beyond the block), P1 as it is (strictly upper); rdiag[j] = 1 / U_jj.
+// panel_load issues every global load into registers, panel_store writes LDS, so that other work can run between.
+constexpr int kPanelV = kB * kB / 4 / 256;     // 16-byte vectors per thread
+template <bool ASYM>
+struct PanelRegs {
+    f32x4 uv[kPanelV], pv[ASYM ? kPanelV : 1];
+    float rd[kPanelV];
+};
+
+// VEC (whole blocks, K a multiple of 4): straight-line 16-byte loads, all in flight together; otherwise guarded
+// element loads.
+template <bool ASYM, bool VEC>
+__device__ __forceinline__ void panel_load_v(PanelRegs<ASYM>& R, const float* U, const float* P1, int64_t K,
+                                             int64_t b0, int bs, int tid) {
+#pragma unroll
+    for (int i = 0; i < kPanelV; ++i) {
+        const int idx = tid + 256 * i, j = idx >> 5, c = (idx & 31) * 4;
+        const int64_t off = (b0 + j) * K + b0 + c;
+        if constexpr (VEC) {
+            R.uv[i] = *reinterpret_cast<const f32x4*>(U + off);
+            if constexpr (ASYM) R.pv[i] = *reinterpret_cast<const f32x4*>(P1 + off);
+            R.rd[i] = U[(b0 + j) * K + b0 + j];
+        } else {
+            f32x4 u = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
+            R.rd[i] = 0.f;
+            if (j < bs) {
+                for (int e = 0; e < 4; ++e)
+                    if (c + e < bs) {
+                        u[e] = U[off + e];
+                        if constexpr (ASYM) q[e] = P1[off + e];
+                    }
+                R.rd[i] = U[(b0 + j) * K + b0 + j];
+            }
+            R.uv[i] = u;
+            if constexpr (ASYM) R.pv[i] = q;
+        }
+    }
+}
+
+template <bool ASYM>
+__device__ __forceinline__ void panel_load(PanelRegs<ASYM>& R, const float* U, const float* P1, int64_t K, int64_t b0,
+                                           int bs, int tid) {
+    if (bs == kB && (K % 4) == 0 && (b0 % 4) == 0) panel_load_v<ASYM, true>(R, U, P1, K, b0, bs, tid);
+    else panel_load_v<ASYM, false>(R, U, P1, K, b0, bs, tid);
+}
+
+template <bool ASYM>
+__device__ __forceinline__ void panel_store(const PanelRegs<ASYM>& R, float* Up, float* Pp, float* rdiag, int bs,
+                                            int tid) {
+#pragma unroll
+    for (int i = 0; i < kPanelV; ++i) {
+        const int idx = tid + 256 * i, j = idx >> 5, c = (idx & 31) * 4;
+        const float r = j < bs ? __builtin_amdgcn_rcpf(R.rd[i]) : 0.f;   // 1 / U_jj to 1 ulp
+        if ((idx & 31) == 0) rdiag[j] = r;
+        for (int e = 0; e < 4; ++e) {
+            const int l = (c + e) & 15, m = (c + e) >> 4;
+            Up[(j * 16 + l) * 8 + m] = c + e > j ? R.uv[i][e] * r : 0.f;
+            if constexpr (ASYM) Pp[(j * 16 + l) * 8 + m] = R.pv[i][e];
+        }
+    }
+}
+
+template <bool ASYM>
+__device__ __forceinline__ void stage_panel(float* Up, float* Pp, float* rdiag, const float* U, const float* P1,
+                                            int64_t K, int64_t b0, int bs, int tid) {
+    PanelRegs<ASYM> R;
+    panel_load<ASYM>(R, U, P1, K, b0, bs, tid);
+    panel_store<ASYM>(R, Up, Pp, rdiag, bs, tid);
+}
+
+// Static groups: the scale (and reciprocal) of every step of the block for the workgroup's 16 channels, [step][channel].
+__device__ __forceinline__ void stage_static_scales(float* Ts, float* Trs, const BlockArgs& p, int64_t b0, int bs,
+                                                    int tid) {
+    for (int idx = tid; idx < kB * kChPerWG; idx += 256) {
+        const int j = idx >> 4;
+        const int64_t nc = (int64_t)blockIdx.x * kChPerWG + (idx & 15);
+        float sc = 1.0f;
+        if (j < bs && nc < p.N) {
+            const int64_t ko = p.perm ? (int64_t)p.perm[b0 + j] : b0 + j;
+            sc = p.gscales[(ko / p.G) * p.N + nc];
+        }
+        Ts[idx] = sc;
+        Trs[idx] = 1.0f / sc;
+    }
+}
+
+// Per-lane set-up of the loop state for the block at b0 (slots from `wsrc`, coordinate 16 m + l at wsrc[16 m + l]).
+template <bool CAE, int SM>
+__device__ __forceinline__ void init_lane(LaneState& st, StepConst& k, const BlockArgs& p, const float* wsrc,
+                                          const float* Up, const float* Pp, const float* Ts, const float* Trs,
+                                          int64_t b0, int tid) {
+    const int l = tid & 15;
+    const int64_t n = (int64_t)blockIdx.x * kChPerWG + (tid >> 4);
+    const bool live = n < p.N;
+    const int64_t nn = live ? n : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        st.qs[q] = 1.0f;
+        st.qrs[q] = 1.0f;
+    }
+    const float* w0row = CAE ? p.W0t + nn * p.ldt + b0 : nullptr;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        st.w[m] = wsrc[16 * m + l];
+        if constexpr (CAE) st.w0[m] = w0row[16 * m + l];
+    }
+    k.Up = Up; k.Pp = Pp; k.Ts = Ts; k.Trs = Trs;
+    if constexpr (SM == kScalePerChannel) {
+        st.s = p.scales[nn];
+        st.rs = p.rscale[nn];
+    } else {
+        st.s = 1.0f;
+        st.rs = 1.0f;
+    }
+    const float z = (float)(1 << (p.bits - 1));
+    k.qmax = (float)((1 << p.bits) - 1);
+    k.clo = -z;
+    k.chi = k.qmax - z;
+    k.l = l;
+    k.ch = tid >> 4;
+    k.G = p.G; k.b0 = b0; k.gscales = p.gscales;
+    k.N = p.N; k.n = n; k.live = live;
+}
+
+// End of a block: codes, errors, pre-rounding values and the loss from the kept pre-rounding values, with the step's
+// arithmetic.  Es (optional): the block's errors are also written to LDS as Es[channel][j] (row pitch kEsPitch).
+constexpr int kEsPitch = kB + 1;
+template <bool ASYM, bool CAE, int SM, bool WHOLE>
+__device__ __forceinline__ void block_epilogue(const LaneState& st, const StepConst& k, const BlockArgs& p,
+                                               const float* rdiag, const float* Ts, const float* Trs, int64_t b0,
+                                               int bs, float* Es) {
+    const int l = k.l;
+    const int64_t n = k.n;
+    const bool live = k.live;
+    const int64_t nn = live ? n : 0;
+    const float z = -k.clo;
+    float loss = 0.f;
+    uint8_t* crow = p.codes_t + nn * p.ldt + b0;
+    float* erow = p.E + nn * p.lde;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int j = 16 * m + l;
+        float s = st.s, rs = st.rs;
+        if constexpr (SM == kScaleDynamic) {
+            s = st.qs[m >> 1];
+            rs = st.qrs[m >> 1];
+        }
+        if constexpr (SM == kScaleStatic) {
+            s = Ts[j * 16 + k.ch];
+            rs = Trs[j * 16 + k.ch];
+        }
+        float eo = 0.f;   // the error the trailing updates use
+        if (WHOLE || j < bs) {
+            const float v = st.w[m] * rs;
+            const float c = signed_code(v, k);
+            const float r = rdiag[j];
+            const float e = fmaf(-c, s, st.w[m]) * r;
+            loss = fmaf(e, e, loss);
+            eo = CAE ? fmaf(-c, s, st.w0[m]) * r : e;
+            if (live) {
+                crow[j] = (uint8_t)(uint32_t)(c + z);
+                if (ASYM && !CAE) p.Wpre[n * p.lde + j] = st.w[m];
+                if (p.pre_round) p.pre_round[(b0 + j) * p.N + n] = v;
+            }
+        } else if (live && ASYM && !CAE) {
+            p.Wpre[n * p.lde + j] = 0.f;
+        }
+        if (live) erow[j] = eo;
+        if (Es) Es[k.ch * kEsPitch + j] = eo;
+    }
+    // the channel's loss: sum over its 16 lanes
+    loss += __shfl_xor(loss, 8, 16);
+    loss += __shfl_xor(loss, 4, 16);
+    loss += __shfl_xor(loss, 2, 16);
+    loss += __shfl_xor(loss, 1, 16);
+    if (l == 0 && live) p.loss_acc[n] += 0.5f * loss;
+}
+
+// One block of 128 coordinates per launch (the asymmetric variants).  WHOLE: the block has all 128 coordinates
+// (every block but a ragged last one), so the steps carry no bounds test.
 template <bool ASYM, bool CAE, int SM, bool WHOLE>
 __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
     __shared__ __attribute__((aligned(16))) float Up[kB * kB];               // [row j][16 lanes][8 slots]
@@ -362,138 +543,237 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
     const int tid = threadIdx.x;
     const int64_t b0 = p.b0;
     const int bs = WHOLE ? kB : p.bs;
-    // Stage the panel rows b0..b0+bs-1, columns b0..b0+127 as [row j][lane l][slot m] for column 16 m + l: U_jk / U_jj
-    // for k > j (zero on and below the diagonal and beyond the block), P1 as it is (strictly upper).  All global loads
-    // are issued before the LDS stores.
-    {
-        constexpr int kV = kB * kB / 4 / 256;     // 16-byte vectors per thread
-        const bool vec = bs == kB && (p.K % 4) == 0 && (b0 % 4) == 0;
-        f32x4 uv[kV], pv[ASYM ? kV : 1];
-        float rd[kV];
-#pragma unroll
-        for (int i = 0; i < kV; ++i) {
-            const int idx = tid + 256 * i, j = idx >> 5, c = (idx & 31) * 4;
-            const int64_t off = (b0 + j) * p.K + b0 + c;
-            f32x4 u = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
-            rd[i] = 0.f;
-            if (vec) {
-                u = *reinterpret_cast<const f32x4*>(p.U + off);
-                if constexpr (ASYM) q = *reinterpret_cast<const f32x4*>(p.P1 + off);
-                rd[i] = p.U[(b0 + j) * p.K + b0 + j];
-            } else if (j < bs) {
-                for (int e = 0; e < 4; ++e)
-                    if (c + e < bs) {
-                        u[e] = p.U[off + e];
-                        if constexpr (ASYM) q[e] = p.P1[off + e];
-                    }
-                rd[i] = p.U[(b0 + j) * p.K + b0 + j];
-            }
-            uv[i] = u;
-            if constexpr (ASYM) pv[i] = q;
-        }
-#pragma unroll
-        for (int i = 0; i < kV; ++i) {
-            const int idx = tid + 256 * i, j = idx >> 5, c = (idx & 31) * 4;
-            const float r = j < bs ? 1.0f / rd[i] : 0.f;
-            if ((idx & 31) == 0) rdiag[j] = r;
-            for (int e = 0; e < 4; ++e) {
-                const int l = (c + e) & 15, m = (c + e) >> 4;
-                Up[(j * 16 + l) * 8 + m] = c + e > j ? uv[i][e] * r : 0.f;
-                if constexpr (ASYM) Pp[(j * 16 + l) * 8 + m] = pv[i][e];
-            }
-        }
-    }
-    if constexpr (SM == kScaleStatic) {
-        for (int idx = tid; idx < kB * kChPerWG; idx += 256) {
-            const int j = idx >> 4;
-            const int64_t nc = (int64_t)blockIdx.x * kChPerWG + (idx & 15);
-            float sc = 1.0f;
-            if (j < bs && nc < p.N) {
-                const int64_t ko = p.perm ? (int64_t)p.perm[b0 + j] : b0 + j;
-                sc = p.gscales[(ko / p.G) * p.N + nc];
-            }
-            Ts[idx] = sc;
-            Trs[idx] = 1.0f / sc;
-        }
-    }
+    stage_panel<ASYM>(Up, Pp, rdiag, p.U, p.P1, p.K, b0, bs, tid);
+    if constexpr (SM == kScaleStatic) stage_static_scales(Ts, Trs, p, b0, bs, tid);
     __syncthreads();
 
-    const int lane = tid & 63, l = lane & 15;
     const int64_t n = (int64_t)blockIdx.x * kChPerWG + (tid >> 4);
-    const bool live = n < p.N;
-    const int64_t nn = live ? n : 0;
-
     LaneState st;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        st.qs[q] = 1.0f;
-        st.qrs[q] = 1.0f;
-    }
-    const float* wrow = p.Wt + nn * p.ldt + b0;
-    const float* w0row = CAE ? p.W0t + nn * p.ldt + b0 : nullptr;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        st.w[m] = wrow[16 * m + l];
-        if constexpr (CAE) st.w0[m] = w0row[16 * m + l];
-    }
     StepConst k;
-    k.Up = Up; k.Pp = Pp; k.Ts = Ts; k.Trs = Trs;
-    if constexpr (SM == kScalePerChannel) {
-        st.s = p.scales[nn];
-        st.rs = p.rscale[nn];
-    } else {
-        st.s = 1.0f;
-        st.rs = 1.0f;
-    }
-    const float z = (float)(1 << (p.bits - 1));
-    k.qmax = (float)((1 << p.bits) - 1);
-    k.clo = -z;
-    k.chi = k.qmax - z;
-    k.l = l;
-    k.ch = tid >> 4;
-    k.G = p.G; k.b0 = b0; k.gscales = p.gscales;
-    k.N = p.N; k.n = n; k.live = live;
+    init_lane<CAE, SM>(st, k, p, p.Wt + (n < p.N ? n : 0) * p.ldt + b0, Up, Pp, Ts, Trs, b0, tid);
     run_steps<ASYM, CAE, SM, WHOLE>(st, k, bs, std::make_integer_sequence<int, kB>{});
+    block_epilogue<ASYM, CAE, SM, WHOLE>(st, k, p, rdiag, Ts, Trs, b0, bs, nullptr);
+}
 
-    // Codes, errors, pre-rounding values and the loss from the kept pre-rounding values, with the step's arithmetic.
-    float loss = 0.f;
-    uint8_t* crow = p.codes_t + nn * p.ldt + b0;
-    float* erow = p.E + nn * p.lde;
+// One super-block of up to kSB coordinates per launch for 16 channels (the variants without the asymmetric term):
+// the channels' weights of the super-block stay in LDS (Ws, 16 x kSB fp32), the blocks run one after the other,
+// and after each block the rows of the super-block still to come get its update W -= E_B U[B, rows] right here,
+// 16 channels x 16 rows per fp32 MFMA tile (v_mfma_f32_16x16x4f32: A = -E (channel x coordinate j), B = U rows; the
+// product is added to Ws once), so no separate product runs between the blocks.  Only the rows after the super-block are left to the trailing
+// product that follows the launch.
+constexpr int kSBS = 8 * kB;          // super-block of the strip kernel (its near rows are updated in-kernel)
+constexpr int kWsPitch = kSBS + 16;   // 16-float pad: the four channels an MFMA accumulator row set touches hit disjoint banks
+constexpr int64_t kStripMaxWG = 256;   // one workgroup per CU of the chip
+
+struct StripArgs {
+    BlockArgs p;
+    int64_t sb0, sb1;      // super-block [sb0, sb1)
+    const uint16_t* Usp;   // the super-block's diagonal block of U in three bf16 parts (split_diag_kernel), per group
+};
+
+// fp32-accurate products on the bf16 MFMA: v = h0 + h1 + h2 + O(2^-24 |v|), each part the round-to-nearest-even bf16
+// of the remainder; the six part products of order <= 2 summed in fp32 equal the fp32 product to that order.  Two
+// values at once, one packed conversion per part; word q holds part q of `lo` (low half) and of `hi` (high half).
+typedef __attribute__((ext_vector_type(2))) float f32x2_q;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_q;
+__device__ __forceinline__ void split3_pair(float lo, float hi, uint32_t& w0, uint32_t& w1, uint32_t& w2) {
+    const f32x2_q v = {lo, hi};
+    const bf16x2_q b0 = __builtin_convertvector(v, bf16x2_q);
+    const f32x2_q r1 = v - __builtin_convertvector(b0, f32x2_q);
+    const bf16x2_q b1 = __builtin_convertvector(r1, bf16x2_q);
+    const f32x2_q r2 = r1 - __builtin_convertvector(b1, f32x2_q);
+    const bf16x2_q b2 = __builtin_convertvector(r2, bf16x2_q);
+    w0 = __builtin_bit_cast(uint32_t, b0);
+    w1 = __builtin_bit_cast(uint32_t, b1);
+    w2 = __builtin_bit_cast(uint32_t, b2);
+}
+
+// Eight values -> their three parts, each as 8 bf16 in 16 bytes (element i = value i).
+__device__ __forceinline__ void split3_oct(const float (&v)[8], u32x4 (&w)[3]) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const int j = 16 * m + l;
-        float s = st.s, rs = st.rs;
-        if constexpr (SM == kScaleDynamic) {
-            s = st.qs[m >> 1];
-            rs = st.qrs[m >> 1];
+    for (int e = 0; e < 4; ++e) {
+        uint32_t x0, x1, x2;
+        split3_pair(v[2 * e], v[2 * e + 1], x0, x1, x2);
+        w[0][e] = x0;
+        w[1][e] = x1;
+        w[2][e] = x2;
+    }
+}
+
+// The diagonal block [sb0, sb0 + kSBS)^2 of every group's U, split into three bf16 parts, in the layout of the
+// near update's MFMA B operand: part q, row octet o (rows sb0 + 8 o .. + 7), column sb0 + r as 8 bf16 at
+// Usp[((q * kSBS / 8 + o) * kSBS + r) * 8] (group g at + g 3 kSBS^2).  Zero beyond K.  One thread per (o, r).
+__global__ __launch_bounds__(256) void split_diag_kernel(const float* U, int64_t K, int64_t u_stride, int64_t sb0,
+                                                         uint16_t* Usp) {
+    const int64_t g = blockIdx.y;
+    U += g * u_stride;
+    Usp += g * (int64_t)3 * kSBS * kSBS;
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    const int o = idx / kSBS, r = idx % kSBS;
+    const int64_t c = sb0 + r;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t j = sb0 + 8 * o + i;
+        v[i] = (j < K && c < K) ? U[j * K + c] : 0.f;
+    }
+    u32x4 w[3];
+    split3_oct(v, w);
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+        *reinterpret_cast<u32x4*>(Usp + (((int64_t)q * (kSBS / 8) + o) * kSBS + r) * 8) = w[q];
+}
+
+// The near update's tile slots of one wave (see the strip kernel): slot I computes tile wave + 4 I from buffer I % 2
+// after issuing the loads of slot I + 1 into buffer (I + 1) % 2.
+template <int I, typename LB, typename UP>
+__device__ __forceinline__ void near_slot(int64_t ntile, int wave, u32x4 (&ub)[2][kB / 32][3], LB& load_b, UP& update) {
+    const int64_t t = wave + 4 * I;
+    if (t >= ntile) return;
+    if (t + 4 < ntile) load_b(t + 4, ub[(I + 1) % 2]);
+    update(t, ub[I % 2]);
+}
+
+template <typename LB, typename UP, int... Is>
+__device__ __forceinline__ void near_slots(int64_t ntile, int wave, u32x4 (&ub)[2][kB / 32][3], LB& load_b, UP& update,
+                                           std::integer_sequence<int, Is...>) {
+    (near_slot<Is>(ntile, wave, ub, load_b, update), ...);
+}
+
+template <bool CAE, int SM>
+__global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
+    __shared__ __attribute__((aligned(16))) float Ws[kChPerWG * kWsPitch];   // [channel][coordinate - sb0]
+    __shared__ __attribute__((aligned(16))) float Up[kB * kB];
+    __shared__ float rdiag[kB];
+    __shared__ float Es[kChPerWG * kEsPitch];                                // [channel][j] this block's errors
+    __shared__ float Ts[SM == kScaleStatic ? kB * kChPerWG : 1];
+    __shared__ float Trs[SM == kScaleStatic ? kB * kChPerWG : 1];
+
+    BlockArgs& p = a.p;
+    if (p.st->flags) return;
+    {
+        const int64_t g = (int64_t)blockIdx.x * kChPerWG / p.gs;
+        p.U += g * p.u_stride;
+        if (p.perm) p.perm += g * p.K;
+        a.Usp += g * (int64_t)3 * kSBS * kSBS;
+    }
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t sb0 = a.sb0, sb1 = a.sb1;
+    const int64_t nbase = (int64_t)blockIdx.x * kChPerWG;
+    // the super-block's weights of the 16 channels (zero for channels beyond N; Wt is zero-padded up to ldt): every
+    // load issued before the LDS stores
+    const int64_t width = ((sb1 - sb0) + kB - 1) / kB * kB;
+    {
+        constexpr int kWV = kChPerWG * kSBS / 4 / 256;   // 16-byte vectors per thread for a full super-block
+        f32x4 wv[kWV];
+#pragma unroll
+        for (int i = 0; i < kWV; ++i) {
+            const int idx = tid + 256 * i, ch = idx / (kSBS / 4);
+            const int64_t c4 = (int64_t)(idx % (kSBS / 4)) * 4;
+            wv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (c4 < width && nbase + ch < p.N) wv[i] = *reinterpret_cast<const f32x4*>(p.Wt + (nbase + ch) * p.ldt + sb0 + c4);
         }
-        if constexpr (SM == kScaleStatic) {
-            s = Ts[j * 16 + k.ch];
-            rs = Trs[j * 16 + k.ch];
-        }
-        if (WHOLE || j < bs) {
-            const float v = st.w[m] * rs;
-            const float c = signed_code(v, k);
-            const float r = rdiag[j];
-            const float e = fmaf(-c, s, st.w[m]) * r;
-            loss = fmaf(e, e, loss);
-            if (live) {
-                crow[j] = (uint8_t)(uint32_t)(c + z);
-                erow[j] = CAE ? fmaf(-c, s, st.w0[m]) * r : e;
-                if (ASYM && !CAE) p.Wpre[n * p.lde + j] = st.w[m];
-                if (p.pre_round) p.pre_round[(b0 + j) * p.N + n] = v;
-            }
-        } else if (live) {
-            erow[j] = 0.f;
-            if (ASYM && !CAE) p.Wpre[n * p.lde + j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < kWV; ++i) {
+            const int idx = tid + 256 * i, ch = idx / (kSBS / 4);
+            const int c4 = (idx % (kSBS / 4)) * 4;
+            *reinterpret_cast<f32x4*>(&Ws[ch * kWsPitch + c4]) = wv[i];
         }
     }
-    // the channel's loss: sum over its 16 lanes
-    loss += __shfl_xor(loss, 8, 16);
-    loss += __shfl_xor(loss, 4, 16);
-    loss += __shfl_xor(loss, 2, 16);
-    loss += __shfl_xor(loss, 1, 16);
-    if (l == 0 && live) p.loss_acc[n] += 0.5f * loss;
+    stage_panel<false>(Up, nullptr, rdiag, p.U, nullptr, p.K, sb0, (int)min<int64_t>(kB, p.K - sb0), tid);
+    if constexpr (SM == kScaleStatic) stage_static_scales(Ts, Trs, p, sb0, (int)min<int64_t>(kB, p.K - sb0), tid);
+    __syncthreads();
+
+    for (int64_t b0 = sb0; b0 < sb1; b0 += kB) {
+        const int bs = (int)min<int64_t>(kB, p.K - b0);
+        // here: this block's panel is staged and Ws holds its compensated weights
+        BlockArgs pb = p;
+        pb.E = p.E + (b0 - sb0);
+        LaneState st;
+        StepConst k;
+        init_lane<CAE, SM>(st, k, pb, &Ws[(tid >> 4) * kWsPitch + (b0 - sb0)], Up, nullptr, Ts, Trs, b0, tid);
+        // the next block's panel: with per-channel scales and no CAE term its loads are issued now and are in flight
+        // during the steps (the other variants have too few registers left and load it after the near update); it is
+        // stored to LDS after the near update either way
+        constexpr bool kEarly = SM == kScalePerChannel && !CAE;
+        const int64_t bn = b0 + kB;
+        const bool next = bn < sb1;
+        const int bsn = next ? (int)min<int64_t>(kB, p.K - bn) : 0;
+        PanelRegs<false> nxt;
+        if (kEarly && next) panel_load<false>(nxt, p.U, nullptr, p.K, bn, bsn, tid);
+        if (bs == kB) {
+            run_steps<false, CAE, SM, true>(st, k, bs, std::make_integer_sequence<int, kB>{});
+            block_epilogue<false, CAE, SM, true>(st, k, pb, rdiag, Ts, Trs, b0, bs, Es);
+        } else {
+            run_steps<false, CAE, SM, false>(st, k, bs, std::make_integer_sequence<int, kB>{});
+            block_epilogue<false, CAE, SM, false>(st, k, pb, rdiag, Ts, Trs, b0, bs, Es);
+        }
+        __syncthreads();   // Es complete; the panel and this block's slots of Ws are no longer read
+
+
+        // rows b1..sb1-1 of the super-block: Ws[ch][r] -= sum_j Es[ch][j] U[b0 + j][r]  (whole blocks only: a ragged
+        // block is the last of the layer)
+        const int64_t b1 = b0 + bs;
+        if (b1 < sb1) {
+            // A operand of 32-coordinate chunk c: parts of -E[channel lane % 16][32 c + 8 (lane / 16) + i], i = 0..7
+            u32x4 ea[kB / 32][3];
+#pragma unroll
+            for (int c = 0; c < kB / 32; ++c) {
+                float v[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[i] = -Es[(lane & 15) * kEsPitch + 32 * c + 8 * (lane >> 4) + i];
+                split3_oct(v, ea[c]);
+            }
+            const int64_t ntile = (sb1 - b1 + 15) / 16;
+            const int oct0 = (int)((b0 - sb0) / 8) + (lane >> 4);
+            // B operand of chunk c for tile t: parts of U[b0 + 32 c + 8 (lane / 16) + i][b1 + 16 t + lane % 16]
+            auto load_b = [&](int64_t t, u32x4 (&bq)[kB / 32][3]) {
+                const int64_t rl = b1 - sb0 + 16 * t + (lane & 15);
+#pragma unroll
+                for (int c = 0; c < kB / 32; ++c)
+#pragma unroll
+                    for (int q = 0; q < 3; ++q)
+                        bq[c][q] = *reinterpret_cast<const u32x4*>(
+                            a.Usp + (((int64_t)q * (kSBS / 8) + oct0 + 4 * c) * kSBS + rl) * 8);
+            };
+            // Ws[channels][tile t] += -E U over the 128 coordinates of the block: per chunk the six part products
+            // (small parts first) on v_mfma_f32_16x16x32_bf16, two accumulators, summed and added to the weights once
+            // (one rounding of the weights per block, as by a separate product with beta = 1)
+            auto update = [&](int64_t t, const u32x4 (&bq)[kB / 32][3]) {
+                f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int c = 0; c < kB / 32; ++c) {
+                    f32x4& ac = acc[c & 1];
+                    auto mm = [&](const u32x4& x, const u32x4& y) {
+                        ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
+                                                                     __builtin_bit_cast(bf16x8, y), ac, 0, 0, 0);
+                    };
+                    mm(ea[c][2], bq[c][0]);
+                    mm(ea[c][1], bq[c][1]);
+                    mm(ea[c][0], bq[c][2]);
+                    mm(ea[c][1], bq[c][0]);
+                    mm(ea[c][0], bq[c][1]);
+                    mm(ea[c][0], bq[c][0]);
+                }
+                const f32x4 sum = acc[0] + acc[1];
+                float* wc = &Ws[(4 * (lane >> 4)) * kWsPitch + (b1 + 16 * t + (lane & 15) - sb0)];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) wc[q * kWsPitch] += sum[q];
+            };
+            // tiles wave + 4 i, i = 0..kSBS/64-1 (at most (kSBS - kB) / 16 tiles per block, a quarter per wave), in
+            // a fully unrolled sequence so that the two operand buffers stay distinct registers: slot i loads the
+            // B operands of slot i + 1 and computes slot i
+            u32x4 ub[2][kB / 32][3];
+            if (wave < ntile) load_b(wave, ub[0]);
+            near_slots(ntile, wave, ub, load_b, update, std::make_integer_sequence<int, (kSBS - kB) / 64>{});
+        }
+        if (next) {   // the near update above does not read the LDS panel
+            if (!kEarly) panel_load<false>(nxt, p.U, nullptr, p.K, bn, bsn, tid);
+            panel_store<false>(nxt, Up, nullptr, rdiag, bsn, tid);
+            if constexpr (SM == kScaleStatic) stage_static_scales(Ts, Trs, p, bn, bsn, tid);
+        }
+        __syncthreads();   // Ws updated and the next panel staged before the next block reads them
+    }
 }
 
 // codes_t (N x ldt) -> codes (K x N view with strides); W_hat = s (c - z) in the weight dtype; losses copy.
@@ -570,10 +850,15 @@ struct QuantLayout {
     float* E;
     float* Wpre;
     float* W0t;
+    uint16_t* Usp;
     size_t bytes;
 };
 
-QuantLayout carve(void* ws, int64_t K, int64_t N, bool asym, bool cae) {
+// The column loop of N channels in `groups` output-channel groups runs on the strip kernel when it has no asymmetric
+// term and one workgroup per CU covers every channel.
+bool strip_path(int64_t N, bool asym) { return !asym && ceil_div(N, kChPerWG) <= kStripMaxWG; }
+
+QuantLayout carve(void* ws, int64_t K, int64_t N, bool asym, bool cae, int64_t groups) {
     const int64_t ldt = ceil_div(std::max<int64_t>(K, 1), kB) * kB;
     Carver c(ws);
     QuantLayout L;
@@ -586,14 +871,15 @@ QuantLayout carve(void* ws, int64_t K, int64_t N, bool asym, bool cae) {
     L.E = c.take<float>((size_t)N * kSB);
     L.Wpre = asym && !cae ? c.take<float>((size_t)N * kSB) : nullptr;
     L.W0t = cae ? c.take<float>((size_t)N * ldt) : nullptr;
+    L.Usp = strip_path(N, asym) ? c.take<uint16_t>((size_t)std::max<int64_t>(groups, 1) * 3 * kSBS * kSBS) : nullptr;
     L.bytes = c.bytes();
     return L;
 }
 
 }  // namespace
 
-size_t quantize_workspace_bytes(int64_t K, int64_t N, bool asym, bool cae) {
-    return carve(nullptr, K, N, asym, cae).bytes;
+size_t quantize_workspace_bytes(int64_t K, int64_t N, bool asym, bool cae, int64_t groups) {
+    return carve(nullptr, K, N, asym, cae, groups).bytes;
 }
 
 gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t stream) {
@@ -601,8 +887,8 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
     const int64_t K = a.K, N = a.N;
     const int64_t ldt = ceil_div(std::max<int64_t>(K, 1), kB) * kB;
     const bool cae = a.cae;
-    QuantLayout L = carve(workspace, K, N, asym, cae);
     const int64_t groups = std::max<int64_t>(a.groups, 1), gs = N / groups;   // output-channel groups
+    QuantLayout L = carve(workspace, K, N, asym, cae, groups);
 
     const int64_t G = a.groupsize;
     const int sm = G == 0 ? kScalePerChannel : (a.static_groups ? kScaleStatic : kScaleDynamic);
@@ -671,8 +957,41 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
         return gemm_f32(g, groups, stream) == hipSuccess;
     };
 
-    for (int64_t sb0 = 0; sb0 < K; sb0 += kSB) {
-        const int64_t sb1 = std::min<int64_t>(K, sb0 + kSB);
+    // Without the asymmetric term, and when one workgroup per CU covers every channel (the strip kernel's LDS
+    // allows one per CU): each super-block of kSBS coordinates in one launch, its near rows updated inside.
+    const bool strip = strip_path(N, asym);
+    const int64_t sbw = strip ? kSBS : kSB;
+    for (int64_t sb0 = 0; sb0 < K; sb0 += sbw) {
+        const int64_t sb1 = std::min<int64_t>(K, sb0 + sbw);
+        if (strip) {
+            StripArgs sa;
+            BlockArgs& p = sa.p;
+            p.Wt = L.Wt; p.ldt = ldt; p.U = a.U; p.P1 = nullptr; p.K = K; p.N = N; p.b0 = sb0; p.bs = 0;
+            p.scales = a.scales; p.rscale = L.rscale; p.bits = a.bits; p.codes_t = L.codes_t;
+            p.E = L.E; p.Wpre = nullptr; p.lde = kSB;
+            p.W0t = L.W0t; p.loss_acc = L.loss_acc; p.pre_round = a.pre_round; p.st = L.st;
+            p.G = G; p.perm = a.perm; p.gscales = a.scales;
+            p.gs = gs; p.u_stride = a.u_stride;
+            sa.sb0 = sb0; sa.sb1 = sb1; sa.Usp = L.Usp;
+            dim3 grid((unsigned)ceil_div(N, kChPerWG));
+            {
+                TimerScope ts(stream, GPTQ_TIMER_LOOP);
+                if (sb0 + kB < sb1) {   // near updates happen: split the diagonal block of every group's U
+                    hipLaunchKernelGGL(split_diag_kernel, dim3(kSBS / 8 * kSBS / 256, (unsigned)groups), dim3(256), 0,
+                                       stream, a.U, K, a.u_stride, sb0, L.Usp);
+                    GPTQ_LAUNCH_CHECK();
+                }
+#define GPTQ_STRIP(C_)                                                                                               \
+    if (sm == kScaleDynamic) hipLaunchKernelGGL((quant_strip_kernel<C_, kScaleDynamic>), grid, dim3(256), 0, stream, sa); \
+    else if (sm == kScaleStatic) hipLaunchKernelGGL((quant_strip_kernel<C_, kScaleStatic>), grid, dim3(256), 0, stream, sa); \
+    else hipLaunchKernelGGL((quant_strip_kernel<C_, kScalePerChannel>), grid, dim3(256), 0, stream, sa);
+                if (cae) { GPTQ_STRIP(true) } else { GPTQ_STRIP(false) }
+#undef GPTQ_STRIP
+                GPTQ_LAUNCH_CHECK();
+            }
+            if (sb1 < K && !trailing(sb1, K, sb0, sb1 - sb0, L.E, nullptr)) return GPTQ_ERR_HIP;
+            continue;
+        }
         for (int64_t b0 = sb0; b0 < sb1; b0 += kB) {
             const int bs = (int)std::min<int64_t>(kB, K - b0);
             float* Eb = L.E + (b0 - sb0);

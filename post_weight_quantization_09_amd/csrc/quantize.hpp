@@ -23,7 +23,7 @@ struct QuantizeArgs {
     float* scales = nullptr; void* W_hat = nullptr; float* losses = nullptr; float* pre_round = nullptr;
 };
 
-size_t quantize_workspace_bytes(int64_t K, int64_t N, bool asym, bool cae);
+size_t quantize_workspace_bytes(int64_t K, int64_t N, bool asym, bool cae, int64_t groups = 1);
 
 // Enqueues the whole loop on `stream`; rejected inputs latch kDevNonFinite in the workspace status word.
 gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t stream);
