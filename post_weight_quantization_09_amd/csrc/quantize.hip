@@ -563,7 +563,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
 // product that follows the launch.
 constexpr int kSBS = 8 * kB;          // super-block of the strip kernel (its near rows are updated in-kernel)
 constexpr int kWsPitch = kSBS + 16;   // 16-float pad: the four channels an MFMA accumulator row set touches hit disjoint banks
-constexpr int64_t kStripMaxWG = 256;   // one workgroup per CU of the chip
+constexpr int64_t kStripMaxWG = 512;   // up to two rounds of one workgroup per CU
 
 struct StripArgs {
     BlockArgs p;
