@@ -138,24 +138,25 @@ __device__ __forceinline__ int slab_off(int row, int col) { return row * kGT + (
 // MFMA fragments of one 16-token k-step for 4 x 32 columns starting at column `base` of a slab: b64 reads of
 // 4 columns x 8 token rows, regrouped by v_perm so that frag[a] holds column base + 4 (l % 32) + a over tokens
 // 16 ks + 8 (l / 32) + 0..7 (lane l).  The reads are row-contiguous across lanes (conflict-free).
+__device__ __forceinline__ u32x2 frag_row(const uint16_t* slab, int base, int ks, int lane, int s8) {
+    const int row = ks * 16 + 8 * (lane >> 5) + s8;
+    return *reinterpret_cast<const u32x2*>(slab + slab_off(row, base + 4 * (lane & 31)));
+}
+// Token rows 2s and 2s+1 of the 8 read rows -> element s of the 4 column fragments.
+__device__ __forceinline__ void frag_regroup(const u32x2 (&raw)[8], int s, u32x4 (&frag)[4]) {
+    const uint32_t lo0 = raw[2 * s].x, lo1 = raw[2 * s + 1].x;
+    const uint32_t hi0 = raw[2 * s].y, hi1 = raw[2 * s + 1].y;
+    frag[0][s] = __builtin_amdgcn_perm(lo1, lo0, 0x05040100u);
+    frag[1][s] = __builtin_amdgcn_perm(lo1, lo0, 0x07060302u);
+    frag[2][s] = __builtin_amdgcn_perm(hi1, hi0, 0x05040100u);
+    frag[3][s] = __builtin_amdgcn_perm(hi1, hi0, 0x07060302u);
+}
 __device__ __forceinline__ void load_frags(const uint16_t* slab, int base, int ks, int lane, u32x4 (&frag)[4]) {
-    const int g = lane >> 5, r32 = lane & 31;
     u32x2 raw[8];
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-        const int row = ks * 16 + 8 * g + s8;
-        raw[s8] = *reinterpret_cast<const u32x2*>(slab + slab_off(row, base + 4 * r32));
-    }
-    // 8 token rows x 4 columns -> 4 column vectors of 8 tokens
+    for (int s8 = 0; s8 < 8; ++s8) raw[s8] = frag_row(slab, base, ks, lane, s8);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const uint32_t lo0 = raw[2 * s].x, lo1 = raw[2 * s + 1].x;
-        const uint32_t hi0 = raw[2 * s].y, hi1 = raw[2 * s + 1].y;
-        frag[0][s] = __builtin_amdgcn_perm(lo1, lo0, 0x05040100u);
-        frag[1][s] = __builtin_amdgcn_perm(lo1, lo0, 0x07060302u);
-        frag[2][s] = __builtin_amdgcn_perm(hi1, hi0, 0x05040100u);
-        frag[3][s] = __builtin_amdgcn_perm(hi1, hi0, 0x07060302u);
-    }
+    for (int s = 0; s < 4; ++s) frag_regroup(raw, s, frag);
 }
 
 // (row, col) of accumulator element r of MFMA block (a, b) for `lane` inside a wave's 128 x 128 quadrant.
@@ -312,11 +313,14 @@ void gram_bf16_kernel(GramArgs p) {
 // consumed.  Wait counts and barriers are explicit: the compiler cannot see that a DMA'd stage belongs to a
 // different ring slot than the one being read and would otherwise drain all loads at every barrier.
 // Per stage st:  [MFMA (st, k-step 0) || LDS reads + v_perm of (st, k-step 1)]
-//                [wait for this wave's loads of st+1; barrier; issue loads of st+RING-1 into the freed slot]
-//                [MFMA (st, k-step 1) || LDS reads + v_perm of (st+1, k-step 0)]
-// Ring depth, measured on MI355X: 3 slots when the token range is split (every XCD's 32 workgroups on the
-// same tokens: 4% faster at 4096 features, 1% at 28672; a deeper ring only queues more requests in the L2);
-// 4 slots for unsplit launches (short token ranges).
+//                [wait for this wave's loads of st+1; barrier]
+//                [MFMA (st, k-step 1) || loads of st+RING-1 into the freed slot, LDS reads + v_perm of
+//                 (st+1, k-step 0)]
+// Ring depth, measured on MI355X with this schedule: 4 slots.  Against 3 slots: 6% faster at 2M tokens x
+// 4096 features, 2% at 131072 x 28672; 5 slots is slower again (the extra requests only queue in the L2).
+// The launch is power-bound on random bf16 data: the shader clock runs at about 1.5-1.6 GHz with loads and
+// MFMAs overlapped, 1.9 GHz for the MFMA work alone (operands resident in LDS) and 2.4 GHz for the loads
+// alone, and the two alone take 79% (2M x 4096) and 72% (131072 x 28672) of the overlapped time.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Wait until at most `later` stages (8 DMA instructions each) of this wave are still in flight, then
@@ -335,7 +339,8 @@ void gram_bf16_lds_kernel(GramArgs p) {
     static_assert(kRing >= 3 && kRing <= 5, "ring slots: 3..5 (32 KB each, 160 KB of LDS)");
     __shared__ __attribute__((aligned(1024))) uint16_t ring[kRing][2][kGK][kGT];
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // the wave index is uniform: keep it (and the LDS addresses derived from it) in scalar registers
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wi = wave >> 1, wj = wave & 1;
     int split, tile;
     const int bid = blockIdx.x;
@@ -355,38 +360,70 @@ void gram_bf16_lds_kernel(GramArgs p) {
 
     // This wave DMAs token rows 8*wave .. 8*wave+7 of both slabs: 8 instructions of 1 KB (two 512-byte
     // rows each: lanes 0-31 the first row, lanes 32-63 the second; lane l lands in, and fetches, 16-byte
-    // chunk l % 32 of its row).
+    // chunk l % 32 of its row).  Instruction j: rows 8*wave + 2*(j/2) + 0..1 of operand j % 2.
     const int lrow = 8 * wave + (lane >> 5);
     const uint16_t* XA = p.XA ? p.XA : p.X;          // A-side operand (the mismatch for the cross term)
     const int64_t lda = p.XA ? p.ldxa : p.ldx;
     const uint16_t* srcA = XA + (int64_t)bi * kGT + (lane & 31) * 8;
     const uint16_t* srcB = p.X + (int64_t)bj * kGT + (lane & 31) * 8;
-    auto issue = [&](int64_t st) {
-        const int slot = (int)((uint32_t)st % (uint32_t)kRing);
-        const int64_t tb = t0 + st * kGK + lrow;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t tok = tb + 2 * i;
-            __builtin_amdgcn_global_load_lds((const void*)(srcA + tok * lda),
-                                             (lds_void_t*)&ring[slot][0][8 * wave + 2 * i][0], 16, 0, 0);
+    auto slot_of = [](int64_t st) { return (int)((uint32_t)st % (uint32_t)kRing); };
+    auto issue_one = [&](int64_t st, int j) {
+        const int slot = slot_of(st);
+        const int64_t tok = t0 + st * kGK + lrow + 2 * (j >> 1);
+        if (j & 1)
             __builtin_amdgcn_global_load_lds((const void*)(srcB + tok * p.ldx),
-                                             (lds_void_t*)&ring[slot][1][8 * wave + 2 * i][0], 16, 0, 0);
-        }
+                                             (lds_void_t*)&ring[slot][1][8 * wave + 2 * (j >> 1)][0], 16, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds((const void*)(srcA + tok * lda),
+                                             (lds_void_t*)&ring[slot][0][8 * wave + 2 * (j >> 1)][0], 16, 0, 0);
+    };
+    auto issue = [&](int64_t st) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) issue_one(st, j);
     };
     auto prep = [&](int64_t st, int ks, u32x4 (&va)[4], u32x4 (&vb)[4]) {
-        const int slot = (int)((uint32_t)st % (uint32_t)kRing);
+        const int slot = slot_of(st);
         load_frags(&ring[slot][0][0][0], wi * 128, ks, lane, va);
         load_frags(&ring[slot][1][0][0], wj * 128, ks, lane, vb);
     };
+    auto mfma1 = [&](int i, const u32x4 (&va)[4], const u32x4 (&vb)[4]) {
+        const int a = i >> 2, b = i & 3;
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[a]),
+                                                           __builtin_bit_cast(bf16x8, vb[b]), acc[a][b], 0, 0, 0);
+    };
+    // One k-step: the 16 MFMAs on (va, vb), each followed by a fixed share of the next k-step's operand work,
+    // pinned in place with scheduling barriers (the scheduler otherwise groups all MFMAs together and leaves
+    // the LDS reads and the regrouping to run on their own): after MFMAs 0-3 the LDS reads of two token rows
+    // of (st_n, ks_n) for A and B; after MFMAs 0-7, if `dma`, DMA instruction i of stage `st_dma`; after MFMAs
+    // 8-15 the regrouping of one fragment element (A for 8-11, B for 12-15).  The last reads are consumed
+    // 4 MFMAs (128 MFMA cycles) after their issue.
+    auto kstep = [&](const u32x4 (&va)[4], const u32x4 (&vb)[4], int64_t st_n, int ks_n, u32x4 (&na)[4],
+                     u32x4 (&nb)[4], bool dma, int64_t st_dma) {
+        const int sl = slot_of(st_n);
+        const uint16_t* slabA = &ring[sl][0][0][0];
+        const uint16_t* slabB = &ring[sl][1][0][0];
+        u32x2 ra[8], rb[8];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            mfma1(i, va, vb);
+            if (i < 8 && dma) issue_one(st_dma, i);
+            if (i < 4) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    ra[2 * i + h] = frag_row(slabA, wi * 128, ks_n, lane, 2 * i + h);
+                    rb[2 * i + h] = frag_row(slabB, wj * 128, ks_n, lane, 2 * i + h);
+                }
+            } else if (i >= 8 && i < 12) {
+                frag_regroup(ra, i - 8, na);
+            } else if (i >= 12) {
+                frag_regroup(rb, i - 12, nb);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
     auto mfma = [&](const u32x4 (&va)[4], const u32x4 (&vb)[4]) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const bf16x8 av = __builtin_bit_cast(bf16x8, va[a]);
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, vb[b]), acc[a][b],
-                                                                   0, 0, 0);
-        }
+        for (int i = 0; i < 16; ++i) mfma1(i, va, vb);
     };
 
     // Stage s is DMA'd kRing-1 stages ahead of its use: issued after the barrier of iteration s-kRing+1,
@@ -398,20 +435,26 @@ void gram_bf16_lds_kernel(GramArgs p) {
         wait_vm_and_barrier((int)pre - 1);           // stage 0 landed for every wave
         prep(0, 0, k0a, k0b);
     }
+    // Steady state (stage st+kRing-1 exists): [k-step 0 of st || operands of (st, 1)] barrier
+    // [k-step 1 of st || DMA of st+kRing-1, operands of (st+1, 0)].  The iteration has no branch.
+    const int64_t nsteady = nst > kRing - 1 ? nst - (kRing - 1) : 0;
 #pragma clang loop unroll(disable)
-    for (int64_t st = 0; st < nst; ++st) {
+    for (int64_t st = 0; st < nsteady; ++st) {
+        kstep(k0a, k0b, st, 1, k1a, k1b, false, 0);
+        // own loads of st+1 landed (stages st+2 .. st+kRing-2 may be pending); everyone is past st-1
+        wait_vm_and_barrier(kRing - 3);
+        kstep(k1a, k1b, st + 1, 0, k0a, k0b, true, st + kRing - 1);
+    }
+    // Drain: the last kRing-1 stages, nothing left to issue.
+#pragma clang loop unroll(disable)
+    for (int64_t st = nsteady; st < nst; ++st) {
         prep(st, 1, k1a, k1b);
         mfma(k0a, k0b);
-        interleave_kstep();
         if (st + 1 < nst) {
-            // own loads of st+1 landed (stages st+2 .. st+kRing-2 may be pending); everyone is past st-1
-            const int64_t last = st + kRing - 2 < nst - 1 ? st + kRing - 2 : nst - 1;
-            wait_vm_and_barrier((int)(last - (st + 1)));
-            if (st + kRing - 1 < nst) issue(st + kRing - 1);
+            wait_vm_and_barrier((int)(nst - 1 - (st + 1)));
             prep(st + 1, 0, k0a, k0b);
         }
         mfma(k1a, k1b);
-        interleave_kstep();
     }
 
     if (!active) return;
@@ -591,10 +634,7 @@ hipError_t gram_bf16(const GramPlan& pl, const uint16_t* X, int64_t ldx, const u
             if (cross) { p.XA = staging; p.ldxa = K; }
             else { p.X = staging; p.ldx = K; }
         }
-        const bool split = pl.splits > 1;
-        if (cross && split) hipLaunchKernelGGL((gram_bf16_lds_kernel<true, 3>), dim3(nblk), dim3(256), 0, stream, p);
-        else if (cross) hipLaunchKernelGGL((gram_bf16_lds_kernel<true, 4>), dim3(nblk), dim3(256), 0, stream, p);
-        else if (split) hipLaunchKernelGGL((gram_bf16_lds_kernel<false, 3>), dim3(nblk), dim3(256), 0, stream, p);
+        if (cross) hipLaunchKernelGGL((gram_bf16_lds_kernel<true, 4>), dim3(nblk), dim3(256), 0, stream, p);
         else hipLaunchKernelGGL((gram_bf16_lds_kernel<false, 4>), dim3(nblk), dim3(256), 0, stream, p);
     } else if (fast) {
         if (cross) hipLaunchKernelGGL((gram_bf16_kernel<true, false, true>), dim3(nblk), dim3(256), 0, stream, p);
