@@ -316,11 +316,11 @@ void gram_bf16_kernel(GramArgs p) {
 //                [wait for this wave's loads of st+1; barrier]
 //                [MFMA (st, k-step 1) || loads of st+RING-1 into the freed slot, LDS reads + v_perm of
 //                 (st+1, k-step 0)]
-// Ring depth, measured on MI355X with this schedule: 4 slots.  Against 3 slots: 6% faster at 2M tokens x
-// 4096 features, 2% at 131072 x 28672; 5 slots is slower again (the extra requests only queue in the L2).
+// Ring depth, measured on MI355X with this schedule (2M tokens x 4096 / 524288 x 28672 features): 4 slots
+// 30.8 / 373 ms, 3 slots 33.6 / 444 ms, 5 slots 34.4 / 416 ms (the extra requests only queue in the L2).
 // The launch is power-bound on random bf16 data: the shader clock runs at about 1.5-1.6 GHz with loads and
 // MFMAs overlapped, 1.9 GHz for the MFMA work alone (operands resident in LDS) and 2.4 GHz for the loads
-// alone, and the two alone take 79% (2M x 4096) and 72% (131072 x 28672) of the overlapped time.
+// alone.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // Wait until at most `later` stages (8 DMA instructions each) of this wave are still in flight, then
@@ -393,10 +393,12 @@ void gram_bf16_lds_kernel(GramArgs p) {
     };
     // One k-step: the 16 MFMAs on (va, vb), each followed by a fixed share of the next k-step's operand work,
     // pinned in place with scheduling barriers (the scheduler otherwise groups all MFMAs together and leaves
-    // the LDS reads and the regrouping to run on their own): after MFMAs 0-3 the LDS reads of two token rows
-    // of (st_n, ks_n) for A and B; after MFMAs 0-7, if `dma`, DMA instruction i of stage `st_dma`; after MFMAs
-    // 8-15 the regrouping of one fragment element (A for 8-11, B for 12-15).  The last reads are consumed
-    // 4 MFMAs (128 MFMA cycles) after their issue.
+    // the LDS reads and the regrouping to run on their own): after MFMA i < 8 the LDS reads of token row i of
+    // (st_n, ks_n) for A and B; after every even MFMA, if `dma`, one of the 8 DMA instructions of stage
+    // `st_dma`; after MFMAs 8-15 the regrouping of one fragment element (A for 8-11, B for 12-15).  Measured
+    // against other placements (2M tokens x 4096 / 524288 x 28672 features): the reads packed into MFMAs 0-3
+    // 31.7 / 418 ms, this 30.8 / 373 ms, the regrouping started at MFMA 6 37.2 / 452 ms, one DMA instruction
+    // after each of MFMAs 0-7 30.9 / 380 ms.
     auto kstep = [&](const u32x4 (&va)[4], const u32x4 (&vb)[4], int64_t st_n, int ks_n, u32x4 (&na)[4],
                      u32x4 (&nb)[4], bool dma, int64_t st_dma) {
         const int sl = slot_of(st_n);
@@ -406,16 +408,13 @@ void gram_bf16_lds_kernel(GramArgs p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             mfma1(i, va, vb);
-            if (i < 8 && dma) issue_one(st_dma, i);
-            if (i < 4) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    ra[2 * i + h] = frag_row(slabA, wi * 128, ks_n, lane, 2 * i + h);
-                    rb[2 * i + h] = frag_row(slabB, wj * 128, ks_n, lane, 2 * i + h);
-                }
-            } else if (i >= 8 && i < 12) {
+            if (dma && (i & 1) == 0) issue_one(st_dma, i >> 1);
+            if (i < 8) {
+                ra[i] = frag_row(slabA, wi * 128, ks_n, lane, i);
+                rb[i] = frag_row(slabB, wj * 128, ks_n, lane, i);
+            } else if (i < 12) {
                 frag_regroup(ra, i - 8, na);
-            } else if (i >= 12) {
+            } else {
                 frag_regroup(rb, i - 12, nb);
             }
             __builtin_amdgcn_sched_barrier(0);
