@@ -555,12 +555,13 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
     block_epilogue<ASYM, CAE, SM, WHOLE>(st, k, p, rdiag, Ts, Trs, b0, bs, nullptr);
 }
 
-// One super-block of up to kSB coordinates per launch for 16 channels (the variants without the asymmetric term):
-// the channels' weights of the super-block stay in LDS (Ws, 16 x kSB fp32), the blocks run one after the other,
+// One super-block of up to kSBS coordinates per launch for 16 channels (the variants without the asymmetric term):
+// the channels' weights of the super-block stay in LDS (Ws, 16 x kSBS fp32), the blocks run one after the other,
 // and after each block the rows of the super-block still to come get its update W -= E_B U[B, rows] right here,
-// 16 channels x 16 rows per fp32 MFMA tile (v_mfma_f32_16x16x4f32: A = -E (channel x coordinate j), B = U rows; the
-// product is added to Ws once), so no separate product runs between the blocks.  Only the rows after the super-block are left to the trailing
-// product that follows the launch.
+// 16 channels x 16 rows per MFMA tile with fp32 accuracy: -E and the U rows each split into three bf16 parts (U's
+// parts prepared once per super-block by split_diag_kernel), the six part products of order <= 2 accumulated by
+// v_mfma_f32_16x16x32_bf16 from zero and the sum added to Ws once.  No separate product runs between the blocks;
+// only the rows after the super-block are left to the trailing product that follows the launch.
 constexpr int kSBS = 8 * kB;          // super-block of the strip kernel (its near rows are updated in-kernel)
 constexpr int kWsPitch = kSBS + 16;   // 16-float pad: the four channels an MFMA accumulator row set touches hit disjoint banks
 constexpr int64_t kStripMaxWG = 512;   // up to two rounds of one workgroup per CU
