@@ -11,6 +11,8 @@
 // with a long reduction take the split-bf16 kernel below (128 x 128 tiles, same structure flags and epilogue).
 #include "gemm_f32.hpp"
 
+#include <type_traits>
+
 namespace gptq {
 
 namespace {
@@ -335,21 +337,29 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
     const bool mask = (p.flags & kGemmAStrictUpperMask) != 0;
 
     f32x16 acc[T::MA][T::NB];
+#pragma unroll
     for (int a = 0; a < T::MA; ++a)
+#pragma unroll
         for (int b = 0; b < T::NB; ++b)
+#pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-    TileIO<TM, TN, TK, TA, TB, FULL> io;
-    // Operands whose k index is strided in memory (A with TA, B without TB) are loaded as single floats: thread
-    // t takes row/column t % T and the 8 consecutive k of group t / T (T = 128 rows per 256 threads; a 256-row
-    // tile takes two such passes), so each load instruction is coalesced along the contiguous index and each
-    // thread ends with k-contiguous values for its planes.
+    // Raw global data of one stage, held in registers from its load to its split-and-store two stages later; two
+    // such sets (stages of even and odd index).  Operands whose k index is strided in memory (A with TA, B without
+    // TB) are loaded as single floats: thread t takes row/column t % 128 and the 8 consecutive k of group t / 128
+    // (a 256-row tile takes two such passes), so each load instruction is coalesced along the contiguous index and
+    // each thread ends with k-contiguous values for its planes.
     constexpr int SA = TA ? TM / 128 : 1, SB = TB ? 1 : TN / 128;
-    float sa[TA ? SA : 1][8], sb[TB ? 1 : SB][8];
-    float sa_scale = 1.f;
-    auto load_strided = [&](const float* X, int64_t ldx, int64_t rows, int64_t kEnd, int64_t r0, int64_t k0, int passes,
-                            bool strict_upper, float (*dst)[8]) {
+    struct Staged {
+        TileIO<TM, TN, TK, TA, TB, FULL> io;
+        float sa[SA][8], sb[SB][8];
+        float sa_scale;
+    };
+    Staged S0, S1;
+    auto load_strided = [&](const float* X, int64_t ldx, int64_t rows, int64_t kEnd, int64_t r0, int64_t k0,
+                            bool strict_upper, float (*dst)[8], int passes) {
         const int r = tid & 127, kq = tid >> 7;
+#pragma unroll
         for (int ps = 0; ps < passes; ++ps) {
             const int64_t row = r0 + 128 * ps + r;
 #pragma unroll
@@ -361,108 +371,181 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
             }
         }
     };
-    auto load = [&](int64_t t) {
+    auto load = [&](int64_t t, Staged& S) {
         const bool second = t >= nt1;
         const int64_t k0 = second ? (t - nt1) * TK : klo + t * TK;
         const float* Ap = second ? A2 : A1; const float* Bp = second ? B2 : B1;
         const int64_t ldA = second ? p.lda2 : p.lda1, ldB = second ? p.ldb2 : p.ldb1;
         const int64_t kEnd = second ? p.K2 : p.K1;
         if constexpr (TA) {
-            load_strided(Ap, ldA, p.M, kEnd, m0, k0, SA, second ? false : mask, sa);
-            sa_scale = second ? p.a2_scale : 1.f;
+            load_strided(Ap, ldA, p.M, kEnd, m0, k0, second ? false : mask, S.sa, SA);
+            S.sa_scale = second ? p.a2_scale : 1.f;
         } else {
-            io.load_a(Ap, ldA, p.M, kEnd, m0, k0, second ? p.vecA2 : p.vecA1, second ? p.a2_scale : 1.0f,
-                      second ? false : mask, tid);
+            S.io.load_a(Ap, ldA, p.M, kEnd, m0, k0, second ? p.vecA2 : p.vecA1, second ? p.a2_scale : 1.0f,
+                        second ? false : mask, tid);
         }
-        if constexpr (TB) io.load_b(Bp, ldB, p.N, kEnd, n0, k0, second ? p.vecB2 : p.vecB1, tid);
-        else load_strided(Bp, ldB, p.N, kEnd, n0, k0, SB, false, sb);
+        if constexpr (TB) S.io.load_b(Bp, ldB, p.N, kEnd, n0, k0, second ? p.vecB2 : p.vecB1, tid);
+        else load_strided(Bp, ldB, p.N, kEnd, n0, k0, false, S.sb, SB);
     };
-    auto store = [&](int buf) {
-        if constexpr (TA) {
-            const int r = tid & 127, kq = tid >> 7;
-            for (int ps = 0; ps < SA; ++ps) {
+    // Split-and-store pieces of a staged stage into LDS buffer `buf`: first the A pieces (one per 16-byte vector,
+    // or one per 128-row pass of a strided A), then the B pieces likewise.
+    constexpr int kPA = TA ? SA : T::NVA, kPB = TB ? T::NVB : SB, kPieces = kPA + kPB;
+    auto store_piece = [&](const Staged& S, int buf, int piece) {
+        if (piece < kPA) {
+            if constexpr (TA) {
+                const int r = tid & 127, kq = tid >> 7, ps = piece;
                 uint32_t w[3][4];
+#pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    split3x2(sa[ps][2 * e] * sa_scale, sa[ps][2 * e + 1] * sa_scale, w[0][e], w[1][e], w[2][e]);
+                    split3x2(S.sa[ps][2 * e] * S.sa_scale, S.sa[ps][2 * e + 1] * S.sa_scale, w[0][e], w[1][e], w[2][e]);
+#pragma unroll
                 for (int q = 0; q < 3; ++q)
                     *reinterpret_cast<u32x4*>(&As[buf][q][128 * ps + r][8 * kq]) = u32x4{w[q][0], w[q][1], w[q][2], w[q][3]};
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < T::NVA; ++i) {
+            } else {
+                const int i = piece;
                 int mi, ki;
-                io.a_pos(i, tid, mi, ki);
-                f32x4 va = io.a[i] * io.a_scale;
-                if (io.a_mask) {
-                    const int d = (int)(io.ak0 - io.am0) + ki - mi;   // k - m of element 0 (|k - m| < 2^31)
-                    for (int e = 0; e < 4; ++e)
-                        if (d + e <= 0) va[e] = 0.f;
+                S.io.a_pos(i, tid, mi, ki);
+                f32x4 va = S.io.a[i] * S.io.a_scale;
+                {   // strict-upper mask as selects (no branch inside the pinned schedule)
+                    const int d = (int)(S.io.ak0 - S.io.am0) + ki - mi;   // k - m of element 0 (|k - m| < 2^31)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) va[e] = (S.io.a_mask && d + e <= 0) ? 0.f : va[e];
                 }
                 uint32_t w[3][2];
+#pragma unroll
                 for (int e = 0; e < 2; ++e) split3x2(va[2 * e], va[2 * e + 1], w[0][e], w[1][e], w[2][e]);
+#pragma unroll
                 for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x2*>(&As[buf][q][mi][ki]) = u32x2{w[q][0], w[q][1]};
             }
-        }
-        if constexpr (TB) {
-#pragma unroll
-            for (int i = 0; i < T::NVB; ++i) {
-                int ni, ki;
-                io.b_pos(i, tid, ni, ki);
-                const f32x4 vb = io.b[i];
-                uint32_t w[3][2];
-                for (int e = 0; e < 2; ++e) split3x2(vb[2 * e], vb[2 * e + 1], w[0][e], w[1][e], w[2][e]);
-                for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x2*>(&Bs[buf][q][ni][ki]) = u32x2{w[q][0], w[q][1]};
-            }
         } else {
-            const int r = tid & 127, kq = tid >> 7;
-            for (int ps = 0; ps < SB; ++ps) {
+            const int pb = piece - kPA;
+            if constexpr (TB) {
+                int ni, ki;
+                S.io.b_pos(pb, tid, ni, ki);
+                const f32x4 vb = S.io.b[pb];
+                uint32_t w[3][2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) split3x2(vb[2 * e], vb[2 * e + 1], w[0][e], w[1][e], w[2][e]);
+#pragma unroll
+                for (int q = 0; q < 3; ++q) *reinterpret_cast<u32x2*>(&Bs[buf][q][ni][ki]) = u32x2{w[q][0], w[q][1]};
+            } else {
+                const int r = tid & 127, kq = tid >> 7, ps = pb;
                 uint32_t w[3][4];
-                for (int e = 0; e < 4; ++e) split3x2(sb[ps][2 * e], sb[ps][2 * e + 1], w[0][e], w[1][e], w[2][e]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) split3x2(S.sb[ps][2 * e], S.sb[ps][2 * e + 1], w[0][e], w[1][e], w[2][e]);
+#pragma unroll
                 for (int q = 0; q < 3; ++q)
                     *reinterpret_cast<u32x4*>(&Bs[buf][q][128 * ps + r][8 * kq]) = u32x4{w[q][0], w[q][1], w[q][2], w[q][3]};
             }
         }
     };
+    auto store_all = [&](const Staged& S, int buf) {
+#pragma unroll
+        for (int pc = 0; pc < kPieces; ++pc) store_piece(S, buf, pc);
+    };
+    // Fragments of one stage: plane q of A block a and of B block b (a lane's 8 k-values, one 16-byte read each).
+    constexpr int kFrag = 3 * (T::MA + T::NB);
+    struct Frags { u32x4 a[3][T::MA], b[3][T::NB]; };
+    const int kk = 8 * (lane >> 5);
+    auto read_frag = [&](Frags& F, int buf, int f) {
+        const int q = f / (T::MA + T::NB), j = f % (T::MA + T::NB);
+        if (j < T::MA)
+            F.a[q][j] = *reinterpret_cast<const u32x4*>(&As[buf][q][wm * (TM / 2) + 32 * j + (lane & 31)][kk]);
+        else
+            F.b[q][j - T::MA] = *reinterpret_cast<const u32x4*>(&Bs[buf][q][wn * (TN / 2) + 32 * (j - T::MA) + (lane & 31)][kk]);
+    };
+    auto read_all = [&](Frags& F, int buf) {
+#pragma unroll
+        for (int f = 0; f < kFrag; ++f) read_frag(F, buf, f);
+    };
+    // MFMA i of a stage: block (a, b) = (i / 6) / NB, (i / 6) % NB; part products small parts first.
+    constexpr int kMfma = 6 * T::MA * T::NB;
+    auto mfma = [&](const Frags& F, int i) {
+        const int blk = i / 6, part = i % 6, a = blk / T::NB, b = blk % T::NB;
+        constexpr int qa[6] = {2, 1, 0, 1, 0, 0}, qb[6] = {0, 1, 2, 0, 1, 0};
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, F.a[qa[part]][a]),
+                                                           __builtin_bit_cast(bf16x8, F.b[qb[part]][b]), acc[a][b], 0, 0, 0);
+    };
 
-    if (nt > 0) {
-        load(0);
-        store(0);
-    }
-    __syncthreads();
-    for (int64_t t = 0; t < nt; ++t) {
-        const int buf = (int)(t & 1);
-        if (t + 1 < nt) load(t + 1);
-        const int kk = 8 * (lane >> 5);
-        u32x4 fa[3][T::MA], fb[3][T::NB];
+    // Software pipeline over stages t (LDS buffer t & 1, staging set t & 1):
+    //   stage t is loaded from global in iteration t-4 (prologue for t < 4), split and stored to LDS in iteration
+    //   t-2, read into fragments in iteration t-1 and multiplied in iteration t; one barrier per iteration.
+    //   Iteration t: [MFMAs of stage t || stores of stage t+2 (staged in set t & 1) into buffer t & 1, then the
+    //   loads of stage t+4 into that set; fragment reads of stage t+1 from buffer (t+1) & 1]  barrier
+    // Each MFMA is followed by a fixed share of that work, pinned with scheduling barriers: the split-and-store
+    // pieces after the first MFMAs, the 12 fragment reads after MFMAs 4-15, the loads after MFMA 16.  Against the
+    // previous loop (one stage loaded, split and stored per iteration around a block of 24 MFMAs, results
+    // bit-identical) the far trailing products of the 28672 x 8192 layer take 44.5 instead of 47.0 ms.
+    Frags F0, F1;
+    auto iter_steady = [&](auto Qc, int64_t t) {
+        constexpr int Q = decltype(Qc)::value;
+        Frags& Fc = Q ? F1 : F0;
+        Frags& Fn = Q ? F0 : F1;
+        Staged& Sq = Q ? S1 : S0;
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-#pragma unroll
-            for (int a = 0; a < T::MA; ++a)
-                fa[q][a] = *reinterpret_cast<const u32x4*>(&As[buf][q][wm * (TM / 2) + 32 * a + (lane & 31)][kk]);
-#pragma unroll
-            for (int b = 0; b < T::NB; ++b)
-                fb[q][b] = *reinterpret_cast<const u32x4*>(&Bs[buf][q][wn * (TN / 2) + 32 * b + (lane & 31)][kk]);
+        for (int i = 0; i < kMfma; ++i) {
+            mfma(Fc, i);
+            if (i < kPieces) store_piece(Sq, Q, i);
+            if (i >= 4 && i < 4 + kFrag) read_frag(Fn, Q ^ 1, i - 4);
+            if (i == 4 + kFrag) load(t + 4, Sq);
+            __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int a = 0; a < T::MA; ++a)
-#pragma unroll
-            for (int b = 0; b < T::NB; ++b) {
-                // small parts first
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[2][a]), __builtin_bit_cast(bf16x8, fb[0][b]), acc[a][b], 0, 0, 0);
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[1][a]), __builtin_bit_cast(bf16x8, fb[1][b]), acc[a][b], 0, 0, 0);
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[0][a]), __builtin_bit_cast(bf16x8, fb[2][b]), acc[a][b], 0, 0, 0);
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[1][a]), __builtin_bit_cast(bf16x8, fb[0][b]), acc[a][b], 0, 0, 0);
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[0][a]), __builtin_bit_cast(bf16x8, fb[1][b]), acc[a][b], 0, 0, 0);
-                acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[0][a]), __builtin_bit_cast(bf16x8, fb[0][b]), acc[a][b], 0, 0, 0);
-            }
-        if (t + 1 < nt) store(buf ^ 1);
         __syncthreads();
+    };
+    auto iter_drain = [&](auto Qc, int64_t t) {
+        constexpr int Q = decltype(Qc)::value;
+        Frags& Fc = Q ? F1 : F0;
+        Frags& Fn = Q ? F0 : F1;
+        Staged& Sq = Q ? S1 : S0;
+#pragma unroll
+        for (int i = 0; i < kMfma; ++i) mfma(Fc, i);
+        if (t + 2 < nt) store_all(Sq, Q);
+        if (t + 4 < nt) load(t + 4, Sq);
+        if (t + 1 < nt) read_all(Fn, Q ^ 1);
+        __syncthreads();
+    };
+    if (nt > 5) {
+        // unconditional prologue, so that the order of the loads in flight is known at the loop entry
+        load(0, S0);
+        load(1, S1);
+        store_all(S0, 0);
+        load(2, S0);
+        __syncthreads();
+        read_all(F0, 0);
+        store_all(S1, 1);
+        load(3, S1);
+        __syncthreads();
+        int64_t t = 0;
+#pragma clang loop unroll(disable)
+        for (; t + 5 < nt; t += 2) {
+            iter_steady(std::integral_constant<int, 0>{}, t);
+            iter_steady(std::integral_constant<int, 1>{}, t + 1);
+        }
+#pragma clang loop unroll(disable)
+        for (; t < nt; t += 2) {
+            iter_drain(std::integral_constant<int, 0>{}, t);
+            if (t + 1 < nt) iter_drain(std::integral_constant<int, 1>{}, t + 1);
+        }
+    } else {
+        // short reductions: one stage at a time
+        for (int64_t t = 0; t < nt; ++t) {
+            load(t, S0);
+            __syncthreads();
+            store_all(S0, 0);
+            __syncthreads();
+            read_all(F0, 0);
+#pragma unroll
+            for (int i = 0; i < kMfma; ++i) mfma(F0, i);
+        }
     }
 
+#pragma unroll
     for (int a = 0; a < T::MA; ++a) {
+#pragma unroll
         for (int b = 0; b < T::NB; ++b) {
             const int64_t col = n0 + wn * (TN / 2) + 32 * b + (lane & 31);
             if (col >= p.N) continue;
+#pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = m0 + wm * (TM / 2) + 32 * a + mfma32_row(r, lane);
                 if (row >= p.M) continue;
