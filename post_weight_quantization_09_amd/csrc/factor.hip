@@ -20,9 +20,11 @@
 // GEMM tile is aligned with the diagonal blocks.  A batch of Hessians ([G]: one per output-channel group)
 // runs the same recursion with every GEMM batched and every diagonal block one launch over the batch.
 #include <algorithm>
+#include <type_traits>
 #include <vector>
 
 #include "factor.hpp"
+
 #include "gemm_f32.hpp"
 #include "timer.hpp"
 
@@ -143,11 +145,25 @@ __global__ __launch_bounds__(1024) void chol_ul_inv_kernel(float* D, int64_t ld,
     __shared__ float Rinv[kNB];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int o = kNB - n;
-    for (int idx = tid; idx < kNB * kNB; idx += 1024) {
-        const int i = idx >> 7, k = idx & (kNB - 1);
-        float v = (i == k) ? 1.0f : 0.0f;
-        if (i >= o && i <= k) v = D[(int64_t)(i - o) * ld + (k - o)];
-        S[i][k] = v;
+    // a whole 128-block with 16-byte rows: thread t takes 16 consecutive entries of row t / 8 (four 16-byte loads
+    // in flight at once instead of sixteen dependent scalar rounds)
+    const bool vec = o == 0 && (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(D) & 15) == 0;
+    if (vec) {
+        const int i = tid >> 3, k0 = (tid & 7) * 16;
+        f32x4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const f32x4*>(D + (int64_t)i * ld + k0 + 4 * q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) S[i][k0 + 4 * q + e] = (i <= k0 + 4 * q + e) ? v[q][e] : 0.0f;
+    } else {
+        for (int idx = tid; idx < kNB * kNB; idx += 1024) {
+            const int i = idx >> 7, k = idx & (kNB - 1);
+            float v = (i == k) ? 1.0f : 0.0f;
+            if (i >= o && i <= k) v = D[(int64_t)(i - o) * ld + (k - o)];
+            S[i][k] = v;
+        }
     }
     __syncthreads();
     unsigned bad = 0;
@@ -203,19 +219,23 @@ __global__ __launch_bounds__(1024) void chol_ul_inv_kernel(float* D, int64_t ld,
         for (int i = 0; i < 16; ++i) S[b0 + i][b0 + j] = u[i];
     }
     __syncthreads();
-    // Merges of pairs (a, c) of size s: T = R_ac U_cc (then stored over R_ac), U_ac = -U_aa T.
-    for (int s = 16; s < kNB; s *= 2) {
-        const int per_side = s >> 4, tpp = per_side * per_side;
-        const int ntile = (kNB / (2 * s)) * tpp;   // 4, 8, 16 tiles of 16 x 16
+    // Merges of pairs (a, c) of size s: T = R_ac U_cc (then stored over R_ac), U_ac = -U_aa T.  The size is a
+    // template constant so that each product's LDS operand reads are unrolled and issued ahead of its MFMA chain.
+    auto merge = [&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int per_side = s >> 4, tpp = per_side * per_side;
+        constexpr int ntile = (kNB / (2 * s)) * tpp;   // 4, 8, 16 tiles of 16 x 16
         const int pair = wave / tpp, w = wave % tpp;
         const int ti = w / per_side, tk = w % per_side;
         const int a0 = 2 * s * pair, c0 = a0 + s;
         const int ar = 16 * ti + (lane & 15), kq = lane >> 4, oc = 16 * tk + (lane & 15);
         f32x4 t = {0.f, 0.f, 0.f, 0.f};
         if (wave < ntile) {
-            for (int m4 = 0; m4 < s; m4 += 4)
-                t = __builtin_amdgcn_mfma_f32_16x16x4f32(R[a0 + ar][c0 + m4 + kq], S[c0 + m4 + kq][c0 + oc], t,
-                                                         0, 0, 0);
+            float x[s / 4], y[s / 4];
+#pragma unroll
+            for (int m = 0; m < s / 4; ++m) { x[m] = R[a0 + ar][c0 + 4 * m + kq]; y[m] = S[c0 + 4 * m + kq][c0 + oc]; }
+#pragma unroll
+            for (int m = 0; m < s / 4; ++m) t = __builtin_amdgcn_mfma_f32_16x16x4f32(x[m], y[m], t, 0, 0, 0);
         }
         __syncthreads();
         if (wave < ntile) {
@@ -225,17 +245,33 @@ __global__ __launch_bounds__(1024) void chol_ul_inv_kernel(float* D, int64_t ld,
         __syncthreads();
         if (wave < ntile) {
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
-            for (int m4 = 0; m4 < s; m4 += 4)
-                u = __builtin_amdgcn_mfma_f32_16x16x4f32(S[a0 + ar][a0 + m4 + kq], R[a0 + m4 + kq][c0 + oc], u,
-                                                         0, 0, 0);
+            float x[s / 4], y[s / 4];
+#pragma unroll
+            for (int m = 0; m < s / 4; ++m) { x[m] = S[a0 + ar][a0 + 4 * m + kq]; y[m] = R[a0 + 4 * m + kq][c0 + oc]; }
+#pragma unroll
+            for (int m = 0; m < s / 4; ++m) u = __builtin_amdgcn_mfma_f32_16x16x4f32(x[m], y[m], u, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r) S[a0 + 16 * ti + 4 * kq + r][c0 + oc] = -u[r];
         }
         __syncthreads();
-    }
-    for (int idx = tid; idx < kNB * kNB; idx += 1024) {
-        const int i = idx >> 7, k = idx & (kNB - 1);
-        if (i >= o && k >= o) D[(int64_t)(i - o) * ld + (k - o)] = (i <= k) ? S[i][k] : 0.0f;
+    };
+    merge(std::integral_constant<int, 16>{});
+    merge(std::integral_constant<int, 32>{});
+    merge(std::integral_constant<int, 64>{});
+    if (vec) {
+        const int i = tid >> 3, k0 = (tid & 7) * 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = (i <= k0 + 4 * q + e) ? S[i][k0 + 4 * q + e] : 0.0f;
+            *reinterpret_cast<f32x4*>(D + (int64_t)i * ld + k0 + 4 * q) = v;
+        }
+    } else {
+        for (int idx = tid; idx < kNB * kNB; idx += 1024) {
+            const int i = idx >> 7, k = idx & (kNB - 1);
+            if (i >= o && k >= o) D[(int64_t)(i - o) * ld + (k - o)] = (i <= k) ? S[i][k] : 0.0f;
+        }
     }
     if (bad && tid == 0) atomicOr(&st->flags, bad);
 }
