@@ -45,3 +45,33 @@ def test_traffic_is_keyed_by_workload(tmp_path, monkeypatch):
     assert bench.measured_traffic("gram_bf16", "c2_q_proj_8b", "abc") is None
     (tmp_path / "profiles" / "gram_bf16_c2_q_proj_8b_traffic.json").write_text(json.dumps(rec))
     assert bench.measured_traffic("gram_bf16", "c2_q_proj_8b", "abc") is None   # a file naming another workload
+
+
+# Per-layer work of each workload as derived independently from the workload definitions (upper-triangle Gram with
+# the diagonal, M multiply-adds per entry, plus the full cross product with asymmetric calibration; lazy-batch
+# trailing products N K (K - B) multiply-adds; 9 (13 with the asymmetric term) bytes per coordinate and channel in
+# the column loop; 2 K^3 / 3 for the factorisation), to three significant figures.
+_FIGURES = {
+    # config: (Gram flop per launch x groups, trailing flop, loop bytes, factorisation flop)
+    "c1_512": (5.38e8, 1.01e8, 2.36e6, 8.95e7),
+    "c2_q_proj_8b": (3.519e13, 6.66e10, 1.51e8, 4.58e10),
+    "c3_down_proj_8b_g4": (2.155e14, 8.34e11, 5.29e8, 7.86e12),
+    "c4_up_proj_8b_gptaq": (1.320e13, 4.66e11, 7.63e8, 4.58e10),
+    "c5_down_proj_70b": (4.310e14, 6.70e12, 2.11e9, 1.571e13),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_FIGURES))
+def test_algorithmic_work_per_layer(name):
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads
+    cfg = workloads.CONFIGS[name]
+    gram, trail, loop, fact = _FIGURES[name]
+    got = (bench.gram_flops(cfg) * cfg.groups, bench.trailing_flops(cfg), bench.loop_bytes(cfg),
+           bench.factor_flops(cfg))
+    for want, have in zip((gram, trail, loop, fact), got):
+        assert abs(have - want) <= 5e-3 * want, (name, want, have)
+    # the loop's latency floor: K dependent steps per round of 256 workgroups of 16 channels
+    rounds = {512: 1, 4096: 1, 8192: 2, 14336: 4}[cfg.N]
+    assert bench.chain_floor_ms(cfg) == pytest.approx(rounds * cfg.K * bench.STEP_CHAIN_NS * 1e-6)
