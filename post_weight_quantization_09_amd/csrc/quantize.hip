@@ -14,13 +14,16 @@
 // [G] / [T] section 2: symmetric per-channel grid, codes 0..2^b-1, zero point 2^(b-1), value s (c - z).
 //
 // Data layout: the working weights are kept transposed, Wt[n][k] (fp32, N x ldt, ldt = K rounded up to
-// 128), so that one channel's block of 128 coordinates is contiguous.  The block kernel gives each
-// channel 16 lanes (one DPP row); lane l holds coordinates 16 m + l, m = 0..7, of the current block in
-// registers, so that the coordinates still free after step j = 16 m + l0 are exactly the slots >= m and
-// the triangular work shrinks with m.  The U panel (and P1 panel) of the block sits in LDS, permuted so
-// that a lane's eight coefficients of row j are two 16-byte reads.  At step j the value w_j is broadcast
-// from its owner lane to the row with DPP row_newbcast; every lane of the row then evaluates the same
-// rounding and error (no further communication), updates its own slots, and the owner keeps the code.
+// 128), so that one channel's block of 128 coordinates is contiguous.  Both loop kernels give each channel
+// 16 lanes (one DPP row); lane l holds coordinates 16 m + l, m = 0..7, of the current block in registers,
+// so that the coordinates still free after step j = 16 m + l0 are exactly the slots >= m and the
+// triangular work shrinks with m.  The U panel (and P1 panel) of the block sits in LDS, permuted so that a
+// lane's eight coefficients of row j are two 16-byte reads.  At step j the value w_j is broadcast from its
+// owner lane to the row with DPP row_newbcast; every lane of the row then evaluates the same rounding and
+// error (no further communication), updates its own slots, and the owner keeps the code.
+// Two kernels run these steps: quant_strip_kernel (no asymmetric term, at most 512 workgroups) does a whole
+// 1024-coordinate super-block per launch with the channels' weights in LDS and the near updates in-kernel;
+// quant_block_kernel does one 128-block per launch, the near updates left to a product after each block.
 #include <algorithm>
 #include <utility>
 
