@@ -59,21 +59,54 @@ __global__ __launch_bounds__(256) void convert_kernel(const void* Wv, int64_t K,
     const int tid = threadIdx.x;
     const int64_t k0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
     const bool n_fast = (w_cs == 1) || (w_rs != 1 && w_cs <= w_rs);
+    // Whole tile, channels contiguous in 16-byte rows, natural order: 16-byte loads along n and 16-byte stores
+    // along k (the general path moves one element per lane and access).
+    constexpr int V = BF16 ? 8 : 4;                  // elements per 16-byte load
+    const bool fast = !perm && w_cs == 1 && k0 + 64 <= K && n0 + 64 <= N && w_rs % V == 0 &&
+                      (reinterpret_cast<uintptr_t>(Wv) & 15) == 0 &&
+                      (!dead || ((reinterpret_cast<uintptr_t>(dead) & 3) == 0 && K % 4 == 0));
     unsigned bad = 0;
-    for (int i = 0; i < 16; ++i) {
-        const int idx = tid + 256 * i;
-        const int a = idx >> 6, b = idx & 63;         // (slow, fast)
-        const int kk = n_fast ? a : b, nn = n_fast ? b : a;
-        const int64_t k = k0 + kk, n = n0 + nn;
-        float v = 0.f;
-        if (k < K && n < N) {
-            const int64_t gK = (int64_t)((uint32_t)n / (uint32_t)gs) * K;
-            const int64_t off = (perm ? (int64_t)perm[gK + k] : k) * w_rs + n * w_cs;
-            if (BF16) v = __uint_as_float((uint32_t)(static_cast<const uint16_t*>(Wv)[off]) << 16);
-            else v = static_cast<const float*>(Wv)[off];
-            if (!isfinite(v)) bad = 1;
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < 64 * (64 / V) / 256; ++i) {
+            const int idx = tid + 256 * i;
+            const int kk = idx / (64 / V), nv = (idx % (64 / V)) * V;
+            const int64_t off = (k0 + kk) * w_rs + n0 + nv;
+            float v[V];
+            if constexpr (BF16) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(Wv) + off);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    v[2 * e] = __uint_as_float(w[e] << 16);
+                    v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+                }
+            } else {
+                const f32x4 w = *reinterpret_cast<const f32x4*>(static_cast<const float*>(Wv) + off);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = w[e];
+            }
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                if (!isfinite(v[e])) bad = 1;
+                tile[kk][nv + e] = v[e];
+            }
         }
-        tile[kk][nn] = v;
+    } else {
+        for (int i = 0; i < 16; ++i) {
+            const int idx = tid + 256 * i;
+            const int a = idx >> 6, b = idx & 63;         // (slow, fast)
+            const int kk = n_fast ? a : b, nn = n_fast ? b : a;
+            const int64_t k = k0 + kk, n = n0 + nn;
+            float v = 0.f;
+            if (k < K && n < N) {
+                const int64_t gK = (int64_t)((uint32_t)n / (uint32_t)gs) * K;
+                const int64_t off = (perm ? (int64_t)perm[gK + k] : k) * w_rs + n * w_cs;
+                if (BF16) v = __uint_as_float((uint32_t)(static_cast<const uint16_t*>(Wv)[off]) << 16);
+                else v = static_cast<const float*>(Wv)[off];
+                if (!isfinite(v)) bad = 1;
+            }
+            tile[kk][nn] = v;
+        }
     }
     __syncthreads();
     // column max over this tile's 64 rows, 4 threads per channel
@@ -85,14 +118,32 @@ __global__ __launch_bounds__(256) void convert_kernel(const void* Wv, int64_t K,
         m = fmaxf(m, __shfl_xor(m, 2, 4));
         if (part == 0 && n0 + nn < N && m > 0.f) atomicMax(&amax_bits[n0 + nn], __float_as_uint(m));
     }
-    for (int i = 0; i < 16; ++i) {
-        const int idx = tid + 256 * i;
-        const int nn = idx >> 6, kk = idx & 63;
-        const int64_t k = k0 + kk, n = n0 + nn;
-        if (n < N && k < ldt) {
-            float v = (k < K) ? tile[kk][nn] : 0.f;
-            if (k < K && dead && dead[(int64_t)((uint32_t)n / (uint32_t)gs) * K + k]) v = 0.f;
-            Wt[n * ldt + k] = v;
+    if (fast) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int idx = tid + 256 * i;
+            const int nn = idx >> 4, kq = (idx & 15) * 4;
+            const int64_t n = n0 + nn;
+            f32x4 v = {tile[kq][nn], tile[kq + 1][nn], tile[kq + 2][nn], tile[kq + 3][nn]};
+            if (dead) {
+                const uint32_t d4 = *reinterpret_cast<const uint32_t*>(
+                    dead + (int64_t)((uint32_t)n / (uint32_t)gs) * K + k0 + kq);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if ((d4 >> (8 * e)) & 0xffu) v[e] = 0.f;
+            }
+            *reinterpret_cast<f32x4*>(Wt + n * ldt + k0 + kq) = v;
+        }
+    } else {
+        for (int i = 0; i < 16; ++i) {
+            const int idx = tid + 256 * i;
+            const int nn = idx >> 6, kk = idx & 63;
+            const int64_t k = k0 + kk, n = n0 + nn;
+            if (n < N && k < ldt) {
+                float v = (k < K) ? tile[kk][nn] : 0.f;
+                if (k < K && dead && dead[(int64_t)((uint32_t)n / (uint32_t)gs) * K + k]) v = 0.f;
+                Wt[n * ldt + k] = v;
+            }
         }
     }
     if (bad) atomicOr(&st->flags, (uint32_t)kDevNonFinite);
@@ -792,6 +843,27 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint8_t* codes_t, i
     __shared__ uint8_t tile[64][65];
     const int tid = threadIdx.x;
     const int64_t k0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+    // Whole tile, codes only, natural order, channels contiguous in 16-byte rows: one 16-byte load of codes_t and
+    // one 16-byte store of codes per thread (the general path moves a byte per lane and access).
+    const bool fast = !W_hat && !perm && c_cs == 1 && k0 + 64 <= K && n0 + 64 <= N && c_rs % 16 == 0 &&
+                      (reinterpret_cast<uintptr_t>(codes) & 15) == 0;
+    if (fast) {
+        {
+            const int nn = tid >> 2, kq = (tid & 3) * 16;
+            const u32x4 c = *reinterpret_cast<const u32x4*>(codes_t + (n0 + nn) * ldt + k0 + kq);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) tile[kq + e][nn] = (uint8_t)(c[e >> 2] >> (8 * (e & 3)));
+        }
+        __syncthreads();
+        const int kk = tid >> 2, nq = (tid & 3) * 16;
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+            o[w] = (uint32_t)tile[kk][nq + 4 * w] | ((uint32_t)tile[kk][nq + 4 * w + 1] << 8) |
+                   ((uint32_t)tile[kk][nq + 4 * w + 2] << 16) | ((uint32_t)tile[kk][nq + 4 * w + 3] << 24);
+        *reinterpret_cast<u32x4*>(codes + (k0 + kk) * c_rs + n0 + nq) = o;
+        return;
+    }
     for (int i = 0; i < 16; ++i) {
         const int idx = tid + 256 * i;
         const int nn = idx >> 6, kk = idx & 63;
