@@ -68,11 +68,15 @@ def loop_bytes(cfg) -> float:
 STEP_CHAIN_NS = 20.0   # one coordinate step's dependent chain: a broadcast and about six dependent fp32 operations
 
 
+def loop_rounds(cfg) -> int:
+    """Rounds of the column loop's workgroups (16 channels each, one per CU at a time): every channel in flight at
+    once when N / 16 <= 256."""
+    return -(-(cfg.N // 16) // 256)
+
+
 def chain_floor_ms(cfg) -> float:
-    """Latency floor of the column loop: K dependent coordinate steps per channel, every channel in flight at once
-    when one workgroup of 16 channels per CU covers them all (N / 16 <= 256), else once per round of 256."""
-    rounds = -(-(cfg.N // 16) // 256)
-    return rounds * cfg.K * STEP_CHAIN_NS * 1e-6
+    """Latency floor of the column loop: K dependent coordinate steps per channel, once per round of workgroups."""
+    return loop_rounds(cfg) * cfg.K * STEP_CHAIN_NS * 1e-6
 
 
 def factor_flops(cfg) -> float:
@@ -260,7 +264,10 @@ def kernel_breakdown(layer: Layer) -> dict:
                         "frac": round(lb / (loop_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if loop_ms > 0 else None,
                         "hbm_floor_ms": round(lb / (PEAK_HBM_GBS * 1e9) * 1e3, 3),
                         "chain_floor_ms": round(chain_floor_ms(cfg), 3),
-                        "ns_per_step": round(loop_ms * 1e6 / steps, 1) if loop_ms > 0 else None},
+                        "ns_per_step": round(loop_ms * 1e6 / steps, 1) if loop_ms > 0 else None,
+                        "workgroup_rounds": loop_rounds(cfg),
+                        "ns_per_step_per_round": round(loop_ms * 1e6 / steps / loop_rounds(cfg), 1)
+                        if loop_ms > 0 else None},
         "factorisation": {"ms": round(t["factor_diag"][0] + t["factor_gemm"][0], 3), "flop": ff,
                           "TFLOP/s": round(ff / ((t["factor_diag"][0] + t["factor_gemm"][0]) * 1e-3) / 1e12, 1)
                           if t["factor_gemm"][0] > 0 else None},
