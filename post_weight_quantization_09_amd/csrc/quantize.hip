@@ -273,6 +273,12 @@ struct BlockArgs {
 // group start (processing order); static groups whose scales were computed from W before the loop.
 enum : int { kScalePerChannel = 0, kScaleDynamic = 1, kScaleStatic = 2 };
 
+// With one scale per channel the loop runs on the weights divided by the scale, v = w / s: the code is then
+// rint(v) clamped, the step's error term v_j - c needs no multiply, and the slot updates v_k -= (U_jk / U_jj)(v_j - c)
+// are those of the weights divided by s.  The errors E_j = (v_j - c) s / U_jj and the outputs are in weight units.
+template <int SM>
+constexpr bool kScaled = SM == kScalePerChannel;
+
 // Per-lane state of the block kernel: 8 strided coordinates of one channel.  A coordinate's slot keeps its value
 // just before rounding: the step that fixes coordinate j leaves slot j alone (the panel's entry (j, j) is zero), and
 // later steps add zero to it (U is upper triangular), so codes, errors and losses are evaluated once at the end of
@@ -281,6 +287,7 @@ struct LaneState {
     float w[8], w0[8];
     float s, rs;                    // scale in force (and its reciprocal)
     float qs[4], qrs[4];            // re-estimated groups: the scale of each 32-coordinate quarter of the block
+    float dp, wup;                  // the previous step's d and update value (its deferred slot updates use them)
 };
 
 struct StepConst {
@@ -294,12 +301,14 @@ struct StepConst {
 };
 
 // Per-step operands read from LDS: this lane's 8 entries of row J of the scaled panel U_Jk / U_JJ (and of P1).
-// They are read kLook - 1 steps ahead, so no LDS latency sits on the chain of dependent steps.
+// Row J is read kAhead steps ahead into a ring of kRing entries, so no LDS latency sits on the chain of dependent
+// steps; the ring also keeps row J - 1, whose update of most slots is applied during step J (see loop_step).
 struct StepOps {
     f32x4 u0, u1, p0, p1;
     float s, rs;
 };
-constexpr int kLook = 4;
+constexpr int kAhead = 3;
+constexpr int kRing = kAhead + 2;
 
 template <int J, bool ASYM, int SM>
 __device__ __forceinline__ void load_ops(StepOps& o, const StepConst& k) {
@@ -308,13 +317,27 @@ __device__ __forceinline__ void load_ops(StepOps& o, const StepConst& k) {
             o.s = k.Ts[J * 16 + k.ch];
             o.rs = k.Trs[J * 16 + k.ch];
         }
-        const f32x4* urow = reinterpret_cast<const f32x4*>(k.Up + (J * 16 + k.l) * 8);
-        o.u0 = urow[0];
-        o.u1 = urow[1];
+        // step J updates slots m..7 only (m = J / 16): entries below m are not read from LDS
+        constexpr int m = J >> 4;
+        const float* urow = k.Up + (J * 16 + k.l) * 8;
+        if constexpr (m < 4) o.u0 = *reinterpret_cast<const f32x4*>(urow);
+        if constexpr (m < 6) {
+            o.u1 = *reinterpret_cast<const f32x4*>(urow + 4);
+        } else {
+            const f32x2 t = *reinterpret_cast<const f32x2*>(urow + 6);
+            o.u1[2] = t[0];
+            o.u1[3] = t[1];
+        }
         if constexpr (ASYM) {
-            const f32x4* prow = reinterpret_cast<const f32x4*>(k.Pp + (J * 16 + k.l) * 8);
-            o.p0 = prow[0];
-            o.p1 = prow[1];
+            const float* prow = k.Pp + (J * 16 + k.l) * 8;
+            if constexpr (m < 4) o.p0 = *reinterpret_cast<const f32x4*>(prow);
+            if constexpr (m < 6) {
+                o.p1 = *reinterpret_cast<const f32x4*>(prow + 4);
+            } else {
+                const f32x2 t = *reinterpret_cast<const f32x2*>(prow + 6);
+                o.p1[2] = t[0];
+                o.p1[3] = t[1];
+            }
         }
     }
 }
@@ -344,19 +367,74 @@ __device__ __forceinline__ float signed_code(float v, const StepConst& k) {
     return __builtin_amdgcn_fmed3f(rintf(v), k.clo, k.chi);
 }
 
+// Entry MM of a lane's 8 panel entries (a, b: entries 0-3 and 4-7).
+template <int MM>
+__device__ __forceinline__ float entry(const f32x4& a, const f32x4& b) {
+    if constexpr (MM < 4) return a[MM];
+    else return b[MM - 4];
+}
+
+// The update of slot MM by a step with error term d: w -= (U_jk / U_jj) d, and with the asymmetric term
+// w += P1_jk wu (o: that step's panel entries).
+template <int MM, bool ASYM>
+__device__ __forceinline__ void slot_update(LaneState& st, const StepOps& o, float d, float wu) {
+    if constexpr (ASYM) st.w[MM] = fmaf(entry<MM>(o.p0, o.p1), wu, fmaf(-entry<MM>(o.u0, o.u1), d, st.w[MM]));
+    else st.w[MM] = fmaf(-entry<MM>(o.u0, o.u1), d, st.w[MM]);
+}
+
+// Step P updates slots P/16 .. 7 (the slots holding coordinates after P).  Of these, the slot holding coordinate
+// P + 1 is updated within step P (the next step broadcasts from it); the others, its "tail", are updated during step
+// P + 1.  tail_slot(P, i) is the i-th slot of that tail, or -1.
+constexpr int tail_slot(int P, int i) {
+    if (P < 0) return -1;
+    int cnt = 0;
+    for (int mm = P >> 4; mm < 8; ++mm) {
+        if (mm == ((P + 1) >> 4)) continue;
+        if (cnt == i) return mm;
+        ++cnt;
+    }
+    return -1;
+}
+
+template <int P, int I, bool ASYM>
+__device__ __forceinline__ void tail_update(LaneState& st, const StepOps& op) {
+    constexpr int mm = tail_slot(P, I);
+    if constexpr (mm >= 0) slot_update<mm, ASYM>(st, op, st.dp, st.wup);
+}
+
+template <int P, bool ASYM>
+__device__ __forceinline__ void tail_all(LaneState& st, const StepOps& op) {
+    tail_update<P, 0, ASYM>(st, op);
+    tail_update<P, 1, ASYM>(st, op);
+    tail_update<P, 2, ASYM>(st, op);
+    tail_update<P, 3, ASYM>(st, op);
+    tail_update<P, 4, ASYM>(st, op);
+    tail_update<P, 5, ASYM>(st, op);
+    tail_update<P, 6, ASYM>(st, op);
+}
+
+#define GPTQ_SB() __builtin_amdgcn_sched_barrier(0)
+
 // One step j of the loop (j compile-time so that slots, DPP lane and LDS offsets are immediates).  The chain
 // from one step to the next is: broadcast w_j, scale, round, clamp, d = w_j - c s, then the update of the slot
 // holding coordinate j + 1.  With the panel holding U_jk / U_jj, w_k -= (U_jk / U_jj) d is the update
 // w_k -= U_jk E_j with E_j = d / U_jj; slot j itself has a zero entry and keeps its pre-rounding value.
 // CAE: the update is taken from the original weight, d = w0_j - c s (the P2 = P1 + I - diag(U)^-1 U form), and the
 // P1 coefficient is w0_j.
-template <int J, bool ASYM, bool CAE, int SM>
-__device__ __forceinline__ void loop_step(LaneState& st, const StepConst& k, StepOps (&ops)[kLook]) {
-    constexpr int m = J >> 4, lj = J & 15;
-    const StepOps& o = ops[J % kLook];
-    // Steps stay in program order: the scheduler would otherwise sink the look-ahead reads to their uses.
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (SM == kScaleDynamic && (J & 31) == 0) {
+// DEFER (whole blocks): only the slot of coordinate j + 1 is updated on the chain; the other slots of step j - 1 are
+// updated here, one between each pair of dependent chain instructions, where the wave would otherwise wait.  Every
+// slot still receives the steps' updates in step order, so the results are those of updating all slots at once.
+// The instruction order is fixed by scheduling barriers (the scheduler would otherwise sink the look-ahead reads to
+// their uses and group the slot updates together).
+template <int J, bool ASYM, bool CAE, int SM, bool DEFER>
+__device__ __forceinline__ void loop_step(LaneState& st, const StepConst& k, StepOps (&ops)[kRing]) {
+    constexpr int m = J >> 4, lj = J & 15, mn = (J + 1) >> 4, P = J - 1;
+    const StepOps& o = ops[J % kRing];
+    const StepOps& op = ops[(J + kRing - 1) % kRing];
+    GPTQ_SB();
+    constexpr bool kRegroup = SM == kScaleDynamic && (J & 31) == 0;
+    if constexpr (kRegroup) {
+        if constexpr (DEFER) tail_all<P, ASYM>(st, op);   // the group maximum reads the current weights
         regroup<J>(st, k);
         st.qs[J >> 5] = st.s;
         st.qrs[J >> 5] = st.rs;
@@ -365,36 +443,81 @@ __device__ __forceinline__ void loop_step(LaneState& st, const StepConst& k, Ste
         st.s = o.s;
         st.rs = o.rs;
     }
-    load_ops<J + kLook - 1, ASYM, SM>(ops[(J + kLook - 1) % kLook], k);
-    const float wj = row_bcast<lj>(st.w[m]);
-    const float c = signed_code(wj * st.rs, k);
-    const float wu = CAE ? row_bcast<lj>(st.w0[m]) : wj;     // value the update is taken from
-    const float d = fmaf(-c, st.s, wu);
-    const float uu[8] = {o.u0.x, o.u0.y, o.u0.z, o.u0.w, o.u1.x, o.u1.y, o.u1.z, o.u1.w};
-    if constexpr (ASYM) {
-        const float pp[8] = {o.p0.x, o.p0.y, o.p0.z, o.p0.w, o.p1.x, o.p1.y, o.p1.z, o.p1.w};
-#pragma unroll
-        for (int mm = m; mm < 8; ++mm) st.w[mm] = fmaf(pp[mm], wu, fmaf(-uu[mm], d, st.w[mm]));
-        asm volatile("" ::"v"(o.p0), "v"(o.p1));
+    load_ops<J + kAhead, ASYM, SM>(ops[(J + kAhead) % kRing], k);
+    if constexpr (DEFER) {
+        constexpr int T0 = kRegroup ? 8 : 0;   // tail of step J - 1 already applied
+        const float wj = row_bcast<lj>(st.w[m]);
+        const float wu = CAE ? row_bcast<lj>(st.w0[m]) : wj;
+        GPTQ_SB();
+        tail_update<P, T0 + 0, ASYM>(st, op);
+        GPTQ_SB();
+        const float x = kScaled<SM> ? wj : wj * st.rs;
+        GPTQ_SB();
+        tail_update<P, T0 + 1, ASYM>(st, op);
+        GPTQ_SB();
+        const float r = rintf(x);
+        GPTQ_SB();
+        tail_update<P, T0 + 2, ASYM>(st, op);
+        GPTQ_SB();
+        const float c = __builtin_amdgcn_fmed3f(r, k.clo, k.chi);
+        GPTQ_SB();
+        tail_update<P, T0 + 3, ASYM>(st, op);
+        GPTQ_SB();
+        const float d = kScaled<SM> ? wu - c : fmaf(-c, st.s, wu);
+        GPTQ_SB();
+        tail_update<P, T0 + 4, ASYM>(st, op);
+        GPTQ_SB();
+        if constexpr (mn < 8) slot_update<mn, ASYM>(st, o, d, wu);
+        GPTQ_SB();
+        tail_update<P, T0 + 5, ASYM>(st, op);
+        tail_update<P, T0 + 6, ASYM>(st, op);
+        st.dp = d;
+        st.wup = wu;
+        // Row J - 1's registers are read for the last time here; keeping all of them live until here stops the
+        // allocator from giving one to another value while the read of row J + kAhead into them is outstanding.
+        asm volatile("" ::"v"(op.u0), "v"(op.u1));
+        if constexpr (ASYM) asm volatile("" ::"v"(op.p0), "v"(op.p1));
     } else {
+        const float wj = row_bcast<lj>(st.w[m]);
+        const float c = signed_code(kScaled<SM> ? wj : wj * st.rs, k);
+        const float wu = CAE ? row_bcast<lj>(st.w0[m]) : wj;     // value the update is taken from
+        const float d = kScaled<SM> ? wu - c : fmaf(-c, st.s, wu);
 #pragma unroll
-        for (int mm = m; mm < 8; ++mm) st.w[mm] = fmaf(-uu[mm], d, st.w[mm]);
+        for (int mm = m; mm < 8; ++mm) {
+            if constexpr (ASYM) {
+                const float pp = mm < 4 ? o.p0[mm & 3] : o.p1[mm & 3];
+                const float uu = mm < 4 ? o.u0[mm & 3] : o.u1[mm & 3];
+                st.w[mm] = fmaf(pp, wu, fmaf(-uu, d, st.w[mm]));
+            } else {
+                const float uu = mm < 4 ? o.u0[mm & 3] : o.u1[mm & 3];
+                st.w[mm] = fmaf(-uu, d, st.w[mm]);
+            }
+        }
+        // The entries of slots below m are not needed, but their registers are the destinations of this step's LDS
+        // read; keeping them live until here stops the allocator from reusing one while the read is in flight.
+        asm volatile("" ::"v"(o.u0), "v"(o.u1));
+        if constexpr (ASYM) asm volatile("" ::"v"(o.p0), "v"(o.p1));
     }
-    // The entries of slots below m are not needed, but their registers are the destinations of this step's LDS
-    // read; keeping them live until here stops the allocator from reusing one while the read is in flight (which
-    // would make the next instruction wait for the read).
-    asm volatile("" ::"v"(o.u0), "v"(o.u1));
 }
 
+// The steps of one block.  WHOLE (all 128 coordinates): deferred slot updates, the last step's tail applied at the
+// end; a ragged block (the last of a layer whose K is not a multiple of 128) updates every slot within its step.
 template <bool ASYM, bool CAE, int SM, bool WHOLE, int... Js>
 __device__ __forceinline__ void run_steps(LaneState& st, const StepConst& k, int bs,
                                           std::integer_sequence<int, Js...>) {
-    StepOps ops[kLook];
+    StepOps ops[kRing];
+    static_assert(kAhead == 3, "the prologue loads kAhead rows");
     load_ops<0, ASYM, SM>(ops[0], k);
     load_ops<1, ASYM, SM>(ops[1], k);
     load_ops<2, ASYM, SM>(ops[2], k);
-    static_assert(kLook == 4, "prologue loads kLook - 1 steps");
-    ((WHOLE || Js < bs ? loop_step<Js, ASYM, CAE, SM>(st, k, ops) : (void)0), ...);
+    st.dp = 0.f;
+    st.wup = 0.f;
+    ((WHOLE || Js < bs ? loop_step<Js, ASYM, CAE, SM, WHOLE>(st, k, ops) : (void)0), ...);
+    if constexpr (WHOLE) {
+        GPTQ_SB();
+        tail_all<kB - 1, ASYM>(st, ops[(kB - 1) % kRing]);
+        asm volatile("" ::"v"(ops[(kB - 1) % kRing].u0), "v"(ops[(kB - 1) % kRing].u1));
+    }
 }
 
 // The panel of the block at b0 (bs rows) for one output-channel group's U (and P1): rows b0..b0+bs-1, columns
@@ -499,13 +622,6 @@ __device__ __forceinline__ void init_lane(LaneState& st, StepConst& k, const Blo
         st.qs[q] = 1.0f;
         st.qrs[q] = 1.0f;
     }
-    const float* w0row = CAE ? p.W0t + nn * p.ldt + b0 : nullptr;
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        st.w[m] = wsrc[16 * m + l];
-        if constexpr (CAE) st.w0[m] = w0row[16 * m + l];
-    }
-    k.Up = Up; k.Pp = Pp; k.Ts = Ts; k.Trs = Trs;
     if constexpr (SM == kScalePerChannel) {
         st.s = p.scales[nn];
         st.rs = p.rscale[nn];
@@ -513,6 +629,17 @@ __device__ __forceinline__ void init_lane(LaneState& st, StepConst& k, const Blo
         st.s = 1.0f;
         st.rs = 1.0f;
     }
+    const float* w0row = CAE ? p.W0t + nn * p.ldt + b0 : nullptr;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        st.w[m] = wsrc[16 * m + l];
+        if constexpr (CAE) st.w0[m] = w0row[16 * m + l];
+        if constexpr (kScaled<SM>) {
+            st.w[m] *= st.rs;
+            if constexpr (CAE) st.w0[m] *= st.rs;
+        }
+    }
+    k.Up = Up; k.Pp = Pp; k.Ts = Ts; k.Trs = Trs;
     const float z = (float)(1 << (p.bits - 1));
     k.qmax = (float)((1 << p.bits) - 1);
     k.clo = -z;
@@ -552,15 +679,15 @@ __device__ __forceinline__ void block_epilogue(const LaneState& st, const StepCo
         }
         float eo = 0.f;   // the error the trailing updates use
         if (WHOLE || j < bs) {
-            const float v = st.w[m] * rs;
+            const float v = kScaled<SM> ? st.w[m] : st.w[m] * rs;
             const float c = signed_code(v, k);
             const float r = rdiag[j];
-            const float e = fmaf(-c, s, st.w[m]) * r;
+            const float e = (kScaled<SM> ? (v - c) * s : fmaf(-c, s, st.w[m])) * r;
             loss = fmaf(e, e, loss);
-            eo = CAE ? fmaf(-c, s, st.w0[m]) * r : e;
+            eo = CAE ? (kScaled<SM> ? (st.w0[m] - c) * s : fmaf(-c, s, st.w0[m])) * r : e;
             if (live) {
                 crow[j] = (uint8_t)(uint32_t)(c + z);
-                if (ASYM && !CAE) p.Wpre[n * p.lde + j] = st.w[m];
+                if (ASYM && !CAE) p.Wpre[n * p.lde + j] = kScaled<SM> ? st.w[m] * s : st.w[m];
                 if (p.pre_round) p.pre_round[(b0 + j) * p.N + n] = v;
             }
         } else if (live && ASYM && !CAE) {
@@ -617,7 +744,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
 // v_mfma_f32_16x16x32_bf16 from zero and the sum added to Ws once.  No separate product runs between the blocks;
 // only the rows after the super-block are left to the trailing product that follows the launch.
 constexpr int kSBS = 8 * kB;          // super-block of the strip kernel (its near rows are updated in-kernel)
-constexpr int kWsPitch = kSBS + 16;   // 16-float pad: the four channels an MFMA accumulator row set touches hit disjoint banks
+constexpr int kWsPitch = kSBS + 12;   // the near update's accesses of one instruction (channels 4 g + q, g = 0..3) hit disjoint banks
 constexpr int64_t kStripMaxWG = 512;   // up to two rounds of one workgroup per CU
 
 struct StripArgs {
@@ -679,19 +806,21 @@ __global__ __launch_bounds__(256) void split_diag_kernel(const float* U, int64_t
         *reinterpret_cast<u32x4*>(Usp + (((int64_t)q * (kSBS / 8) + o) * kSBS + r) * 8) = w[q];
 }
 
-// The near update's tile slots of one wave (see the strip kernel): slot I computes tile wave + 4 I from buffer I % 2
-// after issuing the loads of slot I + 1 into buffer (I + 1) % 2.
+// The near update's tile slots of one wave (see the strip kernel): slot I computes tile wave + 4 I from buffer
+// I % kNearBuf after issuing the loads of slot I + kNearBuf - 1 into buffer (I + kNearBuf - 1) % kNearBuf.
+constexpr int kNearBuf = 2;
 template <int I, typename LB, typename UP>
-__device__ __forceinline__ void near_slot(int64_t ntile, int wave, u32x4 (&ub)[2][kB / 32][3], LB& load_b, UP& update) {
+__device__ __forceinline__ void near_slot(int64_t ntile, int wave, u32x4 (&ub)[kNearBuf][kB / 32][3], LB& load_b,
+                                          UP& update) {
     const int64_t t = wave + 4 * I;
     if (t >= ntile) return;
-    if (t + 4 < ntile) load_b(t + 4, ub[(I + 1) % 2]);
-    update(t, ub[I % 2]);
+    if (t + 4 * (kNearBuf - 1) < ntile) load_b(t + 4 * (kNearBuf - 1), ub[(I + kNearBuf - 1) % kNearBuf]);
+    update(t, ub[I % kNearBuf]);
 }
 
 template <typename LB, typename UP, int... Is>
-__device__ __forceinline__ void near_slots(int64_t ntile, int wave, u32x4 (&ub)[2][kB / 32][3], LB& load_b, UP& update,
-                                           std::integer_sequence<int, Is...>) {
+__device__ __forceinline__ void near_slots(int64_t ntile, int wave, u32x4 (&ub)[kNearBuf][kB / 32][3], LB& load_b,
+                                           UP& update, std::integer_sequence<int, Is...>) {
     (near_slot<Is>(ntile, wave, ub, load_b, update), ...);
 }
 
@@ -818,8 +947,10 @@ __global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
             // tiles wave + 4 i, i = 0..kSBS/64-1 (at most (kSBS - kB) / 16 tiles per block, a quarter per wave), in
             // a fully unrolled sequence so that the two operand buffers stay distinct registers: slot i loads the
             // B operands of slot i + 1 and computes slot i
-            u32x4 ub[2][kB / 32][3];
-            if (wave < ntile) load_b(wave, ub[0]);
+            u32x4 ub[kNearBuf][kB / 32][3];
+#pragma unroll
+            for (int i = 0; i < kNearBuf - 1; ++i)
+                if (wave + 4 * i < ntile) load_b(wave + 4 * i, ub[i]);
             near_slots(ntile, wave, ub, load_b, update, std::make_integer_sequence<int, (kSBS - kB) / 64>{});
         }
         if (next) {   // the near update above does not read the LDS panel
