@@ -806,24 +806,6 @@ __global__ __launch_bounds__(256) void split_diag_kernel(const float* U, int64_t
         *reinterpret_cast<u32x4*>(Usp + (((int64_t)q * (kSBS / 8) + o) * kSBS + r) * 8) = w[q];
 }
 
-// The near update's tile slots of one wave (see the strip kernel): slot I computes tile wave + 4 I from buffer
-// I % kNearBuf after issuing the loads of slot I + kNearBuf - 1 into buffer (I + kNearBuf - 1) % kNearBuf.
-constexpr int kNearBuf = 2;
-template <int I, typename LB, typename UP>
-__device__ __forceinline__ void near_slot(int64_t ntile, int wave, u32x4 (&ub)[kNearBuf][kB / 32][3], LB& load_b,
-                                          UP& update) {
-    const int64_t t = wave + 4 * I;
-    if (t >= ntile) return;
-    if (t + 4 * (kNearBuf - 1) < ntile) load_b(t + 4 * (kNearBuf - 1), ub[(I + kNearBuf - 1) % kNearBuf]);
-    update(t, ub[I % kNearBuf]);
-}
-
-template <typename LB, typename UP, int... Is>
-__device__ __forceinline__ void near_slots(int64_t ntile, int wave, u32x4 (&ub)[kNearBuf][kB / 32][3], LB& load_b,
-                                           UP& update, std::integer_sequence<int, Is...>) {
-    (near_slot<Is>(ntile, wave, ub, load_b, update), ...);
-}
-
 template <bool CAE, int SM>
 __global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
     __shared__ __attribute__((aligned(16))) float Ws[kChPerWG * kWsPitch];   // [channel][coordinate - sb0]
@@ -876,15 +858,11 @@ __global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
         LaneState st;
         StepConst k;
         init_lane<CAE, SM>(st, k, pb, &Ws[(tid >> 4) * kWsPitch + (b0 - sb0)], Up, nullptr, Ts, Trs, b0, tid);
-        // the next block's panel: with per-channel scales and no CAE term its loads are issued now and are in flight
-        // during the steps (the other variants have too few registers left and load it after the near update); it is
-        // stored to LDS after the near update either way
-        constexpr bool kEarly = SM == kScalePerChannel && !CAE;
+        // the next block's panel is loaded after the near update (holding it in registers during the steps and the
+        // near update would take the registers of the near update's second operand buffer)
         const int64_t bn = b0 + kB;
         const bool next = bn < sb1;
         const int bsn = next ? (int)min<int64_t>(kB, p.K - bn) : 0;
-        PanelRegs<false> nxt;
-        if (kEarly && next) panel_load<false>(nxt, p.U, nullptr, p.K, bn, bsn, tid);
         if (bs == kB) {
             run_steps<false, CAE, SM, true>(st, k, bs, std::make_integer_sequence<int, kB>{});
             block_epilogue<false, CAE, SM, true>(st, k, pb, rdiag, Ts, Trs, b0, bs, Es);
@@ -941,20 +919,42 @@ __global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
                 }
                 const f32x4 sum = acc[0] + acc[1];
                 float* wc = &Ws[(4 * (lane >> 4)) * kWsPitch + (b1 + 16 * t + (lane & 15) - sb0)];
+                float cur[4];   // the four reads issued together, then the sums written
 #pragma unroll
-                for (int q = 0; q < 4; ++q) wc[q * kWsPitch] += sum[q];
+                for (int q = 0; q < 4; ++q) cur[q] = wc[q * kWsPitch];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) wc[q * kWsPitch] = cur[q] + sum[q];
             };
-            // tiles wave + 4 i, i = 0..kSBS/64-1 (at most (kSBS - kB) / 16 tiles per block, a quarter per wave), in
-            // a fully unrolled sequence so that the two operand buffers stay distinct registers: slot i loads the
-            // B operands of slot i + 1 and computes slot i
-            u32x4 ub[kNearBuf][kB / 32][3];
-#pragma unroll
-            for (int i = 0; i < kNearBuf - 1; ++i)
-                if (wave + 4 * i < ntile) load_b(wave + 4 * i, ub[i]);
-            near_slots(ntile, wave, ub, load_b, update, std::make_integer_sequence<int, (kSBS - kB) / 64>{});
+            // tiles wave, wave + 4, ... (a quarter of the block's at most (kSBS - kB) / 16 tiles per wave) in a loop
+            // of two tiles on two operand buffers: the B operands of the next tile are loaded while a tile is
+            // computed.  That load is issued on every path (past the wave's last tile it repeats tile ntile - 1, which
+            // is in bounds), so the wait before a tile's products is for that tile's loads alone and never for the
+            // ones just issued.
+            if (wave < ntile) {
+                u32x4 ub0[kB / 32][3], ub1[kB / 32][3];
+                int64_t t = wave;
+                load_b(t, ub0);
+                // scheduling barriers keep each prefetch ahead of the products (the scheduler would otherwise sink
+                // the loads to their uses to save registers)
+                for (;;) {
+                    load_b(min<int64_t>(t + 4, ntile - 1), ub1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    update(t, ub0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    t += 4;
+                    if (t >= ntile) break;
+                    load_b(min<int64_t>(t + 4, ntile - 1), ub0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    update(t, ub1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    t += 4;
+                    if (t >= ntile) break;
+                }
+            }
         }
         if (next) {   // the near update above does not read the LDS panel
-            if (!kEarly) panel_load<false>(nxt, p.U, nullptr, p.K, bn, bsn, tid);
+            PanelRegs<false> nxt;
+            panel_load<false>(nxt, p.U, nullptr, p.K, bn, bsn, tid);
             panel_store<false>(nxt, Up, nullptr, rdiag, bsn, tid);
             if constexpr (SM == kScaleStatic) stage_static_scales(Ts, Trs, p, bn, bsn, tid);
         }
