@@ -740,7 +740,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
 // the channels' weights of the super-block stay in LDS (Ws, 16 x kSBS fp32), the blocks run one after the other,
 // and after each block the rows of the super-block still to come get its update W -= E_B U[B, rows] right here,
 // 16 channels x 16 rows per MFMA tile with fp32 accuracy: -E and the U rows each split into three bf16 parts (U's
-// parts prepared once per super-block by split_diag_kernel), the six part products of order <= 2 accumulated by
+// parts prepared once per super-block by strip_prep_kernel), the six part products of order <= 2 accumulated by
 // v_mfma_f32_16x16x32_bf16 from zero and the sum added to Ws once.  No separate product runs between the blocks;
 // only the rows after the super-block are left to the trailing product that follows the launch.
 constexpr int kSBS = 8 * kB;          // super-block of the strip kernel (its near rows are updated in-kernel)
@@ -750,8 +750,25 @@ constexpr int64_t kStripMaxWG = 512;   // up to two rounds of one workgroup per 
 struct StripArgs {
     BlockArgs p;
     int64_t sb0, sb1;      // super-block [sb0, sb1)
-    const uint16_t* Usp;   // the super-block's diagonal block of U in three bf16 parts (split_diag_kernel), per group
+    const uint16_t* Usp;   // the super-block's diagonal block of U in three bf16 parts (strip_prep_kernel), per group
+    const float* Pnl;      // the super-block's block panels as the kernel stages them in LDS (strip_prep_kernel), per group
 };
+
+// A block's panel as the strip kernel holds it in LDS: the scaled U rows in the step layout, then rdiag, then padding
+// to a whole number of 1 KB DMA transfers (65 of them, one per wave instruction).
+constexpr int kPnl = kB * kB + 256;
+static_assert(kPnl % 256 == 0, "whole 1 KB transfers");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// The prepared panel `src` (kPnl floats in HBM) into LDS `dst` by LDS DMA (no registers): wave w issues transfers
+// w, w + 4, ...; transfer i moves floats 256 i .. 256 i + 255, lane l's 16 bytes to dst + 256 i + 4 l.  The caller
+// waits for them (vmcnt) before the barrier after which they are read.
+__device__ __forceinline__ void panel_dma(float* dst, const float* src, int wave, int lane) {
+    for (int i = wave; i < kPnl / 256; i += 4)
+        __builtin_amdgcn_global_load_lds((const void*)(src + 256 * i + 4 * lane), (lds_void_t*)(dst + 256 * i), 16, 0,
+                                         0);
+}
 
 // fp32-accurate products on the bf16 MFMA: v = h0 + h1 + h2 + O(2^-24 |v|), each part the round-to-nearest-even bf16
 // of the remainder; the six part products of order <= 2 summed in fp32 equal the fp32 product to that order.  Two
@@ -782,35 +799,58 @@ __device__ __forceinline__ void split3_oct(const float (&v)[8], u32x4 (&w)[3]) {
     }
 }
 
-// The diagonal block [sb0, sb0 + kSBS)^2 of every group's U, split into three bf16 parts, in the layout of the
-// near update's MFMA B operand: part q, row octet o (rows sb0 + 8 o .. + 7), column sb0 + r as 8 bf16 at
-// Usp[((q * kSBS / 8 + o) * kSBS + r) * 8] (group g at + g 3 kSBS^2).  Zero beyond K.  One thread per (o, r).
-__global__ __launch_bounds__(256) void split_diag_kernel(const float* U, int64_t K, int64_t u_stride, int64_t sb0,
-                                                         uint16_t* Usp) {
+// Per super-block set-up of the strip kernel, for every group's U (blockIdx.y), in one launch:
+// - blocks [0, nsplit): the diagonal block [sb0, sb0 + kSBS)^2 split into three bf16 parts, in the layout of the near
+//   update's MFMA B operand: part q, row octet o (rows sb0 + 8 o .. + 7), column sb0 + r as 8 bf16 at
+//   Usp[((q * kSBS / 8 + o) * kSBS + r) * 8] (group g at + g 3 kSBS^2).  Zero beyond K.  One thread per (o, r).
+// - the next nblk * kPnl / 256 blocks: the panels of the super-block's blocks as the kernel stages them (the panel
+//   staging of the block kernel, same arithmetic): Pnl[bi kPnl + (j 16 + l) 8 + m] = U_jc / U_jj for c = 16 m + l > j
+//   (0 otherwise and beyond the block), rdiag[j] = 1 / U_jj at Pnl[bi kPnl + kB kB + j]; group g at + g 8 kPnl.
+__global__ __launch_bounds__(256) void strip_prep_kernel(const float* U, int64_t K, int64_t u_stride, int64_t sb0,
+                                                         int64_t sb1, int nsplit, uint16_t* Usp, float* Pnl) {
     const int64_t g = blockIdx.y;
     U += g * u_stride;
-    Usp += g * (int64_t)3 * kSBS * kSBS;
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    const int o = idx / kSBS, r = idx % kSBS;
-    const int64_t c = sb0 + r;
-    float v[8];
+    if ((int)blockIdx.x < nsplit) {
+        Usp += g * (int64_t)3 * kSBS * kSBS;
+        const int idx = blockIdx.x * 256 + threadIdx.x;
+        const int o = idx / kSBS, r = idx % kSBS;
+        const int64_t c = sb0 + r;
+        float v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int64_t j = sb0 + 8 * o + i;
-        v[i] = (j < K && c < K) ? U[j * K + c] : 0.f;
+        for (int i = 0; i < 8; ++i) {
+            const int64_t j = sb0 + 8 * o + i;
+            v[i] = (j < K && c < K) ? U[j * K + c] : 0.f;
+        }
+        u32x4 w[3];
+        split3_oct(v, w);
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            *reinterpret_cast<u32x4*>(Usp + (((int64_t)q * (kSBS / 8) + o) * kSBS + r) * 8) = w[q];
+        return;
     }
-    u32x4 w[3];
-    split3_oct(v, w);
-#pragma unroll
-    for (int q = 0; q < 3; ++q)
-        *reinterpret_cast<u32x4*>(Usp + (((int64_t)q * (kSBS / 8) + o) * kSBS + r) * 8) = w[q];
+    const int idx = ((int)blockIdx.x - nsplit) * 256 + threadIdx.x;
+    const int bi = idx / kPnl, e = idx % kPnl;
+    const int64_t b0 = sb0 + (int64_t)bi * kB;
+    if (b0 >= sb1) return;
+    const int bs = (int)min<int64_t>(kB, K - b0);
+    float* out = Pnl + g * (int64_t)(kSBS / kB) * kPnl + (int64_t)bi * kPnl;
+    if (e < kB * kB) {
+        const int j = e >> 7, l = (e >> 3) & 15, m = e & 7, c = 16 * m + l;
+        const float r = j < bs ? __builtin_amdgcn_rcpf(U[(b0 + j) * K + b0 + j]) : 0.f;
+        const float u = (j < bs && c < bs) ? U[(b0 + j) * K + b0 + c] : 0.f;
+        out[e] = c > j ? u * r : 0.f;
+    } else {
+        const int j = e - kB * kB;
+        out[e] = j < bs ? __builtin_amdgcn_rcpf(U[(b0 + j) * K + b0 + j]) : 0.f;
+    }
 }
 
 template <bool CAE, int SM>
 __global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
     __shared__ __attribute__((aligned(16))) float Ws[kChPerWG * kWsPitch];   // [channel][coordinate - sb0]
-    __shared__ __attribute__((aligned(16))) float Up[kB * kB];
-    __shared__ float rdiag[kB];
+    __shared__ __attribute__((aligned(16))) float Upr[kPnl];   // the block's panel (kB x kB), then rdiag
+    float* const Up = Upr;
+    float* const rdiag = Upr + kB * kB;
     __shared__ float Es[kChPerWG * kEsPitch];                                // [channel][j] this block's errors
     __shared__ float Ts[SM == kScaleStatic ? kB * kChPerWG : 1];
     __shared__ float Trs[SM == kScaleStatic ? kB * kChPerWG : 1];
@@ -822,6 +862,7 @@ __global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
         p.U += g * p.u_stride;
         if (p.perm) p.perm += g * p.K;
         a.Usp += g * (int64_t)3 * kSBS * kSBS;
+        a.Pnl += g * (int64_t)(kSBS / kB) * kPnl;
     }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t sb0 = a.sb0, sb1 = a.sb1;
@@ -829,6 +870,7 @@ __global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
     // the super-block's weights of the 16 channels (zero for channels beyond N; Wt is zero-padded up to ldt): every
     // load issued before the LDS stores
     const int64_t width = ((sb1 - sb0) + kB - 1) / kB * kB;
+    panel_dma(Upr, a.Pnl, wave, lane);   // the first block's panel
     {
         constexpr int kWV = kChPerWG * kSBS / 4 / 256;   // 16-byte vectors per thread for a full super-block
         f32x4 wv[kWV];
@@ -846,8 +888,8 @@ __global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
             *reinterpret_cast<f32x4*>(&Ws[ch * kWsPitch + c4]) = wv[i];
         }
     }
-    stage_panel<false>(Up, nullptr, rdiag, p.U, nullptr, p.K, sb0, (int)min<int64_t>(kB, p.K - sb0), tid);
     if constexpr (SM == kScaleStatic) stage_static_scales(Ts, Trs, p, sb0, (int)min<int64_t>(kB, p.K - sb0), tid);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the panel's DMA transfers have landed
     __syncthreads();
 
     for (int64_t b0 = sb0; b0 < sb1; b0 += kB) {
@@ -858,8 +900,6 @@ __global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
         LaneState st;
         StepConst k;
         init_lane<CAE, SM>(st, k, pb, &Ws[(tid >> 4) * kWsPitch + (b0 - sb0)], Up, nullptr, Ts, Trs, b0, tid);
-        // the next block's panel is loaded after the near update (holding it in registers during the steps and the
-        // near update would take the registers of the near update's second operand buffer)
         const int64_t bn = b0 + kB;
         const bool next = bn < sb1;
         const int bsn = next ? (int)min<int64_t>(kB, p.K - bn) : 0;
@@ -952,12 +992,11 @@ __global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
                 }
             }
         }
-        if (next) {   // the near update above does not read the LDS panel
-            PanelRegs<false> nxt;
-            panel_load<false>(nxt, p.U, nullptr, p.K, bn, bsn, tid);
-            panel_store<false>(nxt, Up, nullptr, rdiag, bsn, tid);
-            if constexpr (SM == kScaleStatic) stage_static_scales(Ts, Trs, p, bn, bsn, tid);
-        }
+        // the next block's panel by DMA after the near update (DMA transfers in flight during the near update's
+        // loop make the compiler wait for every outstanding load there, the tile prefetch included)
+        if (next) panel_dma(Upr, a.Pnl + (int64_t)((bn - sb0) / kB) * kPnl, wave, lane);
+        if (next && SM == kScaleStatic) stage_static_scales(Ts, Trs, p, bn, bsn, tid);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next panel's DMA transfers have landed
         __syncthreads();   // Ws updated and the next panel staged before the next block reads them
     }
 }
@@ -1058,6 +1097,7 @@ struct QuantLayout {
     float* Wpre;
     float* W0t;
     uint16_t* Usp;
+    float* Pnl;
     size_t bytes;
 };
 
@@ -1079,6 +1119,7 @@ QuantLayout carve(void* ws, int64_t K, int64_t N, bool asym, bool cae, int64_t g
     L.Wpre = asym && !cae ? c.take<float>((size_t)N * kSB) : nullptr;
     L.W0t = cae ? c.take<float>((size_t)N * ldt) : nullptr;
     L.Usp = strip_path(N, asym) ? c.take<uint16_t>((size_t)std::max<int64_t>(groups, 1) * 3 * kSBS * kSBS) : nullptr;
+    L.Pnl = strip_path(N, asym) ? c.take<float>((size_t)std::max<int64_t>(groups, 1) * (kSBS / kB) * kPnl) : nullptr;
     L.bytes = c.bytes();
     return L;
 }
@@ -1179,13 +1220,15 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
             p.W0t = L.W0t; p.loss_acc = L.loss_acc; p.pre_round = a.pre_round; p.st = L.st;
             p.G = G; p.perm = a.perm; p.gscales = a.scales;
             p.gs = gs; p.u_stride = a.u_stride;
-            sa.sb0 = sb0; sa.sb1 = sb1; sa.Usp = L.Usp;
+            sa.sb0 = sb0; sa.sb1 = sb1; sa.Usp = L.Usp; sa.Pnl = L.Pnl;
             dim3 grid((unsigned)ceil_div(N, kChPerWG));
             {
                 TimerScope ts(stream, GPTQ_TIMER_LOOP);
-                if (sb0 + kB < sb1) {   // near updates happen: split the diagonal block of every group's U
-                    hipLaunchKernelGGL(split_diag_kernel, dim3(kSBS / 8 * kSBS / 256, (unsigned)groups), dim3(256), 0,
-                                       stream, a.U, K, a.u_stride, sb0, L.Usp);
+                {   // every group's block panels, and the split diagonal block when near updates happen
+                    const int nsplit = sb0 + kB < sb1 ? kSBS / 8 * kSBS / 256 : 0;
+                    const int npanel = (int)ceil_div((sb1 - sb0), kB) * kPnl / 256;
+                    hipLaunchKernelGGL(strip_prep_kernel, dim3((unsigned)(nsplit + npanel), (unsigned)groups),
+                                       dim3(256), 0, stream, a.U, K, a.u_stride, sb0, sb1, nsplit, L.Usp, L.Pnl);
                     GPTQ_LAUNCH_CHECK();
                 }
 #define GPTQ_STRIP(C_)                                                                                               \
