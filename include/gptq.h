@@ -288,7 +288,7 @@ gptq_status_t gptq_quantize_layer(const void* W, gptq_dtype_t w_dtype, int64_t K
  *
  *   Arguments, results and errors: as gptq_quantize_layer (same kernels, same outputs), without workspace.
  *   The layer must fit the array: gptq_workspace_bytes(GPTQ_CALL_QUANTIZE_LAYER, K, N, 0, flags | (P1 ? 2 : 0))
- *   <= 67,108,864 (e.g. K = 4096 with up to 2560 channels), else GPTQ_ERR_WORKSPACE and nothing is enqueued; wider
+ *   <= 67,108,864 (e.g. K = 4096 with up to 2448 channels), else GPTQ_ERR_WORKSPACE and nothing is enqueued; wider
  *   layers can be quantised in channel slices (W, codes, scales and the other outputs offset by the slice).
  *   Every call on a GPU uses that GPU's one array, which keeps the previous call's contents (each call clears what
  *   must start at zero): calls that overlap on one GPU (other streams, other threads) race and must be ordered by
