@@ -38,9 +38,12 @@ printed values, explicit-inverse sequential compensation and exhaustive search o
 Schur property, lazy == eager blocks, the per-channel loss identity, invariance under H -> cH, dead
 coordinates, P1 and P2 against per-step least-squares solves (and the CAE loop against an explicit per-step
 solve of the r1 + r2 residual), Gram identities and bf16 rounding against torch.
-Parity unpinned by the pages: the scale rule of channel_scales (s = 2*absmax/(2^b-1)) and the value 1 given
-to dead diagonals are readings the pages leave open; their implementation is pinned only to their own
-stated definition (properties in the tests), not to a value the pages print.
+The scale rule of channel_scales (s = 2*absmax/(2^b-1), zero point 2^(b-1)) is pinned to the symmetric min-max
+grid that [T2] (a quantiser's grid normally comes from min-max, unlike its fixed teaching grid) and [G] (symmetric
+per channel) describe, built from its definition in the tests.
+Parity unpinned by the pages: the value 1 given to dead diagonals (and the MSE clipping candidates) are readings
+the pages leave open; their implementation is pinned only to their own stated definition (properties in the
+tests), not to a value the pages print.
 """
 from __future__ import annotations
 

@@ -8,6 +8,7 @@ import json
 import os
 
 import numpy as np
+from fractions import Fraction
 import pytest
 import torch
 
@@ -201,6 +202,32 @@ def test_channel_scale_rule_properties():
     r = O.quantize_layer(np.array([[-1.0], [0.51], [7.4]]), np.eye(3), bits=4,
                          scales=np.array([1.0], np.float32))
     assert list(r["codes"][:, 0]) == [7, 9, 15]
+
+
+def test_channel_scale_is_the_symmetric_min_max_grid():
+    """[T] T2 contrasts its fixed teaching grid with the grid a quantiser normally gets from the weights by min-max;
+    [G] makes that grid symmetric per channel.  A min-max grid of 2^b codes spans [lo, hi] in 2^b - 1 equal steps with
+    the zero point rint(-lo / step); for the symmetric range lo = -max|w|, hi = max|w|.  Built here from that
+    definition (float64 range and step, codes by nearest rounding) and compared with the oracle's scales and its
+    fixed zero point 2^(b-1) and codes."""
+    rng = np.random.default_rng(21)
+    W = rng.normal(0, 0.02, size=(64, 9)) * np.exp(rng.normal(0, 1, size=9))
+    W = W.astype(np.float32)
+    for b in (2, 3, 4, 5, 6):
+        s = O.channel_scales(W, b)
+        for n in range(W.shape[1]):
+            w = W[:, n].astype(np.float64)
+            m = np.abs(w).max()
+            lo, hi = -m, m                                    # symmetric range of the channel
+            step = (hi - lo) / (2 ** b - 1)                   # 2^b levels from lo to hi
+            zero = round(Fraction(2 ** b - 1, 2))             # rint(-lo / step) = rint((2^b - 1) / 2), exactly
+            assert zero == 2 ** (b - 1)                       # the oracle's fixed zero point, 8 at 4 bits as in T2
+            assert abs(s[n] - step) <= 2 ** -23 * step        # the oracle's scale is that step (fp32-rounded)
+            # the grid covers the whole range: every weight of the channel, its extremes included, is
+            # reconstructed within half a step (no clipping), rounding each weight on its own (U = I)
+            r = O.quantize_layer(w[:, None], np.eye(len(w)), bits=b, scales=s[n:n + 1])
+            rec = s[n] * (r["codes"][:, 0].astype(np.float64) - zero)
+            assert np.all(np.abs(rec - w) <= 0.5 * step * (1 + 1e-6))
 
 
 def test_tie_codes_adopted_only_in_band():
