@@ -18,7 +18,8 @@
 // 16 lanes (one DPP row); lane l holds coordinates 16 m + l, m = 0..7, of the current block in registers,
 // so that the coordinates still free after step j = 16 m + l0 are exactly the slots >= m and the
 // triangular work shrinks with m.  The U panel (and P1 panel) of the block sits in LDS, permuted so that a
-// lane's eight coefficients of row j are two 16-byte reads.  At step j the value w_j is broadcast from its
+// lane's coefficients of row j for its still-free slots are at most two 16-byte reads (the strip kernel copies it
+// there by DMA from a copy prepared once per super-block by strip_prep_kernel; the block kernel stages it itself).  At step j the value w_j is broadcast from its
 // owner lane to the row with DPP row_newbcast; every lane of the row then evaluates the same rounding and
 // error (no further communication), updates its own slots, and the owner keeps the code.
 // Two kernels run these steps: quant_strip_kernel (no asymmetric term, at most 512 workgroups) does a whole
