@@ -18,8 +18,8 @@
 // 16 lanes (one DPP row); lane l holds coordinates 16 m + l, m = 0..7, of the current block in registers,
 // so that the coordinates still free after step j = 16 m + l0 are exactly the slots >= m and the
 // triangular work shrinks with m.  The U panel (and P1 panel) of the block sits in LDS, permuted so that a
-// lane's coefficients of row j for its still-free slots are at most two 16-byte reads (the strip kernel copies it
-// there by DMA from a copy prepared once per super-block by strip_prep_kernel; the block kernel stages it itself).  At step j the value w_j is broadcast from its
+// lane's coefficients of row j for its still-free slots are at most two 16-byte reads; both kernels copy it there by
+// DMA from a copy prepared once per super-block by strip_prep_kernel.  At step j the value w_j is broadcast from its
 // owner lane to the row with DPP row_newbcast; every lane of the row then evaluates the same rounding and
 // error (no further communication), updates its own slots, and the owner keeps the code.
 // Two kernels run these steps: quant_strip_kernel (no asymmetric term, at most 512 workgroups) does a whole
@@ -268,6 +268,8 @@ struct BlockArgs {
     int64_t gs, u_stride;           // output-channel groups: gs channels each, U and P1 of group g at + g u_stride
     const int32_t* perm;            // act-order (static groups look up the original row's group)
     float* gscales;                 // ng x N: written at group starts (re-estimated) or read (static)
+    const float* Pnl;               // the super-block's block panels of U as staged in LDS (strip_prep_kernel), group 0
+    const float* Ppn;               // the same for P1 (asymmetric term)
 };
 
 // Scale modes of the block kernel: one scale per channel; groups re-estimated from the current weights at each
@@ -521,78 +523,6 @@ __device__ __forceinline__ void run_steps(LaneState& st, const StepConst& k, int
     }
 }
 
-// The panel of the block at b0 (bs rows) for one output-channel group's U (and P1): rows b0..b0+bs-1, columns
-// b0..b0+127, staged in LDS as [row j][lane l][slot m] for column 16 m + l.  U is stored as U_jk / U_jj for k > j
-// (zero on and below the diagonal and beyond the block), P1 as it is (strictly upper); rdiag[j] = 1 / U_jj.
-// panel_load issues every global load into registers, panel_store writes LDS, so that other work can run between.
-constexpr int kPanelV = kB * kB / 4 / 256;     // 16-byte vectors per thread
-template <bool ASYM>
-struct PanelRegs {
-    f32x4 uv[kPanelV], pv[ASYM ? kPanelV : 1];
-    float rd[kPanelV];
-};
-
-// VEC (whole blocks, K a multiple of 4): straight-line 16-byte loads, all in flight together; otherwise guarded
-// element loads.
-template <bool ASYM, bool VEC>
-__device__ __forceinline__ void panel_load_v(PanelRegs<ASYM>& R, const float* U, const float* P1, int64_t K,
-                                             int64_t b0, int bs, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPanelV; ++i) {
-        const int idx = tid + 256 * i, j = idx >> 5, c = (idx & 31) * 4;
-        const int64_t off = (b0 + j) * K + b0 + c;
-        if constexpr (VEC) {
-            R.uv[i] = *reinterpret_cast<const f32x4*>(U + off);
-            if constexpr (ASYM) R.pv[i] = *reinterpret_cast<const f32x4*>(P1 + off);
-            R.rd[i] = U[(b0 + j) * K + b0 + j];
-        } else {
-            f32x4 u = {0.f, 0.f, 0.f, 0.f}, q = {0.f, 0.f, 0.f, 0.f};
-            R.rd[i] = 0.f;
-            if (j < bs) {
-                for (int e = 0; e < 4; ++e)
-                    if (c + e < bs) {
-                        u[e] = U[off + e];
-                        if constexpr (ASYM) q[e] = P1[off + e];
-                    }
-                R.rd[i] = U[(b0 + j) * K + b0 + j];
-            }
-            R.uv[i] = u;
-            if constexpr (ASYM) R.pv[i] = q;
-        }
-    }
-}
-
-template <bool ASYM>
-__device__ __forceinline__ void panel_load(PanelRegs<ASYM>& R, const float* U, const float* P1, int64_t K, int64_t b0,
-                                           int bs, int tid) {
-    if (bs == kB && (K % 4) == 0 && (b0 % 4) == 0) panel_load_v<ASYM, true>(R, U, P1, K, b0, bs, tid);
-    else panel_load_v<ASYM, false>(R, U, P1, K, b0, bs, tid);
-}
-
-template <bool ASYM>
-__device__ __forceinline__ void panel_store(const PanelRegs<ASYM>& R, float* Up, float* Pp, float* rdiag, int bs,
-                                            int tid) {
-#pragma unroll
-    for (int i = 0; i < kPanelV; ++i) {
-        const int idx = tid + 256 * i, j = idx >> 5, c = (idx & 31) * 4;
-        const float r = j < bs ? __builtin_amdgcn_rcpf(R.rd[i]) : 0.f;   // 1 / U_jj to 1 ulp
-        if ((idx & 31) == 0) rdiag[j] = r;
-        for (int e = 0; e < 4; ++e) {
-            const int l = (c + e) & 15, m = (c + e) >> 4;
-            Up[(j * 16 + l) * 8 + m] = c + e > j ? R.uv[i][e] * r : 0.f;
-            if constexpr (ASYM) Pp[(j * 16 + l) * 8 + m] = R.pv[i][e];
-        }
-    }
-}
-
-template <bool ASYM>
-__device__ __forceinline__ void stage_panel(float* Up, float* Pp, float* rdiag, const float* U, const float* P1,
-                                            int64_t K, int64_t b0, int bs, int tid) {
-    PanelRegs<ASYM> R;
-    panel_load<ASYM>(R, U, P1, K, b0, bs, tid);
-    panel_store<ASYM>(R, Up, Pp, rdiag, bs, tid);
-}
-
 // Static groups: the scale (and reciprocal) of every step of the block for the workgroup's 16 channels, [step][channel].
 __device__ __forceinline__ void stage_static_scales(float* Ts, float* Trs, const BlockArgs& p, int64_t b0, int bs,
                                                     int tid) {
@@ -705,13 +635,32 @@ __device__ __forceinline__ void block_epilogue(const LaneState& st, const StepCo
     if (l == 0 && live) p.loss_acc[n] += 0.5f * loss;
 }
 
+// A block's panel as the loop kernels hold it in LDS: the scaled U rows in the step layout, then rdiag, then padding
+// to a whole number of 1 KB DMA transfers (65 of them, one per wave instruction); a P1 panel likewise (unscaled, the
+// rdiag part zero).  Prepared once per super-block by strip_prep_kernel.
+constexpr int kPnl = kB * kB + 256;
+static_assert(kPnl % 256 == 0, "whole 1 KB transfers");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// The prepared panel `src` (kPnl floats in HBM) into LDS `dst` by LDS DMA (no registers): wave w issues transfers
+// w, w + 4, ...; transfer i moves floats 256 i .. 256 i + 255, lane l's 16 bytes to dst + 256 i + 4 l.  The caller
+// waits for them (vmcnt) before the barrier after which they are read.
+__device__ __forceinline__ void panel_dma(float* dst, const float* src, int wave, int lane) {
+    for (int i = wave; i < kPnl / 256; i += 4)
+        __builtin_amdgcn_global_load_lds((const void*)(src + 256 * i + 4 * lane), (lds_void_t*)(dst + 256 * i), 16, 0,
+                                         0);
+}
+
 // One block of 128 coordinates per launch (the asymmetric variants).  WHOLE: the block has all 128 coordinates
 // (every block but a ragged last one), so the steps carry no bounds test.
 template <bool ASYM, bool CAE, int SM, bool WHOLE>
 __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
-    __shared__ __attribute__((aligned(16))) float Up[kB * kB];               // [row j][16 lanes][8 slots]
-    __shared__ __attribute__((aligned(16))) float Pp[ASYM ? kB * kB : 4];    // same layout (asymmetric)
-    __shared__ float rdiag[kB];
+    __shared__ __attribute__((aligned(16))) float Upr[kPnl];                 // [row j][16 lanes][8 slots], then rdiag
+    __shared__ __attribute__((aligned(16))) float Ppr[ASYM ? kPnl : 4];      // same layout (asymmetric)
+    float* const Up = Upr;
+    float* const Pp = Ppr;
+    float* const rdiag = Upr + kB * kB;
     __shared__ float Ts[SM == kScaleStatic ? kB * kChPerWG : 1];           // [step][channel] static scales
     __shared__ float Trs[SM == kScaleStatic ? kB * kChPerWG : 1];
 
@@ -721,12 +670,19 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
         p.U += g * p.u_stride;
         if (p.P1) p.P1 += g * p.u_stride;
         if (p.perm) p.perm += g * p.K;
+        p.Pnl += g * (int64_t)(kSB / kB) * kPnl;
+        if (ASYM) p.Ppn += g * (int64_t)(kSB / kB) * kPnl;
     }
     const int tid = threadIdx.x;
     const int64_t b0 = p.b0;
     const int bs = WHOLE ? kB : p.bs;
-    stage_panel<ASYM>(Up, Pp, rdiag, p.U, p.P1, p.K, b0, bs, tid);
+    {   // the block's prepared panels by DMA (super-blocks start at multiples of kSB)
+        const int64_t bi = (b0 % kSB) / kB;
+        panel_dma(Upr, p.Pnl + bi * kPnl, tid >> 6, tid & 63);
+        if constexpr (ASYM) panel_dma(Ppr, p.Ppn + bi * kPnl, tid >> 6, tid & 63);
+    }
     if constexpr (SM == kScaleStatic) stage_static_scales(Ts, Trs, p, b0, bs, tid);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the panels' DMA transfers have landed
     __syncthreads();
 
     const int64_t n = (int64_t)blockIdx.x * kChPerWG + (tid >> 4);
@@ -745,6 +701,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
 // v_mfma_f32_16x16x32_bf16 from zero and the sum added to Ws once.  No separate product runs between the blocks;
 // only the rows after the super-block are left to the trailing product that follows the launch.
 constexpr int kSBS = 8 * kB;          // super-block of the strip kernel (its near rows are updated in-kernel)
+static_assert(kSBS == kSB, "both loop kernels take their panels from one per-super-block preparation");
 constexpr int kWsPitch = kSBS + 12;   // the near update's accesses of one instruction (channels 4 g + q, g = 0..3) hit disjoint banks
 constexpr int64_t kStripMaxWG = 512;   // up to two rounds of one workgroup per CU
 
@@ -752,24 +709,7 @@ struct StripArgs {
     BlockArgs p;
     int64_t sb0, sb1;      // super-block [sb0, sb1)
     const uint16_t* Usp;   // the super-block's diagonal block of U in three bf16 parts (strip_prep_kernel), per group
-    const float* Pnl;      // the super-block's block panels as the kernel stages them in LDS (strip_prep_kernel), per group
 };
-
-// A block's panel as the strip kernel holds it in LDS: the scaled U rows in the step layout, then rdiag, then padding
-// to a whole number of 1 KB DMA transfers (65 of them, one per wave instruction).
-constexpr int kPnl = kB * kB + 256;
-static_assert(kPnl % 256 == 0, "whole 1 KB transfers");
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// The prepared panel `src` (kPnl floats in HBM) into LDS `dst` by LDS DMA (no registers): wave w issues transfers
-// w, w + 4, ...; transfer i moves floats 256 i .. 256 i + 255, lane l's 16 bytes to dst + 256 i + 4 l.  The caller
-// waits for them (vmcnt) before the barrier after which they are read.
-__device__ __forceinline__ void panel_dma(float* dst, const float* src, int wave, int lane) {
-    for (int i = wave; i < kPnl / 256; i += 4)
-        __builtin_amdgcn_global_load_lds((const void*)(src + 256 * i + 4 * lane), (lds_void_t*)(dst + 256 * i), 16, 0,
-                                         0);
-}
 
 // fp32-accurate products on the bf16 MFMA: v = h0 + h1 + h2 + O(2^-24 |v|), each part the round-to-nearest-even bf16
 // of the remainder; the six part products of order <= 2 summed in fp32 equal the fp32 product to that order.  Two
@@ -800,15 +740,17 @@ __device__ __forceinline__ void split3_oct(const float (&v)[8], u32x4 (&w)[3]) {
     }
 }
 
-// Per super-block set-up of the strip kernel, for every group's U (blockIdx.y), in one launch:
+// Per super-block set-up of the loop kernels, for every group's U (blockIdx.y), in one launch:
 // - blocks [0, nsplit): the diagonal block [sb0, sb0 + kSBS)^2 split into three bf16 parts, in the layout of the near
 //   update's MFMA B operand: part q, row octet o (rows sb0 + 8 o .. + 7), column sb0 + r as 8 bf16 at
 //   Usp[((q * kSBS / 8 + o) * kSBS + r) * 8] (group g at + g 3 kSBS^2).  Zero beyond K.  One thread per (o, r).
-// - the next nblk * kPnl / 256 blocks: the panels of the super-block's blocks as the kernel stages them (the panel
-//   staging of the block kernel, same arithmetic): Pnl[bi kPnl + (j 16 + l) 8 + m] = U_jc / U_jj for c = 16 m + l > j
-//   (0 otherwise and beyond the block), rdiag[j] = 1 / U_jj at Pnl[bi kPnl + kB kB + j]; group g at + g 8 kPnl.
-__global__ __launch_bounds__(256) void strip_prep_kernel(const float* U, int64_t K, int64_t u_stride, int64_t sb0,
-                                                         int64_t sb1, int nsplit, uint16_t* Usp, float* Pnl) {
+// - the next npanel = nblk * kPnl / 256 blocks: the panels of the super-block's blocks as the loop kernels hold them
+//   in LDS: Pnl[bi kPnl + (j 16 + l) 8 + m] = U_jc * rcp(U_jj) for c = 16 m + l > j (0 otherwise and beyond the
+//   block), rdiag[j] = rcp(U_jj) at Pnl[bi kPnl + kB kB + j]; group g at + g 8 kPnl.
+// - with P1, the next npanel blocks: its panels in the same layout, P1_jc as it is (strictly upper), at Ppn.
+__global__ __launch_bounds__(256) void strip_prep_kernel(const float* U, const float* P1, int64_t K, int64_t u_stride,
+                                                         int64_t sb0, int64_t sb1, int nsplit, int npanel,
+                                                         uint16_t* Usp, float* Pnl, float* Ppn) {
     const int64_t g = blockIdx.y;
     U += g * u_stride;
     if ((int)blockIdx.x < nsplit) {
@@ -829,12 +771,19 @@ __global__ __launch_bounds__(256) void strip_prep_kernel(const float* U, int64_t
             *reinterpret_cast<u32x4*>(Usp + (((int64_t)q * (kSBS / 8) + o) * kSBS + r) * 8) = w[q];
         return;
     }
-    const int idx = ((int)blockIdx.x - nsplit) * 256 + threadIdx.x;
+    const bool p1 = (int)blockIdx.x >= nsplit + npanel;   // P1 panels: unscaled, no rdiag
+    const int idx = ((int)blockIdx.x - nsplit - (p1 ? npanel : 0)) * 256 + threadIdx.x;
     const int bi = idx / kPnl, e = idx % kPnl;
     const int64_t b0 = sb0 + (int64_t)bi * kB;
     if (b0 >= sb1) return;
     const int bs = (int)min<int64_t>(kB, K - b0);
-    float* out = Pnl + g * (int64_t)(kSBS / kB) * kPnl + (int64_t)bi * kPnl;
+    float* out = (p1 ? Ppn : Pnl) + g * (int64_t)(kSBS / kB) * kPnl + (int64_t)bi * kPnl;
+    if (p1) {
+        P1 += g * u_stride;
+        const int j = e >> 7, l = (e >> 3) & 15, m = e & 7, c = 16 * m + l;
+        out[e] = (e < kB * kB && j < bs && c < bs) ? P1[(b0 + j) * K + b0 + c] : 0.f;
+        return;
+    }
     if (e < kB * kB) {
         const int j = e >> 7, l = (e >> 3) & 15, m = e & 7, c = 16 * m + l;
         const float r = j < bs ? __builtin_amdgcn_rcpf(U[(b0 + j) * K + b0 + j]) : 0.f;
@@ -863,7 +812,7 @@ __global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
         p.U += g * p.u_stride;
         if (p.perm) p.perm += g * p.K;
         a.Usp += g * (int64_t)3 * kSBS * kSBS;
-        a.Pnl += g * (int64_t)(kSBS / kB) * kPnl;
+        p.Pnl += g * (int64_t)(kSBS / kB) * kPnl;
     }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t sb0 = a.sb0, sb1 = a.sb1;
@@ -871,7 +820,7 @@ __global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
     // the super-block's weights of the 16 channels (zero for channels beyond N; Wt is zero-padded up to ldt): every
     // load issued before the LDS stores
     const int64_t width = ((sb1 - sb0) + kB - 1) / kB * kB;
-    panel_dma(Upr, a.Pnl, wave, lane);   // the first block's panel
+    panel_dma(Upr, p.Pnl, wave, lane);   // the first block's panel
     {
         constexpr int kWV = kChPerWG * kSBS / 4 / 256;   // 16-byte vectors per thread for a full super-block
         f32x4 wv[kWV];
@@ -995,7 +944,7 @@ __global__ __launch_bounds__(256) void quant_strip_kernel(StripArgs a) {
         }
         // the next block's panel by DMA after the near update (DMA transfers in flight during the near update's
         // loop make the compiler wait for every outstanding load there, the tile prefetch included)
-        if (next) panel_dma(Upr, a.Pnl + (int64_t)((bn - sb0) / kB) * kPnl, wave, lane);
+        if (next) panel_dma(Upr, p.Pnl + (int64_t)((bn - sb0) / kB) * kPnl, wave, lane);
         if (next && SM == kScaleStatic) stage_static_scales(Ts, Trs, p, bn, bsn, tid);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the next panel's DMA transfers have landed
         __syncthreads();   // Ws updated and the next panel staged before the next block reads them
@@ -1099,6 +1048,7 @@ struct QuantLayout {
     float* W0t;
     uint16_t* Usp;
     float* Pnl;
+    float* Ppn;
     size_t bytes;
 };
 
@@ -1120,7 +1070,8 @@ QuantLayout carve(void* ws, int64_t K, int64_t N, bool asym, bool cae, int64_t g
     L.Wpre = asym && !cae ? c.take<float>((size_t)N * kSB) : nullptr;
     L.W0t = cae ? c.take<float>((size_t)N * ldt) : nullptr;
     L.Usp = strip_path(N, asym) ? c.take<uint16_t>((size_t)std::max<int64_t>(groups, 1) * 3 * kSBS * kSBS) : nullptr;
-    L.Pnl = strip_path(N, asym) ? c.take<float>((size_t)std::max<int64_t>(groups, 1) * (kSBS / kB) * kPnl) : nullptr;
+    L.Pnl = c.take<float>((size_t)std::max<int64_t>(groups, 1) * (kSBS / kB) * kPnl);
+    L.Ppn = asym ? c.take<float>((size_t)std::max<int64_t>(groups, 1) * (kSBS / kB) * kPnl) : nullptr;
     L.bytes = c.bytes();
     return L;
 }
@@ -1221,7 +1172,8 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
             p.W0t = L.W0t; p.loss_acc = L.loss_acc; p.pre_round = a.pre_round; p.st = L.st;
             p.G = G; p.perm = a.perm; p.gscales = a.scales;
             p.gs = gs; p.u_stride = a.u_stride;
-            sa.sb0 = sb0; sa.sb1 = sb1; sa.Usp = L.Usp; sa.Pnl = L.Pnl;
+            p.Pnl = L.Pnl; p.Ppn = nullptr;
+            sa.sb0 = sb0; sa.sb1 = sb1; sa.Usp = L.Usp;
             dim3 grid((unsigned)ceil_div(N, kChPerWG));
             {
                 TimerScope ts(stream, GPTQ_TIMER_LOOP);
@@ -1229,7 +1181,8 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
                     const int nsplit = sb0 + kB < sb1 ? kSBS / 8 * kSBS / 256 : 0;
                     const int npanel = (int)ceil_div((sb1 - sb0), kB) * kPnl / 256;
                     hipLaunchKernelGGL(strip_prep_kernel, dim3((unsigned)(nsplit + npanel), (unsigned)groups),
-                                       dim3(256), 0, stream, a.U, K, a.u_stride, sb0, sb1, nsplit, L.Usp, L.Pnl);
+                                       dim3(256), 0, stream, a.U, nullptr, K, a.u_stride, sb0, sb1, nsplit, npanel,
+                                       L.Usp, L.Pnl, nullptr);
                     GPTQ_LAUNCH_CHECK();
                 }
 #define GPTQ_STRIP(C_)                                                                                               \
@@ -1243,6 +1196,13 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
             if (sb1 < K && !trailing(sb1, K, sb0, sb1 - sb0, L.E, nullptr)) return GPTQ_ERR_HIP;
             continue;
         }
+        {   // every group's block panels of U (and P1) for this super-block
+            TimerScope ts(stream, GPTQ_TIMER_LOOP);
+            const int npanel = (int)ceil_div((sb1 - sb0), kB) * kPnl / 256;
+            hipLaunchKernelGGL(strip_prep_kernel, dim3((unsigned)(npanel * (asym ? 2 : 1)), (unsigned)groups), dim3(256),
+                               0, stream, a.U, a.P1, K, a.u_stride, sb0, sb1, 0, npanel, nullptr, L.Pnl, L.Ppn);
+            GPTQ_LAUNCH_CHECK();
+        }
         for (int64_t b0 = sb0; b0 < sb1; b0 += kB) {
             const int bs = (int)std::min<int64_t>(kB, K - b0);
             float* Eb = L.E + (b0 - sb0);
@@ -1254,6 +1214,7 @@ gptq_status_t quantize_layer(const QuantizeArgs& a, void* workspace, hipStream_t
             p.W0t = L.W0t; p.loss_acc = L.loss_acc; p.pre_round = a.pre_round; p.st = L.st;
             p.G = G; p.perm = a.perm; p.gscales = a.scales;
             p.gs = gs; p.u_stride = a.u_stride;
+            p.Pnl = L.Pnl; p.Ppn = L.Ppn;
             dim3 grid((unsigned)ceil_div(N, kChPerWG));
             {
             TimerScope ts(stream, GPTQ_TIMER_LOOP);
