@@ -322,22 +322,23 @@ __device__ __forceinline__ void load_ops(StepOps& o, const StepConst& k) {
         }
         // step J updates slots m..7 only (m = J / 16): entries below m are not read from LDS
         constexpr int m = J >> 4;
-        const float* urow = k.Up + (J * 16 + k.l) * 8;
+        // row J: entries 0-3 of the 16 lanes, then entries 4-7 (16 consecutive bytes per lane: conflict-free reads)
+        const float* urow = k.Up + J * 128 + k.l * 4;
         if constexpr (m < 4) o.u0 = *reinterpret_cast<const f32x4*>(urow);
         if constexpr (m < 6) {
-            o.u1 = *reinterpret_cast<const f32x4*>(urow + 4);
+            o.u1 = *reinterpret_cast<const f32x4*>(urow + 64);
         } else {
-            const f32x2 t = *reinterpret_cast<const f32x2*>(urow + 6);
+            const f32x2 t = *reinterpret_cast<const f32x2*>(urow + 66);
             o.u1[2] = t[0];
             o.u1[3] = t[1];
         }
         if constexpr (ASYM) {
-            const float* prow = k.Pp + (J * 16 + k.l) * 8;
+            const float* prow = k.Pp + J * 128 + k.l * 4;
             if constexpr (m < 4) o.p0 = *reinterpret_cast<const f32x4*>(prow);
             if constexpr (m < 6) {
-                o.p1 = *reinterpret_cast<const f32x4*>(prow + 4);
+                o.p1 = *reinterpret_cast<const f32x4*>(prow + 64);
             } else {
-                const f32x2 t = *reinterpret_cast<const f32x2*>(prow + 6);
+                const f32x2 t = *reinterpret_cast<const f32x2*>(prow + 66);
                 o.p1[2] = t[0];
                 o.p1[3] = t[1];
             }
@@ -656,7 +657,7 @@ __device__ __forceinline__ void panel_dma(float* dst, const float* src, int wave
 // (every block but a ragged last one), so the steps carry no bounds test.
 template <bool ASYM, bool CAE, int SM, bool WHOLE>
 __global__ __launch_bounds__(256) void quant_block_kernel(BlockArgs p) {
-    __shared__ __attribute__((aligned(16))) float Upr[kPnl];                 // [row j][16 lanes][8 slots], then rdiag
+    __shared__ __attribute__((aligned(16))) float Upr[kPnl];                 // [row j][slots 0-3, 4-7][16 lanes][4], then rdiag
     __shared__ __attribute__((aligned(16))) float Ppr[ASYM ? kPnl : 4];      // same layout (asymmetric)
     float* const Up = Upr;
     float* const Pp = Ppr;
@@ -745,7 +746,7 @@ __device__ __forceinline__ void split3_oct(const float (&v)[8], u32x4 (&w)[3]) {
 //   update's MFMA B operand: part q, row octet o (rows sb0 + 8 o .. + 7), column sb0 + r as 8 bf16 at
 //   Usp[((q * kSBS / 8 + o) * kSBS + r) * 8] (group g at + g 3 kSBS^2).  Zero beyond K.  One thread per (o, r).
 // - the next npanel = nblk * kPnl / 256 blocks: the panels of the super-block's blocks as the loop kernels hold them
-//   in LDS: Pnl[bi kPnl + (j 16 + l) 8 + m] = U_jc * rcp(U_jj) for c = 16 m + l > j (0 otherwise and beyond the
+//   in LDS: Pnl[bi kPnl + 128 j + 64 (m / 4) + 4 l + m % 4] = U_jc * rcp(U_jj) for c = 16 m + l > j (0 otherwise and beyond the
 //   block), rdiag[j] = rcp(U_jj) at Pnl[bi kPnl + kB kB + j]; group g at + g 8 kPnl.
 // - with P1, the next npanel blocks: its panels in the same layout, P1_jc as it is (strictly upper), at Ppn.
 __global__ __launch_bounds__(256) void strip_prep_kernel(const float* U, const float* P1, int64_t K, int64_t u_stride,
@@ -780,12 +781,12 @@ __global__ __launch_bounds__(256) void strip_prep_kernel(const float* U, const f
     float* out = (p1 ? Ppn : Pnl) + g * (int64_t)(kSBS / kB) * kPnl + (int64_t)bi * kPnl;
     if (p1) {
         P1 += g * u_stride;
-        const int j = e >> 7, l = (e >> 3) & 15, m = e & 7, c = 16 * m + l;
+        const int j = e >> 7, l = (e >> 2) & 15, m = ((e >> 6) & 1) * 4 + (e & 3), c = 16 * m + l;
         out[e] = (e < kB * kB && j < bs && c < bs) ? P1[(b0 + j) * K + b0 + c] : 0.f;
         return;
     }
     if (e < kB * kB) {
-        const int j = e >> 7, l = (e >> 3) & 15, m = e & 7, c = 16 * m + l;
+        const int j = e >> 7, l = (e >> 2) & 15, m = ((e >> 6) & 1) * 4 + (e & 3), c = 16 * m + l;
         const float r = j < bs ? __builtin_amdgcn_rcpf(U[(b0 + j) * K + b0 + j]) : 0.f;
         const float u = (j < bs && c < bs) ? U[(b0 + j) * K + b0 + c] : 0.f;
         out[e] = c > j ? u * r : 0.f;
