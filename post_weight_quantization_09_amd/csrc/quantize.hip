@@ -746,8 +746,8 @@ __device__ __forceinline__ void split3_oct(const float (&v)[8], u32x4 (&w)[3]) {
 //   update's MFMA B operand: part q, row octet o (rows sb0 + 8 o .. + 7), column sb0 + r as 8 bf16 at
 //   Usp[((q * kSBS / 8 + o) * kSBS + r) * 8] (group g at + g 3 kSBS^2).  Zero beyond K.  One thread per (o, r).
 // - the next npanel = nblk * kPnl / 256 blocks: the panels of the super-block's blocks as the loop kernels hold them
-//   in LDS: Pnl[bi kPnl + 128 j + 64 (m / 4) + 4 l + m % 4] = U_jc * rcp(U_jj) for c = 16 m + l > j (0 otherwise and beyond the
-//   block), rdiag[j] = rcp(U_jj) at Pnl[bi kPnl + kB kB + j]; group g at + g 8 kPnl.
+//   in LDS: Pnl[bi kPnl + 128 j + 64 (m / 4) + 4 l + m % 4] = U_jc * rcp(U_jj) for c = 16 m + l > j (0 otherwise
+//   and beyond the block), rdiag[j] = rcp(U_jj) at Pnl[bi kPnl + kB kB + j]; group g at + g 8 kPnl.
 // - with P1, the next npanel blocks: its panels in the same layout, P1_jc as it is (strictly upper), at Ppn.
 __global__ __launch_bounds__(256) void strip_prep_kernel(const float* U, const float* P1, int64_t K, int64_t u_stride,
                                                          int64_t sb0, int64_t sb1, int nsplit, int npanel,
